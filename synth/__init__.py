@@ -1,0 +1,320 @@
+"""Seeded synthetic inputs for the Llama decoder-layer forward.
+
+This module holds model shapes, workload shapes and random draws only.  No step
+of the layer's arithmetic lives here: it draws weights, activations, KV-cache
+contexts, context lengths and block tables, and lays a logical KV context out
+in the paged pool format that the library's header documents.  The CPU oracle
+(through the tests) and the HIP path consume exactly the same tensors.
+
+Shapes come from the DeepSeek-R1-Distill-Llama-70B ``config.json`` printed on
+the page "LLama" (hotelren.com/news/2693952, model-parameters block): hidden
+8192, 64 query heads, 8 KV heads, head_dim 128, intermediate 28672,
+rms_norm_eps 1e-5, rope_theta 5e5 with llama3 scaling (factor 8, low 1, high 4,
+original 8192), max_position_embeddings 131072, bf16.
+
+Value distributions: linear weights N(0, 0.02^2) (``initializer_range``),
+RMSNorm weights 1 + N(0, 0.02^2), hidden states, residual stream and cached
+K/V contexts N(0, 1).  Seeds follow ``1000*(workload_index+1) + 97*layer +
+tensor_id`` with one generator per tensor.  Float draws happen on the device
+the tensor will live on (a GPU machine and this CPU therefore see different
+values, which never matters: every comparison runs both sides on the same
+tensors); integer draws (context lengths, block permutations) always happen
+on the CPU so they are the same everywhere.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+# tensor ids used in seeds
+T_W_IN, T_W_QKV, T_W_O, T_W_POST, T_W_GU, T_W_DOWN = 0, 1, 2, 3, 4, 5
+T_HIDDEN, T_RESIDUAL, T_KCTX, T_VCTX, T_CTXLEN, T_BLOCKPERM = 6, 7, 8, 9, 10, 11
+
+KV_BLOCK = 16
+
+
+@dataclasses.dataclass(frozen=True)
+class ModelShape:
+    hidden_size: int
+    num_attention_heads: int
+    num_key_value_heads: int
+    head_dim: int
+    intermediate_size: int
+    rms_norm_eps: float
+    rope_theta: float
+    rope_scaling: Optional[dict]
+    max_position_embeddings: int
+    dtype: str  # "bf16" or "fp32"
+
+    @property
+    def q_size(self) -> int:
+        return self.num_attention_heads * self.head_dim
+
+    @property
+    def kv_size(self) -> int:
+        return self.num_key_value_heads * self.head_dim
+
+    @property
+    def qkv_size(self) -> int:
+        return self.q_size + 2 * self.kv_size
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def config_dict(self) -> dict:
+        """The model's fields under their ``config.json`` names."""
+        d = {
+            "hidden_size": self.hidden_size,
+            "num_attention_heads": self.num_attention_heads,
+            "num_key_value_heads": self.num_key_value_heads,
+            "head_dim": self.head_dim,
+            "intermediate_size": self.intermediate_size,
+            "rms_norm_eps": self.rms_norm_eps,
+            "rope_theta": self.rope_theta,
+            "rope_scaling": dict(self.rope_scaling) if self.rope_scaling else None,
+            "max_position_embeddings": self.max_position_embeddings,
+            "hidden_act": "silu",
+            "attention_bias": False,
+            "mlp_bias": False,
+            "torch_dtype": "bfloat16" if self.dtype == "bf16" else "float32",
+        }
+        return d
+
+
+LLAMA3_SCALING = {
+    "rope_type": "llama3",
+    "factor": 8.0,
+    "low_freq_factor": 1.0,
+    "high_freq_factor": 4.0,
+    "original_max_position_embeddings": 8192,
+}
+
+LLAMA70B = ModelShape(8192, 64, 8, 128, 28672, 1e-5, 500000.0, LLAMA3_SCALING, 131072, "bf16")
+TINY = ModelShape(256, 4, 2, 64, 688, 1e-5, 10000.0, None, 4096, "fp32")
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One batch shape: ``num_seqs`` sequences, each appending ``q_len`` new
+    tokens after a cached context.  ``ctx`` is either a fixed context length
+    or a (lo, hi) inclusive range drawn per sequence."""
+    index: int
+    name: str
+    model: ModelShape
+    num_seqs: int
+    q_len: int
+    ctx: object = 0
+    layers: int = 1
+    residual_none: bool = False
+    spare_blocks: int = 4
+
+    @property
+    def num_tokens(self) -> int:
+        return self.num_seqs * self.q_len
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload(0, "tiny_prefill_32", TINY, 1, 32, 0, 1, True),
+        Workload(1, "llama70b_decode_b32_ctx2048", LLAMA70B, 32, 1, 2048),
+        Workload(2, "llama70b_prefill_4x2048", LLAMA70B, 4, 2048, 0),
+        Workload(3, "llama70b_prefill_1x32768", LLAMA70B, 1, 32768, 0),
+        Workload(4, "llama70b_ragged_decode_b64_4layer", LLAMA70B, 64, 1, (128, 32768), 4),
+    ]
+}
+WORKLOAD_LIST = sorted(WORKLOADS.values(), key=lambda w: w.index)
+
+
+def seed_of(workload_index: int, layer: int, tensor_id: int) -> int:
+    return 1000 * (workload_index + 1) + 97 * layer + tensor_id
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(seed)
+    return g
+
+
+def draw_normal(shape, seed: int, device, dtype: torch.dtype, mean: float = 0.0,
+                std: float = 1.0, chunk: int = 1 << 26) -> torch.Tensor:
+    """N(mean, std^2) drawn in fp32 and rounded (round-to-nearest-even) to
+    ``dtype``; drawn in chunks so no full fp32 copy of a large tensor exists."""
+    g = _gen(seed, device)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        if mean != 0.0:
+            x.add_(mean)
+        flat[s:e] = x.to(dtype)
+    return out
+
+
+def draw_weights(model: ModelShape, workload_index: int, layer: int, device,
+                 linear_std: float = 0.02, norm_mean: float = 1.0,
+                 norm_std: float = 0.02) -> dict:
+    """Packed weights of one layer, each row-major [out, in]: qkv rows
+    [q heads | k heads | v heads], gate_up rows [gate | up]."""
+    dt = model.torch_dtype
+    H, I = model.hidden_size, model.intermediate_size
+    s = lambda tid: seed_of(workload_index, layer, tid)
+    return {
+        "input_layernorm": draw_normal((H,), s(T_W_IN), device, dt, norm_mean, norm_std),
+        "qkv_proj": draw_normal((model.qkv_size, H), s(T_W_QKV), device, dt, 0.0, linear_std),
+        "o_proj": draw_normal((H, model.q_size), s(T_W_O), device, dt, 0.0, linear_std),
+        "post_attention_layernorm": draw_normal((H,), s(T_W_POST), device, dt, norm_mean, norm_std),
+        "gate_up_proj": draw_normal((2 * I, H), s(T_W_GU), device, dt, 0.0, linear_std),
+        "down_proj": draw_normal((H, I), s(T_W_DOWN), device, dt, 0.0, linear_std),
+    }
+
+
+def draw_activations(model: ModelShape, num_tokens: int, workload_index: int, device,
+                     residual: bool = True, layer: int = 0):
+    """hidden and residual-stream inputs [T, H], both N(0, 1)."""
+    dt = model.torch_dtype
+    h = draw_normal((num_tokens, model.hidden_size), seed_of(workload_index, layer, T_HIDDEN), device, dt)
+    r = None
+    if residual:
+        r = draw_normal((num_tokens, model.hidden_size), seed_of(workload_index, layer, T_RESIDUAL), device, dt)
+    return h, r
+
+
+@dataclasses.dataclass
+class Batch:
+    """Per-call metadata of one forward (host-side copies; ``to(device)``
+    gives the device tensors)."""
+    num_seqs: int
+    q_len: int
+    ctx_lens: list
+    seq_lens: torch.Tensor      # int32 [B], KV length after the call
+    positions: torch.Tensor     # int32 [T]
+    block_table: torch.Tensor   # int32 [B, max_blocks_per_seq], -1 past the end
+    num_blocks: int
+    spare_blocks: list          # block ids referenced by no sequence
+
+    @property
+    def num_tokens(self) -> int:
+        return self.num_seqs * self.q_len
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max().item())
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    def slot(self, b: int, pos: int) -> int:
+        return int(self.block_table[b, pos // KV_BLOCK]) * KV_BLOCK + pos % KV_BLOCK
+
+
+def draw_ctx_lens(workload: Workload) -> list:
+    if isinstance(workload.ctx, tuple):
+        lo, hi = workload.ctx
+        g = _gen(seed_of(workload.index, 0, T_CTXLEN), "cpu")
+        return [int(v) for v in torch.randint(lo, hi + 1, (workload.num_seqs,), generator=g)]
+    return [int(workload.ctx)] * workload.num_seqs
+
+
+def build_batch(workload: Workload, ctx_lens: Optional[list] = None) -> Batch:
+    """Context lengths, positions and a block table whose blocks are placed by
+    a seeded random permutation of the pool (plus a few spare blocks that no
+    sequence references)."""
+    B, q = workload.num_seqs, workload.q_len
+    if ctx_lens is None:
+        ctx_lens = draw_ctx_lens(workload)
+    seq_lens = [c + q for c in ctx_lens]
+    nblk = [(s + KV_BLOCK - 1) // KV_BLOCK for s in seq_lens]
+    total = sum(nblk) + workload.spare_blocks
+    g = _gen(seed_of(workload.index, 0, T_BLOCKPERM), "cpu")
+    perm = torch.randperm(total, generator=g).to(torch.int32)
+    maxb = max(nblk)
+    table = torch.full((B, maxb), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        table[b, : nblk[b]] = perm[off: off + nblk[b]]
+        off += nblk[b]
+    spare = [int(x) for x in perm[off:]]
+    positions = torch.cat([torch.arange(c, c + q, dtype=torch.int32) for c in ctx_lens])
+    return Batch(B, q, list(ctx_lens), torch.tensor(seq_lens, dtype=torch.int32), positions,
+                 table, total, spare)
+
+
+def sentinel_fill(t: torch.Tensor) -> torch.Tensor:
+    """All-ones bit pattern: a NaN in both bf16 and fp32."""
+    if t.dtype == torch.bfloat16:
+        t.view(torch.int16).fill_(-1)
+    else:
+        t.view(torch.int32).fill_(-1)
+    return t
+
+
+def pool_shape(model: ModelShape, num_blocks: int):
+    """K and V planes are each [num_blocks][kv_heads][16][head_dim]."""
+    return (num_blocks, model.num_key_value_heads, KV_BLOCK, model.head_dim)
+
+
+def scatter_context(pool: torch.Tensor, batch: Batch, b: int, ctx: torch.Tensor) -> None:
+    """Lay a logical context ``ctx`` [L, kv_heads, d] of sequence ``b`` into
+    the paged pool at positions 0..L-1."""
+    L = ctx.shape[0]
+    for j in range(0, (L + KV_BLOCK - 1) // KV_BLOCK):
+        blk = int(batch.block_table[b, j])
+        n = min(KV_BLOCK, L - j * KV_BLOCK)
+        pool[blk, :, :n, :] = ctx[j * KV_BLOCK: j * KV_BLOCK + n].transpose(0, 1)
+
+
+def gather_context(pool: torch.Tensor, batch: Batch, b: int, length: int) -> torch.Tensor:
+    """Read positions 0..length-1 of sequence ``b`` out of the paged pool as a
+    logical [length, kv_heads, d] tensor."""
+    nb = (length + KV_BLOCK - 1) // KV_BLOCK
+    if nb == 0:
+        return pool.new_empty((0, pool.shape[1], pool.shape[3]))
+    ids = batch.block_table[b, :nb].long().to(pool.device)
+    blocks = pool.index_select(0, ids)                     # [nb, kv, 16, d]
+    flat = blocks.permute(0, 2, 1, 3).reshape(nb * KV_BLOCK, pool.shape[1], pool.shape[3])
+    return flat[:length]
+
+
+def build_kv_pool(workload: Workload, batch: Batch, layer: int, device):
+    """K and V pools for one layer: every slot sentinel-filled (NaN bits),
+    then each sequence's cached context (positions 0..ctx-1) drawn N(0,1).
+    Cached K counts as already rotated."""
+    model = workload.model
+    shape = pool_shape(model, batch.num_blocks)
+    kp = sentinel_fill(torch.empty(shape, dtype=model.torch_dtype, device=device))
+    vp = sentinel_fill(torch.empty(shape, dtype=model.torch_dtype, device=device))
+    gk = _gen(seed_of(workload.index, layer, T_KCTX), device)
+    gv = _gen(seed_of(workload.index, layer, T_VCTX), device)
+    nkv, d = model.num_key_value_heads, model.head_dim
+    for b, c in enumerate(batch.ctx_lens):
+        if c == 0:
+            continue
+        for gen, pool in ((gk, kp), (gv, vp)):
+            x = torch.randn((c, nkv, d), generator=gen, device=device, dtype=torch.float32)
+            scatter_context(pool, batch, b, x.to(model.torch_dtype))
+    return kp, vp
+
+
+def workload_tensors(workload: Workload, device, layers: Optional[int] = None):
+    """Everything one forward (or a stack of ``layers`` forwards) consumes."""
+    layers = workload.layers if layers is None else layers
+    batch = build_batch(workload)
+    h, r = draw_activations(workload.model, batch.num_tokens, workload.index, device,
+                            residual=not workload.residual_none)
+    per_layer = []
+    for l in range(layers):
+        w = draw_weights(workload.model, workload.index, l, device)
+        kp, vp = build_kv_pool(workload, batch, l, device)
+        per_layer.append({"weights": w, "k_pool": kp, "v_pool": vp})
+    return batch, h, r, per_layer
+
