@@ -1,0 +1,221 @@
+"""Throughput of the Llama-70B-shape decoder-layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one forward of the whole layer (input_layernorm, qkv_proj, RoPE +
+KV write, paged attention, o_proj + residual, post_attention_layernorm,
+gate_up_proj + SiluAndMul, down_proj) over one batch of seeded synthetic
+inputs that are resident in HBM before timing starts.  Default workload: 32
+sequences decoding one token each after a 2048-token cached context (70B
+layer shapes, bf16).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+METRIC = "70B-shape layer tokens/s (prefill, decode) + % MFMA/HBM peak, 1 MI355X"
+
+
+def layer_flops(model, num_tokens, attn_pairs):
+    H, I, Q = model.hidden_size, model.intermediate_size, model.q_size
+    proj = 2 * num_tokens * H * (model.qkv_size + Q + 2 * I) + 2 * num_tokens * I * H
+    return proj + 4 * model.num_attention_heads * model.head_dim * attn_pairs
+
+
+def kernel_bytes(model, name, T, kv_tokens):
+    """Algorithmic HBM bytes of one launch of kernel `name` (bf16): weights
+    read once, activations in and out once, KV read once."""
+    H, I, Q, QKV = model.hidden_size, model.intermediate_size, model.q_size, model.qkv_size
+    e = 2
+    return {
+        "gate_up_silu": 2 * I * H * e + T * H * e + T * I * e,
+        "down_proj": H * I * e + T * I * e + T * H * e,
+        "qkv_proj": QKV * H * e + T * H * e + T * QKV * e,
+        "o_proj_residual": H * Q * e + T * Q * e + 2 * T * H * e,
+        "attention": kv_tokens * 2 * model.kv_size * e + T * Q * e,
+    }.get(name)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama70b_decode_b32_ctx2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange inside the layer)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import llama_decoder_layer_amd as lda
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    model = wl.model
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    batch, hidden, residual, per_layer = synth.workload_tensors(wl, dev)
+    pos, bt, sl = batch.positions.to(dev), batch.block_table.to(dev), batch.seq_lens.to(dev)
+    layers = [lda.Layer(model.config_dict(), p["weights"]) for p in per_layer]
+    T, B = batch.num_tokens, batch.num_seqs
+    ws = layers[0].alloc_workspace(T, B, batch.max_seq_len)
+    bufs = [(torch.empty_like(hidden), torch.empty_like(hidden)) for _ in layers]
+    torch.cuda.synchronize()
+
+    def step():
+        h, r = hidden, residual
+        for L, p, (ho, ro) in zip(layers, per_layer, bufs):
+            L.forward(h, r, pos, p["k_pool"], p["v_pool"], bt, sl, batch.max_seq_len, hidden_out=ho,
+                      residual_out=ro, workspace=ws)
+            h, r = ho, ro
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel durations: HIP events the library records on its stream
+    for L in layers:
+        L.set_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = {}
+    for L in layers:
+        for name, (tot, cnt) in L.timing_read().items():
+            a, c = kt.get(name, (0.0, 0))
+            kt[name] = (a + tot, c + cnt)
+        L.set_timing(False)
+    kernel_avg_ms = {k: v[0] / v[1] for k, v in kt.items()}
+
+    decode = wl.q_len == 1
+    kv_tokens = int(batch.seq_lens.sum())  # keys read by one layer's attention (decode)
+    attn_pairs = sum(sum(c + j + 1 for j in range(wl.q_len)) for c in batch.ctx_lens)
+    tokens_per_step = T
+    value = tokens_per_step / (ms / 1e3)
+
+    if decode:
+        dom = "gate_up_silu"
+        alg = kernel_bytes(model, dom, T, kv_tokens)
+        dur = kernel_avg_ms[dom] / 1e3
+        roof = {"bound": "hbm", "kernel": dom, "achieved": alg / dur / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": alg / dur / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                "algorithmic_bytes": alg, "avg_launch_us": dur * 1e6}
+    else:
+        dom = "gate_up_silu"
+        H, I = model.hidden_size, model.intermediate_size
+        alg = 2 * T * H * 2 * I
+        dur = kernel_avg_ms[dom] / 1e3
+        roof = {"bound": "mfma", "kernel": dom, "achieved": alg / dur / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": alg / dur / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                "algorithmic_flops": alg, "avg_launch_us": dur * 1e6}
+
+    # whole-layer fractions of the roofline
+    step_bytes = len(layers) * (sum(v.numel() * v.element_size() for v in per_layer[0]["weights"].values())
+                                + kv_tokens * 2 * model.kv_size * 2 + 4 * T * model.hidden_size * 2)
+    step_flops = len(layers) * layer_flops(model, T, attn_pairs)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, batch, hidden, residual, per_layer, args.cpu_sample_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if model.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations and KV context, N(0,0.02) weights)",
+        "config": {"workload": wl.name, "num_seqs": B, "q_len": wl.q_len,
+                   "ctx_len": wl.ctx if not isinstance(wl.ctx, tuple) else list(wl.ctx),
+                   "layers": len(layers), "parallelism": "single GPU"},
+        "roofline": roof,
+        "step_fraction": {"hbm": step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                          "mfma": step_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS},
+        "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in sorted(kernel_avg_ms.items())},
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(wl, batch, hidden, residual, per_layer, rows):
+    """The oracle (float64 numpy) on a bounded sample of the same step: the
+    first `rows` tokens of the batch through every layer."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
+    model = wl.model
+    rows = min(rows, batch.num_tokens)
+    if wl.q_len != 1:
+        rows_list = list(range(rows))          # the first tokens of sequence 0
+        seq_ids = [0]
+    else:
+        rows_list = list(range(rows))
+        seq_ids = list(range(rows))
+    cfg = model.config_dict()
+    pos = batch.positions.numpy().astype(np.int64)
+    h = f64(hidden)
+    r = None if residual is None else f64(residual)
+    t0 = time.perf_counter()
+    for p in per_layer:
+        w = {k: f64(v) for k, v in p["weights"].items()}
+        seqs = []
+        for b in seq_ids:
+            c = batch.ctx_lens[b]
+            seqs.append(oracle.Seq(list(range(b * wl.q_len, (b + 1) * wl.q_len)),
+                                   f64(synth.gather_context(p["k_pool"], batch, b, c)),
+                                   f64(synth.gather_context(p["v_pool"], batch, b, c))))
+        o = oracle.decoder_layer(cfg, w, h, r, pos, seqs, want=rows_list)
+        h = h.copy()
+        r = np.zeros_like(h) if r is None else r.copy()
+        h[rows_list] = o["hidden_out"]
+        r[rows_list] = o["residual_out"]
+    dt = time.perf_counter() - t0
+    return {"value": round(rows / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d tokens through %d layer(s), float64 numpy oracle incl. weight widening"
+                      % (rows, batch.num_tokens, len(per_layer)),
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

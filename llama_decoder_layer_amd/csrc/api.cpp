@@ -1,0 +1,497 @@
+// Host side of the C ABI: configuration checks, weight ownership, the RoPE
+// table, workspace carving and the launch sequence of one layer forward.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/llama_layer.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+llama_status fail(llama_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+llama_status hip_fail(hipError_t e, const char* what) {
+  return fail(LLAMA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                      \
+  do {                                           \
+    hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+size_t elem_size(int dtype) { return dtype == LLAMA_DTYPE_BF16 ? 2 : 4; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool is_llama3(const llama_layer_config* c) {
+  return c->rope_type != nullptr && std::strcmp(c->rope_type, "llama3") == 0;
+}
+
+// Angular frequency of RoPE pair i: theta^(-2i/d), then for rope_type llama3
+// the published Llama 3 rescaling by wavelength 2*pi/w: below
+// orig/high_freq_factor unchanged, above orig/low_freq_factor divided by
+// factor, and in between blended (1-s) w/factor + s w with
+// s = (orig/wavelength - low) / (high - low).
+double rope_freq(const llama_layer_config* c, int i) {
+  const double w = std::pow(c->rope_theta, -2.0 * i / c->head_dim);
+  if (!is_llama3(c)) return w;
+  const double orig = c->original_max_position_embeddings;
+  const double lo = c->low_freq_factor, hi = c->high_freq_factor, f = c->rope_factor;
+  const double wavelen = 2.0 * M_PI / w;
+  if (wavelen < orig / hi) return w;
+  if (wavelen > orig / lo) return w / f;
+  const double s = (orig / wavelen - lo) / (hi - lo);
+  return (1.0 - s) * w / f + s * w;
+}
+
+struct TimingMark {
+  const char* name;  // kernel that ran between the previous mark and this one
+  hipEvent_t ev;
+};
+
+}  // namespace
+
+struct llama_layer {
+  llama_layer_config cfg;
+  std::string act, rope_type;
+  int dtype = 0;
+  size_t es = 2;
+  int qkv_n = 0;
+  void* w_in = nullptr;
+  void* w_qkv = nullptr;
+  void* w_o = nullptr;
+  void* w_post = nullptr;
+  void* w_gu = nullptr;
+  void* w_down = nullptr;
+  float2* rope = nullptr;
+
+  bool timing = false;
+  std::vector<std::vector<TimingMark>> marks;  // one list per forward
+  std::vector<hipEvent_t> event_pool;
+  std::map<std::string, std::pair<double, int64_t>> totals;
+};
+
+namespace {
+
+struct Workspace {
+  size_t h, qkv, attn, h2, act, part, total;
+  llk::AttnPlan plan;
+};
+
+Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
+  const llama_layer_config& c = L->cfg;
+  Workspace w{};
+  const int q_len = (B > 0 && T % B == 0) ? T / B : 1;
+  w.plan = llk::attention_plan(T, c.num_attention_heads, c.head_dim, q_len, max_seq_len);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  w.h = take((size_t)T * c.hidden_size * L->es);
+  w.qkv = take((size_t)T * L->qkv_n * L->es);
+  w.attn = take((size_t)T * c.num_attention_heads * c.head_dim * L->es);
+  w.h2 = take((size_t)T * c.hidden_size * L->es);
+  w.act = take((size_t)T * c.intermediate_size * L->es);
+  w.part = take(w.plan.ws_bytes);
+  w.total = off;
+  return w;
+}
+
+hipEvent_t pool_event(llama_layer* L) {
+  if (!L->event_pool.empty()) {
+    hipEvent_t e = L->event_pool.back();
+    L->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records an event after the kernel `name` (or the opening mark when name is
+// NULL) while timing is on.
+struct Marker {
+  llama_layer* L;
+  hipStream_t s;
+  std::vector<TimingMark>* list = nullptr;
+  Marker(llama_layer* L_, hipStream_t s_) : L(L_), s(s_) {
+    if (L->timing) {
+      L->marks.emplace_back();
+      list = &L->marks.back();
+      mark(nullptr);
+    }
+  }
+  void mark(const char* name) {
+    if (!list) return;
+    hipEvent_t e = pool_event(L);
+    if (e && hipEventRecord(e, s) == hipSuccess) list->push_back({name, e});
+  }
+  hipEvent_t extra() {  // an event recorded inside a launcher (between two kernels)
+    return list ? pool_event(L) : nullptr;
+  }
+};
+
+void free_layer(llama_layer* L) {
+  if (!L) return;
+  void* bufs[] = {L->w_in, L->w_qkv, L->w_o, L->w_post, L->w_gu, L->w_down, (void*)L->rope};
+  for (void* p : bufs)
+    if (p) (void)hipFree(p);
+  for (auto& list : L->marks)
+    for (auto& m : list) (void)hipEventDestroy(m.ev);
+  for (hipEvent_t e : L->event_pool) (void)hipEventDestroy(e);
+  delete L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* llama_layer_last_error(void) { return g_err.c_str(); }
+
+llama_status llama_layer_config_validate(const llama_layer_config* c) {
+  if (!c) return fail(LLAMA_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (c->hidden_size <= 0 || c->num_attention_heads <= 0 || c->num_key_value_heads <= 0 ||
+      c->head_dim <= 0 || c->intermediate_size <= 0 || c->max_position_embeddings <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "all sizes must be positive");
+  if (!(c->rms_norm_eps > 0.f)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "rms_norm_eps must be > 0");
+  if (!(c->rope_theta > 1.0)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "rope_theta must be > 1");
+  if (c->dtype != LLAMA_DTYPE_BF16 && c->dtype != LLAMA_DTYPE_FP32)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "unknown dtype %d", c->dtype);
+  if (c->num_attention_heads % c->num_key_value_heads != 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_attention_heads %% num_key_value_heads != 0");
+  if (!c->hidden_act || std::strcmp(c->hidden_act, "silu") != 0)
+    return fail(LLAMA_ERR_UNSUPPORTED, "Unsupported activation: %s. Only silu is supported",
+                c->hidden_act ? c->hidden_act : "(null)");
+  if (c->attention_bias || c->mlp_bias)
+    return fail(LLAMA_ERR_UNSUPPORTED, "attention_bias / mlp_bias are not supported");
+  if (c->rope_type && std::strcmp(c->rope_type, "default") != 0 && std::strcmp(c->rope_type, "llama3") != 0)
+    return fail(LLAMA_ERR_UNSUPPORTED, "rope_type %s is not supported", c->rope_type);
+  if (is_llama3(c)) {
+    if (!(c->rope_factor >= 1.0) || !(c->low_freq_factor > 0.0) ||
+        !(c->high_freq_factor > c->low_freq_factor) || c->original_max_position_embeddings <= 0)
+      return fail(LLAMA_ERR_INVALID_ARGUMENT,
+                  "llama3 rope needs factor >= 1, high_freq_factor > low_freq_factor > 0, "
+                  "original_max_position_embeddings > 0");
+  }
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(LLAMA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
+  if (c->kv_block_size != 16)
+    return fail(LLAMA_ERR_UNSUPPORTED, "kv_block_size %d (supported: 16)", c->kv_block_size);
+  if (c->num_attention_heads / c->num_key_value_heads > 16)
+    return fail(LLAMA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  const int qkv_n = (c->num_attention_heads + 2 * c->num_key_value_heads) * c->head_dim;
+  if (c->dtype == LLAMA_DTYPE_BF16) {
+    if (c->hidden_size % 128 || c->intermediate_size % 128 || c->hidden_size > 16384 || qkv_n % 128 ||
+        (c->num_attention_heads * c->head_dim) % 64)
+      return fail(LLAMA_ERR_UNSUPPORTED,
+                  "bf16 needs hidden_size, intermediate_size and the qkv width to be multiples "
+                  "of 128 and hidden_size <= 16384");
+  } else {
+    if (c->hidden_size % 4 || c->hidden_size > 8192)
+      return fail(LLAMA_ERR_UNSUPPORTED, "fp32 needs hidden_size %% 4 == 0 and <= 8192");
+  }
+  return LLAMA_OK;
+}
+
+llama_status llama_layer_create(const llama_layer_config* config, const llama_layer_weights* w,
+                                void* stream, llama_layer** out) {
+  llama_status st = llama_layer_config_validate(config);
+  if (st != LLAMA_OK) return st;
+  if (!w || !out || !w->input_layernorm || !w->qkv_proj || !w->o_proj || !w->post_attention_layernorm ||
+      !w->gate_up_proj || !w->down_proj)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL weight or output pointer");
+  *out = nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  llama_layer* L = new llama_layer();
+  L->cfg = *config;
+  L->act = config->hidden_act;
+  L->rope_type = config->rope_type ? config->rope_type : "default";
+  L->cfg.hidden_act = L->act.c_str();
+  L->cfg.rope_type = L->rope_type.c_str();
+  L->dtype = config->dtype;
+  L->es = elem_size(config->dtype);
+  const llama_layer_config& c = L->cfg;
+  const size_t H = c.hidden_size, I = c.intermediate_size, Q = (size_t)c.num_attention_heads * c.head_dim;
+  L->qkv_n = (c.num_attention_heads + 2 * c.num_key_value_heads) * c.head_dim;
+
+  struct Item {
+    void** dst;
+    const void* src;
+    size_t bytes;
+  } items[] = {
+      {&L->w_in, w->input_layernorm, H * L->es},
+      {&L->w_qkv, w->qkv_proj, (size_t)L->qkv_n * H * L->es},
+      {&L->w_o, w->o_proj, H * Q * L->es},
+      {&L->w_post, w->post_attention_layernorm, H * L->es},
+      {&L->w_gu, nullptr, 2 * I * H * L->es},
+      {&L->w_down, w->down_proj, H * I * L->es},
+  };
+  for (auto& it : items) {
+    if (hipMalloc(it.dst, it.bytes) != hipSuccess) {
+      free_layer(L);
+      return fail(LLAMA_ERR_OUT_OF_MEMORY, "hipMalloc of %zu bytes for weights failed", it.bytes);
+    }
+    if (it.src) {
+      hipError_t e = hipMemcpyAsync(*it.dst, it.src, it.bytes, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) {
+        free_layer(L);
+        return hip_fail(e, "weight copy");
+      }
+    }
+  }
+  hipError_t e;
+  if (L->dtype == LLAMA_DTYPE_BF16) {
+    e = llk::launch_reorder_gate_up(w->gate_up_proj, (int)I, (int)H, L->w_gu, s);
+  } else {
+    e = hipMemcpyAsync(L->w_gu, w->gate_up_proj, 2 * I * H * L->es, hipMemcpyDeviceToDevice, s);
+  }
+  if (e != hipSuccess) {
+    free_layer(L);
+    return hip_fail(e, "gate_up copy");
+  }
+
+  // RoPE table: angles and cos/sin in double precision, stored as float
+  const int half = c.head_dim / 2;
+  const size_t n = (size_t)c.max_position_embeddings * half;
+  std::vector<double> freq(half);
+  for (int i = 0; i < half; ++i) freq[i] = rope_freq(&c, i);
+  std::vector<float2> table(n);
+  for (size_t p = 0; p < (size_t)c.max_position_embeddings; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double a = (double)p * freq[i];
+      table[p * half + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+    }
+  if (hipMalloc((void**)&L->rope, n * sizeof(float2)) != hipSuccess) {
+    free_layer(L);
+    return fail(LLAMA_ERR_OUT_OF_MEMORY, "hipMalloc of the RoPE table failed");
+  }
+  e = hipMemcpyAsync(L->rope, table.data(), n * sizeof(float2), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // `table` is freed on return
+  if (e != hipSuccess) {
+    free_layer(L);
+    return hip_fail(e, "RoPE table upload");
+  }
+  *out = L;
+  return LLAMA_OK;
+}
+
+size_t llama_layer_workspace_bytes(const llama_layer* L, int32_t num_tokens, int32_t num_seqs,
+                                   int32_t max_seq_len) {
+  if (!L || num_tokens <= 0 || num_seqs <= 0 || max_seq_len <= 0) return 0;
+  return carve(L, num_tokens, num_seqs, max_seq_len).total;
+}
+
+llama_status llama_layer_workspace_tensor(const llama_layer* L, int32_t T, int32_t B, int32_t max_seq_len,
+                                          const char* name, size_t* offset, size_t* bytes) {
+  if (!L || !name || !offset || !bytes || T <= 0 || B <= 0 || max_seq_len <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "bad arguments");
+  Workspace w = carve(L, T, B, max_seq_len);
+  const llama_layer_config& c = L->cfg;
+  struct {
+    const char* n;
+    size_t off, sz;
+  } t[] = {
+      {"h", w.h, (size_t)T * c.hidden_size * L->es},
+      {"qkv", w.qkv, (size_t)T * L->qkv_n * L->es},
+      {"attn", w.attn, (size_t)T * c.num_attention_heads * c.head_dim * L->es},
+      {"h2", w.h2, (size_t)T * c.hidden_size * L->es},
+      {"act", w.act, (size_t)T * c.intermediate_size * L->es},
+  };
+  for (auto& x : t)
+    if (std::strcmp(x.n, name) == 0) {
+      *offset = x.off;
+      *bytes = x.sz;
+      return LLAMA_OK;
+    }
+  return fail(LLAMA_ERR_INVALID_ARGUMENT, "unknown workspace tensor %s", name);
+}
+
+llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void* residual,
+                                 const int32_t* positions, int32_t T, const llama_kv_cache* kv,
+                                 const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                 const int32_t* query_start_loc, int32_t B, int32_t max_seq_len,
+                                 void* hidden_out, void* residual_out, void* workspace, void* stream) {
+  if (!L) return fail(LLAMA_ERR_INVALID_ARGUMENT, "layer is NULL");
+  if (!hidden || !positions || !kv || !kv->k || !kv->v || !block_table || !seq_lens || !hidden_out ||
+      !residual_out || !workspace)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (query_start_loc) return fail(LLAMA_ERR_UNSUPPORTED, "query_start_loc must be NULL");
+  if (T <= 0 || B <= 0 || T % B != 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_tokens %d must be a positive multiple of num_seqs %d", T, B);
+  const int q_len = T / B;
+  const llama_layer_config& c = L->cfg;
+  if (max_seq_len < q_len || max_seq_len > c.max_position_embeddings)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [%d, %d]", max_seq_len, q_len,
+                c.max_position_embeddings);
+  if (max_blocks <= 0 || (int64_t)max_blocks * 16 < max_seq_len)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq %d cannot hold max_seq_len %d", max_blocks,
+                max_seq_len);
+  if (kv->num_blocks <= 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "kv_cache.num_blocks must be positive");
+  if (hidden_out == residual_out) return fail(LLAMA_ERR_INVALID_ARGUMENT, "hidden_out aliases residual_out");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (!aligned16(hidden) || (residual && !aligned16(residual)) || !aligned16(hidden_out) ||
+      !aligned16(residual_out) || !aligned16(kv->k) || !aligned16(kv->v))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "activation and cache pointers must be 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  const Workspace w = carve(L, T, B, max_seq_len);
+  char* ws = (char*)workspace;
+  void* h = ws + w.h;
+  void* qkv = ws + w.qkv;
+  void* attn = ws + w.attn;
+  void* h2 = ws + w.h2;
+  void* act = ws + w.act;
+  float* part = (float*)(ws + w.part);
+  const int H = c.hidden_size, I = c.intermediate_size, nq = c.num_attention_heads,
+            nkv = c.num_key_value_heads, d = c.head_dim;
+  const int dt = L->dtype;
+
+  Marker mk(L, s);
+  hipError_t e;
+  e = llk::launch_add_rmsnorm(dt, hidden, residual, L->w_in, c.rms_norm_eps, T, H, h, residual_out, s);
+  if (e != hipSuccess) return hip_fail(e, "input_layernorm");
+  mk.mark("input_layernorm");
+  e = llk::launch_linear(dt, h, L->w_qkv, T, L->qkv_n, H, llk::kEpiStore, qkv, s);
+  if (e != hipSuccess) return hip_fail(e, "qkv_proj");
+  mk.mark("qkv_proj");
+  e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, q_len, kv->k,
+                          kv->v, s);
+  if (e != hipSuccess) return hip_fail(e, "rope_kv_write");
+  mk.mark("rope_kv_write");
+  hipEvent_t mid = w.plan.parts > 1 ? mk.extra() : nullptr;
+  e = llk::launch_attention(dt, qkv, L->qkv_n, T, positions, nq, nkv, d, kv->k, kv->v, block_table, max_blocks,
+                            q_len, w.plan, part, attn, s, mid);
+  if (e != hipSuccess) return hip_fail(e, "attention");
+  if (mid) mk.list->push_back({"attention", mid});
+  mk.mark(w.plan.parts > 1 ? "attention_combine" : "attention");
+  e = llk::launch_linear(dt, attn, L->w_o, T, H, nq * d, llk::kEpiAdd, residual_out, s);
+  if (e != hipSuccess) return hip_fail(e, "o_proj");
+  mk.mark("o_proj_residual");
+  e = llk::launch_add_rmsnorm(dt, residual_out, nullptr, L->w_post, c.rms_norm_eps, T, H, h2, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "post_attention_layernorm");
+  mk.mark("post_attention_layernorm");
+  e = llk::launch_linear(dt, h2, L->w_gu, T, I, H, llk::kEpiSiluMul, act, s);
+  if (e != hipSuccess) return hip_fail(e, "gate_up_proj");
+  mk.mark("gate_up_silu");
+  e = llk::launch_linear(dt, act, L->w_down, T, H, I, llk::kEpiStore, hidden_out, s);
+  if (e != hipSuccess) return hip_fail(e, "down_proj");
+  mk.mark("down_proj");
+  return LLAMA_OK;
+}
+
+void llama_layer_destroy(llama_layer* L) {
+  if (!L) return;
+  (void)hipDeviceSynchronize();
+  free_layer(L);
+}
+
+llama_status llama_layer_set_timing(llama_layer* L, int32_t enable) {
+  if (!L) return fail(LLAMA_ERR_INVALID_ARGUMENT, "layer is NULL");
+  L->timing = enable != 0;
+  return LLAMA_OK;
+}
+
+int32_t llama_layer_timing_read(llama_layer* L, const char** names, double* total_ms, int64_t* counts,
+                                int32_t cap) {
+  if (!L) {
+    fail(LLAMA_ERR_INVALID_ARGUMENT, "layer is NULL");
+    return -1;
+  }
+  for (auto& list : L->marks) {
+    for (size_t i = 1; i < list.size(); ++i) {
+      if (hipEventSynchronize(list[i].ev) != hipSuccess) continue;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, list[i - 1].ev, list[i].ev) != hipSuccess) continue;
+      auto& tot = L->totals[list[i].name];
+      tot.first += ms;
+      tot.second += 1;
+    }
+    for (auto& m : list) L->event_pool.push_back(m.ev);
+  }
+  L->marks.clear();
+  int32_t n = 0;
+  for (auto& kv : L->totals) {
+    if (n < cap) {
+      if (names) names[n] = kv.first.c_str();  // valid until the next read
+      if (total_ms) total_ms[n] = kv.second.first;
+      if (counts) counts[n] = kv.second.second;
+    }
+    ++n;
+  }
+  static thread_local std::map<std::string, std::pair<double, int64_t>> last;
+  last.swap(L->totals);  // keep name storage alive for the caller
+  L->totals.clear();
+  return n;
+}
+
+llama_status llama_op_linear(int32_t dtype, const void* x, const void* w, int32_t M, int32_t N, int32_t K,
+                             int32_t epilogue, void* out, void* stream) {
+  if (!x || !w || !out) return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "sizes must be positive");
+  if (epilogue < 0 || epilogue > 2) return fail(LLAMA_ERR_INVALID_ARGUMENT, "unknown epilogue %d", epilogue);
+  if (dtype != LLAMA_DTYPE_BF16 && dtype != LLAMA_DTYPE_FP32)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (dtype == LLAMA_DTYPE_BF16) {
+    const int64_t wrows = epilogue == LLAMA_EPI_SILU_MUL ? 2 * (int64_t)N : N;
+    if (K % 64 || wrows % 128)
+      return fail(LLAMA_ERR_INVALID_ARGUMENT, "bf16 needs K %% 64 == 0 and weight rows %% 128 == 0");
+  }
+  hipError_t e = llk::launch_linear(dtype, x, w, M, N, K, epilogue, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "linear");
+  return LLAMA_OK;
+}
+
+llama_status llama_op_reorder_gate_up(const void* src, int32_t inter, int32_t K, void* dst, void* stream) {
+  if (!src || !dst) return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (inter <= 0 || K <= 0 || inter % 16 || K % 8)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "needs intermediate %% 16 == 0 and K %% 8 == 0");
+  if (!aligned16(src) || !aligned16(dst)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (src == dst) return fail(LLAMA_ERR_INVALID_ARGUMENT, "dst aliases src");
+  hipError_t e = llk::launch_reorder_gate_up(src, inter, K, dst, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reorder_gate_up");
+  return LLAMA_OK;
+}
+
+llama_status llama_op_add_rmsnorm(int32_t dtype, const void* x, const void* residual, const void* w, float eps,
+                                  int32_t rows, int32_t hidden, void* normed, void* residual_out, void* stream) {
+  if (!x || !w || !normed) return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (residual && !residual_out) return fail(LLAMA_ERR_INVALID_ARGUMENT, "residual needs residual_out");
+  if (dtype != LLAMA_DTYPE_BF16 && dtype != LLAMA_DTYPE_FP32)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  const int vn = dtype == LLAMA_DTYPE_BF16 ? 8 : 4;
+  if (rows <= 0 || hidden <= 0 || hidden % vn || hidden > 256 * 8 * vn)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "hidden must be a multiple of %d and <= %d", vn, 256 * 8 * vn);
+  if (!(eps > 0.f)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "eps must be > 0");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(normed) || (residual && !aligned16(residual)) ||
+      (residual_out && !aligned16(residual_out)))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  hipError_t e = llk::launch_add_rmsnorm(dtype, x, residual, w, eps, rows, hidden, normed, residual_out,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "add_rmsnorm");
+  return LLAMA_OK;
+}
+
+}  // extern "C"

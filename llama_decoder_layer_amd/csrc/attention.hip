@@ -1,0 +1,258 @@
+// Causal grouped-query attention over the paged KV cache.
+//
+// What is computed (pages "LLama", hotelren.com/news/2693952, section
+// "4 LlamaAttention", and "模型库与算子层 — 代码走读",
+// vllm-learning.pages.dev, section "Attention 层": attention over the cache
+// through the block table): for a query token at position p and query head h,
+// with KV head g = h / (heads / kv_heads),
+//     o_h = sum_{j<=p} softmax_j(q_h . k_j / sqrt(d)) v_j .
+// Keys are read through block_table (16-token blocks of the
+// [blocks][kv_heads][16][d] planes).
+//
+// Work split: one workgroup per (query token, KV head, key partition).  The
+// workgroup serves all query heads of the group from one read of each K/V
+// row.  Scores, max and sums are fp32, with exp2 on log2(e)-scaled scores and
+// an online (running max) softmax across chunks of keys.  With more than one
+// partition each workgroup leaves (max, sum, unnormalised o) and a combine
+// kernel merges the partitions with their log-sum-exp weights, in partition
+// order (deterministic).
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGMax = 16;      // query heads per KV head
+constexpr int kChunk = 128;    // keys per softmax chunk
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void paged_attention_kernel(
+    const T* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
+    const T* __restrict__ kc, const T* __restrict__ vc, const int* __restrict__ block_table,
+    int max_blocks, int q_len, int part_len, int parts, float* __restrict__ partials,
+    T* __restrict__ out) {
+  using V = typename Vec16<T>::type;
+  constexpr int VN = Vec16<T>::N;
+  constexpr int CPT = D / VN;            // 16-byte chunks per key row
+  constexpr int TPP = kThreads / CPT;    // keys per pass
+  const int G = nq / nkv;
+
+  const int t = blockIdx.x;
+  const int g = blockIdx.y;
+  const int part = blockIdx.z;
+  const int p = positions[t];
+  const int b = t / q_len;
+  const int k_begin = part * part_len;
+  const int k_end = min(p + 1, k_begin + part_len);
+  const int* bt = block_table + (size_t)b * max_blocks;
+  const int tid = threadIdx.x;
+
+  __shared__ float sq[kGMax][D];
+  __shared__ float ss[kGMax][kChunk];
+  __shared__ float s_scale[kGMax];
+  __shared__ float s_m[kGMax];
+  __shared__ float s_l[kGMax];
+
+  const int out_per_thread = (G * D + kThreads - 1) / kThreads;  // <= 8 (G<=16, D<=128)
+  if (k_begin >= k_end) {
+    // empty partition: contributes nothing
+    for (int i = tid; i < G * (D + 2); i += kThreads) {
+      const int h = i / (D + 2), e = i % (D + 2);
+      float* dst = partials + (((size_t)t * nq + g * G + h) * parts + part) * (D + 2);
+      dst[e] = (e == 0) ? -INFINITY : 0.f;
+    }
+    return;
+  }
+
+  const float qscale = kLog2e / sqrtf((float)D);
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int h = i / D, e = i % D;
+    sq[h][e] = to_f32(q[(size_t)t * ldq + (size_t)(g * G + h) * D + e]) * qscale;
+  }
+  if (tid < G) {
+    s_m[tid] = -INFINITY;
+    s_l[tid] = 0.f;
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  __syncthreads();
+
+  const int c = tid % CPT;
+  const int lane_key = tid / CPT;
+  const size_t head_off = (size_t)g * kKvBlock * D;
+
+  for (int c0 = k_begin; c0 < k_end; c0 += kChunk) {
+    const int cn = min(kChunk, k_end - c0);
+    // scores of this chunk
+    for (int k0 = 0; k0 < cn; k0 += TPP) {
+      const int kk = k0 + lane_key;
+      float dot[kGMax];
+#pragma unroll
+      for (int h = 0; h < kGMax; ++h) dot[h] = 0.f;
+      if (kk < cn) {
+        const int pos = c0 + kk;
+        const int blk = bt[pos / kKvBlock];
+        const T* krow = kc + (size_t)blk * nkv * kKvBlock * D + head_off + (size_t)(pos % kKvBlock) * D;
+        V kv = ld16<V>(krow + c * VN);
+#pragma unroll
+        for (int h = 0; h < kGMax; ++h) {
+          if (h < G) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < VN; ++e) a = fmaf(sq[h][c * VN + e], to_f32(kv[e]), a);
+            dot[h] = a;
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < kGMax; ++h) {
+        if (h < G) {
+          const float s = group_sum<CPT>(dot[h]);
+          if (c == 0 && kk < cn) ss[h][kk] = s;
+        }
+      }
+    }
+    __syncthreads();
+    // online softmax update, one wave per head
+    for (int h = tid / kWave; h < G; h += kThreads / kWave) {
+      const int ln = tid % kWave;
+      float mx = -INFINITY;
+      for (int k = ln; k < cn; k += kWave) mx = fmaxf(mx, ss[h][k]);
+      mx = wave_max(mx);
+      const float m_old = s_m[h];
+      const float m_new = fmaxf(m_old, mx);
+      float sum = 0.f;
+      for (int k = ln; k < cn; k += kWave) {
+        const float e = exp2f(ss[h][k] - m_new);
+        ss[h][k] = e;
+        sum += e;
+      }
+      sum = wave_sum(sum);
+      if (ln == 0) {
+        const float sc = exp2f(m_old - m_new);  // 0 on the first chunk
+        s_scale[h] = sc;
+        s_l[h] = s_l[h] * sc + sum;
+        s_m[h] = m_new;
+      }
+    }
+    __syncthreads();
+    // P V
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = tid + j * kThreads;
+      if (j < out_per_thread && i < G * D) {
+        const int h = i / D, e = i % D;
+        float a = acc[j] * s_scale[h];
+        for (int k = 0; k < cn; ++k) {
+          const int pos = c0 + k;
+          const int blk = bt[pos / kKvBlock];
+          const T* vrow = vc + (size_t)blk * nkv * kKvBlock * D + head_off + (size_t)(pos % kKvBlock) * D;
+          a = fmaf(ss[h][k], to_f32(vrow[e]), a);
+        }
+        acc[j] = a;
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = tid + j * kThreads;
+    if (j < out_per_thread && i < G * D) {
+      const int h = i / D, e = i % D;
+      const int qh = g * G + h;
+      if (parts == 1) {
+        out[(size_t)t * nq * D + (size_t)qh * D + e] = from_f32<T>(acc[j] / s_l[h]);
+      } else {
+        float* dst = partials + (((size_t)t * nq + qh) * parts + part) * (D + 2);
+        if (e == 0) {
+          dst[0] = s_m[h];
+          dst[1] = s_l[h];
+        }
+        dst[2 + e] = acc[j];
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void attention_combine_kernel(const float* __restrict__ partials, int nq,
+                                                              int parts, T* __restrict__ out) {
+  const int t = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  const float* src = partials + ((size_t)t * nq + h) * parts * (D + 2);
+  float M = -INFINITY;
+  for (int i = 0; i < parts; ++i) M = fmaxf(M, src[(size_t)i * (D + 2)]);
+  float L = 0.f, o = 0.f;
+  for (int i = 0; i < parts; ++i) {
+    const float* pp = src + (size_t)i * (D + 2);
+    const float m = pp[0];
+    if (m == -INFINITY) continue;
+    const float w = exp2f(m - M);
+    L = fmaf(pp[1], w, L);
+    o = fmaf(pp[2 + e], w, o);
+  }
+  out[(size_t)t * nq * D + (size_t)h * D + e] = from_f32<T>(o / L);
+}
+
+template <typename T, int D>
+hipError_t attention_typed(const T* q, int ldq, int T_, const int* positions, int nq, int nkv,
+                           const T* kc, const T* vc, const int* block_table, int max_blocks, int q_len,
+                           const AttnPlan& plan, float* partials, T* out, hipStream_t s,
+                           hipEvent_t mid_event) {
+  dim3 grid(T_, nkv, plan.parts);
+  paged_attention_kernel<T, D><<<grid, kThreads, 0, s>>>(q, ldq, positions, nq, nkv, kc, vc, block_table,
+                                                         max_blocks, q_len, plan.part_len, plan.parts,
+                                                         partials, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.parts == 1) return e;
+  if (mid_event) {
+    e = hipEventRecord(mid_event, s);
+    if (e != hipSuccess) return e;
+  }
+  attention_combine_kernel<T, D><<<dim3(T_, nq), D, 0, s>>>(partials, nq, plan.parts, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+AttnPlan attention_plan(int T, int nq, int d, int q_len, int max_seq_len) {
+  AttnPlan pl;
+  if (q_len == 1) {
+    pl.part_len = 512;
+    pl.parts = (max_seq_len + pl.part_len - 1) / pl.part_len;
+  } else {
+    pl.part_len = max_seq_len;
+    pl.parts = 1;
+  }
+  if (pl.parts < 1) pl.parts = 1;
+  pl.ws_bytes = pl.parts > 1 ? (size_t)T * nq * pl.parts * (d + 2) * sizeof(float) : 0;
+  return pl;
+}
+
+hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
+                            int nkv, int d, const void* k_cache, const void* v_cache,
+                            const int* block_table, int max_blocks, int q_len, const AttnPlan& plan,
+                            float* partials, void* out, hipStream_t s, hipEvent_t mid_event) {
+  if (T <= 0) return hipSuccess;
+  if (dtype == kBF16) {
+    if (d == 128)
+      return attention_typed<bf16, 128>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
+                                        (const bf16*)v_cache, block_table, max_blocks, q_len, plan,
+                                        partials, (bf16*)out, s, mid_event);
+    return attention_typed<bf16, 64>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
+                                     (const bf16*)v_cache, block_table, max_blocks, q_len, plan, partials,
+                                     (bf16*)out, s, mid_event);
+  }
+  if (d == 128)
+    return attention_typed<float, 128>((const float*)q, ldq, T, positions, nq, nkv, (const float*)k_cache,
+                                       (const float*)v_cache, block_table, max_blocks, q_len, plan,
+                                       partials, (float*)out, s, mid_event);
+  return attention_typed<float, 64>((const float*)q, ldq, T, positions, nq, nkv, (const float*)k_cache,
+                                    (const float*)v_cache, block_table, max_blocks, q_len, plan, partials,
+                                    (float*)out, s, mid_event);
+}
+
+}  // namespace llk

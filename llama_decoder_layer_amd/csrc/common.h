@@ -1,0 +1,60 @@
+// Shared device helpers for the gfx950 kernels of the decoder-layer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+static constexpr int kWave = 64;      // CDNA wavefront width
+static constexpr int kKvBlock = 16;   // tokens per paged KV block
+
+// Element <-> fp32.  bf16 -> fp32 is exact; fp32 -> bf16 rounds to nearest
+// even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// 16-byte vector of T: 8 bf16 or 4 fp32.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> {
+  static constexpr int N = 8;
+  typedef bf16x8 type;
+};
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  typedef f32x4 type;
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Sum over a group of `W` consecutive lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// 16-byte global load that bypasses nothing; kept in one place so the load
+// width is visible.
+template <typename V>
+__device__ __forceinline__ V ld16(const void* p) {
+  return *reinterpret_cast<const V*>(p);
+}

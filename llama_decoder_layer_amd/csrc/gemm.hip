@@ -1,0 +1,408 @@
+// Dense projections of the layer: qkv_proj, o_proj, gate_up_proj, down_proj.
+//
+// Every projection is y = x W^T with W stored [out, in] (vllm-learning page
+// "模型库与算子层 — 代码走读", section "Linear 层": F.linear).  Epilogues fuse
+// what follows the projection in the layer:
+//   add       -- o_proj's output joins the residual stream (the add of
+//                post_attention_layernorm, page "LLama", hotelren.com/news/2693952)
+//   silu_mul  -- SiluAndMul after gate_up_proj: silu(x[:d]) * x[:d] of the
+//                merged output ("LLama" page, section "LlamaMLP")
+//
+// bf16 kernels use v_mfma_f32_16x16x32_bf16 with fp32 accumulation and are
+// written in the transposed orientation D[n][m] = W[n,:] . X[m,:]: W rows are
+// the MFMA's A operand, token rows its B operand.  Both operands are K-major
+// in memory, so a lane's 8-element operand slice is one 16-byte load, and an
+// output lane holds four consecutive output features of one token (one
+// 8-byte store).  Within one MFMA the k index a lane supplies only has to
+// agree between A and B, which lets the loads be laid out for coalescing.
+//
+//   skinny kernel (M <= 64 tokens, decode): HBM-bound weight streaming.  One
+//     workgroup owns 32 weight rows; its waves split K and reduce through LDS
+//     in a fixed order (deterministic, no atomics).  Operands come straight
+//     from global memory: W once from HBM, x from L2.
+//   tiled kernel (prefill): 128x128 output tile per workgroup, K in steps of
+//     64 through double-buffered, XOR-swizzled LDS; 2x2 waves of 64x64.
+//   fp32 kernel: plain LDS-tiled FMA kernel for fp32 layers.
+//
+// SiluAndMul layout: the bf16 gate_up weight is re-ordered once (in create)
+// so that each 32-row group holds 16 gate rows then the 16 matching up rows;
+// a lane then holds gate and up of the same four features.
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+namespace {
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+// Store four consecutive features n..n+3 of token m.
+template <int EPI>
+__device__ __forceinline__ void store4(bf16* out, size_t idx, const float v[4]) {
+  bf16x4 o;
+  if (EPI == kEpiAdd) {
+    bf16x4 prev = *reinterpret_cast<const bf16x4*>(out + idx);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(v[r] + static_cast<float>(prev[r]));
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(v[r]);
+  }
+  *reinterpret_cast<bf16x4*>(out + idx) = o;
+}
+
+__device__ __forceinline__ void store4_silu(bf16* out, size_t idx, const float g[4], const float u[4]) {
+  bf16x4 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(silu_f(g[r]) * u[r]);
+  *reinterpret_cast<bf16x4*>(out + idx) = o;
+}
+
+// ------------------------------------------------------------ skinny ------
+
+constexpr int kSkWaves = 4;
+constexpr int kSkRows = 32;  // weight rows per workgroup (two 16-row tiles)
+
+template <int MT, int EPI>
+__global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_bf16(
+    const bf16* __restrict__ X, int M, const bf16* __restrict__ W, int K, bf16* out, int ldo) {
+  constexpr int U = (MT <= 2) ? 8 : 4;  // k-steps (32 each) in flight per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int n0 = blockIdx.x * kSkRows;
+
+  const int S = K / 32;
+  const int s_begin = (wave * S) / kSkWaves;
+  const int s_end = ((wave + 1) * S) / kSkWaves;
+
+  const bf16* wrow0 = W + (size_t)(n0 + r16) * K + g * 8;
+  const bf16* wrow1 = wrow0 + (size_t)16 * K;
+  const bf16* xrow[MT];
+  bool xok[MT];
+#pragma unroll
+  for (int u = 0; u < MT; ++u) {
+    const int m = u * 16 + r16;
+    xok[u] = m < M;
+    xrow[u] = X + (size_t)(xok[u] ? m : 0) * K + g * 8;
+  }
+
+  f32x4 acc[2][MT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16x8 zero8 = {};
+  int s = s_begin;
+  for (; s + U <= s_end; s += U) {
+    bf16x8 a0[U], a1[U], b[U][MT];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const size_t ko = (size_t)(s + i) * 32;
+      a0[i] = ld16<bf16x8>(wrow0 + ko);
+      a1[i] = ld16<bf16x8>(wrow1 + ko);
+#pragma unroll
+      for (int u = 0; u < MT; ++u) b[i][u] = xok[u] ? ld16<bf16x8>(xrow[u] + ko) : zero8;
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) {
+        acc[0][u] = mfma16(a0[i], b[i][u], acc[0][u]);
+        acc[1][u] = mfma16(a1[i], b[i][u], acc[1][u]);
+      }
+  }
+  for (; s < s_end; ++s) {
+    const size_t ko = (size_t)s * 32;
+    bf16x8 a0 = ld16<bf16x8>(wrow0 + ko);
+    bf16x8 a1 = ld16<bf16x8>(wrow1 + ko);
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+      bf16x8 b = xok[u] ? ld16<bf16x8>(xrow[u] + ko) : zero8;
+      acc[0][u] = mfma16(a0, b, acc[0][u]);
+      acc[1][u] = mfma16(a1, b, acc[1][u]);
+    }
+  }
+
+  // cross-wave reduction in wave order
+  __shared__ f32x4 red[kSkWaves][2][MT][kWave];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) red[wave][t][u][lane] = acc[t][u];
+  __syncthreads();
+
+  constexpr int kSlots = 2 * MT * kWave;
+  for (int slot = threadIdx.x; slot < kSlots; slot += kSkWaves * kWave) {
+    const int l = slot & 63;
+    const int u = (slot >> 6) % MT;
+    const int t = (slot >> 6) / MT;
+    const int m = u * 16 + (l & 15);
+    if (m >= M) continue;
+    if (EPI == kEpiSiluMul && t == 1) continue;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < kSkWaves; ++w) {
+      f32x4 p = red[w][t][u][l];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] += p[r];
+    }
+    if (EPI == kEpiSiluMul) {
+      float up[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < kSkWaves; ++w) {
+        f32x4 p = red[w][1][u][l];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) up[r] += p[r];
+      }
+      const int f = blockIdx.x * 16 + 4 * (l >> 4);
+      store4_silu(out, (size_t)m * ldo + f, v, up);
+    } else {
+      const int n = n0 + t * 16 + 4 * (l >> 4);
+      store4<EPI>(out, (size_t)m * ldo + n, v);
+    }
+  }
+}
+
+// ------------------------------------------------------------- tiled ------
+
+constexpr int kTBM = 128;  // tokens per tile
+constexpr int kTBN = 128;  // weight rows per tile
+constexpr int kTBK = 64;
+constexpr int kTThreads = 256;
+
+// element offset of 16-byte chunk c of row `row` in a [rows][64] bf16 tile
+__device__ __forceinline__ int swz(int row, int c) { return row * kTBK + ((c ^ (row & 7)) << 3); }
+
+template <int EPI>
+__global__ __launch_bounds__(kTThreads) void gemm_tile_bf16(const bf16* __restrict__ X, int M,
+                                                            const bf16* __restrict__ W, int N,
+                                                            int K, bf16* out, int ldo) {
+  __shared__ __attribute__((aligned(16))) bf16 sW[2][kTBN * kTBK];
+  __shared__ __attribute__((aligned(16))) bf16 sX[2][kTBM * kTBK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wn = wave >> 1;  // wave's 64-row slice of the weight tile
+  const int wm = wave & 1;   // wave's 64-token slice
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+
+  const int num_m = (M + kTBM - 1) / kTBM;
+  const int tile_m = blockIdx.x % num_m;
+  const int tile_n = blockIdx.x / num_m;
+  const int m0 = tile_m * kTBM;
+  const int n0 = tile_n * kTBN;
+
+  // global -> register staging: 4 chunks of W and 4 of X per thread
+  int ld_row[4], ld_c[4];
+  const bf16* wsrc[4];
+  const bf16* xsrc[4];
+  bool xok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int id = tid + j * kTThreads;
+    ld_row[j] = id >> 3;
+    ld_c[j] = id & 7;
+    wsrc[j] = W + (size_t)(n0 + ld_row[j]) * K + ld_c[j] * 8;
+    const int m = m0 + ld_row[j];
+    xok[j] = m < M;
+    xsrc[j] = X + (size_t)(xok[j] ? m : 0) * K + ld_c[j] * 8;
+  }
+  const bf16x8 zero8 = {};
+  bf16x8 wst[4], xst[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wst[j] = ld16<bf16x8>(wsrc[j] + k0);
+      xst[j] = xok[j] ? ld16<bf16x8>(xsrc[j] + k0) : zero8;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<bf16x8*>(&sW[buf][swz(ld_row[j], ld_c[j])]) = wst[j];
+      *reinterpret_cast<bf16x8*>(&sX[buf][swz(ld_row[j], ld_c[j])]) = xst[j];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / kTBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * kTBK);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = s * 4 + g;
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8*>(&sW[buf][swz(wn * 64 + i * 16 + r16, c)]);
+        b[i] = *reinterpret_cast<const bf16x8*>(&sX[buf][swz(wm * 64 + i * 16 + r16, c)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds features n..n+3 of token m for each (i, j)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 64 + j * 16 + r16;
+    if (m >= M) continue;
+    if (EPI == kEpiSiluMul) {
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const int grp = (n0 + wn * 64 + i * 16) / 32;
+        const int f = grp * 16 + 4 * g;
+        float gv[4], uv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          gv[r] = acc[i][j][r];
+          uv[r] = acc[i + 1][j][r];
+        }
+        store4_silu(out, (size_t)m * ldo + f, gv, uv);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + wn * 64 + i * 16 + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r];
+        store4<EPI>(out, (size_t)m * ldo + n, v);
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------- fp32 ------
+
+constexpr int kF = 16;
+
+template <int EPI>
+__global__ __launch_bounds__(kF* kF) void gemm_f32(const float* __restrict__ X, int M,
+                                                  const float* __restrict__ W, int N, int K,
+                                                  float* out, int ldo) {
+  __shared__ float sx[kF][kF + 1];
+  __shared__ float sw[kF][kF + 1];
+  __shared__ float su[kF][kF + 1];
+  const int tx = threadIdx.x % kF;  // output feature within tile
+  const int ty = threadIdx.x / kF;  // token within tile
+  const int m = blockIdx.y * kF + ty;
+  const int n = blockIdx.x * kF + tx;
+  float acc = 0.f, accu = 0.f;
+  for (int k0 = 0; k0 < K; k0 += kF) {
+    // cooperative loads: row ty of x tile, row ty of W tile (features)
+    const int kk = k0 + tx;
+    const int xm = blockIdx.y * kF + ty;
+    const int wn = blockIdx.x * kF + ty;
+    sx[ty][tx] = (xm < M && kk < K) ? X[(size_t)xm * K + kk] : 0.f;
+    sw[ty][tx] = (wn < N && kk < K) ? W[(size_t)wn * K + kk] : 0.f;
+    if (EPI == kEpiSiluMul) su[ty][tx] = (wn < N && kk < K) ? W[(size_t)(N + wn) * K + kk] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kF; ++k) {
+      acc = fmaf(sx[ty][k], sw[tx][k], acc);
+      if (EPI == kEpiSiluMul) accu = fmaf(sx[ty][k], su[tx][k], accu);
+    }
+    __syncthreads();
+  }
+  if (m < M && n < N) {
+    const size_t o = (size_t)m * ldo + n;
+    if (EPI == kEpiAdd) out[o] = acc + out[o];
+    else if (EPI == kEpiSiluMul) out[o] = silu_f(acc) * accu;
+    else out[o] = acc;
+  }
+}
+
+__global__ void reorder_gate_up_kernel(const bf16* __restrict__ src, int inter, int K, bf16* dst) {
+  const int R = blockIdx.x;
+  const int grp = R >> 5, i = R & 31;
+  const int srow = (i < 16) ? (grp * 16 + i) : (inter + grp * 16 + (i - 16));
+  const bf16x8* s = reinterpret_cast<const bf16x8*>(src + (size_t)srow * K);
+  bf16x8* d = reinterpret_cast<bf16x8*>(dst + (size_t)R * K);
+  for (int c = threadIdx.x; c < K / 8; c += blockDim.x) d[c] = s[c];
+}
+
+template <int EPI>
+hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* out, hipStream_t s) {
+  // rows of W the kernel walks: N (store/add) or 2N (silu_mul)
+  const int wrows = (EPI == kEpiSiluMul) ? 2 * N : N;
+  if (M <= 64) {
+    dim3 grid(wrows / kSkRows);
+    if (M <= 16) gemm_skinny_bf16<1, EPI><<<grid, kSkWaves * kWave, 0, s>>>(x, M, w, K, out, N);
+    else if (M <= 32) gemm_skinny_bf16<2, EPI><<<grid, kSkWaves * kWave, 0, s>>>(x, M, w, K, out, N);
+    else gemm_skinny_bf16<4, EPI><<<grid, kSkWaves * kWave, 0, s>>>(x, M, w, K, out, N);
+  } else {
+    const int num_m = (M + kTBM - 1) / kTBM;
+    dim3 grid(num_m * (wrows / kTBN));
+    gemm_tile_bf16<EPI><<<grid, kTThreads, 0, s>>>(x, M, w, wrows, K, out, N);
+  }
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t linear_f32(const float* x, const float* w, int M, int N, int K, float* out, hipStream_t s) {
+  dim3 grid((N + kF - 1) / kF, (M + kF - 1) / kF);
+  gemm_f32<EPI><<<grid, kF * kF, 0, s>>>(x, M, w, N, K, out, N);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+const char* linear_kernel_name(int dtype, int M) {
+  if (dtype != kBF16) return "gemm_f32";
+  return M <= 64 ? "gemm_skinny_bf16" : "gemm_tile_bf16";
+}
+
+hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, int K, int epi,
+                         void* out, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (dtype == kBF16) {
+    const bf16* xb = (const bf16*)x;
+    const bf16* wb = (const bf16*)w;
+    bf16* ob = (bf16*)out;
+    // the tiled kernel walks weight rows in 128-row tiles
+    if (M > 64) {
+      const int wrows = (epi == kEpiSiluMul) ? 2 * N : N;
+      if (wrows % kTBN != 0) return hipErrorInvalidValue;
+    }
+    switch (epi) {
+      case kEpiStore: return linear_bf16<kEpiStore>(xb, wb, M, N, K, ob, s);
+      case kEpiAdd: return linear_bf16<kEpiAdd>(xb, wb, M, N, K, ob, s);
+      default: return linear_bf16<kEpiSiluMul>(xb, wb, M, N, K, ob, s);
+    }
+  }
+  const float* xf = (const float*)x;
+  const float* wf = (const float*)w;
+  float* of = (float*)out;
+  switch (epi) {
+    case kEpiStore: return linear_f32<kEpiStore>(xf, wf, M, N, K, of, s);
+    case kEpiAdd: return linear_f32<kEpiAdd>(xf, wf, M, N, K, of, s);
+    default: return linear_f32<kEpiSiluMul>(xf, wf, M, N, K, of, s);
+  }
+}
+
+hipError_t launch_reorder_gate_up(const void* src, int inter, int K, void* dst, hipStream_t s) {
+  reorder_gate_up_kernel<<<2 * inter, 256, 0, s>>>((const bf16*)src, inter, K, (bf16*)dst);
+  return hipGetLastError();
+}
+
+}  // namespace llk

@@ -1,0 +1,41 @@
+// Launchers of the gfx950 kernels (host functions, one family per .hip file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace llk {
+
+enum Dtype { kBF16 = 0, kFP32 = 1 };
+enum Epi { kEpiStore = 0, kEpiAdd = 1, kEpiSiluMul = 2 };
+
+// rmsnorm.hip
+hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* res, const void* w, float eps,
+                              int rows, int hidden, void* normed, void* res_out, hipStream_t s);
+
+// gemm.hip: out = x W^T with an epilogue; picks the skinny (M <= 64) or the
+// tiled kernel.
+hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, int K, int epi,
+                         void* out, hipStream_t s);
+hipError_t launch_reorder_gate_up(const void* src, int inter, int K, void* dst, hipStream_t s);
+const char* linear_kernel_name(int dtype, int M);
+
+// rope_kv.hip
+hipError_t launch_rope_kv(int dtype, void* qkv, int T, const int* positions, const float2* table,
+                          int nq, int nkv, int d, const int* block_table, int max_blocks, int q_len,
+                          void* k_cache, void* v_cache, hipStream_t s);
+
+// attention.hip
+struct AttnPlan {
+  int parts;        // key partitions per query (1 = no split)
+  int part_len;     // keys per partition
+  size_t ws_bytes;  // fp32 partial results
+};
+AttnPlan attention_plan(int T, int nq, int d, int q_len, int max_seq_len);
+hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
+                            int nkv, int d, const void* k_cache, const void* v_cache,
+                            const int* block_table, int max_blocks, int q_len,
+                            const AttnPlan& plan, float* partials, void* out, hipStream_t s,
+                            hipEvent_t mid_event);
+
+}  // namespace llk

@@ -179,13 +179,17 @@ class Seq:
 
 def decoder_layer(cfg: dict, w: dict, hidden: np.ndarray, residual: Optional[np.ndarray],
                   positions: np.ndarray, seqs: Sequence[Seq], rnd=None,
-                  want: Optional[Sequence[int]] = None) -> dict:
+                  want: Optional[Sequence[int]] = None, trace: Optional[dict] = None) -> dict:
     """One layer forward.
 
     cfg: config.json-style dict; w: float64 weights (input_layernorm,
     qkv_proj, o_proj, post_attention_layernorm, gate_up_proj, down_proj);
     hidden/residual [T, H] (residual may be None); positions [T]; seqs the
     batch's sequences; rnd None or ``bf16_round``.
+
+    ``trace``, if a dict, receives the intermediate tensors (for locating a
+    disagreement): h [needed rows], q (rotated) [wanted rows], k (rotated)
+    and v [needed rows], attn, h2, act [wanted rows], plus the row lists.
 
     ``want`` restricts the outputs to these token rows (default: all).  K/V
     are still computed for every row of a wanted row's sequence up to that
@@ -269,6 +273,9 @@ def decoder_layer(cfg: dict, w: dict, hidden: np.ndarray, residual: Optional[np.
     # gate_up projection, SiluAndMul, down projection
     act = rnd(silu_and_mul(linear(h2, w["gate_up_proj"])))
     out = linear(act, w["down_proj"])
+    if trace is not None:
+        trace.update({"need_rows": need_rows, "want_rows": want, "h": h, "q": q, "k": k, "v": v,
+                      "attn": attn, "h2": h2, "act": act})
     return {"rows": want, "hidden_out": out, "residual_out": r2,
             "k_new": k_new, "v_new": v_new}
 

@@ -1,0 +1,134 @@
+"""GPU parity of the whole layer forward (llama_layer_forward) against the
+oracle, at sizes the oracle finishes in seconds: several GEMM tiles with
+ragged tails, key partitions, block boundaries, prefill with and without a
+cached context, decode at several batch sizes, the fp32 tiny workload, and
+the first-layer (no residual) path.  Also: the KV cache is written exactly at
+the new tokens' slots and nowhere else, and repeated calls are bitwise
+identical."""
+import numpy as np
+import pytest
+import torch
+
+import llama_decoder_layer_amd as lda
+import synth
+from tests.parity import compare, device_batch, np64, oracle_seqs, oracle_weights, run_oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+# a small bf16 model of the 70B layer's structure: GQA 4:1, head_dim 128,
+# llama3 RoPE with the 70B parameters
+MID = synth.ModelShape(1024, 8, 2, 128, 2816, 1e-5, 500000.0, synth.LLAMA3_SCALING, 131072, "bf16")
+
+
+def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False):
+    model = workload.model
+    batch = synth.build_batch(workload, ctx_lens)
+    print("case", workload.name, "ctx", batch.ctx_lens[:8], "T", batch.num_tokens, flush=True)
+    hidden, residual = synth.draw_activations(model, batch.num_tokens, workload.index, DEV,
+                                              residual=not workload.residual_none)
+    pos, bt, sl = device_batch(batch, DEV)
+    h, r = hidden, residual
+    ref_h = None
+    results = []
+    oracle_in_h, oracle_in_r = hidden, residual
+    for l in range(layers):
+        w = synth.draw_weights(model, workload.index, l, DEV)
+        kp, vp = synth.build_kv_pool(workload, batch, l, DEV)
+        kp0, vp0 = kp.clone(), vp.clone()
+        layer = lda.Layer(model.config_dict(), w)
+        ws = layer.alloc_workspace(batch.num_tokens, batch.num_seqs, batch.max_seq_len)
+        ho, ro = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws)
+        torch.cuda.synchronize()
+        if repeat:
+            kp1, vp1 = kp.clone(), vp.clone()
+            ho2, ro2 = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(ho.view(torch.int16), ho2.view(torch.int16))
+            assert torch.equal(ro.view(torch.int16), ro2.view(torch.int16))
+            assert torch.equal(kp.view(torch.int16), kp1.view(torch.int16))
+            assert torch.equal(vp.view(torch.int16), vp1.view(torch.int16))
+        results.append((w, kp0, vp0, kp, vp, ho, ro))
+        h, r = ho, ro
+        layer.close()
+
+    # oracle: chained on its own (never fed the GPU's outputs)
+    cfg_np_h = oracle_in_h
+    dtype = model.dtype
+    hx = hr_ = None
+    for l, (w, kp0, vp0, kp, vp, ho, ro) in enumerate(results):
+        seqs = oracle_seqs(model, batch, kp0, vp0)
+        if l == 0:
+            exact, rounded = run_oracle(model, oracle_weights(w), oracle_in_h, oracle_in_r, batch, seqs)
+        else:
+            import oracle as orc
+            cfg = model.config_dict()
+            posn = batch.positions.numpy().astype(np.int64)
+            exact = orc.decoder_layer(cfg, oracle_weights(w), prev_exact["hidden_out"], prev_exact["residual_out"],
+                                      posn, seqs)
+            rounded = orc.decoder_layer(cfg, oracle_weights(w), orc.bf16_round(prev_r["hidden_out"]),
+                                        orc.bf16_round(prev_r["residual_out"]), posn, seqs, rnd=orc.bf16_round)
+        prev_exact, prev_r = exact, rounded
+        s1 = compare("hidden_out[%d]" % l, np64(ho), exact["hidden_out"],
+                     None if rounded is None else rounded["hidden_out"], dtype)
+        s2 = compare("residual_out[%d]" % l, np64(ro), exact["residual_out"],
+                     None if rounded is None else rounded["residual_out"], dtype)
+        print("layer", l, "hidden_out", s1, "residual_out", s2, flush=True)
+        if check_kv:
+            _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded)
+
+
+def _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded):
+    ibits = torch.int16 if model.dtype == "bf16" else torch.int32
+    mask = torch.zeros(kp.shape[0], kp.shape[2], dtype=torch.bool)
+    ks, vs, kref, vref, kr, vr = [], [], [], [], [], []
+    for b in range(batch.num_seqs):
+        for j in range(batch.q_len):
+            p = batch.ctx_lens[b] + j
+            blk = int(batch.block_table[b, p // 16])
+            mask[blk, p % 16] = True
+            ks.append(np64(kp[blk, :, p % 16, :]))
+            vs.append(np64(vp[blk, :, p % 16, :]))
+            kref.append(exact["k_new"][b][j])
+            vref.append(exact["v_new"][b][j])
+            if rounded is not None:
+                kr.append(rounded["k_new"][b][j])
+                vr.append(rounded["v_new"][b][j])
+    m = mask.to(kp.device)[:, None, :, None].expand_as(kp)
+    # placement: bit-exact -- every byte outside the new slots is unchanged
+    assert torch.equal(kp.view(ibits)[~m], kp0.view(ibits)[~m])
+    assert torch.equal(vp.view(ibits)[~m], vp0.view(ibits)[~m])
+    compare("k_cache", np.stack(ks), np.stack(kref), np.stack(kr) if kr else None, model.dtype)
+    compare("v_cache", np.stack(vs), np.stack(vref), np.stack(vr) if vr else None, model.dtype)
+
+
+def test_tiny_fp32_prefill():
+    _run(synth.WORKLOADS["tiny_prefill_32"])
+
+
+def test_mid_prefill_ragged_tiles():
+    _run(synth.Workload(20, "mid_prefill_3x100", MID, 3, 100, 0), repeat=True)
+
+
+def test_mid_prefill_on_cached_context():
+    _run(synth.Workload(21, "mid_prefill_2x70_ctx", MID, 2, 70, 0), ctx_lens=[37, 200])
+
+
+def test_mid_decode_block_and_partition_edges():
+    _run(synth.Workload(22, "mid_decode_b6", MID, 6, 1, 0), ctx_lens=[0, 1, 15, 16, 1000, 3000], repeat=True)
+
+
+def test_mid_decode_b40():
+    _run(synth.Workload(23, "mid_decode_b40", MID, 40, 1, (1, 2000)))
+
+
+def test_mid_decode_b65_tiled_path():
+    _run(synth.Workload(24, "mid_decode_b65", MID, 65, 1, (100, 700)))
+
+
+def test_mid_first_layer_no_residual():
+    _run(synth.Workload(25, "mid_decode_b8_nores", MID, 8, 1, (10, 300), residual_none=True))
+
+
+def test_mid_two_layer_stack():
+    _run(synth.Workload(26, "mid_decode_b12_2layer", MID, 12, 1, (50, 900), layers=2), layers=2)
