@@ -113,10 +113,16 @@ typedef struct {
   const void* down_proj;
 } llama_layer_weights;
 
-/* One layer's paged KV cache (device memory owned by the caller).  K and V
- * are separate planes, each [num_blocks][kv_heads][16][head_dim] in the layer
- * dtype: token position p of sequence b lives in block
- * block_table[b][p / 16], row p % 16.  K is stored after RoPE.            */
+/* One layer's paged KV cache (device memory owned by the caller), two planes
+ * in the layer dtype, each num_blocks blocks of 16 token slots per KV head:
+ *   k  [num_blocks][kv_heads][16][head_dim]   (a slot's K row contiguous)
+ *   v  [num_blocks][kv_heads][head_dim][16]   (the 16 slots of one V
+ *                                              component contiguous)
+ * Token position p of sequence b lives in block block_table[b][p / 16],
+ * slot p % 16.  K is stored after RoPE.  The V plane keeps the 16 slots of a
+ * component together so that attention reads V as the key-major operand of
+ * its P.V product with whole-vector loads (the layout vLLM's paged attention
+ * uses for V).                                                              */
 typedef struct {
   void* k;
   void* v;

@@ -100,7 +100,7 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   const llama_layer_config& c = L->cfg;
   Workspace w{};
   const int q_len = (B > 0 && T % B == 0) ? T / B : 1;
-  w.plan = llk::attention_plan(T, c.num_attention_heads, c.head_dim, q_len, max_seq_len);
+  w.plan = llk::attention_plan(T, c.num_attention_heads, c.num_key_value_heads, c.head_dim, q_len, max_seq_len);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;

@@ -6,8 +6,8 @@
 // through the block table): for a query token at position p and query head h,
 // with KV head g = h / (heads / kv_heads),
 //     o_h = sum_{j<=p} softmax_j(q_h . k_j / sqrt(d)) v_j .
-// Keys are read through block_table (16-token blocks of the
-// [blocks][kv_heads][16][d] planes).
+// Keys are read through block_table: 16-slot blocks of the K plane
+// [blocks][kv_heads][16][d] and the V plane [blocks][kv_heads][d][16].
 //
 // Work split: one workgroup per (query token, KV head, key partition).  The
 // workgroup serves all query heads of the group from one read of each K/V
@@ -56,13 +56,8 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(
   __shared__ float s_l[kGMax];
 
   const int out_per_thread = (G * D + kThreads - 1) / kThreads;  // <= 8 (G<=16, D<=128)
-  if (k_begin >= k_end) {
-    // empty partition: contributes nothing
-    for (int i = tid; i < G * (D + 2); i += kThreads) {
-      const int h = i / (D + 2), e = i % (D + 2);
-      float* dst = partials + (((size_t)t * nq + g * G + h) * parts + part) * (D + 2);
-      dst[e] = (e == 0) ? -INFINITY : 0.f;
-    }
+  if (k_begin >= k_end) {  // empty partition: only its max (-inf) is read
+    if (tid < G) partials[(((size_t)t * nq + g * G + tid) * parts + part) * (D + 2)] = -INFINITY;
     return;
   }
 
@@ -149,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(
         for (int k = 0; k < cn; ++k) {
           const int pos = c0 + k;
           const int blk = bt[pos / kKvBlock];
-          const T* vrow = vc + (size_t)blk * nkv * kKvBlock * D + head_off + (size_t)(pos % kKvBlock) * D;
-          a = fmaf(ss[h][k], to_f32(vrow[e]), a);
+          const T* vcol = vc + (size_t)blk * nkv * kKvBlock * D + head_off + (pos % kKvBlock);
+          a = fmaf(ss[h][k], to_f32(vcol[(size_t)e * kKvBlock]), a);
         }
         acc[j] = a;
       }
@@ -200,28 +195,31 @@ __global__ __launch_bounds__(D) void attention_combine_kernel(const float* __res
 template <typename T, int D>
 hipError_t attention_typed(const T* q, int ldq, int T_, const int* positions, int nq, int nkv,
                            const T* kc, const T* vc, const int* block_table, int max_blocks, int q_len,
-                           const AttnPlan& plan, float* partials, T* out, hipStream_t s,
-                           hipEvent_t mid_event) {
+                           const AttnPlan& plan, float* partials, T* out, hipStream_t s) {
   dim3 grid(T_, nkv, plan.parts);
   paged_attention_kernel<T, D><<<grid, kThreads, 0, s>>>(q, ldq, positions, nq, nkv, kc, vc, block_table,
                                                          max_blocks, q_len, plan.part_len, plan.parts,
                                                          partials, out);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.parts == 1) return e;
-  if (mid_event) {
-    e = hipEventRecord(mid_event, s);
-    if (e != hipSuccess) return e;
-  }
-  attention_combine_kernel<T, D><<<dim3(T_, nq), D, 0, s>>>(partials, nq, plan.parts, out);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t combine(int d, int T_, int nq, int parts, const float* partials, void* out, hipStream_t s) {
+  if (d == 128) attention_combine_kernel<T, 128><<<dim3(T_, nq), 128, 0, s>>>(partials, nq, parts, (T*)out);
+  else attention_combine_kernel<T, 64><<<dim3(T_, nq), 64, 0, s>>>(partials, nq, parts, (T*)out);
   return hipGetLastError();
 }
 
 }  // namespace
 
-AttnPlan attention_plan(int T, int nq, int d, int q_len, int max_seq_len) {
+AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_len) {
   AttnPlan pl;
   if (q_len == 1) {
-    pl.part_len = 512;
+    // decode: split the keys so that about 2048 workgroups run, partitions
+    // of 64..1024 keys (a multiple of 64: four waves x 16-slot blocks)
+    long long want = ((long long)max_seq_len * T * nkv + 2047) / 2048;
+    int len = (int)((want + 63) / 64 * 64);
+    pl.part_len = len < 64 ? 64 : (len > 1024 ? 1024 : len);
     pl.parts = (max_seq_len + pl.part_len - 1) / pl.part_len;
   } else {
     pl.part_len = max_seq_len;
@@ -237,22 +235,32 @@ hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int*
                             const int* block_table, int max_blocks, int q_len, const AttnPlan& plan,
                             float* partials, void* out, hipStream_t s, hipEvent_t mid_event) {
   if (T <= 0) return hipSuccess;
-  if (dtype == kBF16) {
-    if (d == 128)
-      return attention_typed<bf16, 128>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
-                                        (const bf16*)v_cache, block_table, max_blocks, q_len, plan,
-                                        partials, (bf16*)out, s, mid_event);
-    return attention_typed<bf16, 64>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
-                                     (const bf16*)v_cache, block_table, max_blocks, q_len, plan, partials,
-                                     (bf16*)out, s, mid_event);
+  hipError_t e;
+  if (dtype == kBF16 && q_len == 1) {
+    e = launch_decode_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table,
+                                     max_blocks, q_len, plan.part_len, plan.parts, partials, out, s);
+  } else if (dtype == kBF16) {
+    e = d == 128 ? attention_typed<bf16, 128>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
+                                              (const bf16*)v_cache, block_table, max_blocks, q_len, plan,
+                                              partials, (bf16*)out, s)
+                 : attention_typed<bf16, 64>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
+                                             (const bf16*)v_cache, block_table, max_blocks, q_len, plan, partials,
+                                             (bf16*)out, s);
+  } else {
+    e = d == 128 ? attention_typed<float, 128>((const float*)q, ldq, T, positions, nq, nkv,
+                                               (const float*)k_cache, (const float*)v_cache, block_table,
+                                               max_blocks, q_len, plan, partials, (float*)out, s)
+                 : attention_typed<float, 64>((const float*)q, ldq, T, positions, nq, nkv, (const float*)k_cache,
+                                              (const float*)v_cache, block_table, max_blocks, q_len, plan,
+                                              partials, (float*)out, s);
   }
-  if (d == 128)
-    return attention_typed<float, 128>((const float*)q, ldq, T, positions, nq, nkv, (const float*)k_cache,
-                                       (const float*)v_cache, block_table, max_blocks, q_len, plan,
-                                       partials, (float*)out, s, mid_event);
-  return attention_typed<float, 64>((const float*)q, ldq, T, positions, nq, nkv, (const float*)k_cache,
-                                    (const float*)v_cache, block_table, max_blocks, q_len, plan, partials,
-                                    (float*)out, s, mid_event);
+  if (e != hipSuccess || plan.parts == 1) return e;
+  if (mid_event) {
+    e = hipEventRecord(mid_event, s);
+    if (e != hipSuccess) return e;
+  }
+  return dtype == kBF16 ? combine<bf16>(d, T, nq, plan.parts, partials, out, s)
+                        : combine<float>(d, T, nq, plan.parts, partials, out, s);
 }
 
 }  // namespace llk

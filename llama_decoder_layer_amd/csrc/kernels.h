@@ -31,11 +31,17 @@ struct AttnPlan {
   int part_len;     // keys per partition
   size_t ws_bytes;  // fp32 partial results
 };
-AttnPlan attention_plan(int T, int nq, int d, int q_len, int max_seq_len);
+AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_len);
 hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
                             int nkv, int d, const void* k_cache, const void* v_cache,
                             const int* block_table, int max_blocks, int q_len,
                             const AttnPlan& plan, float* partials, void* out, hipStream_t s,
                             hipEvent_t mid_event);
+
+// attention_decode.hip (bf16, one query token per sequence)
+hipError_t launch_decode_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
+                                        int d, const void* k_cache, const void* v_cache, const int* block_table,
+                                        int max_blocks, int q_len, int part_len, int parts, float* partials,
+                                        void* out, hipStream_t s);
 
 }  // namespace llk

@@ -11,9 +11,9 @@
 //
 // Cache write: "模型库与算子层 — 代码走读" (vllm-learning.pages.dev, section
 // "Attention 层"): the new k, v are stored before attention reads the cache.
-// Position p of sequence b lives in block block_table[b][p / 16], row p % 16,
-// of the [blocks][kv_heads][16][head_dim] K and V planes.  V is a bit copy of
-// the projection's v.
+// Position p of sequence b lives in block block_table[b][p / 16], slot
+// p % 16: K plane [blocks][kv_heads][16][head_dim], V plane
+// [blocks][kv_heads][head_dim][16].  V is a bit copy of the projection's v.
 //
 // HBM-bound and tiny: one workgroup per token.  q is rotated in place inside
 // the qkv buffer.
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(T* __restrict__ qkv, const
   for (int idx = threadIdx.x; idx < nkv * d; idx += blockDim.x) {
     const int gv = idx / d;
     const int e = idx - gv * d;
-    vc[(((size_t)blk * nkv + gv) * kKvBlock + row) * d + e] = v[idx];
+    vc[(((size_t)blk * nkv + gv) * d + e) * kKvBlock + row] = v[idx];
   }
 }
 

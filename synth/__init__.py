@@ -258,30 +258,40 @@ def sentinel_fill(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
-def pool_shape(model: ModelShape, num_blocks: int):
-    """K and V planes are each [num_blocks][kv_heads][16][head_dim]."""
-    return (num_blocks, model.num_key_value_heads, KV_BLOCK, model.head_dim)
+def pool_shape(model: ModelShape, num_blocks: int, plane: str = "k"):
+    """K plane [num_blocks][kv_heads][16][head_dim]; V plane
+    [num_blocks][kv_heads][head_dim][16] (the library header's layout)."""
+    if plane == "k":
+        return (num_blocks, model.num_key_value_heads, KV_BLOCK, model.head_dim)
+    return (num_blocks, model.num_key_value_heads, model.head_dim, KV_BLOCK)
 
 
-def scatter_context(pool: torch.Tensor, batch: Batch, b: int, ctx: torch.Tensor) -> None:
+def _slot_major(pool: torch.Tensor, plane: str) -> torch.Tensor:
+    """View of a plane as [blocks, kv_heads, 16, d] (a view, not a copy)."""
+    return pool if plane == "k" else pool.transpose(2, 3)
+
+
+def scatter_context(pool: torch.Tensor, batch: Batch, b: int, ctx: torch.Tensor, plane: str = "k") -> None:
     """Lay a logical context ``ctx`` [L, kv_heads, d] of sequence ``b`` into
     the paged pool at positions 0..L-1."""
+    view = _slot_major(pool, plane)
     L = ctx.shape[0]
     for j in range(0, (L + KV_BLOCK - 1) // KV_BLOCK):
         blk = int(batch.block_table[b, j])
         n = min(KV_BLOCK, L - j * KV_BLOCK)
-        pool[blk, :, :n, :] = ctx[j * KV_BLOCK: j * KV_BLOCK + n].transpose(0, 1)
+        view[blk, :, :n, :] = ctx[j * KV_BLOCK: j * KV_BLOCK + n].transpose(0, 1)
 
 
-def gather_context(pool: torch.Tensor, batch: Batch, b: int, length: int) -> torch.Tensor:
+def gather_context(pool: torch.Tensor, batch: Batch, b: int, length: int, plane: str = "k") -> torch.Tensor:
     """Read positions 0..length-1 of sequence ``b`` out of the paged pool as a
     logical [length, kv_heads, d] tensor."""
+    view = _slot_major(pool, plane)
     nb = (length + KV_BLOCK - 1) // KV_BLOCK
     if nb == 0:
-        return pool.new_empty((0, pool.shape[1], pool.shape[3]))
+        return pool.new_empty((0, view.shape[1], view.shape[3]))
     ids = batch.block_table[b, :nb].long().to(pool.device)
-    blocks = pool.index_select(0, ids)                     # [nb, kv, 16, d]
-    flat = blocks.permute(0, 2, 1, 3).reshape(nb * KV_BLOCK, pool.shape[1], pool.shape[3])
+    blocks = view.index_select(0, ids)                     # [nb, kv, 16, d]
+    flat = blocks.permute(0, 2, 1, 3).reshape(nb * KV_BLOCK, view.shape[1], view.shape[3])
     return flat[:length]
 
 
@@ -290,18 +300,17 @@ def build_kv_pool(workload: Workload, batch: Batch, layer: int, device):
     then each sequence's cached context (positions 0..ctx-1) drawn N(0,1).
     Cached K counts as already rotated."""
     model = workload.model
-    shape = pool_shape(model, batch.num_blocks)
-    kp = sentinel_fill(torch.empty(shape, dtype=model.torch_dtype, device=device))
-    vp = sentinel_fill(torch.empty(shape, dtype=model.torch_dtype, device=device))
+    kp = sentinel_fill(torch.empty(pool_shape(model, batch.num_blocks, "k"), dtype=model.torch_dtype, device=device))
+    vp = sentinel_fill(torch.empty(pool_shape(model, batch.num_blocks, "v"), dtype=model.torch_dtype, device=device))
     gk = _gen(seed_of(workload.index, layer, T_KCTX), device)
     gv = _gen(seed_of(workload.index, layer, T_VCTX), device)
     nkv, d = model.num_key_value_heads, model.head_dim
     for b, c in enumerate(batch.ctx_lens):
         if c == 0:
             continue
-        for gen, pool in ((gk, kp), (gv, vp)):
+        for gen, pool, plane in ((gk, kp, "k"), (gv, vp, "v")):
             x = torch.randn((c, nkv, d), generator=gen, device=device, dtype=torch.float32)
-            scatter_context(pool, batch, b, x.to(model.torch_dtype))
+            scatter_context(pool, batch, b, x.to(model.torch_dtype), plane)
     return kp, vp
 
 

@@ -93,7 +93,7 @@ def oracle_seqs(model: synth.ModelShape, batch: synth.Batch, k_pool, v_pool, seq
     for b in ids:
         c = batch.ctx_lens[b]
         kc = np64(synth.gather_context(k_pool, batch, b, c))
-        vc = np64(synth.gather_context(v_pool, batch, b, c))
+        vc = np64(synth.gather_context(v_pool, batch, b, c, "v"))
         rows = list(range(b * batch.q_len, (b + 1) * batch.q_len))
         seqs.append(oracle.Seq(rows, kc, vc))
     return seqs

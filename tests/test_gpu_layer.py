@@ -80,7 +80,7 @@ def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False):
 
 def _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded):
     ibits = torch.int16 if model.dtype == "bf16" else torch.int32
-    mask = torch.zeros(kp.shape[0], kp.shape[2], dtype=torch.bool)
+    mask = torch.zeros(kp.shape[0], 16, dtype=torch.bool)
     ks, vs, kref, vref, kr, vr = [], [], [], [], [], []
     for b in range(batch.num_seqs):
         for j in range(batch.q_len):
@@ -88,16 +88,17 @@ def _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded):
             blk = int(batch.block_table[b, p // 16])
             mask[blk, p % 16] = True
             ks.append(np64(kp[blk, :, p % 16, :]))
-            vs.append(np64(vp[blk, :, p % 16, :]))
+            vs.append(np64(vp[blk, :, :, p % 16]))
             kref.append(exact["k_new"][b][j])
             vref.append(exact["v_new"][b][j])
             if rounded is not None:
                 kr.append(rounded["k_new"][b][j])
                 vr.append(rounded["v_new"][b][j])
-    m = mask.to(kp.device)[:, None, :, None].expand_as(kp)
+    mk = mask.to(kp.device)[:, None, :, None].expand_as(kp)
+    mv = mask.to(vp.device)[:, None, None, :].expand_as(vp)
     # placement: bit-exact -- every byte outside the new slots is unchanged
-    assert torch.equal(kp.view(ibits)[~m], kp0.view(ibits)[~m])
-    assert torch.equal(vp.view(ibits)[~m], vp0.view(ibits)[~m])
+    assert torch.equal(kp.view(ibits)[~mk], kp0.view(ibits)[~mk])
+    assert torch.equal(vp.view(ibits)[~mv], vp0.view(ibits)[~mv])
     compare("k_cache", np.stack(ks), np.stack(kref), np.stack(kr) if kr else None, model.dtype)
     compare("v_cache", np.stack(vs), np.stack(vref), np.stack(vr) if vr else None, model.dtype)
 
