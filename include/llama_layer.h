@@ -73,7 +73,8 @@ typedef enum { LLAMA_DTYPE_BF16 = 0, LLAMA_DTYPE_FP32 = 1 } llama_dtype;
  *     original_max_position_embeddings > 0             -> else INVALID_ARGUMENT
  *   num_attention_heads % num_key_value_heads == 0     -> else INVALID_ARGUMENT
  *   head_dim in {64, 128}; kv_block_size == 16         -> else UNSUPPORTED
- *   bf16: hidden_size, intermediate_size multiples of 128, hidden_size <= 16384;
+ *   bf16: hidden_size, intermediate_size and (heads + 2*kv_heads)*head_dim
+ *     multiples of 128, hidden_size and (heads + 2*kv_heads)*head_dim <= 16384;
  *   fp32: hidden_size multiple of 4, hidden_size <= 8192 -> else UNSUPPORTED
  *   all sizes > 0, rms_norm_eps > 0, rope_theta > 1, dtype known
  *                                                      -> else INVALID_ARGUMENT */

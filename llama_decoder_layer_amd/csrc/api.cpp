@@ -92,8 +92,10 @@ struct llama_layer {
 namespace {
 
 struct Workspace {
-  size_t h, qkv, attn, h2, act, part, total;
+  size_t h, qkv, attn, h2, act, part, gpart, total;
   llk::AttnPlan plan;
+  bool skinny;  // few tokens: weight-streaming projections with split-K partials
+  llk::SkinnyPlan pq, po, pg, pd;
 };
 
 Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
@@ -113,6 +115,20 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.h2 = take((size_t)T * c.hidden_size * L->es);
   w.act = take((size_t)T * c.intermediate_size * L->es);
   w.part = take(w.plan.ws_bytes);
+  const int H = c.hidden_size, Q = c.num_attention_heads * c.head_dim, I = c.intermediate_size;
+  w.skinny = L->dtype == LLAMA_DTYPE_BF16 && T <= 64;
+  size_t gpart = 0;
+  if (w.skinny) {
+    w.pq = llk::skinny_plan(T, L->qkv_n, H, true);
+    w.po = llk::skinny_plan(T, H, Q, true);
+    w.pg = llk::skinny_plan(T, 2 * I, H, false);
+    w.pd = llk::skinny_plan(T, H, I, true);
+    size_t n = (size_t)w.pq.splits * L->qkv_n;
+    if ((size_t)w.po.splits * H > n) n = (size_t)w.po.splits * H;
+    if ((size_t)w.pd.splits * H > n) n = (size_t)w.pd.splits * H;
+    gpart = n * T * sizeof(float);
+  }
+  w.gpart = take(gpart);
   w.total = off;
   return w;
 }
@@ -202,10 +218,10 @@ llama_status llama_layer_config_validate(const llama_layer_config* c) {
   const int qkv_n = (c->num_attention_heads + 2 * c->num_key_value_heads) * c->head_dim;
   if (c->dtype == LLAMA_DTYPE_BF16) {
     if (c->hidden_size % 128 || c->intermediate_size % 128 || c->hidden_size > 16384 || qkv_n % 128 ||
-        (c->num_attention_heads * c->head_dim) % 64)
+        qkv_n > 16384 || (c->num_attention_heads * c->head_dim) % 64)
       return fail(LLAMA_ERR_UNSUPPORTED,
                   "bf16 needs hidden_size, intermediate_size and the qkv width to be multiples "
-                  "of 128 and hidden_size <= 16384");
+                  "of 128, hidden_size <= 16384 and qkv width <= 16384");
   } else {
     if (c->hidden_size % 4 || c->hidden_size > 8192)
       return fail(LLAMA_ERR_UNSUPPORTED, "fp32 needs hidden_size %% 4 == 0 and <= 8192");
@@ -372,11 +388,20 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   e = llk::launch_add_rmsnorm(dt, hidden, residual, L->w_in, c.rms_norm_eps, T, H, h, residual_out, s);
   if (e != hipSuccess) return hip_fail(e, "input_layernorm");
   mk.mark("input_layernorm");
-  e = llk::launch_linear(dt, h, L->w_qkv, T, L->qkv_n, H, llk::kEpiStore, qkv, s);
-  if (e != hipSuccess) return hip_fail(e, "qkv_proj");
-  mk.mark("qkv_proj");
-  e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, q_len, kv->k,
-                          kv->v, s);
+  float* gp = (float*)(ws + w.gpart);
+  if (w.skinny) {
+    e = llk::launch_skinny(h, L->w_qkv, T, L->qkv_n, H, llk::kEpiPartial, w.pq, gp, s);
+    if (e != hipSuccess) return hip_fail(e, "qkv_proj");
+    mk.mark("qkv_proj");
+    e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, q_len, kv->k,
+                            kv->v, s, gp, w.pq.splits);
+  } else {
+    e = llk::launch_linear(dt, h, L->w_qkv, T, L->qkv_n, H, llk::kEpiStore, qkv, s);
+    if (e != hipSuccess) return hip_fail(e, "qkv_proj");
+    mk.mark("qkv_proj");
+    e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, q_len, kv->k,
+                            kv->v, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "rope_kv_write");
   mk.mark("rope_kv_write");
   hipEvent_t mid = w.plan.parts > 1 ? mk.extra() : nullptr;
@@ -385,6 +410,27 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   if (e != hipSuccess) return hip_fail(e, "attention");
   if (mid) mk.list->push_back({"attention", mid});
   mk.mark(w.plan.parts > 1 ? "attention_combine" : "attention");
+  if (w.skinny) {
+    // o_proj as split-K partials; the post-attention norm kernel sums them,
+    // adds the residual and stores the new residual before normalising
+    e = llk::launch_skinny(attn, L->w_o, T, H, nq * d, llk::kEpiPartial, w.po, gp, s);
+    if (e != hipSuccess) return hip_fail(e, "o_proj");
+    mk.mark("o_proj");
+    e = llk::launch_add_rmsnorm(dt, nullptr, residual_out, L->w_post, c.rms_norm_eps, T, H, h2, residual_out, s,
+                                gp, w.po.splits);
+    if (e != hipSuccess) return hip_fail(e, "post_attention_layernorm");
+    mk.mark("post_attention_layernorm");
+    e = llk::launch_skinny(h2, L->w_gu, T, I, H, llk::kEpiSiluMul, w.pg, act, s);
+    if (e != hipSuccess) return hip_fail(e, "gate_up_proj");
+    mk.mark("gate_up_silu");
+    e = llk::launch_skinny(act, L->w_down, T, H, I, llk::kEpiPartial, w.pd, gp, s);
+    if (e != hipSuccess) return hip_fail(e, "down_proj");
+    mk.mark("down_proj");
+    e = llk::launch_splitk_reduce(gp, w.pd.splits, T, H, hidden_out, s);
+    if (e != hipSuccess) return hip_fail(e, "down_proj reduce");
+    mk.mark("down_proj_reduce");
+    return LLAMA_OK;
+  }
   e = llk::launch_linear(dt, attn, L->w_o, T, H, nq * d, llk::kEpiAdd, residual_out, s);
   if (e != hipSuccess) return hip_fail(e, "o_proj");
   mk.mark("o_proj_residual");

@@ -5,7 +5,7 @@
 // what follows the projection in the layer:
 //   add       -- o_proj's output joins the residual stream (the add of
 //                post_attention_layernorm, page "LLama", hotelren.com/news/2693952)
-//   silu_mul  -- SiluAndMul after gate_up_proj: silu(x[:d]) * x[:d] of the
+//   silu_mul  -- SiluAndMul after gate_up_proj: silu(x[:d]) * x[d:] of the
 //                merged output ("LLama" page, section "LlamaMLP")
 //
 // bf16 kernels use v_mfma_f32_16x16x32_bf16 with fp32 accumulation and are
@@ -16,10 +16,7 @@
 // 8-byte store).  Within one MFMA the k index a lane supplies only has to
 // agree between A and B, which lets the loads be laid out for coalescing.
 //
-//   skinny kernel (M <= 64 tokens, decode): HBM-bound weight streaming.  One
-//     workgroup owns 32 weight rows; its waves split K and reduce through LDS
-//     in a fixed order (deterministic, no atomics).  Operands come straight
-//     from global memory: W once from HBM, x from L2.
+//   skinny kernel (M <= 64 tokens, decode): gemm_skinny.hip.
 //   tiled kernel (prefill): 128x128 output tile per workgroup, K in steps of
 //     64 through double-buffered, XOR-swizzled LDS; 2x2 waves of 64x64.
 //   fp32 kernel: plain LDS-tiled FMA kernel for fp32 layers.
@@ -39,7 +36,7 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-// Store four consecutive features n..n+3 of token m.
+// Store four consecutive features n..n+3 of token m (tiled kernel).
 template <int EPI>
 __device__ __forceinline__ void store4(bf16* out, size_t idx, const float v[4]) {
   bf16x4 o;
@@ -59,112 +56,6 @@ __device__ __forceinline__ void store4_silu(bf16* out, size_t idx, const float g
 #pragma unroll
   for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(silu_f(g[r]) * u[r]);
   *reinterpret_cast<bf16x4*>(out + idx) = o;
-}
-
-// ------------------------------------------------------------ skinny ------
-
-constexpr int kSkWaves = 4;
-constexpr int kSkRows = 32;  // weight rows per workgroup (two 16-row tiles)
-
-template <int MT, int EPI>
-__global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_bf16(
-    const bf16* __restrict__ X, int M, const bf16* __restrict__ W, int K, bf16* out, int ldo) {
-  constexpr int U = (MT <= 2) ? 8 : 4;  // k-steps (32 each) in flight per lane
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-  const int n0 = blockIdx.x * kSkRows;
-
-  const int S = K / 32;
-  const int s_begin = (wave * S) / kSkWaves;
-  const int s_end = ((wave + 1) * S) / kSkWaves;
-
-  const bf16* wrow0 = W + (size_t)(n0 + r16) * K + g * 8;
-  const bf16* wrow1 = wrow0 + (size_t)16 * K;
-  const bf16* xrow[MT];
-  bool xok[MT];
-#pragma unroll
-  for (int u = 0; u < MT; ++u) {
-    const int m = u * 16 + r16;
-    xok[u] = m < M;
-    xrow[u] = X + (size_t)(xok[u] ? m : 0) * K + g * 8;
-  }
-
-  f32x4 acc[2][MT];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int u = 0; u < MT; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const bf16x8 zero8 = {};
-  int s = s_begin;
-  for (; s + U <= s_end; s += U) {
-    bf16x8 a0[U], a1[U], b[U][MT];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const size_t ko = (size_t)(s + i) * 32;
-      a0[i] = ld16<bf16x8>(wrow0 + ko);
-      a1[i] = ld16<bf16x8>(wrow1 + ko);
-#pragma unroll
-      for (int u = 0; u < MT; ++u) b[i][u] = xok[u] ? ld16<bf16x8>(xrow[u] + ko) : zero8;
-    }
-#pragma unroll
-    for (int i = 0; i < U; ++i)
-#pragma unroll
-      for (int u = 0; u < MT; ++u) {
-        acc[0][u] = mfma16(a0[i], b[i][u], acc[0][u]);
-        acc[1][u] = mfma16(a1[i], b[i][u], acc[1][u]);
-      }
-  }
-  for (; s < s_end; ++s) {
-    const size_t ko = (size_t)s * 32;
-    bf16x8 a0 = ld16<bf16x8>(wrow0 + ko);
-    bf16x8 a1 = ld16<bf16x8>(wrow1 + ko);
-#pragma unroll
-    for (int u = 0; u < MT; ++u) {
-      bf16x8 b = xok[u] ? ld16<bf16x8>(xrow[u] + ko) : zero8;
-      acc[0][u] = mfma16(a0, b, acc[0][u]);
-      acc[1][u] = mfma16(a1, b, acc[1][u]);
-    }
-  }
-
-  // cross-wave reduction in wave order
-  __shared__ f32x4 red[kSkWaves][2][MT][kWave];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int u = 0; u < MT; ++u) red[wave][t][u][lane] = acc[t][u];
-  __syncthreads();
-
-  constexpr int kSlots = 2 * MT * kWave;
-  for (int slot = threadIdx.x; slot < kSlots; slot += kSkWaves * kWave) {
-    const int l = slot & 63;
-    const int u = (slot >> 6) % MT;
-    const int t = (slot >> 6) / MT;
-    const int m = u * 16 + (l & 15);
-    if (m >= M) continue;
-    if (EPI == kEpiSiluMul && t == 1) continue;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int w = 0; w < kSkWaves; ++w) {
-      f32x4 p = red[w][t][u][l];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] += p[r];
-    }
-    if (EPI == kEpiSiluMul) {
-      float up[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int w = 0; w < kSkWaves; ++w) {
-        f32x4 p = red[w][1][u][l];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) up[r] += p[r];
-      }
-      const int f = blockIdx.x * 16 + 4 * (l >> 4);
-      store4_silu(out, (size_t)m * ldo + f, v, up);
-    } else {
-      const int n = n0 + t * 16 + 4 * (l >> 4);
-      store4<EPI>(out, (size_t)m * ldo + n, v);
-    }
-  }
 }
 
 // ------------------------------------------------------------- tiled ------
@@ -345,16 +236,10 @@ template <int EPI>
 hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* out, hipStream_t s) {
   // rows of W the kernel walks: N (store/add) or 2N (silu_mul)
   const int wrows = (EPI == kEpiSiluMul) ? 2 * N : N;
-  if (M <= 64) {
-    dim3 grid(wrows / kSkRows);
-    if (M <= 16) gemm_skinny_bf16<1, EPI><<<grid, kSkWaves * kWave, 0, s>>>(x, M, w, K, out, N);
-    else if (M <= 32) gemm_skinny_bf16<2, EPI><<<grid, kSkWaves * kWave, 0, s>>>(x, M, w, K, out, N);
-    else gemm_skinny_bf16<4, EPI><<<grid, kSkWaves * kWave, 0, s>>>(x, M, w, K, out, N);
-  } else {
-    const int num_m = (M + kTBM - 1) / kTBM;
-    dim3 grid(num_m * (wrows / kTBN));
-    gemm_tile_bf16<EPI><<<grid, kTThreads, 0, s>>>(x, M, w, wrows, K, out, N);
-  }
+  if (M <= 64) return launch_skinny(x, w, M, N, K, EPI, skinny_plan(M, wrows, K, false), out, s);
+  const int num_m = (M + kTBM - 1) / kTBM;
+  dim3 grid(num_m * (wrows / kTBN));
+  gemm_tile_bf16<EPI><<<grid, kTThreads, 0, s>>>(x, M, w, wrows, K, out, N);
   return hipGetLastError();
 }
 

@@ -1,0 +1,253 @@
+// Weight-streaming projections for few tokens (decode: M <= 64 rows of x).
+//
+// Same product as gemm.hip, y = x W^T with W stored [out, in] (vllm-learning
+// page "模型库与算子层 — 代码走读", section "Linear 层"), but here every
+// weight byte is used by at most 64 tokens, so the kernel is bound by
+// streaming W from HBM once.  Design:
+//   * a workgroup owns 4 waves x NT 16-row tiles of W and one K range
+//     (split-K across workgroups when W has few rows, so that enough
+//     workgroups stream concurrently);
+//   * the x slice of the current K chunk (M x KC) is staged once per
+//     workgroup in XOR-swizzled LDS and shared by the 4 waves, so global
+//     memory traffic is W plus a small fraction of x;
+//   * W fragments are loaded straight from global memory into MFMA operand
+//     registers (A = W rows, 16-byte loads, 64 contiguous bytes per row per
+//     instruction), one full chunk ahead of the MFMAs that use them;
+//   * v_mfma_f32_16x16x32_bf16 computes D[n][m] = W[n,:] . x[m,:]; a lane
+//     ends with four consecutive output features of one token.
+// Epilogues: bf16 store, residual add (in place), SiluAndMul on the re-ordered
+// gate_up weight (each 32-row group = 16 gate rows then 16 up rows), or fp32
+// partial sums [split][M][N] that the consumer reduces in split order
+// (deterministic: no atomics).
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+template <int MT, int NT, int KC, int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_skinny_bf16(const bf16* __restrict__ X, int M,
+                                                             const bf16* __restrict__ W, int K, int kps,
+                                                             void* __restrict__ out, int N) {
+  constexpr int SPC = KC / 32;          // MFMA k-steps per chunk
+  constexpr int XR = MT * 16;           // token rows staged
+  constexpr int XCH = XR * KC / 8;      // 16-byte pieces of the x chunk
+  constexpr int XPT = (XCH + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) bf16 sx[2][XR * KC];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n0 = (blockIdx.x * 4 + wave) * NT * 16;  // this wave's first weight row
+  const int k0 = blockIdx.y * kps;
+  const int nchunk = kps / KC;
+
+  auto xaddr = [](int row, int c) { return row * KC + ((c ^ (row & 7)) << 3); };
+  const bf16x8 zero8 = {};
+  bf16x8 xs[XPT];
+  auto xload = [&](int kc) {
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int id = threadIdx.x + kThreads * j;
+      const int row = id / (KC / 8), c = id % (KC / 8);
+      xs[j] = (id < XCH && row < M) ? ld16<bf16x8>(X + (size_t)row * K + k0 + kc + c * 8) : zero8;
+    }
+  };
+  auto xstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int id = threadIdx.x + kThreads * j;
+      const int row = id / (KC / 8), c = id % (KC / 8);
+      if (id < XCH) *reinterpret_cast<bf16x8*>(&sx[buf][xaddr(row, c)]) = xs[j];
+    }
+  };
+
+  const bf16* wr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) wr[t] = W + (size_t)(n0 + 16 * t + r16) * K + k0 + g * 8;
+  bf16x8 wn[SPC][NT];
+  auto wload = [&](int kc) {
+#pragma unroll
+    for (int s = 0; s < SPC; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wn[s][t] = ld16<bf16x8>(wr[t] + kc + s * 32);
+  };
+
+  f32x4 acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  wload(0);
+  xload(0);
+  xstore(0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    bf16x8 wc[SPC][NT];
+#pragma unroll
+    for (int s = 0; s < SPC; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wc[s][t] = wn[s][t];
+    if (c + 1 < nchunk) {
+      wload((c + 1) * KC);
+      xload((c + 1) * KC);
+    }
+#pragma unroll
+    for (int s = 0; s < SPC; ++s) {
+      bf16x8 xf[MT];
+#pragma unroll
+      for (int u = 0; u < MT; ++u)
+        xf[u] = *reinterpret_cast<const bf16x8*>(&sx[c & 1][xaddr(16 * u + r16, s * 4 + g)]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int u = 0; u < MT; ++u) acc[t][u] = mfma16(wc[s][t], xf[u], acc[t][u]);
+    }
+    if (c + 1 < nchunk) xstore((c + 1) & 1);
+    __syncthreads();
+  }
+
+  // lane holds features n0 + 16t + 4g + (0..3) of token 16u + r16
+#pragma unroll
+  for (int u = 0; u < MT; ++u) {
+    const int m = 16 * u + r16;
+    if (m >= M) continue;
+    if (EPI == kEpiPartial) {
+      float* dst = reinterpret_cast<float*>(out) + ((size_t)blockIdx.y * M + m) * N;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(dst + n0 + 16 * t + 4 * g) = acc[t][u];
+    } else if (EPI == kEpiSiluMul) {
+      bf16* dst = reinterpret_cast<bf16*>(out) + (size_t)m * N;
+#pragma unroll
+      for (int t = 0; t < NT; t += 2) {
+        const int f = ((n0 + 16 * t) >> 5) * 16 + 4 * g;
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(silu_f(acc[t][u][r]) * acc[t + 1][u][r]);
+        *reinterpret_cast<bf16x4*>(dst + f) = o;
+      }
+    } else {
+      bf16* dst = reinterpret_cast<bf16*>(out) + (size_t)m * N;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        bf16x4* p = reinterpret_cast<bf16x4*>(dst + n0 + 16 * t + 4 * g);
+        bf16x4 o;
+        if (EPI == kEpiAdd) {
+          const bf16x4 prev = *p;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[t][u][r] + static_cast<float>(prev[r]));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[t][u][r]);
+        }
+        *p = o;
+      }
+    }
+  }
+}
+
+// out[m][n] = bf16(sum over splits of part[s][m][n]), four features per thread
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int M, int N,
+                                                            bf16* __restrict__ out) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const size_t total = (size_t)M * N;
+  if (i >= total) return;
+  f32x4 a = *reinterpret_cast<const f32x4*>(part + i);
+  for (int s = 1; s < S; ++s) {
+    const f32x4 b = *reinterpret_cast<const f32x4*>(part + (size_t)s * total + i);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] += b[r];
+  }
+  bf16x4 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(a[r]);
+  *reinterpret_cast<bf16x4*>(out + i) = o;
+}
+
+template <int MT, int NT, int KC>
+hipError_t launch3(const bf16* x, int M, const bf16* w, int K, int kps, int epi, void* out, int N, dim3 grid,
+                   hipStream_t s) {
+  switch (epi) {
+    case kEpiStore:
+      gemm_skinny_bf16<MT, NT, KC, kEpiStore><<<grid, kThreads, 0, s>>>(x, M, w, K, kps, out, N);
+      break;
+    case kEpiAdd:
+      gemm_skinny_bf16<MT, NT, KC, kEpiAdd><<<grid, kThreads, 0, s>>>(x, M, w, K, kps, out, N);
+      break;
+    case kEpiSiluMul:
+      gemm_skinny_bf16<MT, NT, KC, kEpiSiluMul><<<grid, kThreads, 0, s>>>(x, M, w, K, kps, out, N);
+      break;
+    default:
+      gemm_skinny_bf16<MT, NT, KC, kEpiPartial><<<grid, kThreads, 0, s>>>(x, M, w, K, kps, out, N);
+  }
+  return hipGetLastError();
+}
+
+template <int MT, int NT>
+hipError_t launch_kc(int kc, const bf16* x, int M, const bf16* w, int K, int kps, int epi, void* out, int N,
+                     dim3 grid, hipStream_t s) {
+  if (kc == 256) return launch3<MT, NT, 256>(x, M, w, K, kps, epi, out, N, grid, s);
+  if (kc == 128) return launch3<MT, NT, 128>(x, M, w, K, kps, epi, out, N, grid, s);
+  return launch3<MT, NT, 64>(x, M, w, K, kps, epi, out, N, grid, s);
+}
+
+}  // namespace
+
+SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split) {
+  SkinnyPlan p;
+  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  // very tall weights (gate_up of the 70B shape): 64 rows per wave, no split
+  const bool tall = p.mt == 2 && wrows % 256 == 0 && wrows >= 49152 && K % 256 == 0;
+  p.nt = tall ? 4 : 2;
+  const int tiles = wrows / (64 * p.nt);
+  p.splits = 1;
+  if (allow_split && tiles < 192) {
+    for (int s : {8, 4, 2})
+      if (K % (s * 64) == 0) {
+        p.splits = s;
+        break;
+      }
+  }
+  const int kps = K / p.splits;
+  if (tall) p.kc = 256;
+  else if (p.mt == 2) p.kc = kps % 128 == 0 ? 128 : 64;
+  else p.kc = kps % 256 == 0 ? 256 : (kps % 128 == 0 ? 128 : 64);
+  return p;
+}
+
+hipError_t launch_skinny(const void* x, const void* w, int M, int N, int K, int epi, const SkinnyPlan& p,
+                         void* out, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  const int wrows = epi == kEpiSiluMul ? 2 * N : N;
+  if (M > 64 || wrows % (64 * p.nt) != 0 || K % (p.splits * p.kc) != 0) return hipErrorInvalidValue;
+  if (epi == kEpiSiluMul && p.splits != 1) return hipErrorInvalidValue;
+  if (p.splits != 1 && epi != kEpiPartial) return hipErrorInvalidValue;
+  dim3 grid(wrows / (64 * p.nt), p.splits);
+  const int kps = K / p.splits;
+  const bf16* xb = (const bf16*)x;
+  const bf16* wb = (const bf16*)w;
+  if (p.mt == 1) return launch_kc<1, 2>(p.kc, xb, M, wb, K, kps, epi, out, N, grid, s);
+  if (p.mt == 2) {
+    if (p.nt == 4) return launch3<2, 4, 256>(xb, M, wb, K, kps, epi, out, N, grid, s);
+    return launch_kc<2, 2>(p.kc, xb, M, wb, K, kps, epi, out, N, grid, s);
+  }
+  return launch_kc<4, 2>(p.kc, xb, M, wb, K, kps, epi, out, N, grid, s);
+}
+
+hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, void* out, hipStream_t s) {
+  const size_t total = (size_t)M * N;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total / 4 + 255) / 256);
+  splitk_reduce_kernel<<<blocks, 256, 0, s>>>(part, S, M, N, (bf16*)out);
+  return hipGetLastError();
+}
+
+}  // namespace llk

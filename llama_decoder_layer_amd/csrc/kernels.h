@@ -7,11 +7,13 @@
 namespace llk {
 
 enum Dtype { kBF16 = 0, kFP32 = 1 };
-enum Epi { kEpiStore = 0, kEpiAdd = 1, kEpiSiluMul = 2 };
+enum Epi { kEpiStore = 0, kEpiAdd = 1, kEpiSiluMul = 2, kEpiPartial = 3 };
 
-// rmsnorm.hip
+// rmsnorm.hip.  With xpart != NULL (bf16 only) the input row is the sum of
+// S fp32 partial rows xpart[s][row][:] instead of x.
 hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* res, const void* w, float eps,
-                              int rows, int hidden, void* normed, void* res_out, hipStream_t s);
+                              int rows, int hidden, void* normed, void* res_out, hipStream_t s,
+                              const float* xpart = nullptr, int S = 0);
 
 // gemm.hip: out = x W^T with an epilogue; picks the skinny (M <= 64) or the
 // tiled kernel.
@@ -20,10 +22,23 @@ hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, 
 hipError_t launch_reorder_gate_up(const void* src, int inter, int K, void* dst, hipStream_t s);
 const char* linear_kernel_name(int dtype, int M);
 
-// rope_kv.hip
+// gemm_skinny.hip: bf16, M <= 64.  N = output features (SiluMul: W has 2N
+// rows).  kEpiPartial writes fp32 partial sums [splits][M][N].
+struct SkinnyPlan {
+  int mt, nt, kc, splits;
+};
+SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split);
+hipError_t launch_skinny(const void* x, const void* w, int M, int N, int K, int epi, const SkinnyPlan& p,
+                         void* out, hipStream_t s);
+hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, void* out, hipStream_t s);
+
+// rope_kv.hip.  With part != NULL (bf16 only) the projection row is first
+// formed as the bf16 rounding of the sum of S fp32 partial rows and stored
+// into qkv.
 hipError_t launch_rope_kv(int dtype, void* qkv, int T, const int* positions, const float2* table,
                           int nq, int nkv, int d, const int* block_table, int max_blocks, int q_len,
-                          void* k_cache, void* v_cache, hipStream_t s);
+                          void* k_cache, void* v_cache, hipStream_t s, const float* part = nullptr,
+                          int S = 0);
 
 // attention.hip
 struct AttnPlan {

@@ -10,6 +10,9 @@
 //
 // HBM-bound: one workgroup per row, 16-byte loads, the row kept in registers
 // between the reduction and the scaling, a wave-shuffle then LDS reduction.
+// After a split-K o_proj the kernel also finishes that projection: it sums
+// the fp32 partial rows, adds the residual, rounds, stores the new residual
+// and normalises it (post_attention_layernorm) in one pass.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,12 +22,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxChunks = 8;  // 16-byte chunks per thread -> H <= 256*8*VEC
 
-template <typename T>
+// S > 0: the input row is the sum of S fp32 partial rows xpart[s][row][:]
+// (a split-K projection's output), added in split order.
+template <typename T, int S>
 __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const T* __restrict__ x,
-                                                               const T* __restrict__ res,
+                                                               const T* res,
                                                                const T* __restrict__ w, float eps,
                                                                int H, T* __restrict__ normed,
-                                                               T* res_out) {
+                                                               T* res_out, const float* __restrict__ xpart,
+                                                               int rows) {
   using V = typename Vec16<T>::type;
   constexpr int VN = Vec16<T>::N;
   const int row = blockIdx.x;
@@ -37,20 +43,47 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const T* __restri
   for (int c = 0; c < kMaxChunks; ++c) {
     const int ci = threadIdx.x + c * kThreads;
     if (ci < nchunk) {
-      V xv = ld16<V>(x + base + (size_t)ci * VN);
+      float xf[VN];
+      V xv;
+      if (S > 0) {
+#pragma unroll
+        for (int e = 0; e < VN; e += 4) {
+          f32x4 v[S > 0 ? S : 1];
+#pragma unroll
+          for (int sp = 0; sp < S; ++sp)
+            v[sp] = *reinterpret_cast<const f32x4*>(xpart + (size_t)sp * rows * H + base + (size_t)ci * VN + e);
+          f32x4 a = v[0];
+#pragma unroll
+          for (int sp = 1; sp < S; ++sp)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[q] += v[sp][q];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xf[e + q] = a[q];
+        }
+      } else {
+        xv = ld16<V>(x + base + (size_t)ci * VN);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) xf[e] = to_f32(xv[e]);
+      }
       V ov;
       if (res != nullptr) {
         V rv = ld16<V>(res + base + (size_t)ci * VN);
 #pragma unroll
         for (int e = 0; e < VN; ++e) {
-          T s = from_f32<T>(to_f32(xv[e]) + to_f32(rv[e]));
+          T s = from_f32<T>(xf[e] + to_f32(rv[e]));
           ov[e] = s;
           r[c][e] = to_f32(s);
+        }
+      } else if (S > 0) {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+          ov[e] = from_f32<T>(xf[e]);
+          r[c][e] = to_f32(ov[e]);
         }
       } else {
         ov = xv;
 #pragma unroll
-        for (int e = 0; e < VN; ++e) r[c][e] = to_f32(xv[e]);
+        for (int e = 0; e < VN; ++e) r[c][e] = xf[e];
       }
       if (res_out != nullptr) *reinterpret_cast<V*>(res_out + base + (size_t)ci * VN) = ov;
 #pragma unroll
@@ -83,15 +116,27 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const T* __restri
 }  // namespace
 
 hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* res, const void* w, float eps,
-                              int rows, int hidden, void* normed, void* res_out, hipStream_t s) {
+                              int rows, int hidden, void* normed, void* res_out, hipStream_t s,
+                              const float* xpart, int S) {
   if (rows <= 0) return hipSuccess;
   if (dtype == kBF16) {
-    add_rmsnorm_kernel<bf16><<<rows, kThreads, 0, s>>>(
-        (const bf16*)x, (const bf16*)res, (const bf16*)w, eps, hidden, (bf16*)normed, (bf16*)res_out);
+    const bf16* r = (const bf16*)res;
+    const bf16* wb = (const bf16*)w;
+    bf16* n = (bf16*)normed;
+    bf16* ro = (bf16*)res_out;
+#define LLK_NORM(SS, XX) add_rmsnorm_kernel<bf16, SS><<<rows, kThreads, 0, s>>>((const bf16*)(XX), r, wb, eps, hidden, n, ro, xpart, rows)
+    if (!xpart) LLK_NORM(0, x);
+    else if (S == 1) LLK_NORM(1, nullptr);
+    else if (S == 2) LLK_NORM(2, nullptr);
+    else if (S == 4) LLK_NORM(4, nullptr);
+    else if (S == 8) LLK_NORM(8, nullptr);
+    else return hipErrorInvalidValue;
+#undef LLK_NORM
   } else {
-    add_rmsnorm_kernel<float><<<rows, kThreads, 0, s>>>(
-        (const float*)x, (const float*)res, (const float*)w, eps, hidden, (float*)normed,
-        (float*)res_out);
+    if (xpart) return hipErrorInvalidValue;
+    add_rmsnorm_kernel<float, 0><<<rows, kThreads, 0, s>>>(
+        (const float*)x, (const float*)res, (const float*)w, eps, hidden, (float*)normed, (float*)res_out,
+        nullptr, rows);
   }
   return hipGetLastError();
 }

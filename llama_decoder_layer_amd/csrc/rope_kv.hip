@@ -15,21 +15,31 @@
 // p % 16: K plane [blocks][kv_heads][16][head_dim], V plane
 // [blocks][kv_heads][head_dim][16].  V is a bit copy of the projection's v.
 //
-// HBM-bound and tiny: one workgroup per token.  q is rotated in place inside
-// the qkv buffer.
+// HBM-bound and tiny: one workgroup per (token, 8 heads).  q is rotated in
+// place inside the qkv buffer.
 #include "common.h"
 #include "kernels.h"
 
 namespace llk {
 namespace {
 
-template <typename T>
+// One workgroup per (token, group of kHeads heads of the qkv row: q heads,
+// then k heads, then v heads).  S > 0: the group's part of the projection
+// row is first formed from S fp32 partial rows part[s][t][:] (a split-K qkv
+// projection), rounded once to the layer dtype, stored into qkv and staged
+// in LDS for the rotation.
+constexpr int kHeads = 8;
+
+template <typename T, int S>
 __global__ __launch_bounds__(256) void rope_kv_kernel(T* __restrict__ qkv, const int* __restrict__ positions,
                                                       const float2* __restrict__ table, int nq, int nkv,
                                                       int d, const int* __restrict__ block_table,
                                                       int max_blocks, int q_len, T* __restrict__ kc,
-                                                      T* __restrict__ vc) {
+                                                      T* __restrict__ vc, const float* __restrict__ part, int T_) {
+  __shared__ float srow[kHeads * 128];
   const int t = blockIdx.x;
+  const int h0 = blockIdx.y * kHeads;
+  const int nh = min(kHeads, nq + 2 * nkv - h0);
   const int half = d >> 1;
   const int ld = (nq + 2 * nkv) * d;
   const int p = positions[t];
@@ -38,46 +48,89 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(T* __restrict__ qkv, const
   const int row = p % kKvBlock;
   T* x = qkv + (size_t)t * ld;
   const float2* cs = table + (size_t)p * half;
+  const int e0 = h0 * d;          // first element of this head group in the row
+  const int ne = nh * d;
 
-  const int pairs = (nq + nkv) * half;
-  for (int idx = threadIdx.x; idx < pairs; idx += blockDim.x) {
-    const int head = idx / half;
-    const int i = idx - head * half;
-    const float2 c = cs[i];
-    const float x0 = to_f32(x[head * d + i]);
-    const float x1 = to_f32(x[head * d + i + half]);
-    const float y0 = fmaf(x0, c.x, -(x1 * c.y));
-    const float y1 = fmaf(x1, c.x, x0 * c.y);
-    if (head < nq) {
-      x[head * d + i] = from_f32<T>(y0);
-      x[head * d + i + half] = from_f32<T>(y1);
-    } else {
-      const int gk = head - nq;
-      T* dst = kc + (((size_t)blk * nkv + gk) * kKvBlock + row) * d;
-      dst[i] = from_f32<T>(y0);
-      dst[i + half] = from_f32<T>(y1);
+  if (S > 0) {
+    for (int i = threadIdx.x * 4; i < ne; i += blockDim.x * 4) {
+      f32x4 v[S > 0 ? S : 1];
+#pragma unroll
+      for (int sp = 0; sp < S; ++sp)
+        v[sp] = *reinterpret_cast<const f32x4*>(part + ((size_t)sp * T_ + t) * ld + e0 + i);
+      f32x4 a = v[0];
+#pragma unroll
+      for (int sp = 1; sp < S; ++sp)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[q] += v[sp][q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const T r = from_f32<T>(a[q]);
+        x[e0 + i + q] = r;
+        srow[i + q] = to_f32(r);
+      }
+    }
+    __syncthreads();
+  }
+  auto val = [&](int i) -> float { return S > 0 ? srow[i - e0] : to_f32(x[i]); };
+
+  for (int idx = threadIdx.x; idx < nh * half; idx += blockDim.x) {
+    const int head = h0 + idx / half;
+    const int i = idx % half;
+    if (head < nq + nkv) {  // q and k heads turn
+      const float2 c = cs[i];
+      const float x0 = val(head * d + i);
+      const float x1 = val(head * d + i + half);
+      const float y0 = fmaf(x0, c.x, -(x1 * c.y));
+      const float y1 = fmaf(x1, c.x, x0 * c.y);
+      if (head < nq) {
+        x[head * d + i] = from_f32<T>(y0);
+        x[head * d + i + half] = from_f32<T>(y1);
+      } else {
+        T* dst = kc + (((size_t)blk * nkv + (head - nq)) * kKvBlock + row) * d;
+        dst[i] = from_f32<T>(y0);
+        dst[i + half] = from_f32<T>(y1);
+      }
+    } else {  // v heads: a copy into the slot-contiguous V plane
+      const int gv = head - nq - nkv;
+      T* dst = vc + ((size_t)blk * nkv + gv) * d * kKvBlock + row;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = i + j * half;
+        dst[(size_t)e * kKvBlock] = S > 0 ? from_f32<T>(srow[head * d + e - e0]) : x[head * d + e];
+      }
     }
   }
-  const T* v = x + (size_t)(nq + nkv) * d;
-  for (int idx = threadIdx.x; idx < nkv * d; idx += blockDim.x) {
-    const int gv = idx / d;
-    const int e = idx - gv * d;
-    vc[(((size_t)blk * nkv + gv) * d + e) * kKvBlock + row] = v[idx];
-  }
+}
+
+template <typename T, int S>
+void launch_typed(T* qkv, int T_, const int* positions, const float2* table, int nq, int nkv, int d,
+                  const int* block_table, int max_blocks, int q_len, T* kc, T* vc, const float* part,
+                  hipStream_t s) {
+  dim3 grid(T_, (nq + 2 * nkv + kHeads - 1) / kHeads);
+  rope_kv_kernel<T, S><<<grid, 256, 0, s>>>(qkv, positions, table, nq, nkv, d, block_table, max_blocks, q_len,
+                                            kc, vc, part, T_);
 }
 
 }  // namespace
 
 hipError_t launch_rope_kv(int dtype, void* qkv, int T, const int* positions, const float2* table,
                           int nq, int nkv, int d, const int* block_table, int max_blocks, int q_len,
-                          void* k_cache, void* v_cache, hipStream_t s) {
+                          void* k_cache, void* v_cache, hipStream_t s, const float* part, int S) {
   if (T <= 0) return hipSuccess;
   if (dtype == kBF16) {
-    rope_kv_kernel<bf16><<<T, 256, 0, s>>>((bf16*)qkv, positions, table, nq, nkv, d, block_table,
-                                            max_blocks, q_len, (bf16*)k_cache, (bf16*)v_cache);
+    bf16* x = (bf16*)qkv;
+    bf16* kc = (bf16*)k_cache;
+    bf16* vc = (bf16*)v_cache;
+    if (!part) launch_typed<bf16, 0>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, nullptr, s);
+    else if (S == 1) launch_typed<bf16, 1>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, part, s);
+    else if (S == 2) launch_typed<bf16, 2>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, part, s);
+    else if (S == 4) launch_typed<bf16, 4>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, part, s);
+    else if (S == 8) launch_typed<bf16, 8>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, part, s);
+    else return hipErrorInvalidValue;
   } else {
-    rope_kv_kernel<float><<<T, 256, 0, s>>>((float*)qkv, positions, table, nq, nkv, d, block_table,
-                                             max_blocks, q_len, (float*)k_cache, (float*)v_cache);
+    if (part) return hipErrorInvalidValue;
+    launch_typed<float, 0>((float*)qkv, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len,
+                           (float*)k_cache, (float*)v_cache, nullptr, s);
   }
   return hipGetLastError();
 }
