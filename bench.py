@@ -45,31 +45,16 @@ def kernel_bytes(model, name, T, kv_tokens):
     }.get(name)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama70b_decode_b32_ctx2048")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=None,
-                    help="tokens of the step the oracle runs (default: all of a decode step, 256 of a prefill)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sequences shard across GPUs with no exchange inside the layer)", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def measure(wl, steps, warmup):
+    """Times `steps` forwards (after `warmup`) of workload `wl`, then the same
+    number again with the library's per-kernel HIP events on."""
     import torch
 
     import llama_decoder_layer_amd as lda
     import synth
 
-    wl = synth.WORKLOADS[args.workload]
     model = wl.model
     dev = "cuda"
-    torch.cuda.set_device(0)
     batch, hidden, residual, per_layer = synth.workload_tensors(wl, dev)
     pos, bt, sl = batch.positions.to(dev), batch.block_table.to(dev), batch.seq_lens.to(dev)
     layers = [lda.Layer(model.config_dict(), p["weights"]) for p in per_layer]
@@ -85,24 +70,24 @@ def main():
                       residual_out=ro, workspace=ws)
             h, r = ho, ro
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = t0.elapsed_time(t1) / steps
 
     # per-kernel durations: HIP events the library records on its stream
     for L in layers:
         L.set_timing(True)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     kt = {}
@@ -113,60 +98,98 @@ def main():
         L.set_timing(False)
     kernel_avg_ms = {k: v[0] / v[1] for k, v in kt.items()}
 
-    decode = wl.q_len == 1
-    kv_tokens = int(batch.seq_lens.sum())  # keys read by one layer's attention (decode)
+    kv_tokens = int(batch.seq_lens.sum())
     attn_pairs = sum(sum(c + j + 1 for j in range(wl.q_len)) for c in batch.ctx_lens)
-    tokens_per_step = T
-    value = tokens_per_step / (ms / 1e3)
-
-    if decode:
-        dom = "gate_up_silu"
+    dom = "gate_up_silu"
+    dur = kernel_avg_ms[dom] / 1e3
+    if wl.q_len == 1:
         alg = kernel_bytes(model, dom, T, kv_tokens)
-        dur = kernel_avg_ms[dom] / 1e3
         roof = {"bound": "hbm", "kernel": dom, "achieved": alg / dur / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": alg / dur / 1e9 / PEAK_HBM_GBS, "traffic": None,
-                "algorithmic_bytes": alg, "avg_launch_us": dur * 1e6}
+                "algorithmic_bytes_per_launch": alg, "avg_launch_us": dur * 1e6}
     else:
-        dom = "gate_up_silu"
         H, I = model.hidden_size, model.intermediate_size
         alg = 2 * T * H * 2 * I
-        dur = kernel_avg_ms[dom] / 1e3
         roof = {"bound": "mfma", "kernel": dom, "achieved": alg / dur / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": alg / dur / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
-                "algorithmic_flops": alg, "avg_launch_us": dur * 1e6}
-
-    # whole-layer fractions of the roofline
+                "algorithmic_flops_per_launch": alg, "avg_launch_us": dur * 1e6}
     step_bytes = len(layers) * (sum(v.numel() * v.element_size() for v in per_layer[0]["weights"].values())
                                 + kv_tokens * 2 * model.kv_size * 2 + 4 * T * model.hidden_size * 2)
     step_flops = len(layers) * layer_flops(model, T, attn_pairs)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        rows = args.cpu_sample_rows or (T if wl.q_len == 1 else 256)
-        cpu = cpu_baseline(wl, batch, hidden, residual, per_layer, rows)
-
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if model.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1) activations and KV context, N(0,0.02) weights)",
-        "config": {"workload": wl.name, "num_seqs": B, "q_len": wl.q_len,
-                   "ctx_len": wl.ctx if not isinstance(wl.ctx, tuple) else list(wl.ctx),
-                   "layers": len(layers), "parallelism": "single GPU"},
+    res = {
+        "workload": wl.name, "value": round(T / (ms / 1e3), 2), "unit": "tokens/s", "ms_per_step": round(ms, 4),
         "roofline": roof,
         "step_fraction": {"hbm": step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
                           "mfma": step_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS},
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in sorted(kernel_avg_ms.items())},
-        "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),
+        "config": {"workload": wl.name, "num_seqs": B, "q_len": wl.q_len,
+                   "ctx_len": wl.ctx if not isinstance(wl.ctx, tuple) else list(wl.ctx),
+                   "layers": len(layers), "parallelism": "single GPU"},
+    }
+    ctx = (batch, hidden, residual, per_layer)
+    return res, ctx
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama70b_decode_b32_ctx2048")
+    ap.add_argument("--extra", default="llama70b_prefill_4x2048",
+                    help="comma-separated workloads measured after the main one ('none' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=None,
+                    help="tokens of the step the oracle runs (default: all of a decode step, 256 of a prefill)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange inside the layer)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    main_res, ctx = measure(wl, args.steps, args.warmup)
+    cpu = None
+    if not args.no_cpu_baseline:
+        batch, hidden, residual, per_layer = ctx
+        rows = args.cpu_sample_rows or (batch.num_tokens if wl.q_len == 1 else 256)
+        cpu = cpu_baseline(wl, batch, hidden, residual, per_layer, rows)
+    del ctx
+    torch.cuda.empty_cache()
+    extra = []
+    if args.extra and args.extra != "none":
+        for name in args.extra.split(","):
+            r, c = measure(synth.WORKLOADS[name], max(3, args.steps // 4), min(args.warmup, 2))
+            del c
+            torch.cuda.empty_cache()
+            extra.append(r)
+
+    out = {
+        "metric": METRIC,
+        "value": main_res["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.model.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations and KV context, N(0,0.02) weights)",
+        "config": main_res["config"],
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "step_fraction": main_res["step_fraction"],
+        "kernel_avg_us": main_res["kernel_avg_us"],
+        "wall_s_timed_region": main_res["wall_s_timed_region"],
+        "extra": extra,
     }
     print(json.dumps(out))
 

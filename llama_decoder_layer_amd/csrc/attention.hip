@@ -239,6 +239,9 @@ hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int*
   if (dtype == kBF16 && q_len == 1) {
     e = launch_decode_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table,
                                      max_blocks, q_len, plan.part_len, plan.parts, partials, out, s);
+  } else if (dtype == kBF16 && plan.parts == 1 && prefill_attention_supported(nq, nkv, d)) {
+    return launch_prefill_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table,
+                                         max_blocks, q_len, out, s);
   } else if (dtype == kBF16) {
     e = d == 128 ? attention_typed<bf16, 128>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
                                               (const bf16*)v_cache, block_table, max_blocks, q_len, plan,

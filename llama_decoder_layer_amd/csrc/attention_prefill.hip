@@ -1,0 +1,301 @@
+// Prefill (many query tokens per sequence) causal GQA attention over the
+// paged KV cache, bf16, flash-style on the matrix cores.
+//
+// Computes, for every new token of a sequence at position p and query head h
+// of KV group g (G = heads / kv_heads query heads per group),
+//     o_h = sum_{j<=p} softmax_j(q_h . k_j / sqrt(d)) v_j
+// -- pages "LLama" (hotelren.com/news/2693952), section "4 LlamaAttention";
+// "模型库与算子层 — 代码走读" (vllm-learning.pages.dev), section "Attention 层"
+// (the new K/V are in the cache before attention reads it, through the
+// block table).  The keys of a query are the sequence's cached context plus
+// its own new tokens up to and including itself.
+//
+// One workgroup = (sequence, KV head g, tile of 16 consecutive query tokens);
+// its 4 waves each take G/4 query heads of the group, so every K/V tile is
+// staged in LDS once for all G heads.  The key loop walks 64-key tiles (four
+// 16-slot cache blocks) with an online softmax in fp32 (exp2 of
+// log2(e)/sqrt(d)-scaled scores), only up to the tile's last query position
+// (causal tile skipping); the diagonal tiles mask key > query position.
+// With v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T : A = 16 keys x 32 d from LDS, B = the 16 queries' q from
+//       registers.  Lane (query = l%16, grp = l/16) receives keys
+//       4*grp .. 4*grp+3 of each 16-key slice.
+//   O += P V    : A = P: lane (query, grp) supplies as its 8 k-slots its own
+//       keys of two 16-key slices -- no data movement for P.  B = V: the LDS
+//       copy of the V tile stores each component's 64 keys in the permuted
+//       order that puts exactly those 8 keys side by side, so the operand is
+//       one 16-byte read (XOR-swizzled rows keep the reads conflict-free).
+// Keys past the sequence's last written slot are staged as zeros, never read
+// from the cache.
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kQ = 16;         // query tokens per workgroup
+constexpr int kKT = 64;        // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// K tile in LDS: [64 keys][D] bf16, 16-byte chunks XOR-swizzled by key.
+template <int D>
+__device__ __forceinline__ int k_off(int key, int c) {
+  constexpr int CH = D / 8;  // chunks per key row
+  return key * D + ((c ^ (key & (CH - 1))) << 3);
+}
+// V tile in LDS: [D][64] bf16; key k = 32m + 16h + 4grp + r sits at
+// position 32m + 8grp + 4h + r; 16-byte chunks XOR-swizzled by component.
+__device__ __forceinline__ int v_pos(int key) {
+  const int m = key >> 5, h = (key >> 4) & 1, grp = (key >> 2) & 3, r = key & 3;
+  return 32 * m + 8 * grp + 4 * h + r;
+}
+__device__ __forceinline__ int v_off(int d, int pos) {
+  return d * kKT + ((((pos >> 3) ^ (d & 7)) << 3) | (pos & 7));
+}
+
+template <int D, int HPW>
+__global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
+    const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
+    const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
+    int max_blocks, int q_len, int num_qtiles, bf16* __restrict__ out) {
+  constexpr int KS = D / 32;   // d-steps of S^T
+  constexpr int DT = D / 16;   // 16-wide d tiles of O
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][kKT * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][D * kKT];
+
+  const int G = nq / nkv;
+  // longest query tiles first
+  const int qt = num_qtiles - 1 - (int)(blockIdx.x % num_qtiles);
+  const int b = blockIdx.x / num_qtiles;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+
+  const int t0 = b * q_len + qt * kQ;                       // first token row of the tile
+  const int nvalid = min(kQ, q_len - qt * kQ);              // query rows of the tile
+  const int p0 = positions[t0];                             // position of the tile's first query
+  const int p_last = positions[b * q_len + q_len - 1];      // last written key of the sequence
+  const int key_end = min(p0 + kQ - 1, p_last) + 1;         // keys this tile needs
+  const int ntiles = (key_end + kKT - 1) / kKT;
+  const int* bt = block_table + (size_t)b * max_blocks;
+  const size_t head_stride = (size_t)kKvBlock * D;
+
+  // q fragments (B operand of S^T): query l16, d = 32s + 8grp
+  const bf16x8 zero8 = {};
+  bf16x8 qf[HPW][KS];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = g * G + wave * HPW + hh;
+    const bool ok = l16 < nvalid;
+    const bf16* src = q + (size_t)(t0 + (ok ? l16 : 0)) * ldq + (size_t)h * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[hh][s] = ok ? ld16<bf16x8>(src + 32 * s) : zero8;
+  }
+
+  // staging: K tile = 64 keys x D (D/8 chunks per key); V tile = 4 blocks of [D][16]
+  constexpr int KCH = kKT * D / 8;                 // 16-byte chunks per K tile
+  constexpr int KPT = KCH / (kWaves * kWave);      // per thread
+  constexpr int VCH = D * 4 * 2;                   // (d, block, half) 16-byte chunks per V tile
+  constexpr int VPT = VCH / (kWaves * kWave);
+  bf16x8 kst[KPT], vst[VPT];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int id = threadIdx.x + i * kWaves * kWave;
+      const int key = id / (D / 8), c = id % (D / 8);
+      const int pos = kt * kKT + key;
+      if (pos < key_end) {
+        const int blk = bt[pos / kKvBlock];
+        kst[i] = ld16<bf16x8>(kc + ((size_t)blk * nkv + g) * head_stride + (size_t)(pos % kKvBlock) * D + c * 8);
+      } else {
+        kst[i] = zero8;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int id = threadIdx.x + i * kWaves * kWave;
+      const int half = id & 1, j = (id >> 1) & 3, d = id >> 3;
+      const int pos = kt * kKT + j * kKvBlock + half * 8;  // first of 8 keys
+      if (pos < key_end) {
+        const int blk = bt[pos / kKvBlock];
+        bf16x8 v = ld16<bf16x8>(vc + ((size_t)blk * nkv + g) * head_stride + (size_t)d * kKvBlock + half * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (pos + e >= key_end) v[e] = static_cast<bf16>(0.f);
+        vst[i] = v;
+      } else {
+        vst[i] = zero8;
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int id = threadIdx.x + i * kWaves * kWave;
+      const int key = id / (D / 8), c = id % (D / 8);
+      *reinterpret_cast<bf16x8*>(&sK[buf][k_off<D>(key, c)]) = kst[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int id = threadIdx.x + i * kWaves * kWave;
+      const int half = id & 1, j = (id >> 1) & 3, d = id >> 3;
+      const int key0 = j * kKvBlock + half * 8;  // keys key0 .. key0+7 = two groups of 4
+#pragma unroll
+      for (int q4 = 0; q4 < 2; ++q4) {
+        bf16x4 piece;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) piece[r] = vst[i][4 * q4 + r];
+        *reinterpret_cast<bf16x4*>(&sV[buf][v_off(d, v_pos(key0 + 4 * q4))]) = piece;
+      }
+    }
+  };
+
+  const float sc = kLog2e / sqrtf((float)D);
+  float m_run[HPW], l_run[HPW];
+  f32x4 o[HPW][DT];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int pq = p0 + l16;  // this lane's query position (S^T layout)
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) gload(kt + 1);
+
+    // S^T for each head: 4 slices of 16 keys
+    f32x4 s4[HPW][4];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s4[hh][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][k_off<D>(16 * j + l16, 4 * s + grp)]);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) s4[hh][j] = mfma16(kf, qf[hh][s], s4[hh][j]);
+      }
+    }
+    const bool diag = kt * kKT + kKT - 1 > p0;  // some key may follow some query
+    bf16x8 pa[HPW][2];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      float sv[4][4];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt * kKT + 16 * j + 4 * grp + r;
+          float v = s4[hh][j][r] * sc;
+          if (diag && key > pq) v = -INFINITY;
+          sv[j][r] = v;
+          bm = fmaxf(bm, v);
+        }
+      bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+      const float m_new = fmaxf(m_run[hh], bm);
+      const float alpha = exp2f(m_run[hh] - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = exp2f(sv[j][r] - m_new);
+          ps += pv;
+          pa[hh][j >> 1][4 * (j & 1) + r] = static_cast<bf16>(pv);
+        }
+      l_run[hh] = l_run[hh] * alpha + ps;
+      m_run[hh] = m_new;
+      float ah[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ah[r] = __shfl(alpha, 4 * grp + r, kWave);
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[hh][i][r] *= ah[r];
+    }
+    // O += P V : two 32-key halves, DT d-tiles
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh) {
+#pragma unroll
+      for (int i = 0; i < DT; ++i) {
+        const int d = 16 * i + l16;
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][v_off(d, 32 * mh + 8 * grp)]);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) o[hh][i] = mfma16(pa[hh][mh], vf, o[hh][i]);
+      }
+    }
+    if (kt + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // normalise and store: lane holds O[query 4grp + r][d = 16i + l16]
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    float lt = l_run[hh];
+    lt += __shfl_xor(lt, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
+    const int h = g * G + wave * HPW + hh;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qi = 4 * grp + r;
+      const float inv = 1.0f / __shfl(lt, qi, kWave);
+      if (qi < nvalid) {
+        bf16* dst = out + (size_t)(t0 + qi) * nq * D + (size_t)h * D + l16;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) dst[16 * i] = static_cast<bf16>(o[hh][i][r] * inv);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool prefill_attention_supported(int nq, int nkv, int d) {
+  const int G = nq / nkv;
+  return (d == 64 || d == 128) && (G == 4 || G == 8 || G == 16);
+}
+
+hipError_t launch_prefill_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
+                                         int d, const void* k_cache, const void* v_cache, const int* block_table,
+                                         int max_blocks, int q_len, void* out, hipStream_t s) {
+  const int G = nq / nkv;
+  const int B = T / q_len;
+  const int nqt = (q_len + kQ - 1) / kQ;
+  dim3 grid(B * nqt, nkv);
+  const bf16* qb = (const bf16*)q;
+  const bf16* kb = (const bf16*)k_cache;
+  const bf16* vb = (const bf16*)v_cache;
+  bf16* ob = (bf16*)out;
+#define LLK_PF(DD, HH)                                                                                    \
+  prefill_attention_mfma<DD, HH><<<grid, kWaves * kWave, 0, s>>>(qb, ldq, positions, nq, nkv, kb, vb,    \
+                                                                 block_table, max_blocks, q_len, nqt, ob)
+  if (d == 128) {
+    if (G == 4) LLK_PF(128, 1);
+    else if (G == 8) LLK_PF(128, 2);
+    else LLK_PF(128, 4);
+  } else {
+    if (G == 4) LLK_PF(64, 1);
+    else if (G == 8) LLK_PF(64, 2);
+    else LLK_PF(64, 4);
+  }
+#undef LLK_PF
+  return hipGetLastError();
+}
+
+}  // namespace llk

@@ -59,4 +59,10 @@ hipError_t launch_decode_attention_bf16(const void* q, int ldq, int T, const int
                                         int max_blocks, int q_len, int part_len, int parts, float* partials,
                                         void* out, hipStream_t s);
 
+// attention_prefill.hip (bf16, q_len > 1, G in {4, 8, 16})
+bool prefill_attention_supported(int nq, int nkv, int d);
+hipError_t launch_prefill_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
+                                         int d, const void* k_cache, const void* v_cache, const int* block_table,
+                                         int max_blocks, int q_len, void* out, hipStream_t s);
+
 }  // namespace llk

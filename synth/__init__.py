@@ -276,10 +276,13 @@ def scatter_context(pool: torch.Tensor, batch: Batch, b: int, ctx: torch.Tensor,
     the paged pool at positions 0..L-1."""
     view = _slot_major(pool, plane)
     L = ctx.shape[0]
-    for j in range(0, (L + KV_BLOCK - 1) // KV_BLOCK):
-        blk = int(batch.block_table[b, j])
-        n = min(KV_BLOCK, L - j * KV_BLOCK)
-        view[blk, :, :n, :] = ctx[j * KV_BLOCK: j * KV_BLOCK + n].transpose(0, 1)
+    full, rem = L // KV_BLOCK, L % KV_BLOCK
+    if full:
+        ids = batch.block_table[b, :full].long().to(pool.device)
+        view[ids] = ctx[: full * KV_BLOCK].reshape(full, KV_BLOCK, ctx.shape[1], ctx.shape[2]).transpose(1, 2)
+    if rem:
+        blk = int(batch.block_table[b, full])
+        view[blk, :, :rem, :] = ctx[full * KV_BLOCK:].transpose(0, 1)
 
 
 def gather_context(pool: torch.Tensor, batch: Batch, b: int, length: int, plane: str = "k") -> torch.Tensor:

@@ -12,6 +12,9 @@ that much plus the stated arithmetic budget:
   * max|gpu - exact| <= max|R - exact| + 1e-2 * RMS(exact);
   * RMS(gpu - exact) <= 2 * RMS(R - exact) + 1e-3 * RMS(exact)  (a guard
     against small systematic errors that the max would hide).
+In a chain of layers the budget is per layer: the output of the l-th layer
+(l = 0, 1, ...) carries the arithmetic of l+1 layers and is allowed
+(l+1) * 1e-2 * RMS (and (l+1) * 1e-3 in the RMS guard) on top of R's distance.
 With no R (a single kernel whose only storage point is its own output) the
 max criterion is max(|gpu - exact| - ulp_bf16/2) <= 1e-2 * RMS(exact).
 A literal max|gpu - exact| <= 1e-2 * RMS cannot hold for bf16 outputs of this
@@ -51,7 +54,7 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
 
 
 def compare(name: str, gpu: np.ndarray, ref_exact: np.ndarray, ref_r: np.ndarray = None,
-            dtype: str = "bf16") -> dict:
+            dtype: str = "bf16", depth: int = 1) -> dict:
     """Asserts the tolerance; returns the statistics."""
     gpu = np.asarray(gpu, np.float64)
     assert gpu.shape == ref_exact.shape, (name, gpu.shape, ref_exact.shape)
@@ -76,8 +79,8 @@ def compare(name: str, gpu: np.ndarray, ref_exact: np.ndarray, ref_r: np.ndarray
     stat["bf16_oracle_rms_err_rel"] = math.sqrt(float(np.mean(rerr * rerr))) / rms
     d = np.abs(gpu - ref_r)
     stat["max_rel_vs_bf16_oracle"] = float(d.max()) / rms
-    assert stat["max_rel"] <= stat["bf16_oracle_max_rel"] + MAX_REL, (name, stat)
-    assert stat["rms_err_rel"] <= 2 * stat["bf16_oracle_rms_err_rel"] + 1e-3, (name, stat)
+    assert stat["max_rel"] <= stat["bf16_oracle_max_rel"] + depth * MAX_REL, (name, stat)
+    assert stat["rms_err_rel"] <= 2 * stat["bf16_oracle_rms_err_rel"] + depth * 1e-3, (name, stat)
     return stat
 
 

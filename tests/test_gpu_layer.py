@@ -19,6 +19,10 @@ DEV = "cuda"
 # a small bf16 model of the 70B layer's structure: GQA 4:1, head_dim 128,
 # llama3 RoPE with the 70B parameters
 MID = synth.ModelShape(1024, 8, 2, 128, 2816, 1e-5, 500000.0, synth.LLAMA3_SCALING, 131072, "bf16")
+# the 70B layer's group size (8 query heads per KV head) at a small width
+MID8 = synth.ModelShape(1024, 8, 1, 128, 2816, 1e-5, 500000.0, synth.LLAMA3_SCALING, 131072, "bf16")
+# head_dim 64 variant
+MID64 = synth.ModelShape(512, 16, 4, 64, 1408, 1e-5, 10000.0, None, 8192, "bf16")
 
 
 def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False):
@@ -70,37 +74,51 @@ def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False):
                                         orc.bf16_round(prev_r["residual_out"]), posn, seqs, rnd=orc.bf16_round)
         prev_exact, prev_r = exact, rounded
         s1 = compare("hidden_out[%d]" % l, np64(ho), exact["hidden_out"],
-                     None if rounded is None else rounded["hidden_out"], dtype)
+                     None if rounded is None else rounded["hidden_out"], dtype, depth=l + 1)
         s2 = compare("residual_out[%d]" % l, np64(ro), exact["residual_out"],
-                     None if rounded is None else rounded["residual_out"], dtype)
+                     None if rounded is None else rounded["residual_out"], dtype, depth=l + 1)
         print("layer", l, "hidden_out", s1, "residual_out", s2, flush=True)
         if check_kv:
-            _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded)
+            _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded, depth=l + 1)
 
 
-def _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded):
-    ibits = torch.int16 if model.dtype == "bf16" else torch.int32
-    mask = torch.zeros(kp.shape[0], 16, dtype=torch.bool)
-    ks, vs, kref, vref, kr, vr = [], [], [], [], [], []
+def _new_slot_mask(batch):
+    """[num_blocks, 16] bool: the slots of the batch's new tokens."""
+    mask = torch.zeros(batch.num_blocks, 16, dtype=torch.bool)
     for b in range(batch.num_seqs):
-        for j in range(batch.q_len):
-            p = batch.ctx_lens[b] + j
-            blk = int(batch.block_table[b, p // 16])
-            mask[blk, p % 16] = True
-            ks.append(np64(kp[blk, :, p % 16, :]))
-            vs.append(np64(vp[blk, :, :, p % 16]))
-            kref.append(exact["k_new"][b][j])
-            vref.append(exact["v_new"][b][j])
-            if rounded is not None:
-                kr.append(rounded["k_new"][b][j])
-                vr.append(rounded["v_new"][b][j])
-    mk = mask.to(kp.device)[:, None, :, None].expand_as(kp)
-    mv = mask.to(vp.device)[:, None, None, :].expand_as(vp)
-    # placement: bit-exact -- every byte outside the new slots is unchanged
+        p = torch.arange(batch.ctx_lens[b], batch.ctx_lens[b] + batch.q_len)
+        mask[batch.block_table[b, p // 16].long(), p % 16] = True
+    return mask
+
+
+def _check_placement(model, batch, kp0, vp0, kp, vp):
+    """Bit-exact: every byte outside the new tokens' slots is unchanged."""
+    ibits = torch.int16 if model.dtype == "bf16" else torch.int32
+    mask = _new_slot_mask(batch).to(kp.device)
+    mk = mask[:, None, :, None].expand_as(kp)
+    mv = mask[:, None, None, :].expand_as(vp)
     assert torch.equal(kp.view(ibits)[~mk], kp0.view(ibits)[~mk])
     assert torch.equal(vp.view(ibits)[~mv], vp0.view(ibits)[~mv])
-    compare("k_cache", np.stack(ks), np.stack(kref), np.stack(kr) if kr else None, model.dtype)
-    compare("v_cache", np.stack(vs), np.stack(vref), np.stack(vr) if vr else None, model.dtype)
+    # and every new slot was written (no sentinel left)
+    assert not torch.isnan(kp[mk].float()).any() and not torch.isnan(vp[mv].float()).any()
+
+
+def _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded, depth=1):
+    _check_placement(model, batch, kp0, vp0, kp, vp)
+    ks, vs, kref, vref, kr, vr = [], [], [], [], [], []
+    for b in range(batch.num_seqs):
+        c, n = batch.ctx_lens[b], int(batch.seq_lens[b])
+        ks.append(np64(synth.gather_context(kp, batch, b, n, "k")[c:]))
+        vs.append(np64(synth.gather_context(vp, batch, b, n, "v")[c:]))
+        kref.append(exact["k_new"][b])
+        vref.append(exact["v_new"][b])
+        if rounded is not None:
+            kr.append(rounded["k_new"][b])
+            vr.append(rounded["v_new"][b])
+    compare("k_cache", np.concatenate(ks), np.concatenate(kref), np.concatenate(kr) if kr else None, model.dtype,
+            depth)
+    compare("v_cache", np.concatenate(vs), np.concatenate(vref), np.concatenate(vr) if vr else None, model.dtype,
+            depth)
 
 
 def test_tiny_fp32_prefill():
@@ -133,3 +151,20 @@ def test_mid_first_layer_no_residual():
 
 def test_mid_two_layer_stack():
     _run(synth.Workload(26, "mid_decode_b12_2layer", MID, 12, 1, (50, 900), layers=2), layers=2)
+
+
+def test_mid8_prefill_ragged_query_tiles():
+    _run(synth.Workload(27, "mid8_prefill_2x100", MID8, 2, 100, 0), repeat=True)
+
+
+def test_mid8_prefill_on_cached_context():
+    _run(synth.Workload(28, "mid8_prefill_3x37_ctx", MID8, 3, 37, 0), ctx_lens=[5, 300, 64])
+
+
+def test_mid8_decode():
+    _run(synth.Workload(29, "mid8_decode_b9", MID8, 9, 1, (1, 1500)))
+
+
+def test_mid64_prefill_and_decode():
+    _run(synth.Workload(30, "mid64_prefill_2x80", MID64, 2, 80, 0), ctx_lens=[0, 19])
+    _run(synth.Workload(31, "mid64_decode_b5", MID64, 5, 1, (3, 700)))
