@@ -24,6 +24,32 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "70B-shape layer tokens/s (prefill, decode) + % MFMA/HBM peak, 1 MI355X"
 
+# HBM bytes per launch of a dominant kernel from rocprofv3 counters: FETCH_SIZE x 2.0 + WRITE_SIZE
+# x 1.0 (factors from a plain 1 GiB copy; profiles/pmc_copy_calibration.md).  Reported only while
+# the kernel's source file is the one the counters were taken on.
+COUNTER_TRAFFIC = {
+    ("llama70b_decode_b32_ctx2048", "gate_up_silu"): {
+        "bytes": 945754556,
+        "source": "llama_decoder_layer_amd/csrc/gemm_skinny.hip",
+        "sha1": "84f1394da564b841f639948be615e777709b46cc",
+        "summary": "profiles/gate_up_silu_decode_b32_ctx2048.md",
+    },
+}
+
+
+def counter_traffic(workload, kernel):
+    import hashlib
+    rec = COUNTER_TRAFFIC.get((workload, kernel))
+    if rec is None:
+        return None
+    try:
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            if hashlib.sha1(f.read()).hexdigest() != rec["sha1"]:
+                return None
+    except OSError:
+        return None
+    return rec["bytes"]
+
 
 def layer_flops(model, num_tokens, attn_pairs):
     H, I, Q = model.hidden_size, model.intermediate_size, model.q_size
@@ -105,7 +131,8 @@ def measure(wl, steps, warmup):
     if wl.q_len == 1:
         alg = kernel_bytes(model, dom, T, kv_tokens)
         roof = {"bound": "hbm", "kernel": dom, "achieved": alg / dur / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": alg / dur / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                "unit": "GB/s", "frac": alg / dur / 1e9 / PEAK_HBM_GBS,
+                "traffic": counter_traffic(wl.name, dom),
                 "algorithmic_bytes_per_launch": alg, "avg_launch_us": dur * 1e6}
     else:
         H, I = model.hidden_size, model.intermediate_size
@@ -142,7 +169,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=None,
                     help="tokens of the step the oracle runs (default: all of a decode step, 256 of a prefill)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes, 3 times (a reference for "
+                         "the HBM byte counters of a profiler), and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "launches": 3}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sequences shard across GPUs with no exchange inside the layer)", file=sys.stderr)
