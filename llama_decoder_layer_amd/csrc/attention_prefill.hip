@@ -63,18 +63,20 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
     const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
     const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
     int max_blocks, int q_len, int num_qtiles, bf16* __restrict__ out) {
-  constexpr int KS = D / 32;   // d-steps of S^T
-  constexpr int DT = D / 16;   // 16-wide d tiles of O
+  constexpr int KS = D / 32;        // d-steps of S^T
+  constexpr int DT = D / 16;        // 16-wide d tiles of O
+  constexpr int CH = D / 8;         // 16-byte chunks per K row
+  constexpr int BCH = kKvBlock * D / 8;   // 16-byte chunks per cache block (K or V)
+  constexpr int SPL = BCH / kWave;        // chunks per lane when one wave stages one block
   __shared__ __attribute__((aligned(16))) bf16 sK[2][kKT * D];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][D * kKT];
 
   const int G = nq / nkv;
-  // longest query tiles first
-  const int qt = num_qtiles - 1 - (int)(blockIdx.x % num_qtiles);
+  const int qt = num_qtiles - 1 - (int)(blockIdx.x % num_qtiles);  // longest tiles first
   const int b = blockIdx.x / num_qtiles;
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
 
   const int t0 = b * q_len + qt * kQ;                       // first token row of the tile
@@ -84,9 +86,9 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
   const int key_end = min(p0 + kQ - 1, p_last) + 1;         // keys this tile needs
   const int ntiles = (key_end + kKT - 1) / kKT;
   const int* bt = block_table + (size_t)b * max_blocks;
-  const size_t head_stride = (size_t)kKvBlock * D;
+  const size_t head_off = (size_t)g * kKvBlock * D;
+  const size_t blk_stride = (size_t)nkv * kKvBlock * D;
 
-  // q fragments (B operand of S^T): query l16, d = 32s + 8grp
   const bf16x8 zero8 = {};
   bf16x8 qf[HPW][KS];
 #pragma unroll
@@ -98,63 +100,70 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
     for (int s = 0; s < KS; ++s) qf[hh][s] = ok ? ld16<bf16x8>(src + 32 * s) : zero8;
   }
 
-  // staging: K tile = 64 keys x D (D/8 chunks per key); V tile = 4 blocks of [D][16]
-  constexpr int KCH = kKT * D / 8;                 // 16-byte chunks per K tile
-  constexpr int KPT = KCH / (kWaves * kWave);      // per thread
-  constexpr int VCH = D * 4 * 2;                   // (d, block, half) 16-byte chunks per V tile
-  constexpr int VPT = VCH / (kWaves * kWave);
-  bf16x8 kst[KPT], vst[VPT];
+  // ---- staging: wave w copies cache block w of each 64-key tile --------
+  // K block: 16 rows of D, chunk c = lane + 64 i -> row c / CH, chunk c % CH
+  // V block: D components of 16 slots, chunk c -> component c / 2, slots
+  //          8*(c%2) .. +7, stored as two 4-key pieces at permuted positions
+  int k_dst[SPL], v_dst[SPL][2];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int c = lane + kWave * i;
+    const int key = wave * kKvBlock + c / CH;
+    k_dst[i] = k_off<D>(key, c % CH);
+    const int d = c >> 1, key0 = wave * kKvBlock + 8 * (c & 1);
+    v_dst[i][0] = v_off(d, v_pos(key0));
+    v_dst[i][1] = v_off(d, v_pos(key0 + 4));
+  }
+  bf16x8 kst[SPL], vst[SPL];
   auto gload = [&](int kt) {
+    const int first = kt * kKT + wave * kKvBlock;  // first key of this wave's block
+    if (first >= key_end) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int id = threadIdx.x + i * kWaves * kWave;
-      const int key = id / (D / 8), c = id % (D / 8);
-      const int pos = kt * kKT + key;
-      if (pos < key_end) {
-        const int blk = bt[pos / kKvBlock];
-        kst[i] = ld16<bf16x8>(kc + ((size_t)blk * nkv + g) * head_stride + (size_t)(pos % kKvBlock) * D + c * 8);
-      } else {
-        kst[i] = zero8;
-      }
+      for (int i = 0; i < SPL; ++i) kst[i] = vst[i] = zero8;
+      return;
     }
+    const int blk = __builtin_amdgcn_readfirstlane(bt[first / kKvBlock]);
+    const bf16* kb = kc + (size_t)blk * blk_stride + head_off;
+    const bf16* vb = vc + (size_t)blk * blk_stride + head_off;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int id = threadIdx.x + i * kWaves * kWave;
-      const int half = id & 1, j = (id >> 1) & 3, d = id >> 3;
-      const int pos = kt * kKT + j * kKvBlock + half * 8;  // first of 8 keys
-      if (pos < key_end) {
-        const int blk = bt[pos / kKvBlock];
-        bf16x8 v = ld16<bf16x8>(vc + ((size_t)blk * nkv + g) * head_stride + (size_t)d * kKvBlock + half * 8);
+    for (int i = 0; i < SPL; ++i) {
+      kst[i] = ld16<bf16x8>(kb + (size_t)(lane + kWave * i) * 8);
+      vst[i] = ld16<bf16x8>(vb + (size_t)(lane + kWave * i) * 8);
+    }
+    if (first + kKvBlock > key_end) {  // the sequence's last, partly written block
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int c = lane + kWave * i;
+        if (first + c / CH >= key_end) kst[i] = zero8;
+        const int s0 = first + 8 * (c & 1);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (pos + e >= key_end) v[e] = static_cast<bf16>(0.f);
-        vst[i] = v;
-      } else {
-        vst[i] = zero8;
+          if (s0 + e >= key_end) vst[i][e] = static_cast<bf16>(0.f);
       }
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int id = threadIdx.x + i * kWaves * kWave;
-      const int key = id / (D / 8), c = id % (D / 8);
-      *reinterpret_cast<bf16x8*>(&sK[buf][k_off<D>(key, c)]) = kst[i];
-    }
+    for (int i = 0; i < SPL; ++i) {
+      *reinterpret_cast<bf16x8*>(&sK[buf][k_dst[i]]) = kst[i];
+      bf16x4 lo, hi;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int id = threadIdx.x + i * kWaves * kWave;
-      const int half = id & 1, j = (id >> 1) & 3, d = id >> 3;
-      const int key0 = j * kKvBlock + half * 8;  // keys key0 .. key0+7 = two groups of 4
-#pragma unroll
-      for (int q4 = 0; q4 < 2; ++q4) {
-        bf16x4 piece;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) piece[r] = vst[i][4 * q4 + r];
-        *reinterpret_cast<bf16x4*>(&sV[buf][v_off(d, v_pos(key0 + 4 * q4))]) = piece;
+      for (int r = 0; r < 4; ++r) {
+        lo[r] = vst[i][r];
+        hi[r] = vst[i][4 + r];
       }
+      *reinterpret_cast<bf16x4*>(&sV[buf][v_dst[i][0]]) = lo;
+      *reinterpret_cast<bf16x4*>(&sV[buf][v_dst[i][1]]) = hi;
     }
   };
+
+  // ---- per-lane operand offsets in LDS (the same for every tile) ---------
+  int k_rd[KS];  // key 16j + l16 (j added below), chunk 4s + grp
+#pragma unroll
+  for (int s = 0; s < KS; ++s) k_rd[s] = k_off<D>(l16, 4 * s + grp);
+  int v_rd[2];   // component 16i + l16 (i added below), positions 32mh + 8grp
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh) v_rd[mh] = v_off(l16, 32 * mh + 8 * grp);
 
   const float sc = kLog2e / sqrtf((float)D);
   float m_run[HPW], l_run[HPW];
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
 #pragma unroll
     for (int i = 0; i < DT; ++i) o[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int pq = p0 + l16;  // this lane's query position (S^T layout)
+  const int pq = p0 + l16;  // this lane's query position
 
   gload(0);
   sstore(0);
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
     const int buf = kt & 1;
     if (kt + 1 < ntiles) gload(kt + 1);
 
-    // S^T for each head: 4 slices of 16 keys
+    // S^T (raw scores) for each head: 4 slices of 16 keys
     f32x4 s4[HPW][4];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
@@ -185,57 +194,64 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][k_off<D>(16 * j + l16, 4 * s + grp)]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][k_rd[s] + 16 * D * j]);
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) s4[hh][j] = mfma16(kf, qf[hh][s], s4[hh][j]);
       }
     }
-    const bool diag = kt * kKT + kKT - 1 > p0;  // some key may follow some query
+    // keys past a query's position exist only in the tiles that reach the
+    // tile's first query position (or hold unwritten slots)
+    const bool diag = kt * kKT + kKT - 1 > p0;
+    if (diag) {
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kt * kKT + 16 * j + 4 * grp + r > pq) s4[hh][j][r] = -INFINITY;
+    }
     bf16x8 pa[HPW][2];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      float sv[4][4];
       float bm = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kt * kKT + 16 * j + 4 * grp + r;
-          float v = s4[hh][j][r] * sc;
-          if (diag && key > pq) v = -INFINITY;
-          sv[j][r] = v;
-          bm = fmaxf(bm, v);
-        }
+        bm = fmaxf(bm, fmaxf(fmaxf(s4[hh][j][0], s4[hh][j][1]), fmaxf(s4[hh][j][2], s4[hh][j][3])));
       bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
       bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
       const float m_new = fmaxf(m_run[hh], bm);
-      const float alpha = exp2f(m_run[hh] - m_new);
+      const float ms = m_new * sc;
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float pv = exp2f(sv[j][r] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s4[hh][j][r], sc, -ms));
           ps += pv;
           pa[hh][j >> 1][4 * (j & 1) + r] = static_cast<bf16>(pv);
         }
-      l_run[hh] = l_run[hh] * alpha + ps;
+      if (__all(m_new == m_run[hh])) {
+        l_run[hh] += ps;  // no query's max moved: O needs no rescale
+      } else {
+        const float alpha = __builtin_amdgcn_exp2f((m_run[hh] - m_new) * sc);
+        l_run[hh] = l_run[hh] * alpha + ps;
+        float ah[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ah[r] = __shfl(alpha, 4 * grp + r, kWave);
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[hh][i][r] *= ah[r];
+      }
       m_run[hh] = m_new;
-      float ah[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ah[r] = __shfl(alpha, 4 * grp + r, kWave);
-#pragma unroll
-      for (int i = 0; i < DT; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[hh][i][r] *= ah[r];
     }
     // O += P V : two 32-key halves, DT d-tiles
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
-        const int d = 16 * i + l16;
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][v_off(d, 32 * mh + 8 * grp)]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][v_rd[mh] + 16 * kKT * i]);
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) o[hh][i] = mfma16(pa[hh][mh], vf, o[hh][i]);
       }

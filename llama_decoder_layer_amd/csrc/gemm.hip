@@ -17,8 +17,10 @@
 // agree between A and B, which lets the loads be laid out for coalescing.
 //
 //   skinny kernel (M <= 64 tokens, decode): gemm_skinny.hip.
-//   tiled kernel (prefill): 128x128 output tile per workgroup, K in steps of
-//     64 through double-buffered, XOR-swizzled LDS; 2x2 waves of 64x64.
+//   tiled kernel (prefill): 256 tokens x 256 weight rows per workgroup with
+//     8 waves of 128 x 64 (128 KiB of LDS), or 128 x 128 with 4 waves of
+//     64 x 64 for shapes the large tile does not fit; K in steps of 64 through
+//     double-buffered, XOR-swizzled LDS; XCD-aware tile order.
 //   fp32 kernel: plain LDS-tiled FMA kernel for fp32 layers.
 //
 // SiluAndMul layout: the bf16 gate_up weight is re-ordered once (in create)
@@ -60,72 +62,80 @@ __device__ __forceinline__ void store4_silu(bf16* out, size_t idx, const float g
 
 // ------------------------------------------------------------- tiled ------
 
-constexpr int kTBM = 128;  // tokens per tile
-constexpr int kTBN = 128;  // weight rows per tile
-constexpr int kTBK = 64;
-constexpr int kTThreads = 256;
+constexpr int kTBK = 64;  // k per LDS stage
 
-// element offset of 16-byte chunk c of row `row` in a [rows][64] bf16 tile
-__device__ __forceinline__ int swz(int row, int c) { return row * kTBK + ((c ^ (row & 7)) << 3); }
+// BM tokens x BN weight rows per workgroup, WM x WN waves (a wave owns
+// BM/WM tokens x BN/WN rows), K in stages of 64 through double-buffered
+// XOR-swizzled LDS (dynamic: up to 128 KiB), operands staged through
+// registers one stage ahead.
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __restrict__ X, int M,
+                                                               const bf16* __restrict__ W, int N, int K,
+                                                               bf16* out, int ldo, int xcd_remap) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;     // wave tile: tokens x weight rows
+  constexpr int SM = TM / 16, SN = TN / 16;     // 16x16 MFMA tiles per wave
+  constexpr int CPR = kTBK / 8;                 // 16-byte chunks per row and stage
+  constexpr int WPT = BN * CPR / NT, XPT = BM * CPR / NT;
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  bf16* sW = smem;                    // [2][BN * 64]
+  bf16* sX = smem + 2 * BN * kTBK;    // [2][BM * 64]
+  auto swz = [](int row, int c) { return row * kTBK + ((c ^ (row & 7)) << 3); };
 
-template <int EPI>
-__global__ __launch_bounds__(kTThreads) void gemm_tile_bf16(const bf16* __restrict__ X, int M,
-                                                            const bf16* __restrict__ W, int N,
-                                                            int K, bf16* out, int ldo) {
-  __shared__ __attribute__((aligned(16))) bf16 sW[2][kTBN * kTBK];
-  __shared__ __attribute__((aligned(16))) bf16 sX[2][kTBM * kTBK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave / WM, wm = wave % WM;
+  const int r16 = lane & 15, g = lane >> 4;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave >> 1;  // wave's 64-row slice of the weight tile
-  const int wm = wave & 1;   // wave's 64-token slice
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
+  // Workgroups are dispatched round-robin over the 8 XCDs; with xcd_remap
+  // each XCD gets a contiguous run of tiles (neighbouring tiles share W and
+  // x panels in that XCD's L2).  Tiles run m-fastest.
+  int bid = blockIdx.x;
+  if (xcd_remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  const int num_m = (M + BM - 1) / BM;
+  const int m0 = (bid % num_m) * BM;
+  const int n0 = (bid / num_m) * BN;
 
-  const int num_m = (M + kTBM - 1) / kTBM;
-  const int tile_m = blockIdx.x % num_m;
-  const int tile_n = blockIdx.x / num_m;
-  const int m0 = tile_m * kTBM;
-  const int n0 = tile_n * kTBN;
-
-  // global -> register staging: 4 chunks of W and 4 of X per thread
-  int ld_row[4], ld_c[4];
-  const bf16* wsrc[4];
-  const bf16* xsrc[4];
-  bool xok[4];
+  const bf16* wsrc[WPT];
+  int wrow[WPT], wch[WPT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int id = tid + j * kTThreads;
-    ld_row[j] = id >> 3;
-    ld_c[j] = id & 7;
-    wsrc[j] = W + (size_t)(n0 + ld_row[j]) * K + ld_c[j] * 8;
-    const int m = m0 + ld_row[j];
+  for (int j = 0; j < WPT; ++j) {
+    const int id = tid + j * NT;
+    wrow[j] = id / CPR;
+    wch[j] = id % CPR;
+    wsrc[j] = W + (size_t)(n0 + wrow[j]) * K + wch[j] * 8;
+  }
+  const bf16* xsrc[XPT];
+  int xrow[XPT], xch[XPT];
+  bool xok[XPT];
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int id = tid + j * NT;
+    xrow[j] = id / CPR;
+    xch[j] = id % CPR;
+    const int m = m0 + xrow[j];
     xok[j] = m < M;
-    xsrc[j] = X + (size_t)(xok[j] ? m : 0) * K + ld_c[j] * 8;
+    xsrc[j] = X + (size_t)(xok[j] ? m : 0) * K + xch[j] * 8;
   }
   const bf16x8 zero8 = {};
-  bf16x8 wst[4], xst[4];
+  bf16x8 wst[WPT], xst[XPT];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wst[j] = ld16<bf16x8>(wsrc[j] + k0);
-      xst[j] = xok[j] ? ld16<bf16x8>(xsrc[j] + k0) : zero8;
-    }
+    for (int j = 0; j < WPT; ++j) wst[j] = ld16<bf16x8>(wsrc[j] + k0);
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) xst[j] = xok[j] ? ld16<bf16x8>(xsrc[j] + k0) : zero8;
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<bf16x8*>(&sW[buf][swz(ld_row[j], ld_c[j])]) = wst[j];
-      *reinterpret_cast<bf16x8*>(&sX[buf][swz(ld_row[j], ld_c[j])]) = xst[j];
-    }
+    for (int j = 0; j < WPT; ++j) *reinterpret_cast<bf16x8*>(&sW[buf * BN * kTBK + swz(wrow[j], wch[j])]) = wst[j];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) *reinterpret_cast<bf16x8*>(&sX[buf * BM * kTBK + swz(xrow[j], xch[j])]) = xst[j];
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[SN][SM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < SN; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < SM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / kTBK;
   gload(0);
@@ -135,18 +145,18 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_bf16(const bf16* __restri
     const int buf = kt & 1;
     if (kt + 1 < nk) gload((kt + 1) * kTBK);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kTBK / 32; ++s) {
       const int c = s * 4 + g;
-      bf16x8 a[4], b[4];
+      bf16x8 b[SM];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8*>(&sW[buf][swz(wn * 64 + i * 16 + r16, c)]);
-        b[i] = *reinterpret_cast<const bf16x8*>(&sX[buf][swz(wm * 64 + i * 16 + r16, c)]);
+      for (int j = 0; j < SM; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&sX[buf * BM * kTBK + swz(wm * TM + j * 16 + r16, c)]);
+#pragma unroll
+      for (int i = 0; i < SN; ++i) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sW[buf * BN * kTBK + swz(wn * TN + i * 16 + r16, c)]);
+#pragma unroll
+        for (int j = 0; j < SM; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
     }
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
@@ -154,14 +164,13 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_bf16(const bf16* __restri
 
   // epilogue: lane holds features n..n+3 of token m for each (i, j)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + wm * 64 + j * 16 + r16;
+  for (int j = 0; j < SM; ++j) {
+    const int m = m0 + wm * TM + j * 16 + r16;
     if (m >= M) continue;
     if (EPI == kEpiSiluMul) {
 #pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const int grp = (n0 + wn * 64 + i * 16) / 32;
-        const int f = grp * 16 + 4 * g;
+      for (int i = 0; i < SN; i += 2) {
+        const int f = ((n0 + wn * TN + i * 16) >> 5) * 16 + 4 * g;
         float gv[4], uv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -172,8 +181,8 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_bf16(const bf16* __restri
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + wn * 64 + i * 16 + 4 * g;
+      for (int i = 0; i < SN; ++i) {
+        const int n = n0 + wn * TN + i * 16 + 4 * g;
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r];
@@ -181,6 +190,21 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_bf16(const bf16* __restri
       }
     }
   }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, bf16* out, int ldo, hipStream_t s) {
+  auto fn = gemm_tile_bf16<BM, BN, WM, WN, EPI>;
+  const size_t lds = (size_t)2 * (BM + BN) * kTBK * sizeof(bf16);
+  static bool attr_set = false;  // per instantiation; the attribute is per function
+  if (lds > 65536 && !attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int nb = ((M + BM - 1) / BM) * (wrows / BN);
+  fn<<<nb, 64 * WM * WN, lds, s>>>(x, M, w, wrows, K, out, ldo, nb % 8 == 0 ? 1 : 0);
+  return hipGetLastError();
 }
 
 // -------------------------------------------------------------- fp32 ------
@@ -237,10 +261,8 @@ hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* 
   // rows of W the kernel walks: N (store/add) or 2N (silu_mul)
   const int wrows = (EPI == kEpiSiluMul) ? 2 * N : N;
   if (M <= 64) return launch_skinny(x, w, M, N, K, EPI, skinny_plan(M, wrows, K, false), out, s);
-  const int num_m = (M + kTBM - 1) / kTBM;
-  dim3 grid(num_m * (wrows / kTBN));
-  gemm_tile_bf16<EPI><<<grid, kTThreads, 0, s>>>(x, M, w, wrows, K, out, N);
-  return hipGetLastError();
+  if (M >= 256 && wrows % 256 == 0) return launch_tile<256, 256, 2, 4, EPI>(x, M, w, wrows, K, out, N, s);
+  return launch_tile<128, 128, 2, 2, EPI>(x, M, w, wrows, K, out, N, s);
 }
 
 template <int EPI>
@@ -264,10 +286,10 @@ hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, 
     const bf16* xb = (const bf16*)x;
     const bf16* wb = (const bf16*)w;
     bf16* ob = (bf16*)out;
-    // the tiled kernel walks weight rows in 128-row tiles
+    // the tiled kernels walk weight rows in 128- or 256-row tiles
     if (M > 64) {
       const int wrows = (epi == kEpiSiluMul) ? 2 * N : N;
-      if (wrows % kTBN != 0) return hipErrorInvalidValue;
+      if (wrows % 128 != 0 || K % kTBK != 0) return hipErrorInvalidValue;
     }
     switch (epi) {
       case kEpiStore: return linear_bf16<kEpiStore>(xb, wb, M, N, K, ob, s);
