@@ -10,9 +10,10 @@
 // block table).  The keys of a query are the sequence's cached context plus
 // its own new tokens up to and including itself.
 //
-// One workgroup = (sequence, KV head g, tile of 16 consecutive query tokens);
-// its 4 waves each take G/4 query heads of the group, so every K/V tile is
-// staged in LDS once for all G heads.  The key loop walks 64-key tiles (four
+// One workgroup = (sequence, KV head g, 32 consecutive query tokens); its
+// waves each take one query head of the group (two for G = 16), so every K/V
+// tile is staged in LDS once for all G heads, and two waves share each SIMD
+// (one wave's softmax overlaps another's MFMAs).  The key loop walks 64-key tiles (four
 // 16-slot cache blocks) with an online softmax in fp32 (exp2 of
 // log2(e)/sqrt(d)-scaled scores), only up to the tile's last query position
 // (causal tile skipping); the diagonal tiles mask key > query position.
@@ -33,8 +34,7 @@
 namespace llk {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kQ = 16;         // query tokens per workgroup
+constexpr int kQ = 16;         // query tokens per MFMA row tile
 constexpr int kKT = 64;        // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -58,8 +58,10 @@ __device__ __forceinline__ int v_off(int d, int pos) {
   return d * kKT + ((((pos >> 3) ^ (d & 7)) << 3) | (pos & 7));
 }
 
-template <int D, int HPW>
-__global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
+// D head dim, HPW query heads per wave, QT 16-query tiles per workgroup,
+// NW waves (NW * HPW = G heads).
+template <int D, int HPW, int QT, int NW>
+__global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
     const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
     const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
     int max_blocks, int q_len, int num_qtiles, bf16* __restrict__ out) {
@@ -68,6 +70,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
   constexpr int CH = D / 8;         // 16-byte chunks per K row
   constexpr int BCH = kKvBlock * D / 8;   // 16-byte chunks per cache block (K or V)
   constexpr int SPL = BCH / kWave;        // chunks per lane when one wave stages one block
+  constexpr int QW = kQ * QT;             // queries per workgroup
+  constexpr int BPT = kKT / kKvBlock;     // cache blocks per key tile (4)
   __shared__ __attribute__((aligned(16))) bf16 sK[2][kKT * D];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][D * kKT];
 
@@ -79,43 +83,49 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
 
-  const int t0 = b * q_len + qt * kQ;                       // first token row of the tile
-  const int nvalid = min(kQ, q_len - qt * kQ);              // query rows of the tile
+  const int t0 = b * q_len + qt * QW;                       // first token row of the tile
+  const int nvalid = min(QW, q_len - qt * QW);              // query rows of the tile
   const int p0 = positions[t0];                             // position of the tile's first query
   const int p_last = positions[b * q_len + q_len - 1];      // last written key of the sequence
-  const int key_end = min(p0 + kQ - 1, p_last) + 1;         // keys this tile needs
+  const int key_end = min(p0 + QW - 1, p_last) + 1;         // keys this tile needs
   const int ntiles = (key_end + kKT - 1) / kKT;
   const int* bt = block_table + (size_t)b * max_blocks;
   const size_t head_off = (size_t)g * kKvBlock * D;
   const size_t blk_stride = (size_t)nkv * kKvBlock * D;
 
   const bf16x8 zero8 = {};
-  bf16x8 qf[HPW][KS];
+  bf16x8 qf[HPW][QT][KS];
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const int h = g * G + wave * HPW + hh;
-    const bool ok = l16 < nvalid;
-    const bf16* src = q + (size_t)(t0 + (ok ? l16 : 0)) * ldq + (size_t)h * D + 8 * grp;
+  for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[hh][s] = ok ? ld16<bf16x8>(src + 32 * s) : zero8;
-  }
+    for (int u = 0; u < QT; ++u) {
+      const int h = g * G + wave * HPW + hh;
+      const int qi = 16 * u + l16;
+      const bool ok = qi < nvalid;
+      const bf16* src = q + (size_t)(t0 + (ok ? qi : 0)) * ldq + (size_t)h * D + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[hh][u][s] = ok ? ld16<bf16x8>(src + 32 * s) : zero8;
+    }
 
-  // ---- staging: wave w copies cache block w of each 64-key tile --------
+  // ---- staging: the 4 cache blocks of a 64-key tile, one wave per block
+  // (waves 4.. of an 8-wave workgroup take no part in staging).
   // K block: 16 rows of D, chunk c = lane + 64 i -> row c / CH, chunk c % CH
   // V block: D components of 16 slots, chunk c -> component c / 2, slots
   //          8*(c%2) .. +7, stored as two 4-key pieces at permuted positions
+  const bool stager = wave < BPT;
   int k_dst[SPL], v_dst[SPL][2];
 #pragma unroll
   for (int i = 0; i < SPL; ++i) {
     const int c = lane + kWave * i;
-    const int key = wave * kKvBlock + c / CH;
+    const int key = (wave % BPT) * kKvBlock + c / CH;
     k_dst[i] = k_off<D>(key, c % CH);
-    const int d = c >> 1, key0 = wave * kKvBlock + 8 * (c & 1);
+    const int d = c >> 1, key0 = (wave % BPT) * kKvBlock + 8 * (c & 1);
     v_dst[i][0] = v_off(d, v_pos(key0));
     v_dst[i][1] = v_off(d, v_pos(key0 + 4));
   }
   bf16x8 kst[SPL], vst[SPL];
   auto gload = [&](int kt) {
+    if (!stager) return;
     const int first = kt * kKT + wave * kKvBlock;  // first key of this wave's block
     if (first >= key_end) {
 #pragma unroll
@@ -143,6 +153,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
     }
   };
   auto sstore = [&](int buf) {
+    if (!stager) return;
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
       *reinterpret_cast<bf16x8*>(&sK[buf][k_dst[i]]) = kst[i];
@@ -166,16 +177,17 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
   for (int mh = 0; mh < 2; ++mh) v_rd[mh] = v_off(l16, 32 * mh + 8 * grp);
 
   const float sc = kLog2e / sqrtf((float)D);
-  float m_run[HPW], l_run[HPW];
-  f32x4 o[HPW][DT];
+  float m_run[HPW][QT], l_run[HPW][QT];
+  f32x4 o[HPW][QT][DT];
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    m_run[hh] = -INFINITY;
-    l_run[hh] = 0.f;
+  for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int i = 0; i < DT; ++i) o[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const int pq = p0 + l16;  // this lane's query position
+    for (int u = 0; u < QT; ++u) {
+      m_run[hh][u] = -INFINITY;
+      l_run[hh][u] = 0.f;
+#pragma unroll
+      for (int i = 0; i < DT; ++i) o[hh][u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   gload(0);
   sstore(0);
@@ -184,68 +196,77 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
     const int buf = kt & 1;
     if (kt + 1 < ntiles) gload(kt + 1);
 
-    // S^T (raw scores) for each head: 4 slices of 16 keys
-    f32x4 s4[HPW][4];
+    // S^T (raw scores): 4 slices of 16 keys per (head, query tile)
+    f32x4 s4[HPW][QT][4];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s4[hh][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < QT; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s4[hh][u][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][k_rd[s] + 16 * D * j]);
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) s4[hh][j] = mfma16(kf, qf[hh][s], s4[hh][j]);
+        for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+          for (int u = 0; u < QT; ++u) s4[hh][u][j] = mfma16(kf, qf[hh][u][s], s4[hh][u][j]);
       }
     }
     // keys past a query's position exist only in the tiles that reach the
     // tile's first query position (or hold unwritten slots)
-    const bool diag = kt * kKT + kKT - 1 > p0;
-    if (diag) {
+    if (kt * kKT + kKT - 1 > p0) {
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh)
+      for (int u = 0; u < QT; ++u) {
+        const int pq = p0 + 16 * u + l16;
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (kt * kKT + 16 * j + 4 * grp + r > pq) s4[hh][u][j][r] = -INFINITY;
+      }
+    }
+    bf16x8 pa[HPW][QT][2];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bm = fmaxf(bm, fmaxf(fmaxf(s4[hh][u][j][0], s4[hh][u][j][1]), fmaxf(s4[hh][u][j][2], s4[hh][u][j][3])));
+        bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+        const float m_new = fmaxf(m_run[hh][u], bm);
+        const float ms = m_new * sc;
+        float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kt * kKT + 16 * j + 4 * grp + r > pq) s4[hh][j][r] = -INFINITY;
-    }
-    bf16x8 pa[HPW][2];
+          for (int r = 0; r < 4; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s4[hh][u][j][r], sc, -ms));
+            ps += pv;
+            pa[hh][u][j >> 1][4 * (j & 1) + r] = static_cast<bf16>(pv);
+          }
+        if (__all(m_new == m_run[hh][u])) {
+          l_run[hh][u] += ps;  // no query's max moved: O needs no rescale
+        } else {
+          const float alpha = __builtin_amdgcn_exp2f((m_run[hh][u] - m_new) * sc);
+          l_run[hh][u] = l_run[hh][u] * alpha + ps;
+          float ah[4];
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      float bm = -INFINITY;
+          for (int r = 0; r < 4; ++r) ah[r] = __shfl(alpha, 4 * grp + r, kWave);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bm = fmaxf(bm, fmaxf(fmaxf(s4[hh][j][0], s4[hh][j][1]), fmaxf(s4[hh][j][2], s4[hh][j][3])));
-      bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-      const float m_new = fmaxf(m_run[hh], bm);
-      const float ms = m_new * sc;
-      float ps = 0.f;
+          for (int i = 0; i < DT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s4[hh][j][r], sc, -ms));
-          ps += pv;
-          pa[hh][j >> 1][4 * (j & 1) + r] = static_cast<bf16>(pv);
+            for (int r = 0; r < 4; ++r) o[hh][u][i][r] *= ah[r];
         }
-      if (__all(m_new == m_run[hh])) {
-        l_run[hh] += ps;  // no query's max moved: O needs no rescale
-      } else {
-        const float alpha = __builtin_amdgcn_exp2f((m_run[hh] - m_new) * sc);
-        l_run[hh] = l_run[hh] * alpha + ps;
-        float ah[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ah[r] = __shfl(alpha, 4 * grp + r, kWave);
-#pragma unroll
-        for (int i = 0; i < DT; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[hh][i][r] *= ah[r];
+        m_run[hh][u] = m_new;
       }
-      m_run[hh] = m_new;
-    }
     // O += P V : two 32-key halves, DT d-tiles
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
@@ -253,31 +274,48 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_attention_mfma(
       for (int i = 0; i < DT; ++i) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][v_rd[mh] + 16 * kKT * i]);
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) o[hh][i] = mfma16(pa[hh][mh], vf, o[hh][i]);
+        for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+          for (int u = 0; u < QT; ++u) o[hh][u][i] = mfma16(pa[hh][u][mh], vf, o[hh][u][i]);
       }
     }
     if (kt + 1 < ntiles) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  // normalise and store: lane holds O[query 4grp + r][d = 16i + l16]
+  // normalise and store: lane holds O[query 16u + 4grp + r][d = 16i + l16]
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    float lt = l_run[hh];
-    lt += __shfl_xor(lt, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
-    const int h = g * G + wave * HPW + hh;
+  for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qi = 4 * grp + r;
-      const float inv = 1.0f / __shfl(lt, qi, kWave);
-      if (qi < nvalid) {
-        bf16* dst = out + (size_t)(t0 + qi) * nq * D + (size_t)h * D + l16;
+    for (int u = 0; u < QT; ++u) {
+      float lt = l_run[hh][u];
+      lt += __shfl_xor(lt, 16, kWave);
+      lt += __shfl_xor(lt, 32, kWave);
+      const int h = g * G + wave * HPW + hh;
 #pragma unroll
-        for (int i = 0; i < DT; ++i) dst[16 * i] = static_cast<bf16>(o[hh][i][r] * inv);
+      for (int r = 0; r < 4; ++r) {
+        const int qi = 16 * u + 4 * grp + r;
+        const float inv = 1.0f / __shfl(lt, 4 * grp + r, kWave);
+        if (qi < nvalid) {
+          bf16* dst = out + (size_t)(t0 + qi) * nq * D + (size_t)h * D + l16;
+#pragma unroll
+          for (int i = 0; i < DT; ++i) dst[16 * i] = static_cast<bf16>(o[hh][u][i][r] * inv);
+        }
       }
     }
-  }
+}
+
+template <int D, int HPW, int QT, int NW>
+hipError_t launch_pf(const void* q, int ldq, int T, const int* positions, int nq, int nkv, const void* k_cache,
+                     const void* v_cache, const int* block_table, int max_blocks, int q_len, void* out,
+                     hipStream_t s) {
+  const int B = T / q_len;
+  const int nqt = (q_len + kQ * QT - 1) / (kQ * QT);
+  dim3 grid(B * nqt, nkv);
+  prefill_attention_mfma<D, HPW, QT, NW><<<grid, NW * kWave, 0, s>>>(
+      (const bf16*)q, ldq, positions, nq, nkv, (const bf16*)k_cache, (const bf16*)v_cache, block_table,
+      max_blocks, q_len, nqt, (bf16*)out);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -291,27 +329,19 @@ hipError_t launch_prefill_attention_bf16(const void* q, int ldq, int T, const in
                                          int d, const void* k_cache, const void* v_cache, const int* block_table,
                                          int max_blocks, int q_len, void* out, hipStream_t s) {
   const int G = nq / nkv;
-  const int B = T / q_len;
-  const int nqt = (q_len + kQ - 1) / kQ;
-  dim3 grid(B * nqt, nkv);
-  const bf16* qb = (const bf16*)q;
-  const bf16* kb = (const bf16*)k_cache;
-  const bf16* vb = (const bf16*)v_cache;
-  bf16* ob = (bf16*)out;
-#define LLK_PF(DD, HH)                                                                                    \
-  prefill_attention_mfma<DD, HH><<<grid, kWaves * kWave, 0, s>>>(qb, ldq, positions, nq, nkv, kb, vb,    \
-                                                                 block_table, max_blocks, q_len, nqt, ob)
+#define LLK_PF(DD, HH, QQ, WW) \
+  return launch_pf<DD, HH, QQ, WW>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, q_len, out, s)
+  // one query head per wave and 32 queries per workgroup: two waves per SIMD
+  // overlap one wave's softmax with another's MFMAs
   if (d == 128) {
-    if (G == 4) LLK_PF(128, 1);
-    else if (G == 8) LLK_PF(128, 2);
-    else LLK_PF(128, 4);
-  } else {
-    if (G == 4) LLK_PF(64, 1);
-    else if (G == 8) LLK_PF(64, 2);
-    else LLK_PF(64, 4);
+    if (G == 4) LLK_PF(128, 1, 2, 4);
+    if (G == 8) LLK_PF(128, 1, 2, 8);
+    LLK_PF(128, 2, 1, 8);
   }
+  if (G == 4) LLK_PF(64, 1, 2, 4);
+  if (G == 8) LLK_PF(64, 1, 2, 8);
+  LLK_PF(64, 2, 1, 8);
 #undef LLK_PF
-  return hipGetLastError();
 }
 
 }  // namespace llk
