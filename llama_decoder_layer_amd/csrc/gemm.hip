@@ -19,8 +19,9 @@
 //   skinny kernel (M <= 64 tokens, decode): gemm_skinny.hip.
 //   tiled kernel (prefill): 256 tokens x 256 weight rows per workgroup with
 //     8 waves of 128 x 64 (128 KiB of LDS), or 128 x 128 with 4 waves of
-//     64 x 64 for shapes the large tile does not fit; K in steps of 64 through
-//     double-buffered, XOR-swizzled LDS; XCD-aware tile order.
+//     64 x 64 for shapes the large tile does not fit; K in steps of 64 loaded
+//     straight from global memory into double-buffered, XOR-swizzled LDS;
+//     XCD-aware tile order.
 //   fp32 kernel: plain LDS-tiled FMA kernel for fp32 layers.
 //
 // SiluAndMul layout: the bf16 gate_up weight is re-ordered once (in create)
@@ -66,23 +67,28 @@ constexpr int kTBK = 64;  // k per LDS stage
 
 // BM tokens x BN weight rows per workgroup, WM x WN waves (a wave owns
 // BM/WM tokens x BN/WN rows), K in stages of 64 through double-buffered
-// XOR-swizzled LDS (dynamic: up to 128 KiB), operands staged through
-// registers one stage ahead.
+// XOR-swizzled LDS (dynamic: up to 128 KiB).  Tiles go straight from global
+// memory into LDS (global_load_lds_dwordx4, no register staging): a wave's
+// load instruction fills 1 KiB of LDS linearly, 16 bytes per lane, so each
+// lane fetches the global chunk that belongs at its LDS slot under the
+// swizzle.  Rows of a ragged token tail read the last valid row instead and
+// are never stored.
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __restrict__ X, int M,
                                                                const bf16* __restrict__ W, int N, int K,
                                                                bf16* out, int ldo, int xcd_remap) {
-  constexpr int NT = 64 * WM * WN;
+  constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;     // wave tile: tokens x weight rows
   constexpr int SM = TM / 16, SN = TN / 16;     // 16x16 MFMA tiles per wave
-  constexpr int CPR = kTBK / 8;                 // 16-byte chunks per row and stage
-  constexpr int WPT = BN * CPR / NT, XPT = BM * CPR / NT;
+  constexpr int WJ = BN / 8 / NW;               // 8-row (1 KiB) pieces of a W stage per wave
+  constexpr int XJ = BM / 8 / NW;
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
   bf16* sW = smem;                    // [2][BN * 64]
   bf16* sX = smem + 2 * BN * kTBK;    // [2][BM * 64]
   auto swz = [](int row, int c) { return row * kTBK + ((c ^ (row & 7)) << 3); };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave / WM, wm = wave % WM;
   const int r16 = lane & 15, g = lane >> 4;
 
@@ -95,40 +101,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
   const int m0 = (bid % num_m) * BM;
   const int n0 = (bid / num_m) * BN;
 
-  const bf16* wsrc[WPT];
-  int wrow[WPT], wch[WPT];
+  // this lane's source chunk in each 8-row piece: LDS slot (row, lane & 7)
+  // holds logical chunk (lane & 7) ^ (row & 7)
+  const int prow = lane >> 3, pc = lane & 7;
+  const bf16* wsrc[WJ];
 #pragma unroll
-  for (int j = 0; j < WPT; ++j) {
-    const int id = tid + j * NT;
-    wrow[j] = id / CPR;
-    wch[j] = id % CPR;
-    wsrc[j] = W + (size_t)(n0 + wrow[j]) * K + wch[j] * 8;
+  for (int j = 0; j < WJ; ++j) {
+    const int row = (j * NW + wave) * 8 + prow;
+    wsrc[j] = W + (size_t)(n0 + row) * K + ((pc ^ (row & 7)) << 3);
   }
-  const bf16* xsrc[XPT];
-  int xrow[XPT], xch[XPT];
-  bool xok[XPT];
+  const bf16* xsrc[XJ];
 #pragma unroll
-  for (int j = 0; j < XPT; ++j) {
-    const int id = tid + j * NT;
-    xrow[j] = id / CPR;
-    xch[j] = id % CPR;
-    const int m = m0 + xrow[j];
-    xok[j] = m < M;
-    xsrc[j] = X + (size_t)(xok[j] ? m : 0) * K + xch[j] * 8;
+  for (int j = 0; j < XJ; ++j) {
+    const int row = (j * NW + wave) * 8 + prow;
+    const int m = min(m0 + row, M - 1);
+    xsrc[j] = X + (size_t)m * K + ((pc ^ (row & 7)) << 3);
   }
-  const bf16x8 zero8 = {};
-  bf16x8 wst[WPT], xst[XPT];
-  auto gload = [&](int k0) {
+  auto issue = [&](int buf, int k0) {
 #pragma unroll
-    for (int j = 0; j < WPT; ++j) wst[j] = ld16<bf16x8>(wsrc[j] + k0);
+    for (int j = 0; j < WJ; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(wsrc[j] + k0),
+          (__attribute__((address_space(3))) void*)(sW + buf * BN * kTBK + (j * NW + wave) * 8 * kTBK), 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < XPT; ++j) xst[j] = xok[j] ? ld16<bf16x8>(xsrc[j] + k0) : zero8;
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) *reinterpret_cast<bf16x8*>(&sW[buf * BN * kTBK + swz(wrow[j], wch[j])]) = wst[j];
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) *reinterpret_cast<bf16x8*>(&sX[buf * BM * kTBK + swz(xrow[j], xch[j])]) = xst[j];
+    for (int j = 0; j < XJ; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(xsrc[j] + k0),
+          (__attribute__((address_space(3))) void*)(sX + buf * BM * kTBK + (j * NW + wave) * 8 * kTBK), 16, 0, 0);
   };
 
   f32x4 acc[SN][SM];
@@ -138,12 +137,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
     for (int j = 0; j < SM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / kTBK;
-  gload(0);
-  sstore(0);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kTBK);
+    if (kt + 1 < nk) issue(buf ^ 1, (kt + 1) * kTBK);
 #pragma unroll
     for (int s = 0; s < kTBK / 32; ++s) {
       const int c = s * 4 + g;
@@ -158,7 +157,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
         for (int j = 0; j < SM; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
       }
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    // the next stage's loads have landed in LDS and every wave is done
+    // reading this one
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
