@@ -75,6 +75,7 @@ struct llama_layer {
   int dtype = 0;
   size_t es = 2;
   int qkv_n = 0;
+  int num_cus = 0;  // compute units of the device the layer was created on
   void* w_in = nullptr;
   void* w_qkv = nullptr;
   void* w_o = nullptr;
@@ -102,7 +103,8 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   const llama_layer_config& c = L->cfg;
   Workspace w{};
   const int q_len = (B > 0 && T % B == 0) ? T / B : 1;
-  w.plan = llk::attention_plan(T, c.num_attention_heads, c.num_key_value_heads, c.head_dim, q_len, max_seq_len);
+  w.plan = llk::attention_plan(T, c.num_attention_heads, c.num_key_value_heads, c.head_dim, q_len, max_seq_len,
+                              L->num_cus);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -119,10 +121,10 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.skinny = L->dtype == LLAMA_DTYPE_BF16 && T <= 64;
   size_t gpart = 0;
   if (w.skinny) {
-    w.pq = llk::skinny_plan(T, L->qkv_n, H, true);
-    w.po = llk::skinny_plan(T, H, Q, true);
-    w.pg = llk::skinny_plan(T, 2 * I, H, false);
-    w.pd = llk::skinny_plan(T, H, I, true);
+    w.pq = llk::skinny_plan(T, L->qkv_n, H, true, L->num_cus);
+    w.po = llk::skinny_plan(T, H, Q, true, L->num_cus);
+    w.pg = llk::skinny_plan(T, 2 * I, H, false, L->num_cus);
+    w.pd = llk::skinny_plan(T, H, I, true, L->num_cus);
     size_t n = (size_t)w.pq.splits * L->qkv_n;
     if ((size_t)w.po.splits * H > n) n = (size_t)w.po.splits * H;
     if ((size_t)w.pd.splits * H > n) n = (size_t)w.pd.splits * H;
@@ -246,6 +248,7 @@ llama_status llama_layer_create(const llama_layer_config* config, const llama_la
   L->cfg.rope_type = L->rope_type.c_str();
   L->dtype = config->dtype;
   L->es = elem_size(config->dtype);
+  L->num_cus = llk::device_cu_count();
   const llama_layer_config& c = L->cfg;
   const size_t H = c.hidden_size, I = c.intermediate_size, Q = (size_t)c.num_attention_heads * c.head_dim;
   L->qkv_n = (c.num_attention_heads + 2 * c.num_key_value_heads) * c.head_dim;

@@ -212,14 +212,19 @@ hipError_t combine(int d, int T_, int nq, int parts, const float* partials, void
 
 }  // namespace
 
-AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_len) {
+AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_len, int num_cus) {
   AttnPlan pl;
   if (q_len == 1) {
-    // decode: split the keys so that about 2048 workgroups run, partitions
-    // of 64..1024 keys (a multiple of 64: four waves x 16-slot blocks)
-    long long want = ((long long)max_seq_len * T * nkv + 2047) / 2048;
-    int len = (int)((want + 63) / 64 * 64);
-    pl.part_len = len < 64 ? 64 : (len > 1024 ? 1024 : len);
+    // decode: long-running workgroups stream best, so the keys of a
+    // (sequence, KV head) are split only as far as needed to give every
+    // compute unit a workgroup; partitions are multiples of 64 keys (four
+    // waves x 16-slot blocks)
+    const int groups = T * nkv;
+    const int cus = num_cus > 0 ? num_cus : 256;
+    const int want = (cus + groups - 1) / groups;
+    int len = (max_seq_len + want - 1) / want;
+    len = (len + 63) / 64 * 64;
+    pl.part_len = len < 64 ? 64 : len;
     pl.parts = (max_seq_len + pl.part_len - 1) / pl.part_len;
   } else {
     pl.part_len = max_seq_len;

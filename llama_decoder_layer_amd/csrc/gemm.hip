@@ -261,7 +261,7 @@ template <int EPI>
 hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* out, hipStream_t s) {
   // rows of W the kernel walks: N (store/add) or 2N (silu_mul)
   const int wrows = (EPI == kEpiSiluMul) ? 2 * N : N;
-  if (M <= 64) return launch_skinny(x, w, M, N, K, EPI, skinny_plan(M, wrows, K, false), out, s);
+  if (M <= 64) return launch_skinny(x, w, M, N, K, EPI, skinny_plan(M, wrows, K, false, device_cu_count()), out, s);
   if (M >= 256 && wrows % 256 == 0) return launch_tile<256, 256, 2, 4, EPI>(x, M, w, wrows, K, out, N, s);
   return launch_tile<128, 128, 2, 2, EPI>(x, M, w, wrows, K, out, N, s);
 }
@@ -274,6 +274,13 @@ hipError_t linear_f32(const float* x, const float* w, int M, int N, int K, float
 }
 
 }  // namespace
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
 
 const char* linear_kernel_name(int dtype, int M) {
   if (dtype != kBF16) return "gemm_f32";

@@ -4,11 +4,13 @@
 // page "模型库与算子层 — 代码走读", section "Linear 层"), but here every
 // weight byte is used by at most 64 tokens, so the kernel is bound by
 // streaming W from HBM once.  Design:
-//   * a workgroup owns 4 waves x NT 16-row tiles of W and one K range
+//   * a workgroup owns NW waves x NT 16-row tiles of W and one K range
 //     (split-K across workgroups when W has few rows, so that enough
-//     workgroups stream concurrently);
+//     workgroups stream concurrently).  NW is 4, or 7 when 7-wave
+//     workgroups tile a tall weight exactly onto the CUs (57344 rows = 256
+//     CUs x 7 waves x 32 rows): no partly empty last round;
 //   * the x slice of the current K chunk (M x KC) is staged once per
-//     workgroup in XOR-swizzled LDS and shared by the 4 waves, so global
+//     workgroup in XOR-swizzled LDS and shared by its waves, so global
 //     memory traffic is W plus a small fraction of x;
 //   * W fragments are loaded straight from global memory into MFMA operand
 //     registers (A = W rows, 16-byte loads, 64 contiguous bytes per row per
@@ -25,7 +27,6 @@
 namespace llk {
 namespace {
 
-constexpr int kThreads = 256;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -33,19 +34,20 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-template <int MT, int NT, int KC, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_skinny_bf16(const bf16* __restrict__ X, int M,
+template <int MT, int NT, int KC, int NW, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(const bf16* __restrict__ X, int M,
                                                              const bf16* __restrict__ W, int K, int kps,
                                                              void* __restrict__ out, int N) {
   constexpr int SPC = KC / 32;          // MFMA k-steps per chunk
   constexpr int XR = MT * 16;           // token rows staged
   constexpr int XCH = XR * KC / 8;      // 16-byte pieces of the x chunk
+  constexpr int kThreads = NW * 64;
   constexpr int XPT = (XCH + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) bf16 sx[2][XR * KC];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int n0 = (blockIdx.x * 4 + wave) * NT * 16;  // this wave's first weight row
+  const int n0 = (blockIdx.x * NW + wave) * NT * 16;  // this wave's first weight row
   const int k0 = blockIdx.y * kps;
   const int nchunk = kps / KC;
 
@@ -172,43 +174,60 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<bf16x4*>(out + i) = o;
 }
 
-template <int MT, int NT, int KC>
+template <int MT, int NT, int KC, int NW>
 hipError_t launch3(const bf16* x, int M, const bf16* w, int K, int kps, int epi, void* out, int N, dim3 grid,
                    hipStream_t s) {
   switch (epi) {
     case kEpiStore:
-      gemm_skinny_bf16<MT, NT, KC, kEpiStore><<<grid, kThreads, 0, s>>>(x, M, w, K, kps, out, N);
+      gemm_skinny_bf16<MT, NT, KC, NW, kEpiStore><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, out, N);
       break;
     case kEpiAdd:
-      gemm_skinny_bf16<MT, NT, KC, kEpiAdd><<<grid, kThreads, 0, s>>>(x, M, w, K, kps, out, N);
+      gemm_skinny_bf16<MT, NT, KC, NW, kEpiAdd><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, out, N);
       break;
     case kEpiSiluMul:
-      gemm_skinny_bf16<MT, NT, KC, kEpiSiluMul><<<grid, kThreads, 0, s>>>(x, M, w, K, kps, out, N);
+      gemm_skinny_bf16<MT, NT, KC, NW, kEpiSiluMul><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, out, N);
       break;
     default:
-      gemm_skinny_bf16<MT, NT, KC, kEpiPartial><<<grid, kThreads, 0, s>>>(x, M, w, K, kps, out, N);
+      gemm_skinny_bf16<MT, NT, KC, NW, kEpiPartial><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, out, N);
   }
   return hipGetLastError();
 }
 
 template <int MT, int NT>
-hipError_t launch_kc(int kc, const bf16* x, int M, const bf16* w, int K, int kps, int epi, void* out, int N,
-                     dim3 grid, hipStream_t s) {
-  if (kc == 256) return launch3<MT, NT, 256>(x, M, w, K, kps, epi, out, N, grid, s);
-  if (kc == 128) return launch3<MT, NT, 128>(x, M, w, K, kps, epi, out, N, grid, s);
-  return launch3<MT, NT, 64>(x, M, w, K, kps, epi, out, N, grid, s);
+hipError_t launch_kc(int kc, int nw, const bf16* x, int M, const bf16* w, int K, int kps, int epi, void* out,
+                     int N, dim3 grid, hipStream_t s) {
+  if (nw == 7) {
+    if (kc == 256) return launch3<MT, NT, 256, 7>(x, M, w, K, kps, epi, out, N, grid, s);
+    if (kc == 128) return launch3<MT, NT, 128, 7>(x, M, w, K, kps, epi, out, N, grid, s);
+    return launch3<MT, NT, 64, 7>(x, M, w, K, kps, epi, out, N, grid, s);
+  }
+  if (kc == 256) return launch3<MT, NT, 256, 4>(x, M, w, K, kps, epi, out, N, grid, s);
+  if (kc == 128) return launch3<MT, NT, 128, 4>(x, M, w, K, kps, epi, out, N, grid, s);
+  return launch3<MT, NT, 64, 4>(x, M, w, K, kps, epi, out, N, grid, s);
 }
 
 }  // namespace
 
-SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split) {
+SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split, int num_cus) {
   SkinnyPlan p;
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  // very tall weights (gate_up of the 70B shape): 64 rows per wave, no split
-  const bool tall = p.mt == 2 && wrows % 256 == 0 && wrows >= 49152 && K % 256 == 0;
-  p.nt = tall ? 4 : 2;
-  const int tiles = wrows / (64 * p.nt);
+  p.nt = 2;
+  p.nw = 4;
   p.splits = 1;
+  // Tall weights (gate_up of the 70B shape): no split.  One workgroup per CU
+  // with 7 waves of 32 rows when that tiles the rows exactly onto the CUs
+  // (no tail round); else 4 waves of 64 (32 for M > 32) rows.
+  const int rows7 = 7 * 32;
+  if (wrows >= 49152 && K % 256 == 0) {
+    if (num_cus > 0 && wrows % rows7 == 0 && (wrows / rows7) % num_cus == 0) {
+      p.nw = 7;
+    } else if (p.mt == 2 && wrows % 256 == 0) {
+      p.nt = 4;
+    }
+    p.kc = 256;
+    return p;
+  }
+  const int tiles = wrows / (16 * p.nw * p.nt);
   if (allow_split && tiles < 192) {
     for (int s : {8, 4, 2})
       if (K % (s * 64) == 0) {
@@ -217,8 +236,7 @@ SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split) {
       }
   }
   const int kps = K / p.splits;
-  if (tall) p.kc = 256;
-  else if (p.mt == 2) p.kc = kps % 128 == 0 ? 128 : 64;
+  if (p.mt == 2) p.kc = kps % 128 == 0 ? 128 : 64;
   else p.kc = kps % 256 == 0 ? 256 : (kps % 128 == 0 ? 128 : 64);
   return p;
 }
@@ -227,19 +245,21 @@ hipError_t launch_skinny(const void* x, const void* w, int M, int N, int K, int 
                          void* out, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const int wrows = epi == kEpiSiluMul ? 2 * N : N;
-  if (M > 64 || wrows % (64 * p.nt) != 0 || K % (p.splits * p.kc) != 0) return hipErrorInvalidValue;
-  if (epi == kEpiSiluMul && p.splits != 1) return hipErrorInvalidValue;
+  const int rows_per_wg = 16 * p.nt * p.nw;
+  if (M > 64 || wrows % rows_per_wg != 0 || K % (p.splits * p.kc) != 0) return hipErrorInvalidValue;
+  if (epi == kEpiSiluMul && (p.splits != 1 || p.nt % 2 != 0)) return hipErrorInvalidValue;
   if (p.splits != 1 && epi != kEpiPartial) return hipErrorInvalidValue;
-  dim3 grid(wrows / (64 * p.nt), p.splits);
+  if (p.nw != 4 && p.nw != 7) return hipErrorInvalidValue;
+  dim3 grid(wrows / rows_per_wg, p.splits);
   const int kps = K / p.splits;
   const bf16* xb = (const bf16*)x;
   const bf16* wb = (const bf16*)w;
-  if (p.mt == 1) return launch_kc<1, 2>(p.kc, xb, M, wb, K, kps, epi, out, N, grid, s);
+  if (p.mt == 1) return launch_kc<1, 2>(p.kc, p.nw, xb, M, wb, K, kps, epi, out, N, grid, s);
   if (p.mt == 2) {
-    if (p.nt == 4) return launch3<2, 4, 256>(xb, M, wb, K, kps, epi, out, N, grid, s);
-    return launch_kc<2, 2>(p.kc, xb, M, wb, K, kps, epi, out, N, grid, s);
+    if (p.nt == 4) return launch3<2, 4, 256, 4>(xb, M, wb, K, kps, epi, out, N, grid, s);
+    return launch_kc<2, 2>(p.kc, p.nw, xb, M, wb, K, kps, epi, out, N, grid, s);
   }
-  return launch_kc<4, 2>(p.kc, xb, M, wb, K, kps, epi, out, N, grid, s);
+  return launch_kc<4, 2>(p.kc, p.nw, xb, M, wb, K, kps, epi, out, N, grid, s);
 }
 
 hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, void* out, hipStream_t s) {

@@ -25,9 +25,10 @@ const char* linear_kernel_name(int dtype, int M);
 // gemm_skinny.hip: bf16, M <= 64.  N = output features (SiluMul: W has 2N
 // rows).  kEpiPartial writes fp32 partial sums [splits][M][N].
 struct SkinnyPlan {
-  int mt, nt, kc, splits;
+  int mt, nt, nw, kc, splits;  // token tiles, row tiles per wave, waves, K chunk, K splits
 };
-SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split);
+SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split, int num_cus);
+int device_cu_count();
 hipError_t launch_skinny(const void* x, const void* w, int M, int N, int K, int epi, const SkinnyPlan& p,
                          void* out, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, void* out, hipStream_t s);
@@ -46,7 +47,7 @@ struct AttnPlan {
   int part_len;     // keys per partition
   size_t ws_bytes;  // fp32 partial results
 };
-AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_len);
+AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_len, int num_cus);
 hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
                             int nkv, int d, const void* k_cache, const void* v_cache,
                             const int* block_table, int max_blocks, int q_len,
