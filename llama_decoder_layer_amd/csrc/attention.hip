@@ -217,13 +217,18 @@ AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_le
   if (q_len == 1) {
     // decode: long-running workgroups stream best, so the keys of a
     // (sequence, KV head) are split only as far as needed to give every
-    // compute unit a workgroup; partitions are multiples of 64 keys (four
-    // waves x 16-slot blocks)
+    // compute unit a workgroup, and no partition is longer than
+    // kMaxDecodePart keys so that one long sequence in a ragged batch does
+    // not leave a single workgroup streaming long after the rest have
+    // finished; partitions are multiples of 64 keys (four waves x 16-slot
+    // blocks)
+    constexpr int kMaxDecodePart = 4096;
     const int groups = T * nkv;
     const int cus = num_cus > 0 ? num_cus : 256;
     const int want = (cus + groups - 1) / groups;
     int len = (max_seq_len + want - 1) / want;
     len = (len + 63) / 64 * 64;
+    if (len > kMaxDecodePart) len = kMaxDecodePart;
     pl.part_len = len < 64 ? 64 : len;
     pl.parts = (max_seq_len + pl.part_len - 1) / pl.part_len;
   } else {

@@ -42,11 +42,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// BPI: cache blocks a wave takes per iteration (its blocks j and j + 4).
-// With two, the P.V product pairs the blocks' keys in one MFMA (a lane's
-// four keys of each block fill its eight k-slots) and the softmax update runs
-// once per 32 keys.
-template <int D, int BPI>
+// Grid: (token * KV heads + KV head, partition).  The KV heads of a token
+// are adjacent in launch order, so the workgroups that run together walk the same
+// scattered cache blocks (the heads of a block are contiguous in the pool).
+template <int D>
 __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
     const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
     const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
@@ -55,7 +54,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
   constexpr int KS = D / 32;  // k-steps of S = K q^T
   constexpr int DT = D / 16;  // 16-wide output tiles of P V
   const int G = nq / nkv;
-  const int t = blockIdx.x, g = blockIdx.y, part = blockIdx.z;
+  const int g = blockIdx.x % nkv, t = blockIdx.x / nkv, part = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
@@ -94,65 +93,43 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
   const int jb = k_begin / kKvBlock, je = (k_end + kKvBlock - 1) / kKvBlock;
   const size_t head_stride = (size_t)kKvBlock * D;
 
-  // fragments of the wave's BPI blocks: K rows (A of S) and V slots (B of P.V)
-  bf16x8 kf[BPI][KS];
-  bf16x4 vf[BPI][DT];
-  auto load = [&](int j0) {
+  // fragments of the wave's next block: K rows (A of S), V slots (B of P.V)
+  bf16x8 kf[KS];
+  bf16x4 vf[DT];
+  auto load = [&](int j) {
+    const int blk = bt[j];
+    const bf16* kb = kc + ((size_t)blk * nkv + g) * head_stride + (size_t)l16 * D + 8 * grp;
+    const bf16* vb = vc + ((size_t)blk * nkv + g) * head_stride + (size_t)l16 * kKvBlock + 4 * grp;
 #pragma unroll
-    for (int u = 0; u < BPI; ++u) {
-      const int j = j0 + u * kWaves;
-      if (j < je) {
-        const int blk = bt[j];
-        const bf16* kb = kc + ((size_t)blk * nkv + g) * head_stride + (size_t)l16 * D + 8 * grp;
-        const bf16* vb = vc + ((size_t)blk * nkv + g) * head_stride + (size_t)l16 * kKvBlock + 4 * grp;
+    for (int s = 0; s < KS; ++s) kf[s] = ld16<bf16x8>(kb + 32 * s);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kf[u][s] = ld16<bf16x8>(kb + 32 * s);
-#pragma unroll
-        for (int i = 0; i < DT; ++i) vf[u][i] = *reinterpret_cast<const bf16x4*>(vb + (size_t)i * 16 * kKvBlock);
-      } else {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kf[u][s] = zero8;
-#pragma unroll
-        for (int i = 0; i < DT; ++i) vf[u][i] = zero4;
-      }
-    }
+    for (int i = 0; i < DT; ++i) vf[i] = *reinterpret_cast<const bf16x4*>(vb + (size_t)i * 16 * kKvBlock);
   };
 
-  constexpr int STEP = kWaves * BPI;
   int j = jb + wave;
   if (j < je) load(j);
-  for (; j < je; j += STEP) {
-    bf16x8 kcur[BPI][KS];
-    bf16x4 vcur[BPI][DT];
+  for (; j < je; j += kWaves) {
+    bf16x8 kcur[KS];
+    bf16x4 vcur[DT];
 #pragma unroll
-    for (int u = 0; u < BPI; ++u) {
+    for (int s = 0; s < KS; ++s) kcur[s] = kf[s];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kcur[u][s] = kf[u][s];
-#pragma unroll
-      for (int i = 0; i < DT; ++i) vcur[u][i] = vf[u][i];
-    }
-    if (j + STEP < je) load(j + STEP);
+    for (int i = 0; i < DT; ++i) vcur[i] = vf[i];
+    if (j + kWaves < je) load(j + kWaves);
 
-    f32x4 sacc[BPI];
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < BPI; ++u) {
-      sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) sacc[u] = mfma16(kcur[u][s], qf[s], sacc[u]);
-    }
+    for (int s = 0; s < KS; ++s) sacc = mfma16(kcur[s], qf[s], sacc);
 
-    bool valid[BPI][4];
-    float sv[BPI][4];
+    bool valid[4];
+    float sv[4];
     float bm = -INFINITY;
+    const int key0 = j * kKvBlock + 4 * grp;
 #pragma unroll
-    for (int u = 0; u < BPI; ++u) {
-      const int key0 = (j + u * kWaves) * kKvBlock + 4 * grp;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        valid[u][r] = (key0 + r >= k_begin) && (key0 + r < k_end);
-        sv[u][r] = valid[u][r] ? sacc[u][r] * sc : -INFINITY;
-        bm = fmaxf(bm, sv[u][r]);
-      }
+    for (int r = 0; r < 4; ++r) {
+      valid[r] = (key0 + r >= k_begin) && (key0 + r < k_end);
+      sv[r] = valid[r] ? sacc[r] * sc : -INFINITY;
+      bm = fmaxf(bm, sv[r]);
     }
     bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
     bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
@@ -161,13 +138,11 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
     float ps = 0.f;
     bf16x8 pa = zero8;
 #pragma unroll
-    for (int u = 0; u < BPI; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(sv[u][r] - m_new);
-        ps += pv;
-        pa[4 * u + r] = static_cast<bf16>(pv);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(sv[r] - m_new);
+      ps += pv;
+      pa[r] = static_cast<bf16>(pv);
+    }
     l_run = l_run * alpha + ps;
     m_run = m_new;
 
@@ -179,9 +154,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
     for (int i = 0; i < DT; ++i) {
       bf16x8 vb = zero8;
 #pragma unroll
-      for (int u = 0; u < BPI; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vb[4 * u + r] = valid[u][r] ? vcur[u][i][r] : static_cast<bf16>(0.f);
+      for (int r = 0; r < 4; ++r) vb[r] = valid[r] ? vcur[i][r] : static_cast<bf16>(0.f);
       f32x4 acc = o[i];
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] *= ah[r];
@@ -230,12 +203,12 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
   }
 }
 
-template <int D, int BPI>
+template <int D>
 hipError_t launch_dec(const void* q, int ldq, int T, const int* positions, int nq, int nkv, const void* k_cache,
                       const void* v_cache, const int* block_table, int max_blocks, int q_len, int part_len,
                       int parts, float* partials, void* out, hipStream_t s) {
-  dim3 grid(T, nkv, parts);
-  decode_attention_mfma<D, BPI><<<grid, kWaves * kWave, 0, s>>>(
+  dim3 grid(T * nkv, parts);
+  decode_attention_mfma<D><<<grid, kWaves * kWave, 0, s>>>(
       (const bf16*)q, ldq, positions, nq, nkv, (const bf16*)k_cache, (const bf16*)v_cache, block_table,
       max_blocks, q_len, part_len, parts, partials, (bf16*)out);
   return hipGetLastError();
@@ -248,10 +221,10 @@ hipError_t launch_decode_attention_bf16(const void* q, int ldq, int T, const int
                                         int max_blocks, int q_len, int part_len, int parts, float* partials,
                                         void* out, hipStream_t s) {
   if (d == 128)
-    return launch_dec<128, 1>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, q_len,
-                              part_len, parts, partials, out, s);
-  return launch_dec<64, 1>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, q_len,
+    return launch_dec<128>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, q_len,
                            part_len, parts, partials, out, s);
+  return launch_dec<64>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, q_len, part_len,
+                        parts, partials, out, s);
 }
 
 }  // namespace llk
