@@ -76,7 +76,7 @@ constexpr int kTBK = 64;  // k per LDS stage
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __restrict__ X, int M,
                                                                const bf16* __restrict__ W, int N, int K,
-                                                               bf16* out, int ldo, int xcd_remap) {
+                                                               WStride ws, bf16* out, int ldo, int xcd_remap) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;     // wave tile: tokens x weight rows
   constexpr int SM = TM / 16, SN = TN / 16;     // 16x16 MFMA tiles per wave
@@ -102,14 +102,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
   const int n0 = (bid / num_m) * BN;
 
   // this lane's source chunk in each 8-row piece: LDS slot (row, lane & 7)
-  // holds logical chunk (lane & 7) ^ (row & 7)
+  // holds logical chunk (lane & 7) ^ (row & 7), i.e. k = 8 * chunk within the
+  // stage; the weight layout's strides place (row, k)
   const int prow = lane >> 3, pc = lane & 7;
   const bf16* wsrc[WJ];
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
-    const int row = (j * NW + wave) * 8 + prow;
-    wsrc[j] = W + (size_t)(n0 + row) * K + ((pc ^ (row & 7)) << 3);
+    const int row = n0 + (j * NW + wave) * 8 + prow;
+    const int ch = pc ^ (row & 7);
+    wsrc[j] = W + (size_t)(row & ~15) * K + (size_t)(row & 15) * ws.rs + (size_t)(ch >> 2) * ws.ks + (ch & 3) * 8;
   }
+  const size_t wstage = (size_t)(kTBK / 32) * ws.ks;  // weight offset of one k stage
   const bf16* xsrc[XJ];
 #pragma unroll
   for (int j = 0; j < XJ; ++j) {
@@ -117,11 +120,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
     const int m = min(m0 + row, M - 1);
     xsrc[j] = X + (size_t)m * K + ((pc ^ (row & 7)) << 3);
   }
-  auto issue = [&](int buf, int k0) {
+  auto issue = [&](int buf, int kt) {
+    const int k0 = kt * kTBK;
 #pragma unroll
     for (int j = 0; j < WJ; ++j)
       __builtin_amdgcn_global_load_lds(
-          (const void*)(wsrc[j] + k0),
+          (const void*)(wsrc[j] + kt * wstage),
           (__attribute__((address_space(3))) void*)(sW + buf * BN * kTBK + (j * NW + wave) * 8 * kTBK), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < XJ; ++j)
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) issue(buf ^ 1, (kt + 1) * kTBK);
+    if (kt + 1 < nk) issue(buf ^ 1, kt + 1);
 #pragma unroll
     for (int s = 0; s < kTBK / 32; ++s) {
       const int c = s * 4 + g;
@@ -194,7 +198,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
 }
 
 template <int BM, int BN, int WM, int WN, int EPI>
-hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, bf16* out, int ldo, hipStream_t s) {
+hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, WStride ws, bf16* out, int ldo,
+                       hipStream_t s) {
   auto fn = gemm_tile_bf16<BM, BN, WM, WN, EPI>;
   const size_t lds = (size_t)2 * (BM + BN) * kTBK * sizeof(bf16);
   static bool attr_set = false;  // per instantiation; the attribute is per function
@@ -204,7 +209,7 @@ hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, bf
     attr_set = true;
   }
   const int nb = ((M + BM - 1) / BM) * (wrows / BN);
-  fn<<<nb, 64 * WM * WN, lds, s>>>(x, M, w, wrows, K, out, ldo, nb % 8 == 0 ? 1 : 0);
+  fn<<<nb, 64 * WM * WN, lds, s>>>(x, M, w, wrows, K, ws, out, ldo, nb % 8 == 0 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -258,12 +263,28 @@ __global__ void reorder_gate_up_kernel(const bf16* __restrict__ src, int inter, 
 }
 
 template <int EPI>
-hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* out, hipStream_t s) {
+hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* out, hipStream_t s, int layout) {
   // rows of W the kernel walks: N (store/add) or 2N (silu_mul)
   const int wrows = (EPI == kEpiSiluMul) ? 2 * N : N;
-  if (M <= 64) return launch_skinny(x, w, M, N, K, EPI, skinny_plan(M, wrows, K, false, device_cu_count()), out, s);
-  if (M >= 256 && wrows % 256 == 0) return launch_tile<256, 256, 2, 4, EPI>(x, M, w, wrows, K, out, N, s);
-  return launch_tile<128, 128, 2, 2, EPI>(x, M, w, wrows, K, out, N, s);
+  if (M <= 64)
+    return launch_skinny(x, w, M, N, K, EPI, skinny_plan(M, wrows, K, false, device_cu_count()), out, s, layout);
+  const WStride ws = weight_stride(layout, K);
+  if (M >= 256 && wrows % 256 == 0) return launch_tile<256, 256, 2, 4, EPI>(x, M, w, wrows, K, ws, out, N, s);
+  return launch_tile<128, 128, 2, 2, EPI>(x, M, w, wrows, K, ws, out, N, s);
+}
+
+// one thread per 16-byte piece of the destination
+__global__ void tile_weight_kernel(const bf16* __restrict__ src, int rows, int K, int inter, bf16* __restrict__ dst) {
+  const size_t piece = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (piece >= (size_t)rows * K / 8) return;
+  const int r = (int)(piece * 8 / K), k = (int)(piece * 8 % K);
+  int sr = r;
+  if (inter > 0) {
+    const int grp = r >> 5, i = r & 31;
+    sr = i < 16 ? grp * 16 + i : inter + grp * 16 + (i - 16);
+  }
+  const size_t o = ((size_t)(r >> 4) * (K / 32) + (k >> 5)) * 512 + (r & 15) * 32 + (k & 31);
+  *reinterpret_cast<bf16x8*>(dst + o) = ld16<bf16x8>(src + (size_t)sr * K + k);
 }
 
 template <int EPI>
@@ -288,21 +309,20 @@ const char* linear_kernel_name(int dtype, int M) {
 }
 
 hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, int K, int epi,
-                         void* out, hipStream_t s) {
+                         void* out, hipStream_t s, int layout) {
   if (M <= 0) return hipSuccess;
   if (dtype == kBF16) {
     const bf16* xb = (const bf16*)x;
     const bf16* wb = (const bf16*)w;
     bf16* ob = (bf16*)out;
+    const int wrows = (epi == kEpiSiluMul) ? 2 * N : N;
+    if (layout == kTiled16x32 && (wrows % 16 != 0 || K % 32 != 0)) return hipErrorInvalidValue;
     // the tiled kernels walk weight rows in 128- or 256-row tiles
-    if (M > 64) {
-      const int wrows = (epi == kEpiSiluMul) ? 2 * N : N;
-      if (wrows % 128 != 0 || K % kTBK != 0) return hipErrorInvalidValue;
-    }
+    if (M > 64 && (wrows % 128 != 0 || K % kTBK != 0)) return hipErrorInvalidValue;
     switch (epi) {
-      case kEpiStore: return linear_bf16<kEpiStore>(xb, wb, M, N, K, ob, s);
-      case kEpiAdd: return linear_bf16<kEpiAdd>(xb, wb, M, N, K, ob, s);
-      default: return linear_bf16<kEpiSiluMul>(xb, wb, M, N, K, ob, s);
+      case kEpiStore: return linear_bf16<kEpiStore>(xb, wb, M, N, K, ob, s, layout);
+      case kEpiAdd: return linear_bf16<kEpiAdd>(xb, wb, M, N, K, ob, s, layout);
+      default: return linear_bf16<kEpiSiluMul>(xb, wb, M, N, K, ob, s, layout);
     }
   }
   const float* xf = (const float*)x;
@@ -317,6 +337,15 @@ hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, 
 
 hipError_t launch_reorder_gate_up(const void* src, int inter, int K, void* dst, hipStream_t s) {
   reorder_gate_up_kernel<<<2 * inter, 256, 0, s>>>((const bf16*)src, inter, K, (bf16*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_weight(const void* src, int rows, int K, int inter, void* dst, hipStream_t s) {
+  if (rows % 16 != 0 || K % 32 != 0 || (inter > 0 && rows != 2 * inter) || (inter > 0 && inter % 16 != 0))
+    return hipErrorInvalidValue;
+  const size_t pieces = (size_t)rows * K / 8;
+  if (pieces == 0) return hipSuccess;
+  tile_weight_kernel<<<(unsigned)((pieces + 255) / 256), 256, 0, s>>>((const bf16*)src, rows, K, inter, (bf16*)dst);
   return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 // streaming W from HBM once.  Design:
 //   * a workgroup owns NW waves x NT 16-row tiles of W and one K range
 //     (split-K across workgroups when W has few rows, so that enough
-//     workgroups stream concurrently).  NW is 4, or 7 when 7-wave
+//     workgroups stream concurrently).  NW is 4 or 5, chosen so that the
+//     workgroup count is a multiple of the CU count, or 7 when 7-wave
 //     workgroups tile a tall weight exactly onto the CUs (57344 rows = 256
 //     CUs x 7 waves x 32 rows): no partly empty last round;
 //   * the x slice of the current K chunk (M x KC) is staged once per
@@ -37,7 +38,7 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 template <int MT, int NT, int KC, int NW, int EPI>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(const bf16* __restrict__ X, int M,
                                                              const bf16* __restrict__ W, int K, int kps,
-                                                             void* __restrict__ out, int N) {
+                                                             WStride ws, void* __restrict__ out, int N) {
   constexpr int SPC = KC / 32;          // MFMA k-steps per chunk
   constexpr int XR = MT * 16;           // token rows staged
   constexpr int XCH = XR * KC / 8;      // 16-byte pieces of the x chunk
@@ -71,15 +72,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(const bf16* __restri
     }
   };
 
+  // lane (r16, g) reads row r16 of each 16-row strip, k-slots 8g .. 8g+7 of
+  // every 32-wide k block (the layout's strides place both)
   const bf16* wr[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) wr[t] = W + (size_t)(n0 + 16 * t + r16) * K + k0 + g * 8;
+  for (int t = 0; t < NT; ++t)
+    wr[t] = W + (size_t)(n0 + 16 * t) * K + (size_t)r16 * ws.rs + (size_t)(k0 / 32) * ws.ks + g * 8;
   bf16x8 wn[SPC][NT];
   auto wload = [&](int kc) {
 #pragma unroll
     for (int s = 0; s < SPC; ++s)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) wn[s][t] = ld16<bf16x8>(wr[t] + kc + s * 32);
+      for (int t = 0; t < NT; ++t) wn[s][t] = ld16<bf16x8>(wr[t] + (size_t)(kc / 32 + s) * ws.ks);
   };
 
   f32x4 acc[NT][MT];
@@ -175,35 +179,38 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 template <int MT, int NT, int KC, int NW>
-hipError_t launch3(const bf16* x, int M, const bf16* w, int K, int kps, int epi, void* out, int N, dim3 grid,
-                   hipStream_t s) {
+hipError_t launch3(const bf16* x, int M, const bf16* w, int K, int kps, WStride ws, int epi, void* out, int N,
+                   dim3 grid, hipStream_t s) {
   switch (epi) {
     case kEpiStore:
-      gemm_skinny_bf16<MT, NT, KC, NW, kEpiStore><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, out, N);
+      gemm_skinny_bf16<MT, NT, KC, NW, kEpiStore><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, ws, out, N);
       break;
     case kEpiAdd:
-      gemm_skinny_bf16<MT, NT, KC, NW, kEpiAdd><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, out, N);
+      gemm_skinny_bf16<MT, NT, KC, NW, kEpiAdd><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, ws, out, N);
       break;
     case kEpiSiluMul:
-      gemm_skinny_bf16<MT, NT, KC, NW, kEpiSiluMul><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, out, N);
+      gemm_skinny_bf16<MT, NT, KC, NW, kEpiSiluMul><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, ws, out, N);
       break;
     default:
-      gemm_skinny_bf16<MT, NT, KC, NW, kEpiPartial><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, out, N);
+      gemm_skinny_bf16<MT, NT, KC, NW, kEpiPartial><<<grid, NW * 64, 0, s>>>(x, M, w, K, kps, ws, out, N);
   }
   return hipGetLastError();
 }
 
-template <int MT, int NT>
-hipError_t launch_kc(int kc, int nw, const bf16* x, int M, const bf16* w, int K, int kps, int epi, void* out,
-                     int N, dim3 grid, hipStream_t s) {
-  if (nw == 7) {
-    if (kc == 256) return launch3<MT, NT, 256, 7>(x, M, w, K, kps, epi, out, N, grid, s);
-    if (kc == 128) return launch3<MT, NT, 128, 7>(x, M, w, K, kps, epi, out, N, grid, s);
-    return launch3<MT, NT, 64, 7>(x, M, w, K, kps, epi, out, N, grid, s);
-  }
-  if (kc == 256) return launch3<MT, NT, 256, 4>(x, M, w, K, kps, epi, out, N, grid, s);
-  if (kc == 128) return launch3<MT, NT, 128, 4>(x, M, w, K, kps, epi, out, N, grid, s);
-  return launch3<MT, NT, 64, 4>(x, M, w, K, kps, epi, out, N, grid, s);
+// The instantiated (MT, NT, KC, NW) shapes; skinny_plan only returns these.
+#define LLK_SKINNY_SHAPES(X)                                                                        \
+  X(1, 2, 64, 4) X(1, 2, 128, 4) X(1, 2, 256, 4) X(1, 2, 256, 7)                                   \
+  X(2, 2, 64, 4) X(2, 2, 128, 4) X(2, 2, 256, 4) X(2, 2, 64, 5) X(2, 2, 256, 7) X(2, 4, 256, 4)  \
+  X(4, 2, 64, 4) X(4, 2, 128, 4) X(4, 2, 256, 4) X(4, 1, 128, 5) X(4, 2, 256, 7)
+
+hipError_t launch_shape(const SkinnyPlan& p, const bf16* x, int M, const bf16* w, int K, int kps, WStride ws,
+                        int epi, void* out, int N, dim3 grid, hipStream_t s) {
+#define LLK_SKINNY_CASE(MT, NT, KC, NW)                      \
+  if (p.mt == MT && p.nt == NT && p.kc == KC && p.nw == NW) \
+    return launch3<MT, NT, KC, NW>(x, M, w, K, kps, ws, epi, out, N, grid, s);
+  LLK_SKINNY_SHAPES(LLK_SKINNY_CASE)
+#undef LLK_SKINNY_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -227,6 +234,26 @@ SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split, int num_cus) {
     p.kc = 256;
     return p;
   }
+  // Split-K: the first candidate whose workgroup count is a whole multiple
+  // of the CU count (every CU streams the same number of workgroups; a
+  // half-filled last round costs up to a fifth of the time).  The 4-wave
+  // candidate suits 8192-row weights, the 5-wave one 10240-row weights.
+  if (allow_split && num_cus > 0 && p.mt >= 2) {
+    struct Cand { int nt, nw, kc, splits; };
+    static const Cand c2[] = {{2, 4, 64, 8}, {2, 5, 64, 8}};
+    static const Cand c4[] = {{2, 4, 256, 8}, {1, 5, 128, 4}};
+    const Cand* c = p.mt == 2 ? c2 : c4;
+    for (int i = 0; i < 2; ++i) {
+      const int rows = 16 * c[i].nt * c[i].nw;
+      if (wrows % rows || K % (c[i].splits * c[i].kc)) continue;
+      if ((wrows / rows) * c[i].splits % num_cus) continue;
+      p.nt = c[i].nt;
+      p.nw = c[i].nw;
+      p.kc = c[i].kc;
+      p.splits = c[i].splits;
+      return p;
+    }
+  }
   const int tiles = wrows / (16 * p.nw * p.nt);
   if (allow_split && tiles < 192) {
     for (int s : {8, 4, 2})
@@ -242,24 +269,17 @@ SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split, int num_cus) {
 }
 
 hipError_t launch_skinny(const void* x, const void* w, int M, int N, int K, int epi, const SkinnyPlan& p,
-                         void* out, hipStream_t s) {
+                         void* out, hipStream_t s, int layout) {
   if (M <= 0) return hipSuccess;
   const int wrows = epi == kEpiSiluMul ? 2 * N : N;
   const int rows_per_wg = 16 * p.nt * p.nw;
   if (M > 64 || wrows % rows_per_wg != 0 || K % (p.splits * p.kc) != 0) return hipErrorInvalidValue;
   if (epi == kEpiSiluMul && (p.splits != 1 || p.nt % 2 != 0)) return hipErrorInvalidValue;
   if (p.splits != 1 && epi != kEpiPartial) return hipErrorInvalidValue;
-  if (p.nw != 4 && p.nw != 7) return hipErrorInvalidValue;
+  if (M > 16 * p.mt || K % 32 != 0) return hipErrorInvalidValue;
   dim3 grid(wrows / rows_per_wg, p.splits);
-  const int kps = K / p.splits;
-  const bf16* xb = (const bf16*)x;
-  const bf16* wb = (const bf16*)w;
-  if (p.mt == 1) return launch_kc<1, 2>(p.kc, p.nw, xb, M, wb, K, kps, epi, out, N, grid, s);
-  if (p.mt == 2) {
-    if (p.nt == 4) return launch3<2, 4, 256, 4>(xb, M, wb, K, kps, epi, out, N, grid, s);
-    return launch_kc<2, 2>(p.kc, p.nw, xb, M, wb, K, kps, epi, out, N, grid, s);
-  }
-  return launch_kc<4, 2>(p.kc, p.nw, xb, M, wb, K, kps, epi, out, N, grid, s);
+  return launch_shape(p, (const bf16*)x, M, (const bf16*)w, K, K / p.splits, weight_stride(layout, K), epi, out,
+                      N, grid, s);
 }
 
 hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, void* out, hipStream_t s) {
