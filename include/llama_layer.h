@@ -163,10 +163,20 @@ LLAMA_API size_t llama_layer_workspace_bytes(const llama_layer* layer, int32_t n
  *   block_table  [num_seqs][max_blocks_per_seq] int32 device.
  *   seq_lens     [num_seqs] int32 device: each sequence's KV length after
  *                this call (its cached context plus its new tokens).
- *   query_start_loc  must be NULL: the T tokens are num_seqs equal runs of
- *                T / num_seqs consecutive rows, one run per sequence, and
- *                the run of sequence b holds positions
- *                seq_lens[b] - T/num_seqs .. seq_lens[b] - 1 in order.
+ *   query_start_loc  NULL: the T tokens are num_seqs equal runs of
+ *                T / num_seqs consecutive rows, one run per sequence.
+ *                Otherwise [num_seqs + 1] int32 device: sequence b owns rows
+ *                query_start_loc[b] .. query_start_loc[b+1] - 1, with
+ *                query_start_loc[0] = 0, query_start_loc[num_seqs] = T and at
+ *                least one row per sequence.  This is a mixed batch: chunked
+ *                prefill on a cached context next to decode sequences (one
+ *                row each) in one call, the per-call metadata that the
+ *                attention backend of the vllm-learning page
+ *                "模型库与算子层 — 代码走读" (section "Attention 层") passes
+ *                with the block table.  At most 4096 sequences.  A mixed
+ *                batch adds one small kernel that maps rows to sequences.
+ *                Either way the run of sequence b holds positions
+ *                seq_lens[b] - n_b .. seq_lens[b] - 1 in order (n_b its rows).
  *   max_seq_len  host-side upper bound of seq_lens (sizes the launch).
  *   hidden_out, residual_out  [T, H] device: the output pair.  residual_out
  *                = (hidden + residual) + o_proj(attention) (the stream value
@@ -178,12 +188,14 @@ LLAMA_API size_t llama_layer_workspace_bytes(const llama_layer* layer, int32_t n
  *                bytes of device memory, 256-byte aligned.
  * The call writes only hidden_out, residual_out, the new tokens' KV slots and
  * the workspace.  Preconditions on device data (block ids < num_blocks,
- * positions < max_position_embeddings and consistent with seq_lens) are not
- * checked on the device.
- * Errors: INVALID_ARGUMENT (NULL pointer, T % num_seqs != 0, T/num_seqs >
- * max_seq_len, max_seq_len > max_position_embeddings or >
- * 16 * max_blocks_per_seq, aliasing outputs), UNSUPPORTED (query_start_loc
- * != NULL), HIP. */
+ * positions < max_position_embeddings and consistent with seq_lens, the
+ * query_start_loc conditions above) are not checked on the device; a
+ * query_start_loc that breaks them gives wrong rows, but the row map stays
+ * inside [0, T) and [0, num_seqs).
+ * Errors: INVALID_ARGUMENT (NULL pointer; T % num_seqs != 0 with
+ * query_start_loc NULL; T < num_seqs; T/num_seqs > max_seq_len; max_seq_len >
+ * max_position_embeddings or > 16 * max_blocks_per_seq; aliasing outputs),
+ * UNSUPPORTED (more than 4096 sequences in a mixed batch), HIP. */
 LLAMA_API llama_status llama_layer_forward(llama_layer* layer, const void* hidden, const void* residual,
                                  const int32_t* positions, int32_t num_tokens,
                                  const llama_kv_cache* kv_cache, const int32_t* block_table,

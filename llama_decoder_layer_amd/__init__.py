@@ -234,6 +234,10 @@ class Layer:
         _dev(seq_lens, "seq_lens", torch.int32)
         _dev(k_cache, "k_cache", self.dtype)
         _dev(v_cache, "v_cache", self.dtype)
+        if query_start_loc is not None:
+            _dev(query_start_loc, "query_start_loc", torch.int32)
+            if tuple(query_start_loc.shape) != (B + 1,):
+                raise ValueError("query_start_loc must have num_seqs + 1 entries")
         if hidden_out is None:
             hidden_out = torch.empty_like(hidden)
         if residual_out is None:

@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "llama_layer")
 LIB = os.path.join(HERE, "libllama_layer.so")
 
-SOURCES = ["api.cpp", "rmsnorm.hip", "gemm.hip", "rope_kv.hip", "attention.hip", "attention_decode.hip", "gemm_skinny.hip", "attention_prefill.hip"]
+SOURCES = ["api.cpp", "rmsnorm.hip", "gemm.hip", "rope_kv.hip", "attention.hip", "attention_decode.hip", "gemm_skinny.hip",
+           "attention_prefill.hip", "batch_map.hip"]
 ARCH = "gfx950"
 
 

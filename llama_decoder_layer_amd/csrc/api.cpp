@@ -94,7 +94,8 @@ struct llama_layer {
 namespace {
 
 struct Workspace {
-  size_t h, qkv, attn, h2, act, part, gpart, total;
+  size_t h, qkv, attn, h2, act, part, gpart, seq_of, ntiles, tiles, total;
+  int tile_cap;  // entries of the prefill tile table (mixed batches)
   llk::AttnPlan plan;
   bool skinny;  // few tokens: weight-streaming projections with split-K partials
   llk::SkinnyPlan pq, po, pg, pd;
@@ -103,8 +104,7 @@ struct Workspace {
 Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   const llama_layer_config& c = L->cfg;
   Workspace w{};
-  const int q_len = (B > 0 && T % B == 0) ? T / B : 1;
-  w.plan = llk::attention_plan(T, c.num_attention_heads, c.num_key_value_heads, c.head_dim, q_len, max_seq_len,
+  w.plan = llk::attention_plan(T, c.num_attention_heads, c.num_key_value_heads, c.head_dim, T == B, max_seq_len,
                               L->num_cus);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -132,6 +132,12 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
     gpart = n * T * sizeof(float);
   }
   w.gpart = take(gpart);
+  // mixed batches: row -> sequence map and the prefill tile table (tiles of
+  // at least 16 rows, so T/16 + B entries bound any sequence mix)
+  w.tile_cap = T / 16 + B + 1;
+  w.seq_of = take((size_t)T * sizeof(int));
+  w.ntiles = take(sizeof(int));
+  w.tiles = take((size_t)w.tile_cap * sizeof(int4));
   w.total = off;
   return w;
 }
@@ -366,10 +372,18 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   if (!hidden || !positions || !kv || !kv->k || !kv->v || !block_table || !seq_lens || !hidden_out ||
       !residual_out || !workspace)
     return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  if (query_start_loc) return fail(LLAMA_ERR_UNSUPPORTED, "query_start_loc must be NULL");
-  if (T <= 0 || B <= 0 || T % B != 0)
-    return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_tokens %d must be a positive multiple of num_seqs %d", T, B);
-  const int q_len = T / B;
+  if (T <= 0 || B <= 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_tokens %d and num_seqs %d must be positive", T, B);
+  if (!query_start_loc && T % B != 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT,
+                "num_tokens %d must be a multiple of num_seqs %d when query_start_loc is NULL", T, B);
+  if (query_start_loc && T < B)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_tokens %d < num_seqs %d: every sequence needs a query row", T, B);
+  // T == B: one query row per sequence (decode), whatever query_start_loc says
+  const bool decode = T == B;
+  const bool mixed = query_start_loc && !decode;
+  if (mixed && B > llk::kMaxMappedSeqs)
+    return fail(LLAMA_ERR_UNSUPPORTED, "num_seqs %d above %d with query_start_loc", B, llk::kMaxMappedSeqs);
+  const int q_len = mixed ? 1 : T / B;  // a lower bound on every sequence's query rows
   const llama_layer_config& c = L->cfg;
   if (max_seq_len < q_len || max_seq_len > c.max_position_embeddings)
     return fail(LLAMA_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [%d, %d]", max_seq_len, q_len,
@@ -400,6 +414,21 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
 
   Marker mk(L, s);
   hipError_t e;
+  llk::SeqMap map;
+  map.q_len = mixed ? 0 : T / B;
+  if (mixed) {
+    const int qw = dt == LLAMA_DTYPE_BF16 && llk::prefill_attention_supported(nq, nkv, d)
+                       ? llk::prefill_tile_rows(nq, nkv, d)
+                       : 16;  // the generic kernel reads only the row map
+    map.seq_of = (const int*)(ws + w.seq_of);
+    map.tiles = (const int4*)(ws + w.tiles);
+    map.ntiles = (const int*)(ws + w.ntiles);
+    map.tile_cap = T / qw + B;
+    e = llk::launch_batch_map(query_start_loc, B, T, qw, (int*)(ws + w.seq_of), (int4*)(ws + w.tiles),
+                              w.tile_cap, (int*)(ws + w.ntiles), s);
+    if (e != hipSuccess) return hip_fail(e, "batch_map");
+    mk.mark("batch_map");
+  }
   e = llk::launch_add_rmsnorm(dt, hidden, residual, L->w_in, c.rms_norm_eps, T, H, h, residual_out, s);
   if (e != hipSuccess) return hip_fail(e, "input_layernorm");
   mk.mark("input_layernorm");
@@ -408,20 +437,20 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
     e = llk::launch_skinny(h, L->w_qkv, T, L->qkv_n, H, llk::kEpiPartial, w.pq, gp, s, L->wlayout);
     if (e != hipSuccess) return hip_fail(e, "qkv_proj");
     mk.mark("qkv_proj");
-    e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, q_len, kv->k,
+    e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, map, kv->k,
                             kv->v, s, gp, w.pq.splits);
   } else {
     e = llk::launch_linear(dt, h, L->w_qkv, T, L->qkv_n, H, llk::kEpiStore, qkv, s, L->wlayout);
     if (e != hipSuccess) return hip_fail(e, "qkv_proj");
     mk.mark("qkv_proj");
-    e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, q_len, kv->k,
+    e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, map, kv->k,
                             kv->v, s);
   }
   if (e != hipSuccess) return hip_fail(e, "rope_kv_write");
   mk.mark("rope_kv_write");
   hipEvent_t mid = w.plan.parts > 1 ? mk.extra() : nullptr;
   e = llk::launch_attention(dt, qkv, L->qkv_n, T, positions, nq, nkv, d, kv->k, kv->v, block_table, max_blocks,
-                            q_len, w.plan, part, attn, s, mid);
+                            map, decode, w.plan, part, attn, s, mid);
   if (e != hipSuccess) return hip_fail(e, "attention");
   if (mid) mk.list->push_back({"attention", mid});
   mk.mark(w.plan.parts > 1 ? "attention_combine" : "attention");

@@ -31,7 +31,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void paged_attention_kernel(
     const T* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
     const T* __restrict__ kc, const T* __restrict__ vc, const int* __restrict__ block_table,
-    int max_blocks, int q_len, int part_len, int parts, float* __restrict__ partials,
+    int max_blocks, SeqMap map, int part_len, int parts, float* __restrict__ partials,
     T* __restrict__ out) {
   using V = typename Vec16<T>::type;
   constexpr int VN = Vec16<T>::N;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(
   const int g = blockIdx.y;
   const int part = blockIdx.z;
   const int p = positions[t];
-  const int b = t / q_len;
+  const int b = map.seq(t);
   const int k_begin = part * part_len;
   const int k_end = min(p + 1, k_begin + part_len);
   const int* bt = block_table + (size_t)b * max_blocks;
@@ -194,11 +194,11 @@ __global__ __launch_bounds__(D) void attention_combine_kernel(const float* __res
 
 template <typename T, int D>
 hipError_t attention_typed(const T* q, int ldq, int T_, const int* positions, int nq, int nkv,
-                           const T* kc, const T* vc, const int* block_table, int max_blocks, int q_len,
+                           const T* kc, const T* vc, const int* block_table, int max_blocks, const SeqMap& map,
                            const AttnPlan& plan, float* partials, T* out, hipStream_t s) {
   dim3 grid(T_, nkv, plan.parts);
   paged_attention_kernel<T, D><<<grid, kThreads, 0, s>>>(q, ldq, positions, nq, nkv, kc, vc, block_table,
-                                                         max_blocks, q_len, plan.part_len, plan.parts,
+                                                         max_blocks, map, plan.part_len, plan.parts,
                                                          partials, out);
   return hipGetLastError();
 }
@@ -212,9 +212,9 @@ hipError_t combine(int d, int T_, int nq, int parts, const float* partials, void
 
 }  // namespace
 
-AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_len, int num_cus) {
+AttnPlan attention_plan(int T, int nq, int nkv, int d, bool decode, int max_seq_len, int num_cus) {
   AttnPlan pl;
-  if (q_len == 1) {
+  if (decode) {
     // decode: long-running workgroups stream best, so the keys of a
     // (sequence, KV head) are split only as far as needed to give every
     // compute unit a workgroup, and no partition is longer than
@@ -242,29 +242,30 @@ AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_le
 
 hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
                             int nkv, int d, const void* k_cache, const void* v_cache,
-                            const int* block_table, int max_blocks, int q_len, const AttnPlan& plan,
-                            float* partials, void* out, hipStream_t s, hipEvent_t mid_event) {
+                            const int* block_table, int max_blocks, const SeqMap& map, bool decode,
+                            const AttnPlan& plan, float* partials, void* out, hipStream_t s, hipEvent_t mid_event) {
   if (T <= 0) return hipSuccess;
   hipError_t e;
-  if (dtype == kBF16 && q_len == 1) {
+  if (dtype == kBF16 && decode) {
+    // one query row per sequence: row t is sequence t
     e = launch_decode_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table,
-                                     max_blocks, q_len, plan.part_len, plan.parts, partials, out, s);
+                                     max_blocks, plan.part_len, plan.parts, partials, out, s);
   } else if (dtype == kBF16 && plan.parts == 1 && prefill_attention_supported(nq, nkv, d)) {
     return launch_prefill_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table,
-                                         max_blocks, q_len, out, s);
+                                         max_blocks, map, out, s);
   } else if (dtype == kBF16) {
     e = d == 128 ? attention_typed<bf16, 128>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
-                                              (const bf16*)v_cache, block_table, max_blocks, q_len, plan,
+                                              (const bf16*)v_cache, block_table, max_blocks, map, plan,
                                               partials, (bf16*)out, s)
                  : attention_typed<bf16, 64>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
-                                             (const bf16*)v_cache, block_table, max_blocks, q_len, plan, partials,
+                                             (const bf16*)v_cache, block_table, max_blocks, map, plan, partials,
                                              (bf16*)out, s);
   } else {
     e = d == 128 ? attention_typed<float, 128>((const float*)q, ldq, T, positions, nq, nkv,
                                                (const float*)k_cache, (const float*)v_cache, block_table,
-                                               max_blocks, q_len, plan, partials, (float*)out, s)
+                                               max_blocks, map, plan, partials, (float*)out, s)
                  : attention_typed<float, 64>((const float*)q, ldq, T, positions, nq, nkv, (const float*)k_cache,
-                                              (const float*)v_cache, block_table, max_blocks, q_len, plan,
+                                              (const float*)v_cache, block_table, max_blocks, map, plan,
                                               partials, (float*)out, s);
   }
   if (e != hipSuccess || plan.parts == 1) return e;

@@ -49,7 +49,7 @@ template <int D>
 __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
     const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
     const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
-    int max_blocks, int q_len, int part_len, int parts, float* __restrict__ partials,
+    int max_blocks, int part_len, int parts, float* __restrict__ partials,
     bf16* __restrict__ out) {
   constexpr int KS = D / 32;  // k-steps of S = K q^T
   constexpr int DT = D / 16;  // 16-wide output tiles of P V
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
   const int p = positions[t];
-  const int b = t / q_len;
+  const int b = t;  // one query row per sequence
   const int k_begin = part * part_len;
   const int k_end = min(p + 1, k_begin + part_len);
 
@@ -205,12 +205,12 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
 
 template <int D>
 hipError_t launch_dec(const void* q, int ldq, int T, const int* positions, int nq, int nkv, const void* k_cache,
-                      const void* v_cache, const int* block_table, int max_blocks, int q_len, int part_len,
+                      const void* v_cache, const int* block_table, int max_blocks, int part_len,
                       int parts, float* partials, void* out, hipStream_t s) {
   dim3 grid(T * nkv, parts);
   decode_attention_mfma<D><<<grid, kWaves * kWave, 0, s>>>(
       (const bf16*)q, ldq, positions, nq, nkv, (const bf16*)k_cache, (const bf16*)v_cache, block_table,
-      max_blocks, q_len, part_len, parts, partials, (bf16*)out);
+      max_blocks, part_len, parts, partials, (bf16*)out);
   return hipGetLastError();
 }
 
@@ -218,12 +218,12 @@ hipError_t launch_dec(const void* q, int ldq, int T, const int* positions, int n
 
 hipError_t launch_decode_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
                                         int d, const void* k_cache, const void* v_cache, const int* block_table,
-                                        int max_blocks, int q_len, int part_len, int parts, float* partials,
+                                        int max_blocks, int part_len, int parts, float* partials,
                                         void* out, hipStream_t s) {
   if (d == 128)
-    return launch_dec<128>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, q_len,
+    return launch_dec<128>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks,
                            part_len, parts, partials, out, s);
-  return launch_dec<64>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, q_len, part_len,
+  return launch_dec<64>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, part_len,
                         parts, partials, out, s);
 }
 

@@ -64,7 +64,7 @@ template <int D, int HPW, int QT, int NW>
 __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
     const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
     const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
-    int max_blocks, int q_len, int num_qtiles, bf16* __restrict__ out) {
+    int max_blocks, SeqMap map, int num_qtiles, bf16* __restrict__ out) {
   constexpr int KS = D / 32;        // d-steps of S^T
   constexpr int DT = D / 16;        // 16-wide d tiles of O
   constexpr int CH = D / 8;         // 16-byte chunks per K row
@@ -76,17 +76,33 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
   __shared__ __attribute__((aligned(16))) bf16 sV[2][D * kKT];
 
   const int G = nq / nkv;
-  const int qt = num_qtiles - 1 - (int)(blockIdx.x % num_qtiles);  // longest tiles first
-  const int b = blockIdx.x / num_qtiles;
+  // this workgroup's query tile: qt of sequence b, whose rows are
+  // t_begin .. t_begin+qn-1.  Uniform batch: from the grid, longest tiles
+  // first; mixed batch: from the tile table (a bound-sized grid; workgroups
+  // past the table's length have nothing to do).
+  int b, qt, t_begin, qn;
+  if (map.tiles) {
+    if ((int)blockIdx.x >= *map.ntiles) return;
+    const int4 e = map.tiles[blockIdx.x];
+    b = e.x;
+    qt = e.y;
+    t_begin = e.z;
+    qn = e.w;
+  } else {
+    qt = num_qtiles - 1 - (int)(blockIdx.x % num_qtiles);
+    b = blockIdx.x / num_qtiles;
+    t_begin = b * map.q_len;
+    qn = map.q_len;
+  }
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
 
-  const int t0 = b * q_len + qt * QW;                       // first token row of the tile
-  const int nvalid = min(QW, q_len - qt * QW);              // query rows of the tile
+  const int t0 = t_begin + qt * QW;                         // first token row of the tile
+  const int nvalid = min(QW, qn - qt * QW);                 // query rows of the tile
   const int p0 = positions[t0];                             // position of the tile's first query
-  const int p_last = positions[b * q_len + q_len - 1];      // last written key of the sequence
+  const int p_last = positions[t_begin + qn - 1];           // last written key of the sequence
   const int key_end = min(p0 + QW - 1, p_last) + 1;         // keys this tile needs
   const int ntiles = (key_end + kKT - 1) / kKT;
   const int* bt = block_table + (size_t)b * max_blocks;
@@ -307,16 +323,29 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
 
 template <int D, int HPW, int QT, int NW>
 hipError_t launch_pf(const void* q, int ldq, int T, const int* positions, int nq, int nkv, const void* k_cache,
-                     const void* v_cache, const int* block_table, int max_blocks, int q_len, void* out,
+                     const void* v_cache, const int* block_table, int max_blocks, const SeqMap& map, void* out,
                      hipStream_t s) {
-  const int B = T / q_len;
-  const int nqt = (q_len + kQ * QT - 1) / (kQ * QT);
-  dim3 grid(B * nqt, nkv);
+  int nqt = 0, wgs;
+  if (map.tiles) {
+    wgs = map.tile_cap;
+  } else {
+    nqt = (map.q_len + kQ * QT - 1) / (kQ * QT);
+    wgs = T / map.q_len * nqt;
+  }
+  if (wgs <= 0) return hipSuccess;
+  dim3 grid(wgs, nkv);
   prefill_attention_mfma<D, HPW, QT, NW><<<grid, NW * kWave, 0, s>>>(
       (const bf16*)q, ldq, positions, nq, nkv, (const bf16*)k_cache, (const bf16*)v_cache, block_table,
-      max_blocks, q_len, nqt, (bf16*)out);
+      max_blocks, map, nqt, (bf16*)out);
   return hipGetLastError();
 }
+
+// (HPW, QT, NW) per head dimension and group size: one query head per wave
+// and 32 queries per workgroup where the group allows; two waves per SIMD
+// overlap one wave's softmax with another's MFMAs
+#define LLK_PF_CONFIGS(X)                                         \
+  X(128, 4, 1, 2, 4) X(128, 8, 1, 2, 8) X(128, 16, 2, 1, 8)       \
+  X(64, 4, 1, 2, 4) X(64, 8, 1, 2, 8) X(64, 16, 2, 1, 8)
 
 }  // namespace
 
@@ -325,23 +354,26 @@ bool prefill_attention_supported(int nq, int nkv, int d) {
   return (d == 64 || d == 128) && (G == 4 || G == 8 || G == 16);
 }
 
+int prefill_tile_rows(int nq, int nkv, int d) {
+  const int G = nq / nkv;
+#define LLK_PF_ROWS(DD, GG, HH, QQ, WW) \
+  if (d == DD && G == GG) return kQ * QQ;
+  LLK_PF_CONFIGS(LLK_PF_ROWS)
+#undef LLK_PF_ROWS
+  return 0;
+}
+
 hipError_t launch_prefill_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
                                          int d, const void* k_cache, const void* v_cache, const int* block_table,
-                                         int max_blocks, int q_len, void* out, hipStream_t s) {
+                                         int max_blocks, const SeqMap& map, void* out, hipStream_t s) {
   const int G = nq / nkv;
-#define LLK_PF(DD, HH, QQ, WW) \
-  return launch_pf<DD, HH, QQ, WW>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, q_len, out, s)
-  // one query head per wave and 32 queries per workgroup: two waves per SIMD
-  // overlap one wave's softmax with another's MFMAs
-  if (d == 128) {
-    if (G == 4) LLK_PF(128, 1, 2, 4);
-    if (G == 8) LLK_PF(128, 1, 2, 8);
-    LLK_PF(128, 2, 1, 8);
-  }
-  if (G == 4) LLK_PF(64, 1, 2, 4);
-  if (G == 8) LLK_PF(64, 1, 2, 8);
-  LLK_PF(64, 2, 1, 8);
-#undef LLK_PF
+  if (!map.tiles && (map.q_len <= 0 || T % map.q_len != 0)) return hipErrorInvalidValue;
+#define LLK_PF_CASE(DD, GG, HH, QQ, WW) \
+  if (d == DD && G == GG)               \
+    return launch_pf<DD, HH, QQ, WW>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, map, out, s);
+  LLK_PF_CONFIGS(LLK_PF_CASE)
+#undef LLK_PF_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace llk

@@ -53,11 +53,33 @@ hipError_t launch_skinny(const void* x, const void* w, int M, int N, int K, int 
                          void* out, hipStream_t s, int layout = kRowMajor);
 hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, void* out, hipStream_t s);
 
+// Token rows -> sequences.  A uniform batch (query_start_loc NULL) has q_len
+// consecutive rows per sequence, so row t belongs to sequence t / q_len.  A
+// mixed batch (per-sequence query counts) carries seq_of[t] and, for the
+// prefill attention kernel, a table of query tiles; launch_batch_map writes
+// both from query_start_loc.
+struct SeqMap {
+  int q_len = 0;                 // rows per sequence of a uniform batch
+  const int* seq_of = nullptr;   // [T] sequence of each row (mixed batch)
+  const int4* tiles = nullptr;   // (sequence, tile, first row, rows) per entry
+  const int* ntiles = nullptr;   // valid entries in tiles
+  int tile_cap = 0;              // capacity of tiles: the prefill grid bound
+  __device__ __forceinline__ int seq(int t) const { return seq_of ? seq_of[t] : t / q_len; }
+};
+
+// batch_map.hip.  One workgroup.  Row starts are clamped to [0, T] and rows
+// that no sequence claims map to sequence 0, so a malformed query_start_loc
+// gives wrong rows but no out-of-range access.  Tiles hold qw query rows;
+// a sequence's tiles are listed longest (last) first.
+constexpr int kMaxMappedSeqs = 4096;
+hipError_t launch_batch_map(const int* query_start_loc, int B, int T, int qw, int* seq_of, int4* tiles,
+                            int tile_cap, int* ntiles, hipStream_t s);
+
 // rope_kv.hip.  With part != NULL (bf16 only) the projection row is first
 // formed as the bf16 rounding of the sum of S fp32 partial rows and stored
 // into qkv.
 hipError_t launch_rope_kv(int dtype, void* qkv, int T, const int* positions, const float2* table,
-                          int nq, int nkv, int d, const int* block_table, int max_blocks, int q_len,
+                          int nq, int nkv, int d, const int* block_table, int max_blocks, const SeqMap& map,
                           void* k_cache, void* v_cache, hipStream_t s, const float* part = nullptr,
                           int S = 0);
 
@@ -67,23 +89,27 @@ struct AttnPlan {
   int part_len;     // keys per partition
   size_t ws_bytes;  // fp32 partial results
 };
-AttnPlan attention_plan(int T, int nq, int nkv, int d, int q_len, int max_seq_len, int num_cus);
+// decode: every sequence has exactly one query row this call
+AttnPlan attention_plan(int T, int nq, int nkv, int d, bool decode, int max_seq_len, int num_cus);
 hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
                             int nkv, int d, const void* k_cache, const void* v_cache,
-                            const int* block_table, int max_blocks, int q_len,
+                            const int* block_table, int max_blocks, const SeqMap& map, bool decode,
                             const AttnPlan& plan, float* partials, void* out, hipStream_t s,
                             hipEvent_t mid_event);
 
 // attention_decode.hip (bf16, one query token per sequence)
 hipError_t launch_decode_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
                                         int d, const void* k_cache, const void* v_cache, const int* block_table,
-                                        int max_blocks, int q_len, int part_len, int parts, float* partials,
+                                        int max_blocks, int part_len, int parts, float* partials,
                                         void* out, hipStream_t s);
 
-// attention_prefill.hip (bf16, q_len > 1, G in {4, 8, 16})
+// attention_prefill.hip (bf16, G in {4, 8, 16}).  A uniform batch launches
+// one workgroup per (sequence, query tile, KV head); a mixed batch one per
+// entry of map.tiles, whose tiles must hold prefill_tile_rows() rows.
 bool prefill_attention_supported(int nq, int nkv, int d);
+int prefill_tile_rows(int nq, int nkv, int d);
 hipError_t launch_prefill_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
                                          int d, const void* k_cache, const void* v_cache, const int* block_table,
-                                         int max_blocks, int q_len, void* out, hipStream_t s);
+                                         int max_blocks, const SeqMap& map, void* out, hipStream_t s);
 
 }  // namespace llk

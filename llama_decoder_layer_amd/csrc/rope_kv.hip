@@ -34,7 +34,7 @@ template <typename T, int S>
 __global__ __launch_bounds__(256) void rope_kv_kernel(T* __restrict__ qkv, const int* __restrict__ positions,
                                                       const float2* __restrict__ table, int nq, int nkv,
                                                       int d, const int* __restrict__ block_table,
-                                                      int max_blocks, int q_len, T* __restrict__ kc,
+                                                      int max_blocks, SeqMap map, T* __restrict__ kc,
                                                       T* __restrict__ vc, const float* __restrict__ part, int T_) {
   __shared__ float srow[kHeads * 128];
   const int t = blockIdx.x;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(T* __restrict__ qkv, const
   const int half = d >> 1;
   const int ld = (nq + 2 * nkv) * d;
   const int p = positions[t];
-  const int b = t / q_len;
+  const int b = map.seq(t);
   const int blk = block_table[(size_t)b * max_blocks + p / kKvBlock];
   const int row = p % kKvBlock;
   T* x = qkv + (size_t)t * ld;
@@ -104,32 +104,32 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(T* __restrict__ qkv, const
 
 template <typename T, int S>
 void launch_typed(T* qkv, int T_, const int* positions, const float2* table, int nq, int nkv, int d,
-                  const int* block_table, int max_blocks, int q_len, T* kc, T* vc, const float* part,
+                  const int* block_table, int max_blocks, const SeqMap& map, T* kc, T* vc, const float* part,
                   hipStream_t s) {
   dim3 grid(T_, (nq + 2 * nkv + kHeads - 1) / kHeads);
-  rope_kv_kernel<T, S><<<grid, 256, 0, s>>>(qkv, positions, table, nq, nkv, d, block_table, max_blocks, q_len,
+  rope_kv_kernel<T, S><<<grid, 256, 0, s>>>(qkv, positions, table, nq, nkv, d, block_table, max_blocks, map,
                                             kc, vc, part, T_);
 }
 
 }  // namespace
 
 hipError_t launch_rope_kv(int dtype, void* qkv, int T, const int* positions, const float2* table,
-                          int nq, int nkv, int d, const int* block_table, int max_blocks, int q_len,
+                          int nq, int nkv, int d, const int* block_table, int max_blocks, const SeqMap& map,
                           void* k_cache, void* v_cache, hipStream_t s, const float* part, int S) {
   if (T <= 0) return hipSuccess;
   if (dtype == kBF16) {
     bf16* x = (bf16*)qkv;
     bf16* kc = (bf16*)k_cache;
     bf16* vc = (bf16*)v_cache;
-    if (!part) launch_typed<bf16, 0>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, nullptr, s);
-    else if (S == 1) launch_typed<bf16, 1>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, part, s);
-    else if (S == 2) launch_typed<bf16, 2>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, part, s);
-    else if (S == 4) launch_typed<bf16, 4>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, part, s);
-    else if (S == 8) launch_typed<bf16, 8>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len, kc, vc, part, s);
+    if (!part) launch_typed<bf16, 0>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, nullptr, s);
+    else if (S == 1) launch_typed<bf16, 1>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, s);
+    else if (S == 2) launch_typed<bf16, 2>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, s);
+    else if (S == 4) launch_typed<bf16, 4>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, s);
+    else if (S == 8) launch_typed<bf16, 8>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, s);
     else return hipErrorInvalidValue;
   } else {
     if (part) return hipErrorInvalidValue;
-    launch_typed<float, 0>((float*)qkv, T, positions, table, nq, nkv, d, block_table, max_blocks, q_len,
+    launch_typed<float, 0>((float*)qkv, T, positions, table, nq, nkv, d, block_table, max_blocks, map,
                            (float*)k_cache, (float*)v_cache, nullptr, s);
   }
   return hipGetLastError();

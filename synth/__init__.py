@@ -24,6 +24,7 @@ on the CPU so they are the same everywhere.
 from __future__ import annotations
 
 import dataclasses
+import itertools
 import math
 from typing import Optional
 
@@ -101,7 +102,9 @@ TINY = ModelShape(256, 4, 2, 64, 688, 1e-5, 10000.0, None, 4096, "fp32")
 class Workload:
     """One batch shape: ``num_seqs`` sequences, each appending ``q_len`` new
     tokens after a cached context.  ``ctx`` is either a fixed context length
-    or a (lo, hi) inclusive range drawn per sequence."""
+    or a (lo, hi) inclusive range drawn per sequence.  A mixed batch instead
+    lists ``mix``: one (new tokens, cached context) pair per sequence, in row
+    order (q_len is then 0)."""
     index: int
     name: str
     model: ModelShape
@@ -111,10 +114,17 @@ class Workload:
     layers: int = 1
     residual_none: bool = False
     spare_blocks: int = 4
+    mix: Optional[tuple] = None
 
     @property
     def num_tokens(self) -> int:
+        if self.mix is not None:
+            return sum(q for q, _ in self.mix)
         return self.num_seqs * self.q_len
+
+    @property
+    def mixed(self) -> bool:
+        return self.mix is not None
 
 
 WORKLOADS = {
@@ -125,6 +135,10 @@ WORKLOADS = {
         Workload(2, "llama70b_prefill_4x2048", LLAMA70B, 4, 2048, 0),
         Workload(3, "llama70b_prefill_1x32768", LLAMA70B, 1, 32768, 0),
         Workload(4, "llama70b_ragged_decode_b64_4layer", LLAMA70B, 64, 1, (128, 32768), 4),
+        # a chunked-prefill step: 32 decode sequences at context 2048 plus one
+        # 512-token prefill chunk on a 4096-token context, in one call
+        Workload(5, "llama70b_mixed_chunk512_decode32", LLAMA70B, 33, 0,
+                 mix=tuple([(1, 2048)] * 32 + [(512, 4096)])),
     ]
 }
 WORKLOAD_LIST = sorted(WORKLOADS.values(), key=lambda w: w.index)
@@ -191,7 +205,8 @@ def draw_activations(model: ModelShape, num_tokens: int, workload_index: int, de
 @dataclasses.dataclass
 class Batch:
     """Per-call metadata of one forward (host-side copies; ``to(device)``
-    gives the device tensors)."""
+    gives the device tensors).  Sequence b owns rows ``rows(b)``; a mixed
+    batch (``q_lens`` set, ``q_len`` 0) also carries ``query_start_loc``."""
     num_seqs: int
     q_len: int
     ctx_lens: list
@@ -200,10 +215,35 @@ class Batch:
     block_table: torch.Tensor   # int32 [B, max_blocks_per_seq], -1 past the end
     num_blocks: int
     spare_blocks: list          # block ids referenced by no sequence
+    q_lens: Optional[list] = None
+
+    @property
+    def mixed(self) -> bool:
+        return self.q_lens is not None
 
     @property
     def num_tokens(self) -> int:
-        return self.num_seqs * self.q_len
+        return sum(self.q_lens) if self.mixed else self.num_seqs * self.q_len
+
+    def new_rows(self, b: int) -> int:
+        return self.q_lens[b] if self.mixed else self.q_len
+
+    def row_start(self, b: int) -> int:
+        return sum(self.q_lens[:b]) if self.mixed else b * self.q_len
+
+    def rows(self, b: int) -> range:
+        s = self.row_start(b)
+        return range(s, s + self.new_rows(b))
+
+    @property
+    def query_start_loc(self) -> Optional[torch.Tensor]:
+        """int32 [B+1] row offsets of a mixed batch (None for a uniform one)."""
+        if not self.mixed:
+            return None
+        return torch.tensor([0] + list(itertools.accumulate(self.q_lens)), dtype=torch.int32)
+
+    def seq_of_row(self) -> list:
+        return [b for b in range(self.num_seqs) for _ in self.rows(b)]
 
     @property
     def max_seq_len(self) -> int:
@@ -229,6 +269,10 @@ def build_batch(workload: Workload, ctx_lens: Optional[list] = None) -> Batch:
     """Context lengths, positions and a block table whose blocks are placed by
     a seeded random permutation of the pool (plus a few spare blocks that no
     sequence references)."""
+    if workload.mixed:
+        return build_mixed_batch(workload.index, [q for q, _ in workload.mix],
+                                 list(ctx_lens) if ctx_lens is not None else [c for _, c in workload.mix],
+                                 workload.spare_blocks)
     B, q = workload.num_seqs, workload.q_len
     if ctx_lens is None:
         ctx_lens = draw_ctx_lens(workload)
@@ -247,6 +291,30 @@ def build_batch(workload: Workload, ctx_lens: Optional[list] = None) -> Batch:
     positions = torch.cat([torch.arange(c, c + q, dtype=torch.int32) for c in ctx_lens])
     return Batch(B, q, list(ctx_lens), torch.tensor(seq_lens, dtype=torch.int32), positions,
                  table, total, spare)
+
+
+def build_mixed_batch(workload_index: int, q_lens: list, ctx_lens: list, spare_blocks: int = 4) -> Batch:
+    """A mixed batch: sequence b has ctx_lens[b] cached positions and
+    q_lens[b] >= 1 new rows (one row: a decode step; more: a prefill chunk on
+    its context); rows are grouped by sequence in order.  Blocks are placed
+    by a seeded random permutation, as in build_batch."""
+    B = len(q_lens)
+    if B != len(ctx_lens) or min(q_lens) < 1:
+        raise ValueError("one (q_len >= 1, ctx) pair per sequence")
+    seq_lens = [c + q for c, q in zip(ctx_lens, q_lens)]
+    nblk = [(s + KV_BLOCK - 1) // KV_BLOCK for s in seq_lens]
+    total = sum(nblk) + spare_blocks
+    g = _gen(seed_of(workload_index, 0, T_BLOCKPERM), "cpu")
+    perm = torch.randperm(total, generator=g).to(torch.int32)
+    table = torch.full((B, max(nblk)), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        table[b, : nblk[b]] = perm[off: off + nblk[b]]
+        off += nblk[b]
+    spare = [int(x) for x in perm[off:]]
+    positions = torch.cat([torch.arange(c, c + q, dtype=torch.int32) for c, q in zip(ctx_lens, q_lens)])
+    return Batch(B, 0, list(ctx_lens), torch.tensor(seq_lens, dtype=torch.int32), positions, table, total, spare,
+                 list(q_lens))
 
 
 def sentinel_fill(t: torch.Tensor) -> torch.Tensor:

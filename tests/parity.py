@@ -97,8 +97,7 @@ def oracle_seqs(model: synth.ModelShape, batch: synth.Batch, k_pool, v_pool, seq
         c = batch.ctx_lens[b]
         kc = np64(synth.gather_context(k_pool, batch, b, c))
         vc = np64(synth.gather_context(v_pool, batch, b, c, "v"))
-        rows = list(range(b * batch.q_len, (b + 1) * batch.q_len))
-        seqs.append(oracle.Seq(rows, kc, vc))
+        seqs.append(oracle.Seq(list(batch.rows(b)), kc, vc))
     return seqs
 
 
@@ -117,3 +116,9 @@ def run_oracle(model, weights_np, hidden, residual, batch, seqs, want=None, both
 
 def device_batch(batch: synth.Batch, device):
     return (batch.positions.to(device), batch.block_table.to(device), batch.seq_lens.to(device))
+
+
+def device_qsl(batch: synth.Batch, device):
+    """query_start_loc on the device, or None for a uniform batch."""
+    q = batch.query_start_loc
+    return None if q is None else q.to(device)

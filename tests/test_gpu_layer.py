@@ -11,7 +11,7 @@ import torch
 
 import llama_decoder_layer_amd as lda
 import synth
-from tests.parity import compare, device_batch, np64, oracle_seqs, oracle_weights, run_oracle
+from tests.parity import compare, device_batch, device_qsl, np64, oracle_seqs, oracle_weights, run_oracle
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -25,13 +25,17 @@ MID8 = synth.ModelShape(1024, 8, 1, 128, 2816, 1e-5, 500000.0, synth.LLAMA3_SCAL
 MID64 = synth.ModelShape(512, 16, 4, 64, 1408, 1e-5, 10000.0, None, 8192, "bf16")
 
 
-def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False):
+def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False, qsl=None):
+    """qsl: "auto" = query_start_loc of a mixed batch (None otherwise); a
+    tensor to pass one explicitly (e.g. for a uniform batch)."""
     model = workload.model
     batch = synth.build_batch(workload, ctx_lens)
     print("case", workload.name, "ctx", batch.ctx_lens[:8], "T", batch.num_tokens, flush=True)
     hidden, residual = synth.draw_activations(model, batch.num_tokens, workload.index, DEV,
                                               residual=not workload.residual_none)
     pos, bt, sl = device_batch(batch, DEV)
+    if qsl is None:
+        qsl = device_qsl(batch, DEV)
     h, r = hidden, residual
     ref_h = None
     results = []
@@ -42,11 +46,12 @@ def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False):
         kp0, vp0 = kp.clone(), vp.clone()
         layer = lda.Layer(model.config_dict(), w)
         ws = layer.alloc_workspace(batch.num_tokens, batch.num_seqs, batch.max_seq_len)
-        ho, ro = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws)
+        ho, ro = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws, query_start_loc=qsl)
         torch.cuda.synchronize()
         if repeat:
             kp1, vp1 = kp.clone(), vp.clone()
-            ho2, ro2 = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws)
+            ho2, ro2 = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws,
+                                     query_start_loc=qsl)
             torch.cuda.synchronize()
             assert torch.equal(ho.view(torch.int16), ho2.view(torch.int16))
             assert torch.equal(ro.view(torch.int16), ro2.view(torch.int16))
@@ -80,13 +85,14 @@ def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False):
         print("layer", l, "hidden_out", s1, "residual_out", s2, flush=True)
         if check_kv:
             _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded, depth=l + 1)
+    return [(ho, ro, kp, vp) for (_, _, _, kp, vp, ho, ro) in results]
 
 
 def _new_slot_mask(batch):
     """[num_blocks, 16] bool: the slots of the batch's new tokens."""
     mask = torch.zeros(batch.num_blocks, 16, dtype=torch.bool)
     for b in range(batch.num_seqs):
-        p = torch.arange(batch.ctx_lens[b], batch.ctx_lens[b] + batch.q_len)
+        p = torch.arange(batch.ctx_lens[b], batch.ctx_lens[b] + batch.new_rows(b))
         mask[batch.block_table[b, p // 16].long(), p % 16] = True
     return mask
 
@@ -168,3 +174,63 @@ def test_mid8_decode():
 def test_mid64_prefill_and_decode():
     _run(synth.Workload(30, "mid64_prefill_2x80", MID64, 2, 80, 0), ctx_lens=[0, 19])
     _run(synth.Workload(31, "mid64_decode_b5", MID64, 5, 1, (3, 700)))
+
+
+# ---- mixed batches: per-sequence query counts through query_start_loc ----
+
+def test_mid_mixed_prefill_chunks_and_decode():
+    # decode rows, prefill chunks on cached contexts and a fresh prefill in one
+    # call; 123 rows: the tiled projections and the query-tile table
+    mix = ((1, 300), (37, 50), (64, 0), (1, 2000), (20, 777))
+    _run(synth.Workload(32, "mid_mixed_5seq", MID, len(mix), 0, mix=mix), repeat=True)
+
+
+def test_mid8_mixed_few_rows():
+    # 24 rows: the weight-streaming projections with a mixed attention batch
+    mix = ((1, 100), (1, 1500), (17, 40), (5, 0))
+    _run(synth.Workload(33, "mid8_mixed_4seq", MID8, len(mix), 0, mix=mix))
+
+
+def test_mid64_mixed():
+    mix = ((33, 10), (1, 500), (2, 700))
+    _run(synth.Workload(34, "mid64_mixed_3seq", MID64, len(mix), 0, mix=mix))
+
+
+def test_tiny_fp32_mixed():
+    # fp32 and a 2:1 group: the generic attention kernel reads the row map
+    mix = ((1, 20), (9, 3), (4, 0))
+    _run(synth.Workload(35, "tiny_mixed_3seq", synth.TINY, len(mix), 0, mix=mix))
+
+
+def test_explicit_query_start_loc_matches_uniform():
+    # a uniform batch given its query_start_loc takes the tile-table path (and
+    # a decode batch the decode path): results are bit-identical to NULL
+    for wl, ctx in [(synth.Workload(36, "mid8_prefill_2x100_q", MID8, 2, 100, 0), [0, 33]),
+                    (synth.Workload(37, "mid_decode_b7_q", MID, 7, 1, 0), [3, 15, 16, 17, 400, 1000, 2500])]:
+        batch = synth.build_batch(wl, ctx)
+        qsl = torch.arange(0, batch.num_tokens + 1, wl.q_len, dtype=torch.int32, device=DEV)
+        a = _run(wl, ctx_lens=ctx, check_kv=False)
+        b = _run(wl, ctx_lens=ctx, check_kv=False, qsl=qsl)
+        for x, y in zip(a[0], b[0]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_query_start_loc_host_checks():
+    model = MID
+    wl = synth.Workload(38, "mid_mixed_checks", model, 3, 0, mix=((1, 10), (2, 5), (1, 7)))
+    batch = synth.build_batch(wl)
+    hidden, residual = synth.draw_activations(model, batch.num_tokens, wl.index, DEV)
+    pos, bt, sl = device_batch(batch, DEV)
+    w = synth.draw_weights(model, wl.index, 0, DEV)
+    kp, vp = synth.build_kv_pool(wl, batch, 0, DEV)
+    layer = lda.Layer(model.config_dict(), w)
+    try:
+        with pytest.raises(ValueError):  # wrong length, caught by the binding
+            layer.forward(hidden, residual, pos, kp, vp, bt, sl, batch.max_seq_len,
+                          query_start_loc=torch.zeros(3, dtype=torch.int32, device=DEV))
+        with pytest.raises(lda.LlamaError, match="every sequence needs a query row"):
+            # two rows for three sequences
+            layer.forward(hidden[:2], residual[:2], pos[:2], kp, vp, bt, sl, batch.max_seq_len,
+                          query_start_loc=torch.tensor([0, 1, 1, 2], dtype=torch.int32, device=DEV))
+    finally:
+        layer.close()

@@ -56,3 +56,22 @@ def test_pool_round_trip_and_layout():
     blk = int(b.block_table[2, 0])
     assert torch.equal(vp[blk, 1, 5, 3], x[3, 1, 5])   # V: [block][head][component][slot]
     assert torch.equal(kp[blk, 1, 3, 5], x[3, 1, 5])   # K: [block][head][slot][component]
+
+
+def test_mixed_batch_rows_positions_and_offsets():
+    mix = ((1, 300), (37, 50), (64, 0), (1, 16))
+    wl = synth.Workload(90, "mixed_check", synth.TINY, len(mix), 0, mix=mix)
+    batch = synth.build_batch(wl)
+    assert batch.mixed and batch.num_tokens == 103 == wl.num_tokens
+    assert batch.query_start_loc.tolist() == [0, 1, 38, 102, 103]
+    assert [list(batch.rows(b)) for b in (0, 3)] == [[0], [102]]
+    assert batch.seq_of_row() == [0] + [1] * 37 + [2] * 64 + [3]
+    # each sequence's rows continue its cached context
+    for b, (q, c) in enumerate(mix):
+        assert batch.positions[batch.rows(b).start: batch.rows(b).stop].tolist() == list(range(c, c + q))
+        assert int(batch.seq_lens[b]) == c + q
+        nblk = (c + q + 15) // 16
+        assert (batch.block_table[b, :nblk] >= 0).all() and (batch.block_table[b, nblk:] == -1).all()
+    # every referenced block is distinct and inside the pool
+    used = batch.block_table[batch.block_table >= 0]
+    assert used.unique().numel() == used.numel() and int(used.max()) < batch.num_blocks
