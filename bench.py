@@ -83,6 +83,7 @@ def measure(wl, steps, warmup):
     dev = "cuda"
     batch, hidden, residual, per_layer = synth.workload_tensors(wl, dev)
     pos, bt, sl = batch.positions.to(dev), batch.block_table.to(dev), batch.seq_lens.to(dev)
+    qsl = None if batch.query_start_loc is None else batch.query_start_loc.to(dev)
     layers = [lda.Layer(model.config_dict(), p["weights"]) for p in per_layer]
     T, B = batch.num_tokens, batch.num_seqs
     ws = layers[0].alloc_workspace(T, B, batch.max_seq_len)
@@ -93,7 +94,7 @@ def measure(wl, steps, warmup):
         h, r = hidden, residual
         for L, p, (ho, ro) in zip(layers, per_layer, bufs):
             L.forward(h, r, pos, p["k_pool"], p["v_pool"], bt, sl, batch.max_seq_len, hidden_out=ho,
-                      residual_out=ro, workspace=ws)
+                      residual_out=ro, workspace=ws, query_start_loc=qsl)
             h, r = ho, ro
 
     for _ in range(warmup):
@@ -125,10 +126,12 @@ def measure(wl, steps, warmup):
     kernel_avg_ms = {k: v[0] / v[1] for k, v in kt.items()}
 
     kv_tokens = int(batch.seq_lens.sum())
-    attn_pairs = sum(sum(c + j + 1 for j in range(wl.q_len)) for c in batch.ctx_lens)
+    # causal (query, key) pairs: a sequence with c cached and n new rows
+    attn_pairs = sum(n * c + n * (n + 1) // 2 for c, n in
+                     ((batch.ctx_lens[b], batch.new_rows(b)) for b in range(B)))
     dom = "gate_up_silu"
     dur = kernel_avg_ms[dom] / 1e3
-    if wl.q_len == 1:
+    if T == B:  # decode: one row per sequence, the step streams weights and KV
         alg = kernel_bytes(model, dom, T, kv_tokens)
         roof = {"bound": "hbm", "kernel": dom, "achieved": alg / dur / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": alg / dur / 1e9 / PEAK_HBM_GBS,
@@ -150,9 +153,13 @@ def measure(wl, steps, warmup):
                           "mfma": step_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS},
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in sorted(kernel_avg_ms.items())},
         "wall_s_timed_region": round(wall, 3),
-        "config": {"workload": wl.name, "num_seqs": B, "q_len": wl.q_len,
-                   "ctx_len": wl.ctx if not isinstance(wl.ctx, tuple) else list(wl.ctx),
-                   "layers": len(layers), "parallelism": "single GPU"},
+        "config": ({"workload": wl.name, "num_seqs": B, "q_len": wl.q_len,
+                    "ctx_len": wl.ctx if not isinstance(wl.ctx, tuple) else list(wl.ctx),
+                    "layers": len(layers), "parallelism": "single GPU"} if not wl.mixed else
+                   {"workload": wl.name, "num_seqs": B, "num_tokens": T,
+                    "mix": "%d decode rows at context %d + one %d-row prefill chunk on context %d" % (
+                        sum(1 for q, _ in wl.mix if q == 1), wl.mix[0][1], wl.mix[-1][0], wl.mix[-1][1]),
+                    "layers": len(layers), "parallelism": "single GPU"}),
     }
     ctx = (batch, hidden, residual, per_layer)
     return res, ctx
@@ -197,7 +204,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         batch, hidden, residual, per_layer = ctx
-        rows = args.cpu_sample_rows or (batch.num_tokens if wl.q_len == 1 else 256)
+        rows = args.cpu_sample_rows or (batch.num_tokens if batch.num_tokens == batch.num_seqs else 256)
         cpu = cpu_baseline(wl, batch, hidden, residual, per_layer, rows)
     del ctx
     torch.cuda.empty_cache()
@@ -252,7 +259,8 @@ def cpu_baseline(wl, batch, hidden, residual, per_layer, rows, min_seconds=10.0)
     model = wl.model
     rows = min(rows, batch.num_tokens)
     rows_list = list(range(rows))
-    seq_ids = sorted({r // wl.q_len for r in rows_list})
+    seq_of = batch.seq_of_row()
+    seq_ids = sorted({seq_of[r] for r in rows_list})
     cfg = model.config_dict()
     pos = batch.positions.numpy().astype(np.int64)
     h0 = f64(hidden)
@@ -267,7 +275,7 @@ def cpu_baseline(wl, batch, hidden, residual, per_layer, rows, min_seconds=10.0)
         h, r = h0, r0
         for w_t, c in zip(weights, ctx):
             w = {k: f64(v) for k, v in w_t.items()}
-            seqs = [oracle.Seq(list(range(b * wl.q_len, (b + 1) * wl.q_len)), kc, vc) for b, kc, vc in c]
+            seqs = [oracle.Seq(list(batch.rows(b)), kc, vc) for b, kc, vc in c]
             o = oracle.decoder_layer(cfg, w, h, r, pos, seqs, want=rows_list)
             h = h.copy()
             r = np.zeros_like(h) if r is None else r.copy()

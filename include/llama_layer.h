@@ -248,7 +248,7 @@ typedef enum {
  * device, row-major, dtype `dtype`, 16-byte aligned; fp32 accumulation.
  * bf16 needs K % 64 == 0 and W's row count (N, or 2N for SILU_MUL) % 128 == 0;
  * fp32 takes any sizes and, for SILU_MUL, W in the plain [gate | up] order.
- * M <= 64 runs the weight-streaming kernel the decode path uses, larger M the
+ * M <= 128 runs the weight-streaming kernel the decode path uses, larger M the
  * tiled kernel of the prefill path.  Errors: INVALID_ARGUMENT (NULL, sizes,
  * alignment), HIP. */
 LLAMA_API llama_status llama_op_linear(int32_t dtype, const void* x, const void* w, int32_t M, int32_t N,

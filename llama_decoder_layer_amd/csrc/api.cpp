@@ -119,7 +119,7 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.act = take((size_t)T * c.intermediate_size * L->es);
   w.part = take(w.plan.ws_bytes);
   const int H = c.hidden_size, Q = c.num_attention_heads * c.head_dim, I = c.intermediate_size;
-  w.skinny = L->dtype == LLAMA_DTYPE_BF16 && T <= 64;
+  w.skinny = L->dtype == LLAMA_DTYPE_BF16 && T <= llk::kSkinnyMaxM;
   size_t gpart = 0;
   if (w.skinny) {
     w.pq = llk::skinny_plan(T, L->qkv_n, H, true, L->num_cus);

@@ -16,7 +16,7 @@
 // 8-byte store).  Within one MFMA the k index a lane supplies only has to
 // agree between A and B, which lets the loads be laid out for coalescing.
 //
-//   skinny kernel (M <= 64 tokens, decode): gemm_skinny.hip.
+//   skinny kernel (M <= 128 tokens, decode): gemm_skinny.hip.
 //   tiled kernel (prefill): 256 tokens x 256 weight rows per workgroup with
 //     8 waves of 128 x 64 (128 KiB of LDS), or 128 x 128 with 4 waves of
 //     64 x 64 for shapes the large tile does not fit; K in steps of 64 loaded
@@ -287,7 +287,7 @@ template <int EPI>
 hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* out, hipStream_t s, int layout) {
   // rows of W the kernel walks: N (store/add) or 2N (silu_mul)
   const int wrows = (EPI == kEpiSiluMul) ? 2 * N : N;
-  if (M <= 64)
+  if (M <= kSkinnyMaxM)
     return launch_skinny(x, w, M, N, K, EPI, skinny_plan(M, wrows, K, false, device_cu_count()), out, s, layout);
   const WStride ws = weight_stride(layout, K);
   if (M >= 256 && wrows % 256 == 0) return launch_tile<256, 256, 2, 4, EPI>(x, M, w, wrows, K, ws, out, N, s);
@@ -326,7 +326,7 @@ int device_cu_count() {
 
 const char* linear_kernel_name(int dtype, int M) {
   if (dtype != kBF16) return "gemm_f32";
-  return M <= 64 ? "gemm_skinny_bf16" : "gemm_tile_bf16";
+  return M <= kSkinnyMaxM ? "gemm_skinny_bf16" : "gemm_tile_bf16";
 }
 
 hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, int K, int epi,
@@ -339,7 +339,7 @@ hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, 
     const int wrows = (epi == kEpiSiluMul) ? 2 * N : N;
     if (layout == kTiled16x32 && (wrows % 16 != 0 || K % 32 != 0)) return hipErrorInvalidValue;
     // the tiled kernels walk weight rows in 128- or 256-row tiles
-    if (M > 64 && (wrows % 128 != 0 || K % kTBK != 0)) return hipErrorInvalidValue;
+    if (M > kSkinnyMaxM && (wrows % 128 != 0 || K % kTBK != 0)) return hipErrorInvalidValue;
     switch (epi) {
       case kEpiStore: return linear_bf16<kEpiStore>(xb, wb, M, N, K, ob, s, layout);
       case kEpiAdd: return linear_bf16<kEpiAdd>(xb, wb, M, N, K, ob, s, layout);

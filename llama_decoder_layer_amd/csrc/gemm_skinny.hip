@@ -1,4 +1,4 @@
-// Weight-streaming projections for few tokens (decode: M <= 64 rows of x).
+// Weight-streaming projections for few tokens (decode: M <= 128 rows of x).
 //
 // Same product as gemm.hip, y = x W^T with W stored [out, in] (vllm-learning
 // page "模型库与算子层 — 代码走读", section "Linear 层"), but here every
@@ -201,7 +201,8 @@ hipError_t launch3(const bf16* x, int M, const bf16* w, int K, int kps, WStride 
 #define LLK_SKINNY_SHAPES(X)                                                                        \
   X(1, 2, 64, 4) X(1, 2, 128, 4) X(1, 2, 256, 4) X(1, 2, 256, 7)                                   \
   X(2, 2, 64, 4) X(2, 2, 128, 4) X(2, 2, 256, 4) X(2, 2, 64, 5) X(2, 2, 256, 7) X(2, 4, 256, 4)  \
-  X(4, 2, 64, 4) X(4, 2, 128, 4) X(4, 2, 256, 4) X(4, 1, 128, 5) X(4, 2, 256, 7)
+  X(4, 2, 64, 4) X(4, 2, 128, 4) X(4, 2, 256, 4) X(4, 1, 128, 5) X(4, 2, 256, 7)                   \
+  X(8, 2, 64, 4) X(8, 2, 128, 4) X(8, 1, 128, 5) X(8, 2, 128, 7)
 
 hipError_t launch_shape(const SkinnyPlan& p, const bf16* x, int M, const bf16* w, int K, int kps, WStride ws,
                         int epi, void* out, int N, dim3 grid, hipStream_t s) {
@@ -217,7 +218,7 @@ hipError_t launch_shape(const SkinnyPlan& p, const bf16* x, int M, const bf16* w
 
 SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split, int num_cus) {
   SkinnyPlan p;
-  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
   p.nt = 2;
   p.nw = 4;
   p.splits = 1;
@@ -231,7 +232,7 @@ SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split, int num_cus) {
     } else if (p.mt == 2 && wrows % 256 == 0) {
       p.nt = 4;
     }
-    p.kc = 256;
+    p.kc = p.mt == 8 ? 128 : 256;  // 8 token tiles: the x chunk pair must fit 64 KiB of LDS
     return p;
   }
   // Split-K: the first candidate whose workgroup count is a whole multiple
@@ -242,7 +243,8 @@ SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split, int num_cus) {
     struct Cand { int nt, nw, kc, splits; };
     static const Cand c2[] = {{2, 4, 64, 8}, {2, 5, 64, 8}};
     static const Cand c4[] = {{2, 4, 256, 8}, {1, 5, 128, 4}};
-    const Cand* c = p.mt == 2 ? c2 : c4;
+    static const Cand c8[] = {{2, 4, 128, 8}, {1, 5, 128, 4}};
+    const Cand* c = p.mt == 2 ? c2 : (p.mt == 4 ? c4 : c8);
     for (int i = 0; i < 2; ++i) {
       const int rows = 16 * c[i].nt * c[i].nw;
       if (wrows % rows || K % (c[i].splits * c[i].kc)) continue;
@@ -263,7 +265,7 @@ SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split, int num_cus) {
       }
   }
   const int kps = K / p.splits;
-  if (p.mt == 2) p.kc = kps % 128 == 0 ? 128 : 64;
+  if (p.mt == 2 || p.mt == 8) p.kc = kps % 128 == 0 ? 128 : 64;
   else p.kc = kps % 256 == 0 ? 256 : (kps % 128 == 0 ? 128 : 64);
   return p;
 }
@@ -273,7 +275,7 @@ hipError_t launch_skinny(const void* x, const void* w, int M, int N, int K, int 
   if (M <= 0) return hipSuccess;
   const int wrows = epi == kEpiSiluMul ? 2 * N : N;
   const int rows_per_wg = 16 * p.nt * p.nw;
-  if (M > 64 || wrows % rows_per_wg != 0 || K % (p.splits * p.kc) != 0) return hipErrorInvalidValue;
+  if (M > kSkinnyMaxM || wrows % rows_per_wg != 0 || K % (p.splits * p.kc) != 0) return hipErrorInvalidValue;
   if (epi == kEpiSiluMul && (p.splits != 1 || p.nt % 2 != 0)) return hipErrorInvalidValue;
   if (p.splits != 1 && epi != kEpiPartial) return hipErrorInvalidValue;
   if (M > 16 * p.mt || K % 32 != 0) return hipErrorInvalidValue;

@@ -30,7 +30,7 @@ struct WStride {
 };
 inline WStride weight_stride(int layout, int K) { return layout == kTiled16x32 ? WStride{32, 512} : WStride{K, 32}; }
 
-// gemm.hip: out = x W^T with an epilogue; picks the skinny (M <= 64) or the
+// gemm.hip: out = x W^T with an epilogue; picks the skinny (M <= 128) or the
 // tiled kernel.  bf16 weights in `layout` (rows % 16 == 0 and K % 32 == 0
 // for kTiled16x32); fp32 weights are row-major.
 hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, int K, int epi,
@@ -42,8 +42,9 @@ hipError_t launch_reorder_gate_up(const void* src, int inter, int K, void* dst, 
 hipError_t launch_tile_weight(const void* src, int rows, int K, int inter, void* dst, hipStream_t s);
 const char* linear_kernel_name(int dtype, int M);
 
-// gemm_skinny.hip: bf16, M <= 64.  N = output features (SiluMul: W has 2N
+// gemm_skinny.hip: bf16, M <= kSkinnyMaxM.  N = output features (SiluMul: W has 2N
 // rows).  kEpiPartial writes fp32 partial sums [splits][M][N].
+constexpr int kSkinnyMaxM = 128;
 struct SkinnyPlan {
   int mt, nt, nw, kc, splits;  // token tiles, row tiles per wave, waves, K chunk, K splits
 };

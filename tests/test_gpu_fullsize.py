@@ -11,7 +11,7 @@ import torch
 import llama_decoder_layer_amd as lda
 import oracle
 import synth
-from tests.parity import compare, device_batch, np64, oracle_seqs, oracle_weights, run_oracle
+from tests.parity import compare, device_batch, device_qsl, np64, oracle_seqs, oracle_weights, run_oracle
 from tests.test_gpu_layer import _check_kv, _check_placement
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -25,7 +25,7 @@ def _forward(wl, batch, layer_idx, h, r):
     kp0, vp0 = kp.clone(), vp.clone()
     layer = lda.Layer(model.config_dict(), w)
     pos, bt, sl = device_batch(batch, DEV)
-    ho, ro = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len)
+    ho, ro = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, query_start_loc=device_qsl(batch, DEV))
     torch.cuda.synchronize()
     layer.close()
     return w, kp0, vp0, kp, vp, ho, ro
@@ -34,9 +34,9 @@ def _forward(wl, batch, layer_idx, h, r):
 def _sample_rows(batch, per_seq):
     rows = []
     for b in range(batch.num_seqs):
-        q = batch.q_len
+        q, s = batch.new_rows(b), batch.row_start(b)
         picks = sorted({0, 1, 15, 16, 17, q // 3, q // 2, q - 17, q - 2, q - 1} | set(per_seq))
-        rows += [b * q + i for i in picks if 0 <= i < q]
+        rows += [s + i for i in picks if 0 <= i < q]
     return rows
 
 
@@ -127,3 +127,10 @@ def test_c4_ragged_decode_4layer_sampled_sequences():
         hr, rr = hr.copy(), rr.copy()
         hr[pick], rr[pick] = oracle.bf16_round(rd["hidden_out"]), oracle.bf16_round(rd["residual_out"])
         del wn
+
+
+@pytest.mark.timeout(600)
+def test_mixed_chunk512_decode32_sampled_rows():
+    # one call with 32 decode rows (context 2048) and a 512-row prefill chunk
+    # on a 4096-token context: every decode row, sampled chunk rows
+    _check_prefill("llama70b_mixed_chunk512_decode32", extra=(255, 256, 511))

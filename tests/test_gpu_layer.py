@@ -234,3 +234,9 @@ def test_query_start_loc_host_checks():
                           query_start_loc=torch.tensor([0, 1, 1, 2], dtype=torch.int32, device=DEV))
     finally:
         layer.close()
+
+
+def test_mid_decode_b128_and_b129():
+    # 128 rows: the largest weight-streaming batch (8 token tiles); 129: tiled
+    _run(synth.Workload(39, "mid_decode_b128", MID, 128, 1, (1, 600)))
+    _run(synth.Workload(40, "mid_decode_b129", MID, 129, 1, (1, 600)))

@@ -29,7 +29,7 @@ def test_linear_store(M, N, K):
     compare("linear", np64(y), ref, dtype="bf16")
 
 
-@pytest.mark.parametrize("M", [5, 32, 64, 200])
+@pytest.mark.parametrize("M", [5, 32, 64, 100, 200])
 def test_linear_add(M):
     print("linear_add", M, flush=True)
     N, K = 1024, 768
@@ -43,7 +43,7 @@ def test_linear_add(M):
     compare("linear_add", np64(out), exact, dtype="bf16")
 
 
-@pytest.mark.parametrize("M", [3, 32, 64, 129])
+@pytest.mark.parametrize("M", [3, 32, 64, 100, 129])
 def test_linear_silu_mul(M):
     print("linear_silu", M, flush=True)
     I, K = 384, 512
