@@ -94,7 +94,7 @@ struct llama_layer {
 namespace {
 
 struct Workspace {
-  size_t h, qkv, attn, h2, act, part, gpart, seq_of, ntiles, tiles, total;
+  size_t h, qkv, attn, h2, act, part, gpart, tpart, tpart_bytes, seq_of, ntiles, tiles, total;
   int tile_cap;  // entries of the prefill tile table (mixed batches)
   llk::AttnPlan plan;
   bool skinny;  // few tokens: weight-streaming projections with split-K partials
@@ -132,6 +132,16 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
     gpart = n * T * sizeof(float);
   }
   w.gpart = take(gpart);
+  // tiled projections that split K keep their fp32 partials here
+  w.tpart_bytes = 0;
+  if (L->dtype == LLAMA_DTYPE_BF16 && !w.skinny) {
+    const int dims[4][2] = {{L->qkv_n, H}, {H, Q}, {2 * I, H}, {H, I}};  // weight rows, K
+    for (auto& dk : dims) {
+      const size_t b = llk::tile_plan(T, dk[0], dk[1], L->num_cus).partial_bytes;
+      if (b > w.tpart_bytes) w.tpart_bytes = b;
+    }
+  }
+  w.tpart = take(w.tpart_bytes);
   // mixed batches: row -> sequence map and the prefill tile table (tiles of
   // at least 16 rows, so T/16 + B entries bound any sequence mix)
   w.tile_cap = T / 16 + B + 1;
@@ -433,6 +443,7 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   if (e != hipSuccess) return hip_fail(e, "input_layernorm");
   mk.mark("input_layernorm");
   float* gp = (float*)(ws + w.gpart);
+  float* tp = (float*)(ws + w.tpart);
   if (w.skinny) {
     e = llk::launch_skinny(h, L->w_qkv, T, L->qkv_n, H, llk::kEpiPartial, w.pq, gp, s, L->wlayout);
     if (e != hipSuccess) return hip_fail(e, "qkv_proj");
@@ -440,7 +451,7 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
     e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, map, kv->k,
                             kv->v, s, gp, w.pq.splits);
   } else {
-    e = llk::launch_linear(dt, h, L->w_qkv, T, L->qkv_n, H, llk::kEpiStore, qkv, s, L->wlayout);
+    e = llk::launch_linear(dt, h, L->w_qkv, T, L->qkv_n, H, llk::kEpiStore, qkv, s, L->wlayout, tp, w.tpart_bytes);
     if (e != hipSuccess) return hip_fail(e, "qkv_proj");
     mk.mark("qkv_proj");
     e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, map, kv->k,
@@ -475,16 +486,18 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
     mk.mark("down_proj_reduce");
     return LLAMA_OK;
   }
-  e = llk::launch_linear(dt, attn, L->w_o, T, H, nq * d, llk::kEpiAdd, residual_out, s, L->wlayout);
+  e = llk::launch_linear(dt, attn, L->w_o, T, H, nq * d, llk::kEpiAdd, residual_out, s, L->wlayout, tp,
+                         w.tpart_bytes);
   if (e != hipSuccess) return hip_fail(e, "o_proj");
   mk.mark("o_proj_residual");
   e = llk::launch_add_rmsnorm(dt, residual_out, nullptr, L->w_post, c.rms_norm_eps, T, H, h2, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "post_attention_layernorm");
   mk.mark("post_attention_layernorm");
-  e = llk::launch_linear(dt, h2, L->w_gu, T, I, H, llk::kEpiSiluMul, act, s, L->wlayout);
+  e = llk::launch_linear(dt, h2, L->w_gu, T, I, H, llk::kEpiSiluMul, act, s, L->wlayout, tp, w.tpart_bytes);
   if (e != hipSuccess) return hip_fail(e, "gate_up_proj");
   mk.mark("gate_up_silu");
-  e = llk::launch_linear(dt, act, L->w_down, T, H, I, llk::kEpiStore, hidden_out, s, L->wlayout);
+  e = llk::launch_linear(dt, act, L->w_down, T, H, I, llk::kEpiStore, hidden_out, s, L->wlayout, tp,
+                         w.tpart_bytes);
   if (e != hipSuccess) return hip_fail(e, "down_proj");
   mk.mark("down_proj");
   return LLAMA_OK;

@@ -77,7 +77,7 @@ constexpr int kGroupM = 8;  // token tiles per group in the XCD-local tile order
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __restrict__ X, int M,
                                                                const bf16* __restrict__ W, int N, int K,
-                                                               WStride ws, bf16* out, int ldo, int group_m) {
+                                                               WStride ws, void* out, int ldo, int group_m, int kps) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;     // wave tile: tokens x weight rows
   constexpr int SM = TM / 16, SN = TN / 16;     // 16x16 MFMA tiles per wave
@@ -129,12 +129,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
     wsrc[j] = W + (size_t)(row & ~15) * K + (size_t)(row & 15) * ws.rs + (size_t)(ch >> 2) * ws.ks + (ch & 3) * 8;
   }
   const size_t wstage = (size_t)(kTBK / 32) * ws.ks;  // weight offset of one k stage
+  // split-K: this workgroup's k range is [blockIdx.y * kps, +kps)
+  const int k_split = blockIdx.y * kps;
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) wsrc[j] += (size_t)(k_split / 32) * ws.ks;
   const bf16* xsrc[XJ];
 #pragma unroll
   for (int j = 0; j < XJ; ++j) {
     const int row = (j * NW + wave) * 8 + prow;
     const int m = min(m0 + row, M - 1);
-    xsrc[j] = X + (size_t)m * K + ((pc ^ (row & 7)) << 3);
+    xsrc[j] = X + (size_t)m * K + blockIdx.y * kps + ((pc ^ (row & 7)) << 3);
   }
   auto issue = [&](int buf, int kt) {
     const int k0 = kt * kTBK;
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
 #pragma unroll
     for (int j = 0; j < SM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / kTBK;
+  const int nk = kps / kTBK;
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -188,7 +192,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
   for (int j = 0; j < SM; ++j) {
     const int m = m0 + wm * TM + j * 16 + r16;
     if (m >= M) continue;
-    if (EPI == kEpiSiluMul) {
+    if (EPI == kEpiPartial) {  // fp32 partial sums [split][M][ldo] (ldo = weight rows)
+      float* dst = reinterpret_cast<float*>(out) + ((size_t)blockIdx.y * M + m) * ldo;
+#pragma unroll
+      for (int i = 0; i < SN; ++i) *reinterpret_cast<f32x4*>(dst + n0 + wn * TN + i * 16 + 4 * g) = acc[i][j];
+    } else if (EPI == kEpiSiluMul) {
 #pragma unroll
       for (int i = 0; i < SN; i += 2) {
         const int f = ((n0 + wn * TN + i * 16) >> 5) * 16 + 4 * g;
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
           gv[r] = acc[i][j][r];
           uv[r] = acc[i + 1][j][r];
         }
-        store4_silu(out, (size_t)m * ldo + f, gv, uv);
+        store4_silu(reinterpret_cast<bf16*>(out), (size_t)m * ldo + f, gv, uv);
       }
     } else {
 #pragma unroll
@@ -207,15 +215,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r];
-        store4<EPI>(out, (size_t)m * ldo + n, v);
+        store4<EPI>(reinterpret_cast<bf16*>(out), (size_t)m * ldo + n, v);
       }
     }
   }
 }
 
+// splits > 1 (EPI = kEpiPartial): fp32 partials [splits][M][wrows] in out
 template <int BM, int BN, int WM, int WN, int EPI>
-hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, WStride ws, bf16* out, int ldo,
-                       hipStream_t s) {
+hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, WStride ws, void* out, int ldo,
+                       hipStream_t s, int splits = 1) {
   auto fn = gemm_tile_bf16<BM, BN, WM, WN, EPI>;
   const size_t lds = (size_t)2 * (BM + BN) * kTBK * sizeof(bf16);
   static bool attr_set = false;  // per instantiation; the attribute is per function
@@ -230,8 +239,48 @@ hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, WS
   // beyond that, grouped order (26.9 -> 25.8 ms on 32768 x 57344 x 8192).
   const int num_m = (M + BM - 1) / BM;
   const int group_m = num_m > 32 && (wrows / BN) % 8 == 0 ? kGroupM : 0;
-  fn<<<nb, 64 * WM * WN, lds, s>>>(x, M, w, wrows, K, ws, out, ldo, group_m);
+  fn<<<dim3(nb, splits), 64 * WM * WN, lds, s>>>(x, M, w, wrows, K, ws, out, ldo, group_m, K / splits);
   return hipGetLastError();
+}
+
+// out[m][n] (bf16) from S fp32 partial rows, summed in split order, with the
+// projection's epilogue: store, residual add (out holds the addend) or
+// SiluAndMul over the re-ordered gate_up rows (each 32-row group: 16 gate
+// rows, then the 16 matching up rows).  Four output features per thread.
+template <int EPI>
+__global__ __launch_bounds__(256) void tile_reduce_kernel(const float* __restrict__ part, int S, int M, int wrows,
+                                                          int N, bf16* __restrict__ out) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (size_t)M * N) return;
+  const size_t m = i / N;
+  const int n = (int)(i % N);
+  const size_t plane = (size_t)M * wrows;
+  const float* src = part + m * wrows;
+  f32x4 a, u;
+  const int ga = EPI == kEpiSiluMul ? (n >> 4) * 32 + (n & 15) : n;  // gate (or plain) column
+  a = *reinterpret_cast<const f32x4*>(src + ga);
+  if (EPI == kEpiSiluMul) u = *reinterpret_cast<const f32x4*>(src + ga + 16);
+  for (int k = 1; k < S; ++k) {
+    const f32x4 b = *reinterpret_cast<const f32x4*>(src + k * plane + ga);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] += b[r];
+    if (EPI == kEpiSiluMul) {
+      const f32x4 c = *reinterpret_cast<const f32x4*>(src + k * plane + ga + 16);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[r] += c[r];
+    }
+  }
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = a[r];
+  if (EPI == kEpiSiluMul) {
+    float uv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) uv[r] = u[r];
+    store4_silu(out, i, v, uv);
+  } else {
+    store4<EPI>(out, i, v);
+  }
 }
 
 // -------------------------------------------------------------- fp32 ------
@@ -284,13 +333,23 @@ __global__ void reorder_gate_up_kernel(const bf16* __restrict__ src, int inter, 
 }
 
 template <int EPI>
-hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* out, hipStream_t s, int layout) {
+hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* out, hipStream_t s, int layout,
+                       float* part, size_t part_cap) {
   // rows of W the kernel walks: N (store/add) or 2N (silu_mul)
   const int wrows = (EPI == kEpiSiluMul) ? 2 * N : N;
   if (M <= kSkinnyMaxM)
     return launch_skinny(x, w, M, N, K, EPI, skinny_plan(M, wrows, K, false, device_cu_count()), out, s, layout);
   const WStride ws = weight_stride(layout, K);
-  if (M >= 256 && wrows % 256 == 0) return launch_tile<256, 256, 2, 4, EPI>(x, M, w, wrows, K, ws, out, N, s);
+  const TilePlan tp = tile_plan(M, wrows, K, device_cu_count());
+  if (tp.splits > 1 && part && tp.partial_bytes <= part_cap) {
+    hipError_t e = tp.big ? launch_tile<256, 256, 2, 4, kEpiPartial>(x, M, w, wrows, K, ws, part, wrows, s, tp.splits)
+                          : launch_tile<128, 128, 2, 2, kEpiPartial>(x, M, w, wrows, K, ws, part, wrows, s, tp.splits);
+    if (e != hipSuccess) return e;
+    const size_t quads = (size_t)M * N / 4;
+    tile_reduce_kernel<EPI><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(part, tp.splits, M, wrows, N, out);
+    return hipGetLastError();
+  }
+  if (tp.big) return launch_tile<256, 256, 2, 4, EPI>(x, M, w, wrows, K, ws, out, N, s);
   return launch_tile<128, 128, 2, 2, EPI>(x, M, w, wrows, K, ws, out, N, s);
 }
 
@@ -317,6 +376,18 @@ hipError_t linear_f32(const float* x, const float* w, int M, int N, int K, float
 
 }  // namespace
 
+TilePlan tile_plan(int M, int wrows, int K, int num_cus) {
+  TilePlan p;
+  p.big = M >= 256 && wrows % 256 == 0;
+  const int bm = p.big ? 256 : 128;
+  const int tiles = ((M + bm - 1) / bm) * (wrows / bm);
+  const int cus = num_cus > 0 ? num_cus : 256;
+  p.splits = 1;
+  for (int s = 2; s <= 8 && tiles * p.splits < cus && K % (s * kTBK) == 0; s *= 2) p.splits = s;
+  p.partial_bytes = p.splits > 1 ? (size_t)p.splits * M * wrows * sizeof(float) : 0;
+  return p;
+}
+
 int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -330,7 +401,7 @@ const char* linear_kernel_name(int dtype, int M) {
 }
 
 hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, int K, int epi,
-                         void* out, hipStream_t s, int layout) {
+                         void* out, hipStream_t s, int layout, float* part, size_t part_cap) {
   if (M <= 0) return hipSuccess;
   if (dtype == kBF16) {
     const bf16* xb = (const bf16*)x;
@@ -341,9 +412,9 @@ hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, 
     // the tiled kernels walk weight rows in 128- or 256-row tiles
     if (M > kSkinnyMaxM && (wrows % 128 != 0 || K % kTBK != 0)) return hipErrorInvalidValue;
     switch (epi) {
-      case kEpiStore: return linear_bf16<kEpiStore>(xb, wb, M, N, K, ob, s, layout);
-      case kEpiAdd: return linear_bf16<kEpiAdd>(xb, wb, M, N, K, ob, s, layout);
-      default: return linear_bf16<kEpiSiluMul>(xb, wb, M, N, K, ob, s, layout);
+      case kEpiStore: return linear_bf16<kEpiStore>(xb, wb, M, N, K, ob, s, layout, part, part_cap);
+      case kEpiAdd: return linear_bf16<kEpiAdd>(xb, wb, M, N, K, ob, s, layout, part, part_cap);
+      default: return linear_bf16<kEpiSiluMul>(xb, wb, M, N, K, ob, s, layout, part, part_cap);
     }
   }
   const float* xf = (const float*)x;

@@ -33,8 +33,21 @@ inline WStride weight_stride(int layout, int K) { return layout == kTiled16x32 ?
 // gemm.hip: out = x W^T with an epilogue; picks the skinny (M <= 128) or the
 // tiled kernel.  bf16 weights in `layout` (rows % 16 == 0 and K % 32 == 0
 // for kTiled16x32); fp32 weights are row-major.
+// With part (capacity part_cap bytes) a bf16 product whose tiles would leave
+// CUs idle splits K (tile_plan) into fp32 partials there, then a reduce
+// kernel applies the epilogue; without it the product runs unsplit.
 hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, int K, int epi,
-                         void* out, hipStream_t s, int layout = kRowMajor);
+                         void* out, hipStream_t s, int layout = kRowMajor, float* part = nullptr,
+                         size_t part_cap = 0);
+// Tiled-kernel plan for M > kSkinnyMaxM: 256 x 256 tiles from 256 tokens on
+// (else 128 x 128), and K split in 2, 4 or 8 while the tiles alone number
+// fewer than the CUs.
+struct TilePlan {
+  bool big;
+  int splits;
+  size_t partial_bytes;  // fp32 partials the split needs (0 unsplit)
+};
+TilePlan tile_plan(int M, int wrows, int K, int num_cus);
 hipError_t launch_reorder_gate_up(const void* src, int inter, int K, void* dst, hipStream_t s);
 // Row-major bf16 [rows][K] -> kTiled16x32.  With inter > 0 the source is the
 // merged gate_up weight [2*inter][K] and the rows are re-ordered on the way
