@@ -210,6 +210,63 @@ LLAMA_API void llama_layer_destroy(llama_layer* layer);
 /* Message of the calling thread's last failed call ("" if none). */
 LLAMA_API const char* llama_layer_last_error(void);
 
+/* ---- the decoder stack ---------------------------------------------------- */
+
+/* num_layers decoder layers followed by the model body's final RMSNorm: page
+ * "LLama" (hotelren.com/news/2693952), section "最终 RMSNorm", and page
+ * yeyulingfeng.com/a/605382.html, section "2.1 LlamaModel.forward()".  The
+ * layers hand (hidden, residual) on, the first with no residual, and the final
+ * norm takes hidden + residual: out = RMSNorm(hidden_N + residual_N; w_final).
+ * There is no embedding and no lm_head: the input is the embedded hidden state. */
+typedef struct llama_stack llama_stack;
+
+/* weights: host array of num_layers layer weight sets (as for
+ * llama_layer_create); final_norm: [H] device.  The stack copies everything;
+ * the caller may free its buffers once the call returns.  Errors as
+ * llama_layer_create, plus INVALID_ARGUMENT for num_layers <= 0. */
+LLAMA_API llama_status llama_stack_create(const llama_layer_config* config, int32_t num_layers,
+                                          const llama_layer_weights* weights, const void* final_norm, void* stream,
+                                          llama_stack** out);
+
+/* Workspace bytes of a stack forward with these bounds (0 on bad input). */
+LLAMA_API size_t llama_stack_workspace_bytes(const llama_stack* stack, int32_t num_tokens, int32_t num_seqs,
+                                             int32_t max_seq_len);
+
+/* One forward through every layer and the final norm.  Arguments as
+ * llama_layer_forward, except: kv_caches is a host array of num_layers caches
+ * (layer l reads and writes kv_caches[l]); there is no residual input; out
+ * [T, H] device receives the final norm's output.  The layers' (hidden,
+ * residual) pair lives in the workspace. */
+LLAMA_API llama_status llama_stack_forward(llama_stack* stack, const void* hidden, const int32_t* positions,
+                                           int32_t num_tokens, const llama_kv_cache* kv_caches,
+                                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                                           const int32_t* seq_lens, const int32_t* query_start_loc,
+                                           int32_t num_seqs, int32_t max_seq_len, void* out, void* workspace,
+                                           void* stream);
+
+/* Frees the stack's device memory (synchronises the device first). */
+LLAMA_API void llama_stack_destroy(llama_stack* stack);
+
+/* A HIP graph of one llama_stack_forward with exactly these arguments,
+ * captured on `stream` (which must not be the default stream) and
+ * instantiated.  The graph keeps the pointers, not the contents: between
+ * launches the caller may rewrite hidden, positions, seq_lens, block_table and
+ * query_start_loc in place (same sizes), and each launch runs the whole forward
+ * on what they then hold.  Per-kernel timing must be off.  Errors:
+ * INVALID_ARGUMENT, the forward's own errors (the capture is then abandoned),
+ * HIP. */
+typedef struct llama_graph llama_graph;
+LLAMA_API llama_status llama_stack_graph_create(llama_stack* stack, const void* hidden, const int32_t* positions,
+                                                int32_t num_tokens, const llama_kv_cache* kv_caches,
+                                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                                const int32_t* seq_lens, const int32_t* query_start_loc,
+                                                int32_t num_seqs, int32_t max_seq_len, void* out, void* workspace,
+                                                void* stream, llama_graph** graph);
+/* Launches the graph on `stream` (asynchronous). */
+LLAMA_API llama_status llama_graph_launch(llama_graph* graph, void* stream);
+/* Frees the graph (synchronises the device first). */
+LLAMA_API void llama_graph_destroy(llama_graph* graph);
+
 /* ---- inspection -------------------------------------------------------- */
 
 /* Byte offset and size, inside the workspace of a forward with these bounds,

@@ -113,6 +113,21 @@ def lib() -> ctypes.CDLL:
     L.llama_op_reorder_gate_up.argtypes = [vp, i32, i32, vp, vp]
     L.llama_op_add_rmsnorm.restype = st
     L.llama_op_add_rmsnorm.argtypes = [i32, vp, vp, vp, ctypes.c_float, i32, i32, vp, vp, vp]
+    L.llama_stack_create.restype = st
+    L.llama_stack_create.argtypes = [ctypes.POINTER(Config), i32, ctypes.POINTER(Weights), vp, vp, ctypes.POINTER(vp)]
+    L.llama_stack_workspace_bytes.restype = ctypes.c_size_t
+    L.llama_stack_workspace_bytes.argtypes = [vp, i32, i32, i32]
+    fwd = [vp, vp, vp, i32, ctypes.POINTER(KvCache), vp, i32, vp, vp, i32, i32, vp, vp, vp]
+    L.llama_stack_forward.restype = st
+    L.llama_stack_forward.argtypes = fwd
+    L.llama_stack_destroy.restype = None
+    L.llama_stack_destroy.argtypes = [vp]
+    L.llama_stack_graph_create.restype = st
+    L.llama_stack_graph_create.argtypes = fwd + [ctypes.POINTER(vp)]
+    L.llama_graph_launch.restype = st
+    L.llama_graph_launch.argtypes = [vp, vp]
+    L.llama_graph_destroy.restype = None
+    L.llama_graph_destroy.argtypes = [vp]
     _lib = L
     return L
 
@@ -120,7 +135,9 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["llama_layer_config_validate", "llama_layer_create", "llama_layer_workspace_bytes",
             "llama_layer_forward", "llama_layer_destroy", "llama_layer_last_error",
             "llama_layer_workspace_tensor", "llama_layer_set_timing", "llama_layer_timing_read",
-            "llama_op_linear", "llama_op_reorder_gate_up", "llama_op_add_rmsnorm"]
+            "llama_op_linear", "llama_op_reorder_gate_up", "llama_op_add_rmsnorm",
+            "llama_stack_create", "llama_stack_workspace_bytes", "llama_stack_forward", "llama_stack_destroy",
+            "llama_stack_graph_create", "llama_graph_launch", "llama_graph_destroy"]
 
 
 def _check(status: int) -> None:
@@ -274,6 +291,112 @@ class Layer:
         if n < 0:
             _check(Status.INVALID_ARGUMENT)
         return {names[i].decode(): (ms[i], cnt[i]) for i in range(min(n, cap))}
+
+
+class Stack:
+    """num_layers decoder layers plus the final RMSNorm (llama_stack_create):
+    the model body from embedded hidden states to the normed output."""
+
+    def __init__(self, cfg: dict, layer_weights: list, final_norm: torch.Tensor, stream=None):
+        self.cfg = dict(cfg)
+        self.num_layers = len(layer_weights)
+        self.dtype = layer_weights[0]["qkv_proj"].dtype
+        self._config = make_config(cfg, _dtype_of(self.dtype))
+        ws = (Weights * self.num_layers)()
+        for l, weights in enumerate(layer_weights):
+            for n in Layer.WEIGHT_NAMES:
+                setattr(ws[l], n, _dev(weights[n], n, self.dtype).data_ptr())
+        _dev(final_norm, "final_norm", self.dtype)
+        h = ctypes.c_void_p()
+        _check(lib().llama_stack_create(ctypes.byref(self._config), self.num_layers, ws, _ptr(final_norm),
+                                        _stream(stream), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().llama_stack_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, num_tokens: int, num_seqs: int, max_seq_len: int) -> int:
+        return int(lib().llama_stack_workspace_bytes(self._h, num_tokens, num_seqs, max_seq_len))
+
+    def alloc_workspace(self, num_tokens: int, num_seqs: int, max_seq_len: int, device=None) -> torch.Tensor:
+        n = self.workspace_bytes(num_tokens, num_seqs, max_seq_len)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+
+    def _args(self, hidden, positions, kv_caches, block_table, seq_lens, max_seq_len, out, workspace,
+              query_start_loc):
+        T, B = hidden.shape[0], seq_lens.shape[0]
+        _dev(hidden, "hidden", self.dtype)
+        _dev(positions, "positions", torch.int32)
+        _dev(block_table, "block_table", torch.int32)
+        _dev(seq_lens, "seq_lens", torch.int32)
+        if len(kv_caches) != self.num_layers:
+            raise ValueError("one (k, v) cache pair per layer")
+        kvs = (KvCache * self.num_layers)()
+        for l, (k, v) in enumerate(kv_caches):
+            _dev(k, "k_cache", self.dtype)
+            _dev(v, "v_cache", self.dtype)
+            kvs[l] = KvCache(k.data_ptr(), v.data_ptr(), k.shape[0])
+        if query_start_loc is not None:
+            _dev(query_start_loc, "query_start_loc", torch.int32)
+            if tuple(query_start_loc.shape) != (B + 1,):
+                raise ValueError("query_start_loc must have num_seqs + 1 entries")
+        _dev(out, "out", self.dtype)
+        if workspace.numel() < self.workspace_bytes(T, B, max_seq_len):
+            raise ValueError("workspace too small")
+        self._kvs = kvs  # kept alive: a graph reads the array only at capture, a forward during the call
+        return (self._h, _ptr(hidden), _ptr(positions), T, kvs, _ptr(block_table), block_table.shape[1],
+                _ptr(seq_lens), _ptr(query_start_loc), B, int(max_seq_len), _ptr(out), _ptr(workspace))
+
+    def forward(self, hidden, positions, kv_caches, block_table, seq_lens, max_seq_len: int, out=None,
+                workspace=None, stream=None, query_start_loc=None):
+        """kv_caches: list of (k_cache, v_cache), one per layer.  Returns out."""
+        if out is None:
+            out = torch.empty_like(hidden)
+        if workspace is None:
+            workspace = self.alloc_workspace(hidden.shape[0], seq_lens.shape[0], max_seq_len, hidden.device)
+        a = self._args(hidden, positions, kv_caches, block_table, seq_lens, max_seq_len, out, workspace,
+                       query_start_loc)
+        _check(lib().llama_stack_forward(*a, _stream(stream)))
+        return out
+
+    def capture(self, hidden, positions, kv_caches, block_table, seq_lens, max_seq_len: int, out, workspace,
+                stream, query_start_loc=None) -> "Graph":
+        """A HIP graph of one forward with these buffers (llama_stack_graph_create)."""
+        a = self._args(hidden, positions, kv_caches, block_table, seq_lens, max_seq_len, out, workspace,
+                       query_start_loc)
+        g = ctypes.c_void_p()
+        _check(lib().llama_stack_graph_create(*a, _stream(stream), ctypes.byref(g)))
+        return Graph(g, keep=(hidden, positions, kv_caches, block_table, seq_lens, out, workspace, query_start_loc))
+
+
+class Graph:
+    """A captured stack forward (llama_graph)."""
+
+    def __init__(self, handle, keep):
+        self._h = handle
+        self._keep = keep  # the buffers the graph points at stay alive with it
+
+    def launch(self, stream=None):
+        _check(lib().llama_graph_launch(self._h, _stream(stream)))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().llama_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, epilogue: Epilogue = Epilogue.STORE, out=None, stream=None):

@@ -597,4 +597,177 @@ llama_status llama_op_add_rmsnorm(int32_t dtype, const void* x, const void* resi
   return LLAMA_OK;
 }
 
+// ---------------------------------------------------------------- stack ----
+
+struct llama_stack {
+  std::vector<llama_layer*> layers;
+  void* w_final = nullptr;  // final norm weight [H]
+  float eps = 0.f;
+  int dtype = 0;
+  size_t es = 2;
+  int H = 0;
+};
+
+struct llama_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+void free_stack(llama_stack* S) {
+  if (!S) return;
+  for (llama_layer* L : S->layers) free_layer(L);
+  if (S->w_final) (void)hipFree(S->w_final);
+  delete S;
+}
+
+// the stack's own workspace: the (hidden, residual) pair the layers update
+// in place, after the region one layer forward needs
+struct StackWs {
+  size_t layer, h, r, total;
+};
+StackWs carve_stack(const llama_stack* S, int T, int B, int max_seq_len) {
+  StackWs w{};
+  w.layer = 0;
+  size_t off = align256(carve(S->layers[0], T, B, max_seq_len).total);
+  w.h = off;
+  off += align256((size_t)T * S->H * S->es);
+  w.r = off;
+  off += align256((size_t)T * S->H * S->es);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+llama_status llama_stack_create(const llama_layer_config* config, int32_t num_layers,
+                                const llama_layer_weights* weights, const void* final_norm, void* stream,
+                                llama_stack** out) {
+  if (!out) return fail(LLAMA_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (!config || !weights || !final_norm) return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (num_layers <= 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_layers %d must be positive", num_layers);
+  llama_status st = llama_layer_config_validate(config);
+  if (st != LLAMA_OK) return st;
+  llama_stack* S = new llama_stack();
+  S->dtype = config->dtype;
+  S->es = config->dtype == LLAMA_DTYPE_BF16 ? 2 : 4;
+  S->H = config->hidden_size;
+  S->eps = config->rms_norm_eps;
+  for (int l = 0; l < num_layers; ++l) {
+    llama_layer* L = nullptr;
+    st = llama_layer_create(config, &weights[l], stream, &L);
+    if (st != LLAMA_OK) {
+      free_stack(S);
+      return st;
+    }
+    S->layers.push_back(L);
+  }
+  const size_t bytes = (size_t)S->H * S->es;
+  if (hipMalloc(&S->w_final, bytes) != hipSuccess) {
+    free_stack(S);
+    return fail(LLAMA_ERR_OUT_OF_MEMORY, "hipMalloc of the final norm weight failed");
+  }
+  hipError_t e = hipMemcpyAsync(S->w_final, final_norm, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) {
+    free_stack(S);
+    return hip_fail(e, "final norm copy");
+  }
+  *out = S;
+  return LLAMA_OK;
+}
+
+size_t llama_stack_workspace_bytes(const llama_stack* S, int32_t T, int32_t B, int32_t max_seq_len) {
+  if (!S || T <= 0 || B <= 0 || max_seq_len <= 0) return 0;
+  return carve_stack(S, T, B, max_seq_len).total;
+}
+
+llama_status llama_stack_forward(llama_stack* S, const void* hidden, const int32_t* positions, int32_t T,
+                                 const llama_kv_cache* kv_caches, const int32_t* block_table, int32_t max_blocks,
+                                 const int32_t* seq_lens, const int32_t* query_start_loc, int32_t B,
+                                 int32_t max_seq_len, void* out, void* workspace, void* stream) {
+  if (!S) return fail(LLAMA_ERR_INVALID_ARGUMENT, "stack is NULL");
+  if (!hidden || !kv_caches || !out || !workspace) return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (T <= 0 || B <= 0 || max_seq_len <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_tokens, num_seqs and max_seq_len must be positive");
+  if (!aligned16(out)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
+  const StackWs w = carve_stack(S, T, B, max_seq_len);
+  char* ws = (char*)workspace;
+  void* h = ws + w.h;
+  void* r = ws + w.r;
+  for (size_t l = 0; l < S->layers.size(); ++l) {
+    // layer 0 reads the input with no residual; later layers update (h, r) in place
+    const void* hin = l == 0 ? hidden : h;
+    const void* rin = l == 0 ? nullptr : r;
+    const llama_status st = llama_layer_forward(S->layers[l], hin, rin, positions, T, &kv_caches[l], block_table,
+                                                max_blocks, seq_lens, query_start_loc, B, max_seq_len, h, r,
+                                                ws + w.layer, stream);
+    if (st != LLAMA_OK) return st;
+  }
+  // final norm of hidden + residual
+  hipError_t e = llk::launch_add_rmsnorm(S->dtype, h, r, S->w_final, S->eps, T, S->H, out, nullptr,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "final norm");
+  return LLAMA_OK;
+}
+
+void llama_stack_destroy(llama_stack* S) {
+  if (!S) return;
+  (void)hipDeviceSynchronize();
+  free_stack(S);
+}
+
+llama_status llama_stack_graph_create(llama_stack* S, const void* hidden, const int32_t* positions, int32_t T,
+                                      const llama_kv_cache* kv_caches, const int32_t* block_table,
+                                      int32_t max_blocks, const int32_t* seq_lens, const int32_t* query_start_loc,
+                                      int32_t B, int32_t max_seq_len, void* out, void* workspace, void* stream,
+                                      llama_graph** graph_out) {
+  if (!graph_out) return fail(LLAMA_ERR_INVALID_ARGUMENT, "graph_out is NULL");
+  *graph_out = nullptr;
+  if (!S) return fail(LLAMA_ERR_INVALID_ARGUMENT, "stack is NULL");
+  if (!stream) return fail(LLAMA_ERR_INVALID_ARGUMENT, "capture needs a stream other than the default stream");
+  for (llama_layer* L : S->layers)
+    if (L->timing) return fail(LLAMA_ERR_INVALID_ARGUMENT, "turn per-kernel timing off before capturing");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+  const llama_status st = llama_stack_forward(S, hidden, positions, T, kv_caches, block_table, max_blocks, seq_lens,
+                                              query_start_loc, B, max_seq_len, out, workspace, stream);
+  std::string err = st != LLAMA_OK ? g_err : std::string();
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(s, &g);  // always: leaves the stream out of capture mode
+  if (st != LLAMA_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return fail(st, "%s", err.c_str());
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  llama_graph* G = new llama_graph();
+  G->graph = g;
+  e = hipGraphInstantiate(&G->exec, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    delete G;
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  *graph_out = G;
+  return LLAMA_OK;
+}
+
+llama_status llama_graph_launch(llama_graph* G, void* stream) {
+  if (!G || !G->exec) return fail(LLAMA_ERR_INVALID_ARGUMENT, "graph is NULL");
+  hipError_t e = hipGraphLaunch(G->exec, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  return LLAMA_OK;
+}
+
+void llama_graph_destroy(llama_graph* G) {
+  if (!G) return;
+  (void)hipDeviceSynchronize();
+  if (G->exec) (void)hipGraphExecDestroy(G->exec);
+  if (G->graph) (void)hipGraphDestroy(G->graph);
+  delete G;
+}
+
 }  // extern "C"

@@ -5,9 +5,9 @@ baseline leg of ``bench.py`` may import this package.  It shares no code with
 the HIP library and imports nothing from it.
 """
 from .layer import (STORAGE_POINTS, Seq, apply_rope, attend, bf16_round, decoder_layer,
-                    decoder_stack, fused_add_rms_norm, linear, rms_norm, rope_frequencies,
-                    silu, silu_and_mul)
+                    decoder_stack, fused_add_rms_norm, linear, model_forward, rms_norm,
+                    rope_frequencies, silu, silu_and_mul)
 
 __all__ = ["STORAGE_POINTS", "Seq", "apply_rope", "attend", "bf16_round", "decoder_layer",
-           "decoder_stack", "fused_add_rms_norm", "linear", "rms_norm", "rope_frequencies",
+           "decoder_stack", "fused_add_rms_norm", "linear", "model_forward", "rms_norm", "rope_frequencies",
            "silu", "silu_and_mul"]

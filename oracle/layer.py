@@ -302,3 +302,20 @@ def decoder_stack(cfg: dict, layers: Sequence[dict], hidden, residual, positions
         rn[rows] = rnd_(o["residual_out"])
         h, r = hn, rn
     return outs
+
+
+def model_forward(cfg: dict, layers: Sequence[dict], final_norm_w: np.ndarray, hidden, positions,
+                  seqs_per_layer: Sequence[Sequence[Seq]], rnd=None):
+    """The model body without embedding and lm_head.  The layers run in order,
+    the first with no residual, each handing (hidden, residual) to the next;
+    the final RMSNorm then normalises hidden + residual -- page "LLama"
+    (hotelren.com/news/2693952), section "最终 RMSNorm"; page
+    yeyulingfeng.com/a/605382.html, section "2.1 LlamaModel.forward()" (its
+    third step, the final norm of the pair).  Returns (output, per-layer
+    result dicts)."""
+    rnd_ = rnd or _identity
+    outs = decoder_stack(cfg, layers, hidden, None, positions, seqs_per_layer, rnd=rnd)
+    h = rnd_(outs[-1]["hidden_out"])
+    r = rnd_(outs[-1]["residual_out"])
+    out, _ = fused_add_rms_norm(h, r, final_norm_w, cfg["rms_norm_eps"], rnd=rnd_)
+    return out, outs

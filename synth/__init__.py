@@ -33,6 +33,7 @@ import torch
 # tensor ids used in seeds
 T_W_IN, T_W_QKV, T_W_O, T_W_POST, T_W_GU, T_W_DOWN = 0, 1, 2, 3, 4, 5
 T_HIDDEN, T_RESIDUAL, T_KCTX, T_VCTX, T_CTXLEN, T_BLOCKPERM = 6, 7, 8, 9, 10, 11
+T_W_FINAL = 12  # the model body's final norm (drawn with layer 0's seed base)
 
 KV_BLOCK = 16
 
@@ -139,6 +140,8 @@ WORKLOADS = {
         # 512-token prefill chunk on a 4096-token context, in one call
         Workload(5, "llama70b_mixed_chunk512_decode32", LLAMA70B, 33, 0,
                  mix=tuple([(1, 2048)] * 32 + [(512, 4096)])),
+        # the 70B model body: 80 layers and the final norm, 32 decode rows
+        Workload(6, "llama70b_stack80_decode_b32_ctx2048", LLAMA70B, 32, 1, 2048, 80),
     ]
 }
 WORKLOAD_LIST = sorted(WORKLOADS.values(), key=lambda w: w.index)
@@ -189,6 +192,14 @@ def draw_weights(model: ModelShape, workload_index: int, layer: int, device,
         "gate_up_proj": draw_normal((2 * I, H), s(T_W_GU), device, dt, 0.0, linear_std),
         "down_proj": draw_normal((H, I), s(T_W_DOWN), device, dt, 0.0, linear_std),
     }
+
+
+def draw_final_norm(model: ModelShape, workload_index: int, device, norm_mean: float = 1.0,
+                    norm_std: float = 0.02) -> torch.Tensor:
+    """The final RMSNorm weight of a layer stack, 1 + N(0, 0.02^2) like the
+    layers' norm weights."""
+    return draw_normal((model.hidden_size,), seed_of(workload_index, 0, T_W_FINAL), device, model.torch_dtype,
+                       norm_mean, norm_std)
 
 
 def draw_activations(model: ModelShape, num_tokens: int, workload_index: int, device,

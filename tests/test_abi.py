@@ -96,3 +96,17 @@ def test_host_argument_errors_need_no_gpu():
     assert L.llama_op_add_rmsnorm(0, fake, fake, fake, 1e-5, 4, 128, fake, None, None) == lda.Status.INVALID_ARGUMENT
     assert L.llama_op_reorder_gate_up(fake, 24, 128, fake, None) == lda.Status.INVALID_ARGUMENT
     assert L.llama_op_reorder_gate_up(fake, 32, 128, fake, None) == lda.Status.INVALID_ARGUMENT  # aliasing
+    # the stack and its graphs
+    cfg = lda.make_config(synth.LLAMA70B.config_dict(), lda.Dtype.BF16)
+    out = ctypes.c_void_p()
+    w = (lda.Weights * 1)()
+    assert L.llama_stack_create(ctypes.byref(cfg), 0, w, fake, None, ctypes.byref(out)) == lda.Status.INVALID_ARGUMENT
+    assert b"num_layers" in L.llama_layer_last_error()
+    assert L.llama_stack_create(ctypes.byref(cfg), 1, None, fake, None, ctypes.byref(out)) == lda.Status.INVALID_ARGUMENT
+    assert L.llama_stack_workspace_bytes(None, 1, 1, 1) == 0
+    assert L.llama_stack_forward(None, fake, fake, 1, None, fake, 1, fake, None, 1, 1, fake, fake,
+                                 None) == lda.Status.INVALID_ARGUMENT
+    g = ctypes.c_void_p()
+    assert L.llama_stack_graph_create(None, fake, fake, 1, None, fake, 1, fake, None, 1, 1, fake, fake, fake,
+                                      ctypes.byref(g)) == lda.Status.INVALID_ARGUMENT
+    assert L.llama_graph_launch(None, None) == lda.Status.INVALID_ARGUMENT

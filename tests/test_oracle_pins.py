@@ -321,6 +321,35 @@ def test_layer_matches_unfused_library_formulation(scaling, ctx):
     np.testing.assert_allclose(out0["hidden_out"] + out0["residual_out"], ref, rtol=1e-10, atol=1e-10)
 
 
+def test_model_forward_matches_unfused_stack_and_final_norm():
+    """The model body: three layers handing the pair on, then the final norm
+    of hidden + residual, equals the unfused formulation chained on one
+    residual stream followed by torch's RMSNorm."""
+    cfg = _cfg()
+    rng = np.random.default_rng(9)
+    ws = [_weights(cfg, rng) for _ in range(3)]
+    final_w = 1.0 + 0.5 * rng.standard_normal(cfg["hidden_size"])
+    T, ctx = 6, 4
+    nkv, d = cfg["num_key_value_heads"], cfg["head_dim"]
+    ctxs = [(rng.standard_normal((ctx, nkv, d)), rng.standard_normal((ctx, nkv, d))) for _ in ws]
+    hidden = rng.standard_normal((T, cfg["hidden_size"]))
+    pos = np.arange(ctx, ctx + T)
+    seqs = [[oracle.Seq(range(T), kc, vc)] for kc, vc in ctxs]
+    out, per_layer = oracle.model_forward(cfg, ws, final_w, hidden, pos, seqs)
+    freqs = np.array([cfg["rope_theta"] ** (-2.0 * i / d) for i in range(d // 2)])
+    stream = hidden
+    for w, (kc, vc) in zip(ws, ctxs):
+        stream = _layer_unfused_torch(cfg, w, stream, pos, kc, vc, freqs)
+    ref = F.rms_norm(torch.from_numpy(stream), (cfg["hidden_size"],), weight=torch.from_numpy(final_w),
+                     eps=cfg["rms_norm_eps"]).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-10)
+    assert len(per_layer) == 3
+    # the norm sees the sum: with a unit weight every row has mean square ms / (ms + eps)
+    out1, _ = oracle.model_forward(cfg, ws, np.ones(cfg["hidden_size"]), hidden, pos, seqs)
+    ms = np.mean(stream ** 2, axis=1)
+    np.testing.assert_allclose(np.mean(out1 ** 2, axis=1), ms / (ms + cfg["rms_norm_eps"]), rtol=1e-12)
+
+
 def test_layer_kv_append_values():
     """The appended K is the rotated k projection, V the raw v projection."""
     cfg = _cfg()
