@@ -49,7 +49,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-STORAGE_POINTS = ("r", "h", "qkv", "q_rot", "k_rot", "attn", "r2", "h2", "act")
+STORAGE_POINTS = ("r", "h", "qkv", "q_norm", "k_norm", "q_rot", "k_rot", "attn", "r2", "h2", "act",
+                  "moe_part")
 
 
 def bf16_round(x) -> np.ndarray:
@@ -183,7 +184,10 @@ def decoder_layer(cfg: dict, w: dict, hidden: np.ndarray, residual: Optional[np.
     """One layer forward.
 
     cfg: config.json-style dict; w: float64 weights (input_layernorm,
-    qkv_proj, o_proj, post_attention_layernorm, gate_up_proj, down_proj);
+    qkv_proj, o_proj, post_attention_layernorm, gate_up_proj, down_proj; a
+    mixture-of-experts layer -- ``cfg["num_experts"]`` > 0 -- has router
+    [E, H], experts_gate_up [E, 2I, H] and experts_down [E, H, I] in place of
+    the last two, and ``cfg["qk_norm"]`` adds q_norm, k_norm [head_dim]);
     hidden/residual [T, H] (residual may be None); positions [T]; seqs the
     batch's sequences; rnd None or ``bf16_round``.
 
@@ -235,6 +239,11 @@ def decoder_layer(cfg: dict, w: dict, hidden: np.ndarray, residual: Optional[np.
     want_idx = np.array([need_pos[row] for row in want], dtype=np.int64)
     q = rnd(linear(h[want_idx], wq)).reshape(-1, nq, d)
 
+    # Qwen3: per-head RMSNorm of q and k before RoPE (oracle/moe.py)
+    if cfg.get("qk_norm"):
+        k = rnd(rms_norm(k, w["k_norm"], eps))
+        q = rnd(rms_norm(q, w["q_norm"], eps))
+
     # RoPE on q and k only
     pos_need = positions[need]
     k = rnd(apply_rope(k, pos_need, freqs))
@@ -270,12 +279,23 @@ def decoder_layer(cfg: dict, w: dict, hidden: np.ndarray, residual: Optional[np.
     r2 = y + r_w
     h2, r2s = fused_add_rms_norm(y, r_w, w["post_attention_layernorm"], eps, rnd)
 
-    # gate_up projection, SiluAndMul, down projection
-    act = rnd(silu_and_mul(linear(h2, w["gate_up_proj"])))
-    out = linear(act, w["down_proj"])
+    if cfg.get("num_experts", 0) > 0:
+        # sparse MoE block in place of the MLP (oracle/moe.py)
+        from .moe import sparse_moe_block
+        moe = sparse_moe_block(h2, w["router"], w["experts_gate_up"], w["experts_down"],
+                               cfg["num_experts_per_tok"], cfg.get("norm_topk_prob", True), rnd)
+        out = moe["out"]
+        act = None
+    else:
+        # gate_up projection, SiluAndMul, down projection
+        act = rnd(silu_and_mul(linear(h2, w["gate_up_proj"])))
+        out = linear(act, w["down_proj"])
+        moe = None
     if trace is not None:
         trace.update({"need_rows": need_rows, "want_rows": want, "h": h, "q": q, "k": k, "v": v,
                       "attn": attn, "h2": h2, "act": act})
+        if moe is not None:
+            trace.update({"router_logits": moe["logits"], "topk_ids": moe["ids"], "topk_weights": moe["weights"]})
     return {"rows": want, "hidden_out": out, "residual_out": r2,
             "k_new": k_new, "v_new": v_new}
 

@@ -34,6 +34,7 @@ import torch
 T_W_IN, T_W_QKV, T_W_O, T_W_POST, T_W_GU, T_W_DOWN = 0, 1, 2, 3, 4, 5
 T_HIDDEN, T_RESIDUAL, T_KCTX, T_VCTX, T_CTXLEN, T_BLOCKPERM = 6, 7, 8, 9, 10, 11
 T_W_FINAL = 12  # the model body's final norm (drawn with layer 0's seed base)
+T_W_ROUTER, T_W_EXP13, T_W_EXP2, T_W_QNORM, T_W_KNORM = 13, 14, 15, 16, 17
 
 KV_BLOCK = 16
 
@@ -50,6 +51,14 @@ class ModelShape:
     rope_scaling: Optional[dict]
     max_position_embeddings: int
     dtype: str  # "bf16" or "fp32"
+    # a mixture-of-experts layer (num_experts > 0) replaces the MLP by
+    # num_experts FFNs of width moe_intermediate_size, num_experts_per_tok
+    # chosen per token; qk_norm adds a per-head RMSNorm of q and k
+    num_experts: int = 0
+    num_experts_per_tok: int = 0
+    moe_intermediate_size: int = 0
+    norm_topk_prob: bool = True
+    qk_norm: bool = False
 
     @property
     def q_size(self) -> int:
@@ -84,6 +93,12 @@ class ModelShape:
             "mlp_bias": False,
             "torch_dtype": "bfloat16" if self.dtype == "bf16" else "float32",
         }
+        if self.num_experts:
+            d.update({"num_experts": self.num_experts, "num_experts_per_tok": self.num_experts_per_tok,
+                      "moe_intermediate_size": self.moe_intermediate_size,
+                      "norm_topk_prob": self.norm_topk_prob})
+        if self.qk_norm:
+            d["qk_norm"] = True
         return d
 
 
@@ -97,6 +112,12 @@ LLAMA3_SCALING = {
 
 LLAMA70B = ModelShape(8192, 64, 8, 128, 28672, 1e-5, 500000.0, LLAMA3_SCALING, 131072, "bf16")
 TINY = ModelShape(256, 4, 2, 64, 688, 1e-5, 10000.0, None, 4096, "fp32")
+# Qwen3-30B-A3B (config.json on the page "LLama", section
+# "Qwen3MoeForCausalLM"): every layer is sparse (decoder_sparse_step 1, no
+# mlp_only_layers), so intermediate_size (the dense width) is never used.
+QWEN3MOE = ModelShape(2048, 32, 4, 128, 6144, 1e-6, 1e7, None, 262144, "bf16",
+                      num_experts=128, num_experts_per_tok=8, moe_intermediate_size=768,
+                      norm_topk_prob=True, qk_norm=True)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -142,6 +163,9 @@ WORKLOADS = {
                  mix=tuple([(1, 2048)] * 32 + [(512, 4096)])),
         # the 70B model body: 80 layers and the final norm, 32 decode rows
         Workload(6, "llama70b_stack80_decode_b32_ctx2048", LLAMA70B, 32, 1, 2048, 80),
+        # the Qwen3-MoE layer on the same two batch shapes as the 70B layer
+        Workload(7, "qwen3moe_decode_b32_ctx2048", QWEN3MOE, 32, 1, 2048),
+        Workload(8, "qwen3moe_prefill_4x2048", QWEN3MOE, 4, 2048, 0),
     ]
 }
 WORKLOAD_LIST = sorted(WORKLOADS.values(), key=lambda w: w.index)
@@ -180,18 +204,32 @@ def draw_weights(model: ModelShape, workload_index: int, layer: int, device,
                  linear_std: float = 0.02, norm_mean: float = 1.0,
                  norm_std: float = 0.02) -> dict:
     """Packed weights of one layer, each row-major [out, in]: qkv rows
-    [q heads | k heads | v heads], gate_up rows [gate | up]."""
+    [q heads | k heads | v heads], gate_up rows [gate | up].  A
+    mixture-of-experts model has router [E, H], experts_gate_up [E, 2I, H]
+    (each expert [gate | up]) and experts_down [E, H, I] instead of the MLP;
+    qk_norm adds q_norm and k_norm [head_dim] (drawn like the norm weights)."""
     dt = model.torch_dtype
     H, I = model.hidden_size, model.intermediate_size
     s = lambda tid: seed_of(workload_index, layer, tid)
-    return {
+    w = {
         "input_layernorm": draw_normal((H,), s(T_W_IN), device, dt, norm_mean, norm_std),
         "qkv_proj": draw_normal((model.qkv_size, H), s(T_W_QKV), device, dt, 0.0, linear_std),
         "o_proj": draw_normal((H, model.q_size), s(T_W_O), device, dt, 0.0, linear_std),
         "post_attention_layernorm": draw_normal((H,), s(T_W_POST), device, dt, norm_mean, norm_std),
-        "gate_up_proj": draw_normal((2 * I, H), s(T_W_GU), device, dt, 0.0, linear_std),
-        "down_proj": draw_normal((H, I), s(T_W_DOWN), device, dt, 0.0, linear_std),
     }
+    if model.num_experts:
+        E, Ie = model.num_experts, model.moe_intermediate_size
+        w["router"] = draw_normal((E, H), s(T_W_ROUTER), device, dt, 0.0, linear_std)
+        w["experts_gate_up"] = draw_normal((E, 2 * Ie, H), s(T_W_EXP13), device, dt, 0.0, linear_std)
+        w["experts_down"] = draw_normal((E, H, Ie), s(T_W_EXP2), device, dt, 0.0, linear_std)
+    else:
+        w["gate_up_proj"] = draw_normal((2 * I, H), s(T_W_GU), device, dt, 0.0, linear_std)
+        w["down_proj"] = draw_normal((H, I), s(T_W_DOWN), device, dt, 0.0, linear_std)
+    if model.qk_norm:
+        d = model.head_dim
+        w["q_norm"] = draw_normal((d,), s(T_W_QNORM), device, dt, norm_mean, norm_std)
+        w["k_norm"] = draw_normal((d,), s(T_W_KNORM), device, dt, norm_mean, norm_std)
+    return w
 
 
 def draw_final_norm(model: ModelShape, workload_index: int, device, norm_mean: float = 1.0,
