@@ -97,14 +97,38 @@ typedef struct {
   int32_t mlp_bias;                 /* must be 0 */
   int32_t dtype;                    /* llama_dtype of weights, activations, KV cache */
   int32_t kv_block_size;            /* tokens per KV-cache block; must be 16 */
+  /* Mixture of experts (the Qwen3-MoE layer: page "LLama", sections
+   * "Qwen3MoeForCausalLM" and "Qwen3MoeSparseMoeBlock"; page "模型库与算子层 —
+   * 代码走读", section "Fused MoE").  num_experts = 0: the dense LlamaMLP.
+   * num_experts > 0: the MLP becomes a sparse block -- a router [E, H] gives
+   * each token a logit per expert; its num_experts_per_tok experts with the
+   * largest softmax probabilities (equal ones: lower expert first) each run
+   * down(silu(x Wg^T) * (x Wu^T)) with their own weights; the outputs are
+   * summed weighted by those probabilities, divided by their sum when
+   * norm_topk_prob != 0.  bf16 only; num_experts a multiple of 16 up to 256,
+   * 1 <= num_experts_per_tok <= min(num_experts, 64), moe_intermediate_size a
+   * multiple of 128, hidden_size a multiple of 256      -> else UNSUPPORTED */
+  int32_t num_experts;
+  int32_t num_experts_per_tok;
+  int32_t moe_intermediate_size;
+  int32_t norm_topk_prob;
+  /* qk_norm != 0: each q and k head is RMS-normalised over head_dim (weights
+   * q_norm / k_norm, eps rms_norm_eps) before RoPE, as Qwen3 attention does. */
+  int32_t qk_norm;
 } llama_layer_config;
 
 /* Device pointers to the layer's weights in the layer dtype:
  *   input_layernorm, post_attention_layernorm  [hidden_size]
  *   qkv_proj      [(heads + 2*kv_heads) * head_dim, hidden_size]
  *   o_proj        [hidden_size, heads * head_dim]
- *   gate_up_proj  [2 * intermediate_size, hidden_size]
- *   down_proj     [hidden_size, intermediate_size]                           */
+ *   gate_up_proj  [2 * intermediate_size, hidden_size]      (dense layers)
+ *   down_proj     [hidden_size, intermediate_size]          (dense layers)
+ *   q_norm, k_norm  [head_dim]                              (qk_norm only)
+ *   router        [num_experts, hidden_size]                (MoE layers)
+ *   experts_gate_up [num_experts, 2 * moe_intermediate_size, hidden_size],
+ *                 each expert [gate | up]: the fused layer's w13 (MoE layers)
+ *   experts_down  [num_experts, hidden_size, moe_intermediate_size]: w2
+ * Pointers a configuration does not use may be NULL.                        */
 typedef struct {
   const void* input_layernorm;
   const void* qkv_proj;
@@ -112,6 +136,11 @@ typedef struct {
   const void* post_attention_layernorm;
   const void* gate_up_proj;
   const void* down_proj;
+  const void* q_norm;
+  const void* k_norm;
+  const void* router;
+  const void* experts_gate_up;
+  const void* experts_down;
 } llama_layer_weights;
 
 /* One layer's paged KV cache (device memory owned by the caller), two planes
@@ -181,7 +210,10 @@ LLAMA_API size_t llama_layer_workspace_bytes(const llama_layer* layer, int32_t n
  *   hidden_out, residual_out  [T, H] device: the output pair.  residual_out
  *                = (hidden + residual) + o_proj(attention) (the stream value
  *                after attention), hidden_out = down_proj(SiluAndMul(
- *                gate_up_proj(RMSNorm(residual_out)))).  hidden_out may alias
+ *                gate_up_proj(RMSNorm(residual_out)))), or the sparse MoE
+ *                block of RMSNorm(residual_out) in an MoE layer; each
+ *                expert's weighted output is rounded to the layer dtype
+ *                before the sum over a token's experts.  hidden_out may alias
  *                hidden and residual_out may alias residual; the two outputs
  *                must not alias each other.
  *   workspace    >= llama_layer_workspace_bytes(layer, T, num_seqs, max_seq_len)
@@ -276,8 +308,10 @@ LLAMA_API void llama_graph_destroy(llama_graph* graph);
  *                          q after RoPE, its k part k before RoPE
  *   "attn" [T, heads*d]    attention output
  *   "h2"   [T, H]          post_attention_layernorm output
- *   "act"  [T, I]          SiluAndMul output
- * Returns INVALID_ARGUMENT for an unknown name. */
+ *   "act"  [T, I]          SiluAndMul output (dense layers)
+ *   "router_logits" [T, E] float32, "topk_ids" [T, k] int32 (best first),
+ *   "topk_weights" [T, k] float32   the MoE routing (MoE layers)
+ * Returns INVALID_ARGUMENT for an unknown name or one the layer lacks. */
 LLAMA_API llama_status llama_layer_workspace_tensor(const llama_layer* layer, int32_t num_tokens,
                                           int32_t num_seqs, int32_t max_seq_len, const char* name,
                                           size_t* offset, size_t* bytes);

@@ -65,12 +65,18 @@ class Config(ctypes.Structure):
         ("mlp_bias", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("kv_block_size", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("num_experts_per_tok", ctypes.c_int32),
+        ("moe_intermediate_size", ctypes.c_int32),
+        ("norm_topk_prob", ctypes.c_int32),
+        ("qk_norm", ctypes.c_int32),
     ]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "input_layernorm", "qkv_proj", "o_proj", "post_attention_layernorm", "gate_up_proj", "down_proj")]
+        "input_layernorm", "qkv_proj", "o_proj", "post_attention_layernorm", "gate_up_proj", "down_proj",
+        "q_norm", "k_norm", "router", "experts_gate_up", "experts_down")]
 
 
 class KvCache(ctypes.Structure):
@@ -196,7 +202,21 @@ def make_config(cfg: dict, dtype: Dtype) -> Config:
     c.mlp_bias = int(bool(cfg.get("mlp_bias", False)))
     c.dtype = int(dtype)
     c.kv_block_size = int(cfg.get("kv_block_size", 16))
+    c.num_experts = int(cfg.get("num_experts", 0))
+    c.num_experts_per_tok = int(cfg.get("num_experts_per_tok", 0))
+    c.moe_intermediate_size = int(cfg.get("moe_intermediate_size", 0))
+    c.norm_topk_prob = int(bool(cfg.get("norm_topk_prob", True)))
+    c.qk_norm = int(bool(cfg.get("qk_norm", False)))
     return c
+
+
+def make_weights(weights: dict, dtype) -> Weights:
+    """Weights struct from a dict of device tensors (absent names stay NULL)."""
+    w = Weights()
+    for n, _ in Weights._fields_:
+        if weights.get(n) is not None:
+            setattr(w, n, _dev(weights[n], n, dtype).data_ptr())
+    return w
 
 
 def validate(cfg, dtype: Dtype = Dtype.BF16) -> Status:
@@ -207,15 +227,15 @@ def validate(cfg, dtype: Dtype = Dtype.BF16) -> Status:
 class Layer:
     """One decoder layer on the current device (llama_layer_create)."""
 
-    WEIGHT_NAMES = ("input_layernorm", "qkv_proj", "o_proj", "post_attention_layernorm", "gate_up_proj", "down_proj")
+    WEIGHT_NAMES = tuple(n for n, _ in Weights._fields_)
+    # workspace tensors that are not in the layer dtype
+    _WS_DTYPES = {"router_logits": torch.float32, "topk_ids": torch.int32, "topk_weights": torch.float32}
 
     def __init__(self, cfg: dict, weights: dict, stream=None):
         self.cfg = dict(cfg)
         self.dtype = weights["qkv_proj"].dtype
         self._config = make_config(cfg, _dtype_of(self.dtype))
-        w = Weights()
-        for n in self.WEIGHT_NAMES:
-            setattr(w, n, _dev(weights[n], n, self.dtype).data_ptr())
+        w = make_weights(weights, self.dtype)
         h = ctypes.c_void_p()
         _check(lib().llama_layer_create(ctypes.byref(self._config), ctypes.byref(w), _stream(stream),
                                         ctypes.byref(h)))
@@ -276,7 +296,7 @@ class Layer:
         _check(lib().llama_layer_workspace_tensor(self._h, num_tokens, num_seqs, max_seq_len, name.encode(),
                                                   ctypes.byref(off), ctypes.byref(nb)))
         raw = workspace[off.value: off.value + nb.value]
-        return raw.view(self.dtype).view(num_tokens, -1)
+        return raw.view(self._WS_DTYPES.get(name, self.dtype)).view(num_tokens, -1)
 
     def set_timing(self, enable: bool) -> None:
         _check(lib().llama_layer_set_timing(self._h, int(bool(enable))))
@@ -304,8 +324,7 @@ class Stack:
         self._config = make_config(cfg, _dtype_of(self.dtype))
         ws = (Weights * self.num_layers)()
         for l, weights in enumerate(layer_weights):
-            for n in Layer.WEIGHT_NAMES:
-                setattr(ws[l], n, _dev(weights[n], n, self.dtype).data_ptr())
+            ws[l] = make_weights(weights, self.dtype)
         _dev(final_norm, "final_norm", self.dtype)
         h = ctypes.c_void_p()
         _check(lib().llama_stack_create(ctypes.byref(self._config), self.num_layers, ws, _ptr(final_norm),

@@ -83,6 +83,12 @@ struct llama_layer {
   void* w_post = nullptr;
   void* w_gu = nullptr;
   void* w_down = nullptr;
+  void* w_qn = nullptr;      // q_norm / k_norm (qk_norm)
+  void* w_kn = nullptr;
+  void* w_router = nullptr;  // MoE: router, expert gate_up (tiled, re-ordered), expert down (tiled)
+  void* w_e13 = nullptr;
+  void* w_e2 = nullptr;
+  int E = 0, topk = 0, moe_I = 0;
   float2* rope = nullptr;
 
   bool timing = false;
@@ -96,6 +102,9 @@ namespace {
 struct Workspace {
   size_t h, qkv, attn, h2, act, part, gpart, tpart, tpart_bytes, seq_of, ntiles, tiles, total;
   int tile_cap;  // entries of the prefill tile table (mixed batches)
+  // MoE routing and expert buffers (P = T * topk pairs)
+  size_t logits, ids, wts, seg, sorted, active, nactive, mtiles, mntiles, mact, mpart;
+  int moe_tile_cap;
   llk::AttnPlan plan;
   bool skinny;  // few tokens: weight-streaming projections with split-K partials
   llk::SkinnyPlan pq, po, pg, pd;
@@ -116,7 +125,7 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.qkv = take((size_t)T * L->qkv_n * L->es);
   w.attn = take((size_t)T * c.num_attention_heads * c.head_dim * L->es);
   w.h2 = take((size_t)T * c.hidden_size * L->es);
-  w.act = take((size_t)T * c.intermediate_size * L->es);
+  w.act = take(L->E ? 0 : (size_t)T * c.intermediate_size * L->es);
   w.part = take(w.plan.ws_bytes);
   const int H = c.hidden_size, Q = c.num_attention_heads * c.head_dim, I = c.intermediate_size;
   w.skinny = L->dtype == LLAMA_DTYPE_BF16 && T <= llk::kSkinnyMaxM;
@@ -124,11 +133,13 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   if (w.skinny) {
     w.pq = llk::skinny_plan(T, L->qkv_n, H, true, L->num_cus);
     w.po = llk::skinny_plan(T, H, Q, true, L->num_cus);
-    w.pg = llk::skinny_plan(T, 2 * I, H, false, L->num_cus);
-    w.pd = llk::skinny_plan(T, H, I, true, L->num_cus);
     size_t n = (size_t)w.pq.splits * L->qkv_n;
     if ((size_t)w.po.splits * H > n) n = (size_t)w.po.splits * H;
-    if ((size_t)w.pd.splits * H > n) n = (size_t)w.pd.splits * H;
+    if (!L->E) {
+      w.pg = llk::skinny_plan(T, 2 * I, H, false, L->num_cus);
+      w.pd = llk::skinny_plan(T, H, I, true, L->num_cus);
+      if ((size_t)w.pd.splits * H > n) n = (size_t)w.pd.splits * H;
+    }
     gpart = n * T * sizeof(float);
   }
   w.gpart = take(gpart);
@@ -136,7 +147,8 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.tpart_bytes = 0;
   if (L->dtype == LLAMA_DTYPE_BF16 && !w.skinny) {
     const int dims[4][2] = {{L->qkv_n, H}, {H, Q}, {2 * I, H}, {H, I}};  // weight rows, K
-    for (auto& dk : dims) {
+    for (int i = 0; i < (L->E ? 2 : 4); ++i) {
+      const int* dk = dims[i];
       const size_t b = llk::tile_plan(T, dk[0], dk[1], L->num_cus).partial_bytes;
       if (b > w.tpart_bytes) w.tpart_bytes = b;
     }
@@ -148,6 +160,19 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.seq_of = take((size_t)T * sizeof(int));
   w.ntiles = take(sizeof(int));
   w.tiles = take((size_t)w.tile_cap * sizeof(int4));
+  const size_t P = L->E ? (size_t)T * L->topk : 0;
+  w.moe_tile_cap = L->E ? (int)(P / llk::kMoeTileRows) + L->E + 1 : 0;
+  w.logits = take((size_t)T * L->E * sizeof(float));
+  w.ids = take(P * sizeof(int));
+  w.wts = take(P * sizeof(float));
+  w.seg = take(L->E ? (size_t)(L->E + 1) * sizeof(int) : 0);
+  w.sorted = take(P * sizeof(int));
+  w.active = take((size_t)L->E * sizeof(int));
+  w.nactive = take(L->E ? sizeof(int) : 0);
+  w.mtiles = take((size_t)w.moe_tile_cap * sizeof(int4));
+  w.mntiles = take(L->E ? sizeof(int) : 0);
+  w.mact = take(P * L->moe_I * L->es);
+  w.mpart = take(P * H * L->es);
   w.total = off;
   return w;
 }
@@ -201,13 +226,49 @@ hipError_t alloc_weight(void** p, size_t bytes) {
 
 void free_layer(llama_layer* L) {
   if (!L) return;
-  void* bufs[] = {L->w_in, L->w_qkv, L->w_o, L->w_post, L->w_gu, L->w_down, (void*)L->rope};
+  void* bufs[] = {L->w_in,  L->w_qkv,    L->w_o,   L->w_post, L->w_gu,          L->w_down,
+                  L->w_qn,  L->w_kn,     L->w_router, L->w_e13, L->w_e2, (void*)L->rope};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   for (auto& list : L->marks)
     for (auto& m : list) (void)hipEventDestroy(m.ev);
   for (hipEvent_t e : L->event_pool) (void)hipEventDestroy(e);
   delete L;
+}
+
+// The sparse MoE block on the post-attention norm output h2 [T, H]: router +
+// top-k, grouping of the (token, expert) pairs by expert, the expert GEMMs,
+// and the weighted sum into out.
+llama_status moe_block(llama_layer* L, const Workspace& w, char* ws, const void* h2, int T, void* out,
+                       hipStream_t s, Marker& mk) {
+  const int H = L->cfg.hidden_size, P = T * L->topk;
+  llk::MoeRouting r;
+  r.seg = (int*)(ws + w.seg);
+  r.sorted = (int*)(ws + w.sorted);
+  r.active = (int*)(ws + w.active);
+  r.nactive = (int*)(ws + w.nactive);
+  r.tiles = (int4*)(ws + w.mtiles);
+  r.ntiles = (int*)(ws + w.mntiles);
+  r.tile_cap = w.moe_tile_cap;
+  r.wts = (float*)(ws + w.wts);
+  int* ids = (int*)(ws + w.ids);
+  hipError_t e = llk::launch_moe_route(h2, T, H, L->w_router, L->E, L->topk, L->cfg.norm_topk_prob != 0,
+                                       (float*)(ws + w.logits), ids, r.wts, s);
+  if (e != hipSuccess) return hip_fail(e, "moe router");
+  mk.mark("moe_router_topk");
+  e = llk::launch_moe_align(ids, P, L->E, llk::kMoeTileRows, r, s);
+  if (e != hipSuccess) return hip_fail(e, "moe align");
+  mk.mark("moe_align");
+  hipEvent_t mid = mk.extra();
+  e = llk::launch_moe_experts(h2, T, H, L->topk, L->w_e13, L->w_e2, L->E, L->moe_I, L->wlayout, r, ws + w.mact,
+                              ws + w.mpart, s, mid);
+  if (e != hipSuccess) return hip_fail(e, "moe experts");
+  if (mid) mk.list->push_back({"moe_gate_up_silu", mid});
+  mk.mark("moe_down");
+  e = llk::launch_moe_sum(ws + w.mpart, T, L->topk, H, out, s);
+  if (e != hipSuccess) return hip_fail(e, "moe sum");
+  mk.mark("moe_sum");
+  return LLAMA_OK;
 }
 
 }  // namespace
@@ -258,6 +319,17 @@ llama_status llama_layer_config_validate(const llama_layer_config* c) {
     if (c->hidden_size % 4 || c->hidden_size > 8192)
       return fail(LLAMA_ERR_UNSUPPORTED, "fp32 needs hidden_size %% 4 == 0 and <= 8192");
   }
+  if (c->num_experts < 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_experts must be >= 0");
+  if (c->num_experts > 0) {
+    if (c->dtype != LLAMA_DTYPE_BF16) return fail(LLAMA_ERR_UNSUPPORTED, "mixture-of-experts layers are bf16 only");
+    if (c->num_experts_per_tok <= 0 || c->num_experts_per_tok > c->num_experts || c->moe_intermediate_size <= 0)
+      return fail(LLAMA_ERR_INVALID_ARGUMENT, "need 1 <= num_experts_per_tok <= num_experts and moe_intermediate_size > 0");
+    if (c->num_experts % 16 || c->num_experts > 256 || c->num_experts_per_tok > 64 ||
+        c->moe_intermediate_size % 128 || c->hidden_size % 256)
+      return fail(LLAMA_ERR_UNSUPPORTED,
+                  "MoE needs num_experts a multiple of 16 up to 256, num_experts_per_tok <= 64, "
+                  "moe_intermediate_size a multiple of 128 and hidden_size a multiple of 256");
+  }
   return LLAMA_OK;
 }
 
@@ -265,9 +337,13 @@ llama_status llama_layer_create(const llama_layer_config* config, const llama_la
                                 void* stream, llama_layer** out) {
   llama_status st = llama_layer_config_validate(config);
   if (st != LLAMA_OK) return st;
-  if (!w || !out || !w->input_layernorm || !w->qkv_proj || !w->o_proj || !w->post_attention_layernorm ||
-      !w->gate_up_proj || !w->down_proj)
+  if (!w || !out || !w->input_layernorm || !w->qkv_proj || !w->o_proj || !w->post_attention_layernorm)
     return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL weight or output pointer");
+  if (config->num_experts > 0 ? (!w->router || !w->experts_gate_up || !w->experts_down)
+                              : (!w->gate_up_proj || !w->down_proj))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL MLP or expert weight pointer");
+  if (config->qk_norm && (!w->q_norm || !w->k_norm))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "qk_norm needs q_norm and k_norm");
   *out = nullptr;
   hipStream_t s = (hipStream_t)stream;
   llama_layer* L = new llama_layer();
@@ -282,35 +358,55 @@ llama_status llama_layer_create(const llama_layer_config* config, const llama_la
   const llama_layer_config& c = L->cfg;
   const size_t H = c.hidden_size, I = c.intermediate_size, Q = (size_t)c.num_attention_heads * c.head_dim;
   L->qkv_n = (c.num_attention_heads + 2 * c.num_key_value_heads) * c.head_dim;
+  L->E = c.num_experts;
+  L->topk = L->E ? c.num_experts_per_tok : 0;
+  L->moe_I = L->E ? c.moe_intermediate_size : 0;
+  const size_t E = L->E, Ie = L->moe_I;
 
   // bf16 projection weights are kept in the 16x32-tiled layout (gate_up also
   // re-ordered into 16 gate + 16 up rows per 32-row group); norm weights and
   // fp32 weights are plain copies.
   const bool tile = L->dtype == LLAMA_DTYPE_BF16;
   L->wlayout = tile ? llk::kTiled16x32 : llk::kRowMajor;
+  // The router stays row-major (its kernel reads whole rows); each expert's
+  // gate_up is tiled and re-ordered on its own, and the stacked expert down
+  // weights tile as one matrix (every expert starts on a 16-row strip).
   struct Item {
     void** dst;
     const void* src;
     int rows, cols, inter;  // rows = 0: a plain copy of `cols` elements
+    int count;              // matrices stacked in src (experts), 0: not used
+    bool tiled;
   } items[] = {
-      {&L->w_in, w->input_layernorm, 0, (int)H, 0},
-      {&L->w_qkv, w->qkv_proj, L->qkv_n, (int)H, 0},
-      {&L->w_o, w->o_proj, (int)H, (int)Q, 0},
-      {&L->w_post, w->post_attention_layernorm, 0, (int)H, 0},
-      {&L->w_gu, w->gate_up_proj, (int)(2 * I), (int)H, (int)I},
-      {&L->w_down, w->down_proj, (int)H, (int)I, 0},
+      {&L->w_in, w->input_layernorm, 0, (int)H, 0, 1, false},
+      {&L->w_qkv, w->qkv_proj, L->qkv_n, (int)H, 0, 1, tile},
+      {&L->w_o, w->o_proj, (int)H, (int)Q, 0, 1, tile},
+      {&L->w_post, w->post_attention_layernorm, 0, (int)H, 0, 1, false},
+      {&L->w_gu, w->gate_up_proj, (int)(2 * I), (int)H, (int)I, E ? 0 : 1, tile},
+      {&L->w_down, w->down_proj, (int)H, (int)I, 0, E ? 0 : 1, tile},
+      {&L->w_qn, w->q_norm, 0, c.head_dim, 0, c.qk_norm ? 1 : 0, false},
+      {&L->w_kn, w->k_norm, 0, c.head_dim, 0, c.qk_norm ? 1 : 0, false},
+      {&L->w_router, w->router, 0, (int)(E * H), 0, E ? 1 : 0, false},
+      {&L->w_e13, w->experts_gate_up, (int)(2 * Ie), (int)H, (int)Ie, (int)E, true},
+      {&L->w_e2, w->experts_down, (int)(E * H), (int)Ie, 0, E ? 1 : 0, true},
   };
-  hipError_t e;
+  hipError_t e = hipSuccess;
   for (auto& it : items) {
-    const size_t bytes = (size_t)(it.rows ? it.rows : 1) * it.cols * L->es;
+    if (it.count == 0) continue;
+    const size_t one = (size_t)(it.rows ? it.rows : 1) * it.cols * L->es;
+    const size_t bytes = one * it.count;
     if (alloc_weight(it.dst, bytes) != hipSuccess) {
       free_layer(L);
       return fail(LLAMA_ERR_OUT_OF_MEMORY, "hipMalloc of %zu bytes for weights failed", bytes);
     }
-    if (tile && it.rows)
-      e = llk::launch_tile_weight(it.src, it.rows, it.cols, it.inter, *it.dst, s);
-    else
-      e = hipMemcpyAsync(*it.dst, it.src, bytes, hipMemcpyDeviceToDevice, s);
+    for (int m = 0; m < it.count && e == hipSuccess; ++m) {
+      const char* src = (const char*)it.src + m * one;
+      char* dst = (char*)*it.dst + m * one;
+      if (it.tiled && it.rows)
+        e = llk::launch_tile_weight(src, it.rows, it.cols, it.inter, dst, s);
+      else
+        e = hipMemcpyAsync(dst, src, one, hipMemcpyDeviceToDevice, s);
+    }
     if (e != hipSuccess) {
       free_layer(L);
       return hip_fail(e, "weight copy");
@@ -362,10 +458,13 @@ llama_status llama_layer_workspace_tensor(const llama_layer* L, int32_t T, int32
       {"qkv", w.qkv, (size_t)T * L->qkv_n * L->es},
       {"attn", w.attn, (size_t)T * c.num_attention_heads * c.head_dim * L->es},
       {"h2", w.h2, (size_t)T * c.hidden_size * L->es},
-      {"act", w.act, (size_t)T * c.intermediate_size * L->es},
+      {"act", w.act, L->E ? 0 : (size_t)T * c.intermediate_size * L->es},
+      {"router_logits", w.logits, (size_t)T * L->E * sizeof(float)},
+      {"topk_ids", w.ids, (size_t)T * L->topk * sizeof(int)},
+      {"topk_weights", w.wts, (size_t)T * L->topk * sizeof(float)},
   };
   for (auto& x : t)
-    if (std::strcmp(x.n, name) == 0) {
+    if (std::strcmp(x.n, name) == 0 && x.sz > 0) {
       *offset = x.off;
       *bytes = x.sz;
       return LLAMA_OK;
@@ -444,18 +543,24 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   mk.mark("input_layernorm");
   float* gp = (float*)(ws + w.gpart);
   float* tp = (float*)(ws + w.tpart);
+  llk::QkNorm qkn;
+  if (c.qk_norm) {
+    qkn.q = L->w_qn;
+    qkn.k = L->w_kn;
+    qkn.eps = c.rms_norm_eps;
+  }
   if (w.skinny) {
     e = llk::launch_skinny(h, L->w_qkv, T, L->qkv_n, H, llk::kEpiPartial, w.pq, gp, s, L->wlayout);
     if (e != hipSuccess) return hip_fail(e, "qkv_proj");
     mk.mark("qkv_proj");
     e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, map, kv->k,
-                            kv->v, s, gp, w.pq.splits);
+                            kv->v, s, gp, w.pq.splits, qkn);
   } else {
     e = llk::launch_linear(dt, h, L->w_qkv, T, L->qkv_n, H, llk::kEpiStore, qkv, s, L->wlayout, tp, w.tpart_bytes);
     if (e != hipSuccess) return hip_fail(e, "qkv_proj");
     mk.mark("qkv_proj");
     e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, map, kv->k,
-                            kv->v, s);
+                            kv->v, s, nullptr, 0, qkn);
   }
   if (e != hipSuccess) return hip_fail(e, "rope_kv_write");
   mk.mark("rope_kv_write");
@@ -475,6 +580,7 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
                                 gp, w.po.splits);
     if (e != hipSuccess) return hip_fail(e, "post_attention_layernorm");
     mk.mark("post_attention_layernorm");
+    if (L->E) return moe_block(L, w, ws, h2, T, hidden_out, s, mk);
     e = llk::launch_skinny(h2, L->w_gu, T, I, H, llk::kEpiSiluMul, w.pg, act, s, L->wlayout);
     if (e != hipSuccess) return hip_fail(e, "gate_up_proj");
     mk.mark("gate_up_silu");
@@ -493,6 +599,7 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   e = llk::launch_add_rmsnorm(dt, residual_out, nullptr, L->w_post, c.rms_norm_eps, T, H, h2, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "post_attention_layernorm");
   mk.mark("post_attention_layernorm");
+  if (L->E) return moe_block(L, w, ws, h2, T, hidden_out, s, mk);
   e = llk::launch_linear(dt, h2, L->w_gu, T, I, H, llk::kEpiSiluMul, act, s, L->wlayout, tp, w.tpart_bytes);
   if (e != hipSuccess) return hip_fail(e, "gate_up_proj");
   mk.mark("gate_up_silu");

@@ -91,11 +91,17 @@ hipError_t launch_batch_map(const int* query_start_loc, int B, int T, int qw, in
 
 // rope_kv.hip.  With part != NULL (bf16 only) the projection row is first
 // formed as the bf16 rounding of the sum of S fp32 partial rows and stored
-// into qkv.
+// into qkv.  A QkNorm with weights set (Qwen3) RMS-normalises each q and k
+// head before the rotation.
+struct QkNorm {
+  const void* q = nullptr;  // [head_dim] in the layer dtype, or NULL: no norm
+  const void* k = nullptr;
+  float eps = 0.f;
+};
 hipError_t launch_rope_kv(int dtype, void* qkv, int T, const int* positions, const float2* table,
                           int nq, int nkv, int d, const int* block_table, int max_blocks, const SeqMap& map,
                           void* k_cache, void* v_cache, hipStream_t s, const float* part = nullptr,
-                          int S = 0);
+                          int S = 0, const QkNorm& qkn = QkNorm());
 
 // attention.hip
 struct AttnPlan {
@@ -125,5 +131,34 @@ int prefill_tile_rows(int nq, int nkv, int d);
 hipError_t launch_prefill_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
                                          int d, const void* k_cache, const void* v_cache, const int* block_table,
                                          int max_blocks, const SeqMap& map, void* out, hipStream_t s);
+
+// moe.hip: the sparse MoE block (bf16).  Pair p = t * topk + slot.
+// launch_moe_route: logits [T, E] fp32, ids and wts [T * topk] (E % 16 == 0,
+// E <= 256, H % 64 == 0, topk <= min(E, 64)).  launch_moe_align groups the
+// pairs by expert (one workgroup) into the routing tables below, with tiles of
+// at most bm pair rows.  launch_moe_experts: act [P, I] (sorted rows) and part
+// [P, H] (pair rows, weighted) from the expert weights w13 [E][2I][H] (each
+// expert's gate_up re-ordered, 16 gate + 16 up rows per 32) and w2 [E][H][I],
+// both kTiled16x32; H % 256 == 0, I % 128 == 0.  launch_moe_sum: out [T, H]
+// = sum over slots of part, in slot order.
+constexpr int kMoeTileRows = 256;
+struct MoeRouting {
+  int* seg = nullptr;       // [E + 1] first sorted position of each expert
+  int* sorted = nullptr;    // [P] pair of each sorted position
+  int* active = nullptr;    // [E] experts with pairs, ascending
+  int* nactive = nullptr;   // [1]
+  int4* tiles = nullptr;    // [tile_cap] (expert, first sorted row, rows, 0)
+  int* ntiles = nullptr;    // [1]
+  int tile_cap = 0;         // >= P / bm + E
+  float* wts = nullptr;     // [P] routing weight of each pair
+};
+bool moe_streaming(int T);
+hipError_t launch_moe_route(const void* x, int T, int H, const void* router, int E, int topk, bool norm,
+                            float* logits, int* ids, float* wts, hipStream_t s);
+hipError_t launch_moe_align(const int* ids, int P, int E, int bm, const MoeRouting& r, hipStream_t s);
+hipError_t launch_moe_experts(const void* x, int T, int H, int topk, const void* w13, const void* w2, int E, int I,
+                              int layout, const MoeRouting& r, void* act, void* part, hipStream_t s,
+                              hipEvent_t mid = nullptr);  // recorded between the two GEMMs
+hipError_t launch_moe_sum(const void* part, int T, int topk, int H, void* out, hipStream_t s);
 
 }  // namespace llk

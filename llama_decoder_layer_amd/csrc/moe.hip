@@ -1,0 +1,607 @@
+// Sparse mixture-of-experts block of a Qwen3-MoE layer.
+//
+// What it computes: page "LLama" (hotelren.com/news/2693952), box
+// "Qwen3MoeSparseMoeBlock", and page "模型库与算子层 — 代码走读"
+// (vllm-learning.pages.dev), section "Fused MoE": a replicated linear router
+// gives each token one logit per expert, the token keeps its top-k experts,
+// each expert is a gated FFN (silu(x Wg^T) * (x Wu^T), then its down
+// projection) with merged expert weights w13 [E, 2I, H] and w2 [E, H, I], and
+// the token's output is the sum of its experts' outputs weighted by the gate
+// probabilities: the softmax over all experts, renormalised over the kept k
+// when norm_topk_prob is set.
+//
+// Kernels, in launch order:
+//   moe_router_kernel  logits [T, E] fp32 = x Wr^T on MFMA (one wave per 16
+//                      tokens x 16 experts, whole K);
+//   moe_topk_kernel    one wave per token: softmax statistics, k rounds of a
+//                      wave arg-max (ties: lower expert), renormalisation;
+//                      ids [T*k] and weights [T*k], pair p = t*k + slot;
+//   moe_align_kernel   one workgroup: per-expert counts, the pairs grouped by
+//                      expert ("sorted" positions), the active-expert list and
+//                      a table of row tiles (expert, first row, rows);
+//   expert GEMMs       gate_up + SiluAndMul over each expert's gathered token
+//                      rows into act [P, I] (sorted order), then down with the
+//                      routing weight applied before the bf16 store, scattered
+//                      to part [P, H] by pair.  Few pairs per expert (decode):
+//                      weight-streaming kernel over the active experts; many
+//                      (prefill): 256 x 256 MFMA tiles over the tile table;
+//   moe_sum_kernel     out[t] = sum over slots of part[t*k + slot], in slot
+//                      order, fp32 accumulation.
+// No atomics touch the results: the order of pairs inside an expert's group
+// (set by LDS atomics) changes which rows share a tile, never a row's value.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+namespace {
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+// ------------------------------------------------------------- router -----
+
+// D[e][t] = Wr[e,:] . x[t,:]: the router row is the MFMA's A operand, the
+// token row its B operand; a lane ends with experts e0 + 4g .. +3 of token
+// t0 + r16.  Grid (ceil(T/16), ceil(E/64)), four waves of 16 experts.
+__global__ __launch_bounds__(256) void moe_router_kernel(const bf16* __restrict__ x, int T, int H,
+                                                         const bf16* __restrict__ wr, int E,
+                                                         float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * 16;
+  const int e0 = (blockIdx.y * 4 + wave) * 16;
+  if (e0 >= E) return;
+  const int t = min(t0 + r16, T - 1);
+  const bf16* xa = x + (size_t)t * H + g * 8;
+  const bf16* wa = wr + (size_t)(e0 + r16) * H + g * 8;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k = 0; k < H; k += 64) {
+    const bf16x8 a0 = ld16<bf16x8>(wa + k), b0 = ld16<bf16x8>(xa + k);
+    const bf16x8 a1 = ld16<bf16x8>(wa + k + 32), b1 = ld16<bf16x8>(xa + k + 32);
+    acc0 = mfma16(a0, b0, acc0);
+    acc1 = mfma16(a1, b1, acc1);
+  }
+  if (t0 + r16 < T) {
+    f32x4 s;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = acc0[r] + acc1[r];
+    *reinterpret_cast<f32x4*>(logits + (size_t)(t0 + r16) * E + e0 + 4 * g) = s;
+  }
+}
+
+// One wave per token; lane l holds experts l, l + 64, ... (EPL of them).
+template <int EPL>
+__global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                       int norm, int* __restrict__ ids, float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+  }
+  float m = v[0];
+#pragma unroll
+  for (int j = 1; j < EPL; ++j) m = fmaxf(m, v[j]);
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (lane + 64 * j < E) s += expf(v[j] - m);
+  s = wave_sum(s);
+  int my_id = 0;
+  float my_p = 0.f;
+  for (int r = 0; r < k; ++r) {
+    float bv = v[0];
+    int bi = lane;
+#pragma unroll
+    for (int j = 1; j < EPL; ++j)
+      if (v[j] > bv) {  // a later slot of this lane has a larger index: strict
+        bv = v[j];
+        bi = lane + 64 * j;
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == r) {
+      my_id = bi;
+      my_p = expf(bv - m) / s;
+    }
+    // the owner drops the winner from later rounds
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j == bi) v[j] = -INFINITY;
+  }
+  const float wsum = wave_sum(lane < k ? my_p : 0.f);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = min(max(my_id, 0), E - 1);
+    wts[(size_t)t * k + lane] = norm ? my_p / wsum : my_p;
+  }
+}
+
+// ---------------------------------------------------------- alignment -----
+
+constexpr int kMaxExperts = 256;
+
+__global__ __launch_bounds__(1024) void moe_align_kernel(const int* __restrict__ ids, int P, int E, int bm,
+                                                         int* __restrict__ seg, int* __restrict__ sorted,
+                                                         int* __restrict__ active, int* __restrict__ nactive,
+                                                         int4* __restrict__ tiles, int tile_cap,
+                                                         int* __restrict__ ntiles) {
+  __shared__ int cnt[kMaxExperts], cur[kMaxExperts], toff[kMaxExperts], aidx[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < E) cnt[tid] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[min(max(ids[p], 0), E - 1)], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0, nt = 0, na = 0;
+    for (int e = 0; e < E; ++e) {
+      seg[e] = run;
+      cur[e] = run;
+      toff[e] = nt;
+      aidx[e] = cnt[e] > 0 ? na++ : -1;
+      run += cnt[e];
+      nt += (cnt[e] + bm - 1) / bm;
+    }
+    seg[E] = run;
+    *nactive = na;
+    *ntiles = min(nt, tile_cap);
+  }
+  __syncthreads();
+  if (tid < E && cnt[tid] > 0) {
+    const int e = tid, c = cnt[e];
+    active[aidx[e]] = e;
+    for (int i = 0; i * bm < c; ++i) {
+      const int idx = toff[e] + i;
+      if (idx < tile_cap) tiles[idx] = make_int4(e, cur[e] + i * bm, min(bm, c - i * bm), 0);
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024) {
+    const int e = min(max(ids[p], 0), E - 1);
+    sorted[atomicAdd(&cur[e], 1)] = p;
+  }
+}
+
+// ------------------------------------------------ expert GEMM: streaming --
+
+enum MoeEpi { kMoeGateUp = 0, kMoeDown = 1 };
+
+// Workgroup (j, rb): active expert j, weight rows [rb * NW*NT*16, +NW*NT*16)
+// of that expert, all of its pair rows in passes of 16*MT.  Gate_up: x rows
+// gathered by token (pair / k) from X [T, K]; out act [P, ldo] at the sorted
+// row.  Down: x rows are act's sorted rows; out part [P, ldo] at the pair's
+// row, times its routing weight.
+template <int MT, int NT, int KC, int NW, int EPI>
+__global__ __launch_bounds__(NW * 64) void moe_stream_kernel(const bf16* __restrict__ X, int topk,
+                                                             const bf16* __restrict__ W, int wrows, int K,
+                                                             WStride ws, const int* __restrict__ seg,
+                                                             const int* __restrict__ sorted,
+                                                             const int* __restrict__ active,
+                                                             const int* __restrict__ nactive,
+                                                             const float* __restrict__ wts,
+                                                             bf16* __restrict__ out, int ldo) {
+  constexpr int SPC = KC / 32;
+  constexpr int XR = MT * 16;
+  constexpr int XCH = XR * KC / 8;
+  constexpr int kThreads = NW * 64;
+  constexpr int XPT = (XCH + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) bf16 sx[2][XR * KC];
+  if ((int)blockIdx.x >= *nactive) return;
+  const int e = active[blockIdx.x];
+  const int r0 = seg[e], n = seg[e + 1] - r0;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n0 = (blockIdx.y * NW + wave) * NT * 16;
+  const int nchunk = K / KC;
+  const bf16* We = W + (size_t)e * wrows * K;
+
+  auto xaddr = [](int row, int c) { return row * KC + ((c ^ (row & 7)) << 3); };
+  const bf16x8 zero8 = {};
+  const bf16* wr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) wr[t] = We + (size_t)(n0 + 16 * t) * K + (size_t)r16 * ws.rs + g * 8;
+
+  for (int c0 = 0; c0 < n; c0 += XR) {
+    const int rows = min(XR, n - c0);
+    // this thread's x pieces: source row pointers for the pass
+    const bf16* xp[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int id = threadIdx.x + kThreads * j;
+      const int row = id / (KC / 8), c = id % (KC / 8);
+      xp[j] = nullptr;
+      if (id < XCH && row < rows) {
+        const int src = EPI == kMoeGateUp ? sorted[r0 + c0 + row] / topk : r0 + c0 + row;
+        xp[j] = X + (size_t)src * K + c * 8;
+      }
+    }
+    bf16x8 xs[XPT];
+    auto xload = [&](int kc) {
+#pragma unroll
+      for (int j = 0; j < XPT; ++j) xs[j] = xp[j] ? ld16<bf16x8>(xp[j] + kc) : zero8;
+    };
+    auto xstore = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < XPT; ++j) {
+        const int id = threadIdx.x + kThreads * j;
+        const int row = id / (KC / 8), c = id % (KC / 8);
+        if (id < XCH) *reinterpret_cast<bf16x8*>(&sx[buf][xaddr(row, c)]) = xs[j];
+      }
+    };
+    bf16x8 wn[SPC][NT];
+    auto wload = [&](int kc) {
+#pragma unroll
+      for (int s = 0; s < SPC; ++s)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) wn[s][t] = ld16<bf16x8>(wr[t] + (size_t)(kc / 32 + s) * ws.ks);
+    };
+    f32x4 acc[NT][MT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    wload(0);
+    xload(0);
+    xstore(0);
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+      bf16x8 wc[SPC][NT];
+#pragma unroll
+      for (int s = 0; s < SPC; ++s)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) wc[s][t] = wn[s][t];
+      if (c + 1 < nchunk) {
+        wload((c + 1) * KC);
+        xload((c + 1) * KC);
+      }
+#pragma unroll
+      for (int s = 0; s < SPC; ++s) {
+        bf16x8 xf[MT];
+#pragma unroll
+        for (int u = 0; u < MT; ++u)
+          xf[u] = *reinterpret_cast<const bf16x8*>(&sx[c & 1][xaddr(16 * u + r16, s * 4 + g)]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int u = 0; u < MT; ++u) acc[t][u] = mfma16(wc[s][t], xf[u], acc[t][u]);
+      }
+      if (c + 1 < nchunk) xstore((c + 1) & 1);
+      __syncthreads();
+    }
+
+    // lane holds features n0 + 16t + 4g + (0..3) of pass row 16u + r16
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+      const int m = 16 * u + r16;
+      if (m >= rows) continue;
+      if (EPI == kMoeGateUp) {
+        bf16* dst = out + (size_t)(r0 + c0 + m) * ldo;
+#pragma unroll
+        for (int t = 0; t < NT; t += 2) {
+          const int f = ((n0 + 16 * t) >> 5) * 16 + 4 * g;
+          bf16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(silu_f(acc[t][u][r]) * acc[t + 1][u][r]);
+          *reinterpret_cast<bf16x4*>(dst + f) = o;
+        }
+      } else {
+        const int p = sorted[r0 + c0 + m];
+        const float wgt = wts[p];
+        bf16* dst = out + (size_t)p * ldo;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          bf16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[t][u][r] * wgt);
+          *reinterpret_cast<bf16x4*>(dst + n0 + 16 * t + 4 * g) = o;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------- expert GEMM: tiles --
+
+constexpr int kTBK = 64;
+constexpr int kEntriesPerChunk = 2;
+
+// BM pair rows x BN weight rows of one expert per workgroup (an entry of the
+// tile table x one weight tile), K in stages of 64 straight from global
+// memory into double-buffered XOR-swizzled LDS, as the dense tiled kernel.
+// Work order: chunks of kEntriesPerChunk entries x all weight tiles are
+// dealt to the 8 XCDs in turn, so that the weight tiles of one entry, which
+// share its gathered x rows, run together on one XCD.  Waves are numbered
+// with the weight-tile index fastest (SIMD = wave % 4 holds one wave of
+// each token half): a partly filled tile skips the MFMAs of its empty
+// 16-row sub-tiles and the saving spreads over all four SIMDs.
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void moe_tile_kernel(const bf16* __restrict__ X, int topk,
+                                                                const bf16* __restrict__ W, int wrows, int K,
+                                                                WStride ws, const int4* __restrict__ tiles,
+                                                                const int* __restrict__ ntiles,
+                                                                const int* __restrict__ sorted,
+                                                                const float* __restrict__ wts,
+                                                                bf16* __restrict__ out, int ldo) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int SM = TM / 16, SN = TN / 16;
+  constexpr int WJ = BN / 8 / NW;
+  constexpr int XJ = BM / 8 / NW;
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  bf16* sW = smem;
+  bf16* sX = smem + 2 * BN * kTBK;
+  auto swz = [](int row, int c) { return row * kTBK + ((c ^ (row & 7)) << 3); };
+
+  const int nn = wrows / BN;
+  const int C = nn * kEntriesPerChunk;
+  const int i8 = blockIdx.x >> 3;
+  const int L = ((i8 / C) * 8 + (blockIdx.x & 7)) * C + i8 % C;
+  const int entry = L / nn, n_t = L % nn;
+  if (entry >= *ntiles) return;
+  const int4 tl = tiles[entry];
+  const int r0 = tl.y, rows = tl.z;
+  const bf16* We = W + (size_t)tl.x * wrows * K;
+  const int n0 = n_t * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int prow = lane >> 3, pc = lane & 7;
+
+  const bf16* wsrc[WJ];
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    const int row = n0 + (j * NW + wave) * 8 + prow;
+    const int ch = pc ^ (row & 7);
+    wsrc[j] = We + (size_t)(row & ~15) * K + (size_t)(row & 15) * ws.rs + (size_t)(ch >> 2) * ws.ks + (ch & 3) * 8;
+  }
+  const size_t wstage = (size_t)(kTBK / 32) * ws.ks;
+  const bf16* xsrc[XJ];
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int row = (j * NW + wave) * 8 + prow;
+    const int i = min(row, rows - 1);  // rows past the entry repeat its last row, never stored
+    const int src = EPI == kMoeGateUp ? sorted[r0 + i] / topk : r0 + i;
+    xsrc[j] = X + (size_t)src * K + ((pc ^ (row & 7)) << 3);
+  }
+  auto issue = [&](int buf, int kt) {
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(wsrc[j] + kt * wstage),
+          (__attribute__((address_space(3))) void*)(sW + buf * BN * kTBK + (j * NW + wave) * 8 * kTBK), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < XJ; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(xsrc[j] + kt * kTBK),
+          (__attribute__((address_space(3))) void*)(sX + buf * BM * kTBK + (j * NW + wave) * 8 * kTBK), 16, 0, 0);
+  };
+
+  // 16-row sub-tiles of this wave that hold pair rows (wave-uniform)
+  const int act_sub = min(SM, max(0, (rows - wm * TM + 15) / 16));
+
+  f32x4 acc[SN][SM];
+#pragma unroll
+  for (int i = 0; i < SN; ++i)
+#pragma unroll
+    for (int j = 0; j < SM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one k stage of this wave's MFMAs over its first `nsub` 16-row sub-tiles
+  auto stage = [&](int buf, auto full) {
+#pragma unroll
+    for (int s = 0; s < kTBK / 32; ++s) {
+      const int c = s * 4 + g;
+      bf16x8 b[SM];
+#pragma unroll
+      for (int j = 0; j < SM; ++j)
+        if (decltype(full)::value || j < act_sub)
+          b[j] = *reinterpret_cast<const bf16x8*>(&sX[buf * BM * kTBK + swz(wm * TM + j * 16 + r16, c)]);
+#pragma unroll
+      for (int i = 0; i < SN; ++i) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sW[buf * BN * kTBK + swz(wn * TN + i * 16 + r16, c)]);
+#pragma unroll
+        for (int j = 0; j < SM; ++j)
+          if (decltype(full)::value || j < act_sub) acc[i][j] = mfma16(a, b[j], acc[i][j]);
+      }
+    }
+  };
+  const int nk = K / kTBK;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (act_sub == SM) {
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) issue((kt & 1) ^ 1, kt + 1);
+      stage(kt & 1, std::true_type());
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) issue((kt & 1) ^ 1, kt + 1);
+      if (act_sub > 0) stage(kt & 1, std::false_type());
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < SM; ++j) {
+    const int m = wm * TM + j * 16 + r16;
+    if (m >= rows) continue;
+    if (EPI == kMoeGateUp) {
+      bf16* dst = out + (size_t)(r0 + m) * ldo;
+#pragma unroll
+      for (int i = 0; i < SN; i += 2) {
+        const int f = ((n0 + wn * TN + i * 16) >> 5) * 16 + 4 * g;
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(silu_f(acc[i][j][r]) * acc[i + 1][j][r]);
+        *reinterpret_cast<bf16x4*>(dst + f) = o;
+      }
+    } else {
+      const int p = sorted[r0 + m];
+      const float wgt = wts[p];
+      bf16* dst = out + (size_t)p * ldo;
+#pragma unroll
+      for (int i = 0; i < SN; ++i) {
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[i][j][r] * wgt);
+        *reinterpret_cast<bf16x4*>(dst + n0 + wn * TN + i * 16 + 4 * g) = o;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- combine ----
+
+// out[t][n .. n+7] = bf16(sum over slots of part[t*k + slot][n .. n+7])
+__global__ __launch_bounds__(256) void moe_sum_kernel(const bf16* __restrict__ part, int T, int k, int H,
+                                                      bf16* __restrict__ out) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= (size_t)T * H) return;
+  const size_t t = i / H;
+  const int n = (int)(i % H);
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const bf16x8 v = ld16<bf16x8>(part + (t * k + j) * H + n);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) a[r] += static_cast<float>(v[r]);
+  }
+  bf16x8 o;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) o[r] = static_cast<bf16>(a[r]);
+  *reinterpret_cast<bf16x8*>(out + i) = o;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+hipError_t launch_moe_tile(const bf16* x, int topk, const bf16* w, int wrows, int K, WStride ws, const MoeRouting& r,
+                           bf16* out, int ldo, hipStream_t s) {
+  auto fn = moe_tile_kernel<BM, BN, WM, WN, EPI>;
+  const size_t lds = (size_t)2 * (BM + BN) * kTBK * sizeof(bf16);
+  static bool attr_set = false;
+  if (lds > 65536 && !attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int nn = wrows / BN;
+  const size_t C8 = (size_t)8 * nn * kEntriesPerChunk;
+  const size_t work = (size_t)r.tile_cap * nn;
+  const size_t grid = (work + C8 - 1) / C8 * C8;
+  fn<<<(unsigned)grid, 64 * WM * WN, lds, s>>>(x, topk, w, wrows, K, ws, r.tiles, r.ntiles, r.sorted, r.wts, out,
+                                               ldo);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_moe_stream(const bf16* x, int topk, const bf16* w, int wrows, int K, WStride ws,
+                             const MoeRouting& r, int E, int mt, bf16* out, int ldo, hipStream_t s) {
+  constexpr int NT = 2, NW = 4;
+  const int rows_per_wg = 16 * NT * NW;
+  if (wrows % rows_per_wg) return hipErrorInvalidValue;
+  const dim3 grid(E, wrows / rows_per_wg);
+  const bool kc256 = K % 256 == 0;
+  if (mt == 1) {
+    if (kc256)
+      moe_stream_kernel<1, NT, 256, NW, EPI><<<grid, NW * 64, 0, s>>>(x, topk, w, wrows, K, ws, r.seg, r.sorted,
+                                                                     r.active, r.nactive, r.wts, out, ldo);
+    else
+      moe_stream_kernel<1, NT, 128, NW, EPI><<<grid, NW * 64, 0, s>>>(x, topk, w, wrows, K, ws, r.seg, r.sorted,
+                                                                     r.active, r.nactive, r.wts, out, ldo);
+  } else {
+    if (kc256)
+      moe_stream_kernel<2, NT, 256, NW, EPI><<<grid, NW * 64, 0, s>>>(x, topk, w, wrows, K, ws, r.seg, r.sorted,
+                                                                     r.active, r.nactive, r.wts, out, ldo);
+    else
+      moe_stream_kernel<2, NT, 128, NW, EPI><<<grid, NW * 64, 0, s>>>(x, topk, w, wrows, K, ws, r.seg, r.sorted,
+                                                                     r.active, r.nactive, r.wts, out, ldo);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool moe_streaming(int T) { return T <= kSkinnyMaxM; }
+
+hipError_t launch_moe_route(const void* x, int T, int H, const void* router, int E, int topk, bool norm,
+                            float* logits, int* ids, float* wts, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (E <= 0 || E > kMaxExperts || E % 16 || H % 64 || topk < 1 || topk > 64 || topk > E)
+    return hipErrorInvalidValue;
+  moe_router_kernel<<<dim3((T + 15) / 16, (E + 63) / 64), 256, 0, s>>>((const bf16*)x, T, H, (const bf16*)router,
+                                                                        E, logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  const int epl = (E + 63) / 64;
+  switch (epl) {
+    case 1: moe_topk_kernel<1><<<blocks, 256, 0, s>>>(logits, T, E, topk, norm ? 1 : 0, ids, wts); break;
+    case 2: moe_topk_kernel<2><<<blocks, 256, 0, s>>>(logits, T, E, topk, norm ? 1 : 0, ids, wts); break;
+    case 3: moe_topk_kernel<3><<<blocks, 256, 0, s>>>(logits, T, E, topk, norm ? 1 : 0, ids, wts); break;
+    default: moe_topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, topk, norm ? 1 : 0, ids, wts); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_align(const int* ids, int P, int E, int bm, const MoeRouting& r, hipStream_t s) {
+  if (P <= 0) return hipSuccess;
+  if (E <= 0 || E > kMaxExperts || bm <= 0) return hipErrorInvalidValue;
+  moe_align_kernel<<<1, 1024, 0, s>>>(ids, P, E, bm, r.seg, r.sorted, r.active, r.nactive, r.tiles, r.tile_cap,
+                                      r.ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_experts(const void* x, int T, int H, int topk, const void* w13, const void* w2, int E, int I,
+                              int layout, const MoeRouting& r, void* act, void* part, hipStream_t s,
+                              hipEvent_t mid) {
+  if (T <= 0) return hipSuccess;
+  if (layout != kTiled16x32 || H % 256 || I % 128) return hipErrorInvalidValue;
+  const bf16* xb = (const bf16*)x;
+  bf16* ab = (bf16*)act;
+  bf16* pb = (bf16*)part;
+  const WStride ws13 = weight_stride(layout, H), ws2 = weight_stride(layout, I);
+  hipError_t e;
+  if (moe_streaming(T)) {
+    // one 16-row pass covers an expert's pairs when they average <= 12
+    const int mt = T * topk <= 12 * E ? 1 : 2;
+    e = launch_moe_stream<kMoeGateUp>(xb, topk, (const bf16*)w13, 2 * I, H, ws13, r, E, mt, ab, I, s);
+    if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
+    if (e != hipSuccess) return e;
+    return launch_moe_stream<kMoeDown>(ab, topk, (const bf16*)w2, H, I, ws2, r, E, mt, pb, H, s);
+  }
+  e = launch_moe_tile<256, 256, 2, 4, kMoeGateUp>(xb, topk, (const bf16*)w13, 2 * I, H, ws13, r, ab, I, s);
+  if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
+  if (e != hipSuccess) return e;
+  return launch_moe_tile<256, 256, 2, 4, kMoeDown>(ab, topk, (const bf16*)w2, H, I, ws2, r, pb, H, s);
+}
+
+hipError_t launch_moe_sum(const void* part, int T, int topk, int H, void* out, hipStream_t s) {
+  const size_t total = (size_t)T * H;
+  if (total == 0) return hipSuccess;
+  if (H % 8) return hipErrorInvalidValue;
+  moe_sum_kernel<<<(unsigned)((total / 8 + 255) / 256), 256, 0, s>>>((const bf16*)part, T, topk, H, (bf16*)out);
+  return hipGetLastError();
+}
+
+}  // namespace llk

@@ -15,6 +15,11 @@
 // p % 16: K plane [blocks][kv_heads][16][head_dim], V plane
 // [blocks][kv_heads][head_dim][16].  V is a bit copy of the projection's v.
 //
+// Qwen3 attention (qk_norm): before the rotation each q and k head is
+// divided by the root of its mean square plus eps and multiplied by the
+// q_norm / k_norm weight [head_dim], in fp32, and rounded once to the layer
+// dtype, as a stored RMSNorm output.
+//
 // HBM-bound and tiny: one workgroup per (token, 8 heads).  q is rotated in
 // place inside the qkv buffer.
 #include "common.h"
@@ -35,7 +40,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(T* __restrict__ qkv, const
                                                       const float2* __restrict__ table, int nq, int nkv,
                                                       int d, const int* __restrict__ block_table,
                                                       int max_blocks, SeqMap map, T* __restrict__ kc,
-                                                      T* __restrict__ vc, const float* __restrict__ part, int T_) {
+                                                      T* __restrict__ vc, const float* __restrict__ part, int T_,
+                                                      const T* __restrict__ qn, const T* __restrict__ kn,
+                                                      float eps) {
   __shared__ float srow[kHeads * 128];
   const int t = blockIdx.x;
   const int h0 = blockIdx.y * kHeads;
@@ -78,8 +85,18 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(T* __restrict__ qkv, const
     const int i = idx % half;
     if (head < nq + nkv) {  // q and k heads turn
       const float2 c = cs[i];
-      const float x0 = val(head * d + i);
-      const float x1 = val(head * d + i + half);
+      float x0 = val(head * d + i);
+      float x1 = val(head * d + i + half);
+      if (qn) {
+        // the `half` lanes of one head are consecutive and aligned (a whole
+        // wave for d = 128, half a wave for d = 64) and all take this branch
+        float ss = x0 * x0 + x1 * x1;
+        ss = half == 64 ? group_sum<64>(ss) : group_sum<32>(ss);
+        const float inv = rsqrtf(ss / (float)d + eps);
+        const T* wn = head < nq ? qn : kn;
+        x0 = to_f32(from_f32<T>(x0 * inv * to_f32(wn[i])));
+        x1 = to_f32(from_f32<T>(x1 * inv * to_f32(wn[i + half])));
+      }
       const float y0 = fmaf(x0, c.x, -(x1 * c.y));
       const float y1 = fmaf(x1, c.x, x0 * c.y);
       if (head < nq) {
@@ -105,32 +122,34 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(T* __restrict__ qkv, const
 template <typename T, int S>
 void launch_typed(T* qkv, int T_, const int* positions, const float2* table, int nq, int nkv, int d,
                   const int* block_table, int max_blocks, const SeqMap& map, T* kc, T* vc, const float* part,
-                  hipStream_t s) {
+                  const QkNorm& qkn, hipStream_t s) {
   dim3 grid(T_, (nq + 2 * nkv + kHeads - 1) / kHeads);
   rope_kv_kernel<T, S><<<grid, 256, 0, s>>>(qkv, positions, table, nq, nkv, d, block_table, max_blocks, map,
-                                            kc, vc, part, T_);
+                                            kc, vc, part, T_, (const T*)qkn.q, (const T*)qkn.k, qkn.eps);
 }
 
 }  // namespace
 
 hipError_t launch_rope_kv(int dtype, void* qkv, int T, const int* positions, const float2* table,
                           int nq, int nkv, int d, const int* block_table, int max_blocks, const SeqMap& map,
-                          void* k_cache, void* v_cache, hipStream_t s, const float* part, int S) {
+                          void* k_cache, void* v_cache, hipStream_t s, const float* part, int S,
+                          const QkNorm& qkn) {
   if (T <= 0) return hipSuccess;
+  if (qkn.q && (d != 64 && d != 128)) return hipErrorInvalidValue;
   if (dtype == kBF16) {
     bf16* x = (bf16*)qkv;
     bf16* kc = (bf16*)k_cache;
     bf16* vc = (bf16*)v_cache;
-    if (!part) launch_typed<bf16, 0>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, nullptr, s);
-    else if (S == 1) launch_typed<bf16, 1>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, s);
-    else if (S == 2) launch_typed<bf16, 2>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, s);
-    else if (S == 4) launch_typed<bf16, 4>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, s);
-    else if (S == 8) launch_typed<bf16, 8>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, s);
+    if (!part) launch_typed<bf16, 0>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, nullptr, qkn, s);
+    else if (S == 1) launch_typed<bf16, 1>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, qkn, s);
+    else if (S == 2) launch_typed<bf16, 2>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, qkn, s);
+    else if (S == 4) launch_typed<bf16, 4>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, qkn, s);
+    else if (S == 8) launch_typed<bf16, 8>(x, T, positions, table, nq, nkv, d, block_table, max_blocks, map, kc, vc, part, qkn, s);
     else return hipErrorInvalidValue;
   } else {
     if (part) return hipErrorInvalidValue;
     launch_typed<float, 0>((float*)qkv, T, positions, table, nq, nkv, d, block_table, max_blocks, map,
-                           (float*)k_cache, (float*)v_cache, nullptr, s);
+                           (float*)k_cache, (float*)v_cache, nullptr, qkn, s);
   }
   return hipGetLastError();
 }

@@ -122,3 +122,55 @@ def device_qsl(batch: synth.Batch, device):
     """query_start_loc on the device, or None for a uniform batch."""
     q = batch.query_start_loc
     return None if q is None else q.to(device)
+
+
+def moe_fix_routing(cfg: dict, w_np: dict, trace: dict, result: dict, gpu_ids: np.ndarray, rnd=None,
+                    delta: float = 2e-2) -> int:
+    """Where several expert sets are correct, compare what is unique and check
+    that the rest is valid.  For every output row whose GPU expert set differs
+    from the oracle's: the oracle's own choice must be within ``delta`` * RMS
+    (router logits) of a tie, every GPU expert must be within that distance of
+    the k-th best logit, and the row's expected output is then the oracle's
+    mixture over the GPU's experts (weights from the oracle's logits).
+    ``gpu_ids`` [rows, k] in the result's row order.  Updates
+    result["hidden_out"] in place; returns the number of such rows."""
+    rnd = rnd or (lambda x: x)
+    logits = trace["router_logits"]
+    ids = trace["topk_ids"]
+    k = cfg["num_experts_per_tok"]
+    tol = delta * math.sqrt(float(np.mean(logits * logits)))
+    margins = oracle.topk_margin(logits, k)
+    fixed = 0
+    for i in range(ids.shape[0]):
+        g = [int(e) for e in gpu_ids[i]]
+        assert len(set(g)) == k, ("repeated expert", i, g)
+        if set(g) == set(int(e) for e in ids[i]):
+            continue
+        assert margins[i] <= tol, ("expert sets differ on a clear choice", i, margins[i], tol)
+        kth = np.sort(logits[i])[::-1][k - 1]
+        assert all(logits[i, e] >= kth - tol for e in g), ("GPU expert far from the top k", i, g)
+        p = oracle.softmax(logits[i:i + 1])[0][g]
+        if cfg.get("norm_topk_prob", True):
+            p = p / p.sum()
+        result["hidden_out"][i] = oracle.mix_experts(trace["h2"][i:i + 1], np.array([g]), p[None, :],
+                                                     w_np["experts_gate_up"], w_np["experts_down"], rnd)[0]
+        fixed += 1
+    return fixed
+
+
+def moe_check_weights(cfg: dict, trace: dict, gpu_ids: np.ndarray, gpu_w: np.ndarray, gpu_logits: np.ndarray,
+                      atol: float = 2e-3) -> None:
+    """GPU router logits against the oracle's (1e-2 * RMS) and the GPU's
+    routing weights against the oracle's probabilities of the GPU's experts."""
+    logits = trace["router_logits"]
+    rms = math.sqrt(float(np.mean(logits * logits)))
+    err = float(np.abs(gpu_logits - logits).max())
+    assert err <= 1e-2 * rms, ("router logits", err, rms)
+    p = oracle.softmax(logits)
+    sel = np.take_along_axis(p, gpu_ids.astype(np.int64), axis=1)
+    if cfg.get("norm_topk_prob", True):
+        sel = sel / sel.sum(axis=1, keepdims=True)
+    assert float(np.abs(gpu_w - sel).max()) <= atol, ("routing weights", float(np.abs(gpu_w - sel).max()))
+    # best first
+    g = np.take_along_axis(gpu_logits, gpu_ids.astype(np.int64), axis=1)
+    assert np.all(np.diff(g, axis=1) <= 0), "experts not listed best first"

@@ -110,3 +110,51 @@ def test_host_argument_errors_need_no_gpu():
     assert L.llama_stack_graph_create(None, fake, fake, 1, None, fake, 1, fake, None, 1, 1, fake, fake, fake,
                                       ctypes.byref(g)) == lda.Status.INVALID_ARGUMENT
     assert L.llama_graph_launch(None, None) == lda.Status.INVALID_ARGUMENT
+
+
+def _moe_cfg(**over):
+    cfg = synth.QWEN3MOE.config_dict()
+    cfg.update(over)
+    return cfg
+
+
+def test_validate_qwen3_moe_config_ok():
+    assert lda.validate(_moe_cfg()) == lda.Status.OK
+    c = lda.make_config(_moe_cfg(), lda.Dtype.BF16)
+    assert (c.num_experts, c.num_experts_per_tok, c.moe_intermediate_size, c.norm_topk_prob, c.qk_norm) == \
+        (128, 8, 768, 1, 1)
+
+
+@pytest.mark.parametrize("over,dtype,expect", [
+    ({}, lda.Dtype.FP32, lda.Status.UNSUPPORTED),                       # MoE is bf16 only
+    ({"num_experts": 100}, lda.Dtype.BF16, lda.Status.UNSUPPORTED),     # not a multiple of 16
+    ({"num_experts": 512}, lda.Dtype.BF16, lda.Status.UNSUPPORTED),
+    ({"num_experts_per_tok": 0}, lda.Dtype.BF16, lda.Status.INVALID_ARGUMENT),
+    ({"num_experts": 16, "num_experts_per_tok": 17}, lda.Dtype.BF16, lda.Status.INVALID_ARGUMENT),
+    ({"moe_intermediate_size": 200}, lda.Dtype.BF16, lda.Status.UNSUPPORTED),
+    ({"hidden_size": 1152}, lda.Dtype.BF16, lda.Status.UNSUPPORTED),    # % 128 but not % 256
+    ({"num_experts": -1}, lda.Dtype.BF16, lda.Status.INVALID_ARGUMENT),
+])
+def test_validate_rejects_moe(over, dtype, expect):
+    assert lda.validate(_moe_cfg(**over), dtype) == expect
+    assert lda.lib().llama_layer_last_error()
+
+
+def test_create_needs_expert_and_norm_weights():
+    L = lda.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    cfg = lda.make_config(_moe_cfg(), lda.Dtype.BF16)
+    w = lda.Weights()
+    for n in ("input_layernorm", "qkv_proj", "o_proj", "post_attention_layernorm", "q_norm", "k_norm"):
+        setattr(w, n, fake.value)
+    out = ctypes.c_void_p()
+    # no router / expert weights
+    assert L.llama_layer_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(out)) == \
+        lda.Status.INVALID_ARGUMENT
+    assert b"expert" in L.llama_layer_last_error()
+    for n in ("router", "experts_gate_up", "experts_down"):
+        setattr(w, n, fake.value)
+    w.q_norm = None
+    assert L.llama_layer_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(out)) == \
+        lda.Status.INVALID_ARGUMENT
+    assert b"qk_norm" in L.llama_layer_last_error()

@@ -1,0 +1,121 @@
+"""GPU parity of the Qwen3-MoE layer (llama_layer_forward with num_experts > 0
+and qk_norm) against the oracle: decode batches on the weight-streaming expert
+kernel (one and two 16-row passes per expert), prefill on the tiled expert
+kernel (full and partly filled tiles), a mixed batch, the routing (router
+logits, chosen experts, their weights), the KV cache, and bitwise-repeatable
+output despite the atomics that group pairs by expert."""
+import numpy as np
+import pytest
+import torch
+
+import llama_decoder_layer_amd as lda
+import oracle
+import synth
+from tests.parity import (compare, device_batch, device_qsl, moe_check_weights, moe_fix_routing, np64,
+                          oracle_seqs, oracle_weights)
+from tests.test_gpu_layer import _check_kv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+# the Qwen3-MoE layer's structure at a small width: 8 query heads per KV head,
+# head_dim 128, theta 1e7 without scaling, eps 1e-6, q/k norm, top-4 of 32
+# experts (the 30B model: top-8 of 128)
+MOE = synth.ModelShape(1024, 8, 1, 128, 2816, 1e-6, 1e7, None, 32768, "bf16",
+                       num_experts=32, num_experts_per_tok=4, moe_intermediate_size=256,
+                       norm_topk_prob=True, qk_norm=True)
+# top-8 of 64, wider experts, GQA 4:1
+MOE8 = synth.ModelShape(1024, 8, 2, 128, 2816, 1e-6, 1e7, None, 32768, "bf16",
+                        num_experts=64, num_experts_per_tok=8, moe_intermediate_size=384,
+                        norm_topk_prob=True, qk_norm=True)
+
+
+def _routing(layer, ws, T, B, max_seq_len):
+    ids = layer.workspace_tensor(ws, "topk_ids", T, B, max_seq_len).cpu().numpy()
+    wts = np64(layer.workspace_tensor(ws, "topk_weights", T, B, max_seq_len))
+    logits = np64(layer.workspace_tensor(ws, "router_logits", T, B, max_seq_len))
+    return ids, wts, logits
+
+
+def run_moe_layer(workload, ctx_lens=None, repeat=False, want=None):
+    """One MoE layer forward on the GPU and the oracle on the same tensors;
+    checks outputs, routing and the KV cache.  Returns the GPU outputs."""
+    model = workload.model
+    batch = synth.build_batch(workload, ctx_lens)
+    T, B = batch.num_tokens, batch.num_seqs
+    print("case", workload.name, "T", T, "B", B, "ctx", batch.ctx_lens[:6], flush=True)
+    hidden, residual = synth.draw_activations(model, T, workload.index, DEV, residual=not workload.residual_none)
+    pos, bt, sl = device_batch(batch, DEV)
+    qsl = device_qsl(batch, DEV)
+    w = synth.draw_weights(model, workload.index, 0, DEV)
+    kp, vp = synth.build_kv_pool(workload, batch, 0, DEV)
+    kp0, vp0 = kp.clone(), vp.clone()
+    layer = lda.Layer(model.config_dict(), w)
+    ws = layer.alloc_workspace(T, B, batch.max_seq_len)
+    ho, ro = layer.forward(hidden, residual, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws,
+                           query_start_loc=qsl)
+    torch.cuda.synchronize()
+    ids, wts, logits = _routing(layer, ws, T, B, batch.max_seq_len)
+    if repeat:
+        ho1, ro1 = ho.clone(), ro.clone()
+        kp.copy_(kp0)
+        vp.copy_(vp0)
+        layer.forward(hidden, residual, pos, kp, vp, bt, sl, batch.max_seq_len, hidden_out=ho, residual_out=ro,
+                      workspace=ws, query_start_loc=qsl)
+        torch.cuda.synchronize()
+        assert torch.equal(ho.view(torch.int16), ho1.view(torch.int16))
+        assert torch.equal(ro.view(torch.int16), ro1.view(torch.int16))
+    layer.close()
+
+    cfg = model.config_dict()
+    w_np = oracle_weights(w)
+    seqs = oracle_seqs(model, batch, kp0, vp0)
+    h = np64(hidden)
+    r = None if residual is None else np64(residual)
+    p = batch.positions.numpy().astype(np.int64)
+    tr_e, tr_r = {}, {}
+    exact = oracle.decoder_layer(cfg, w_np, h, r, p, seqs, want=want, trace=tr_e)
+    rounded = oracle.decoder_layer(cfg, w_np, h, r, p, seqs, rnd=oracle.bf16_round, want=want, trace=tr_r)
+    rows = exact["rows"]
+    moe_check_weights(cfg, tr_r, ids[rows], wts[rows], logits[rows])
+    n_fix = moe_fix_routing(cfg, w_np, tr_e, exact, ids[rows])
+    n_fix_r = moe_fix_routing(cfg, w_np, tr_r, rounded, ids[rows], rnd=oracle.bf16_round)
+    s1 = compare("hidden_out", np64(ho)[rows], exact["hidden_out"], rounded["hidden_out"])
+    s2 = compare("residual_out", np64(ro)[rows], exact["residual_out"], rounded["residual_out"])
+    print("rows with a near-tie expert choice", n_fix, n_fix_r, "hidden_out", s1, "residual_out", s2, flush=True)
+    if want is None:
+        _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded)
+    return ho, ro, ids
+
+
+def test_moe_decode_b24_streaming():
+    run_moe_layer(synth.Workload(200, "moe_decode_b24", MOE, 24, 1, (60, 700)))
+
+
+def test_moe_decode_b128_two_passes():
+    # 128 tokens x 4 = 512 pairs on 32 experts: 16 per expert on average, so
+    # the streaming kernel takes its two-pass (32-row) shape
+    run_moe_layer(synth.Workload(201, "moe_decode_b128", MOE, 128, 1, (20, 300)))
+
+
+def test_moe8_decode_b32():
+    run_moe_layer(synth.Workload(202, "moe8_decode_b32", MOE8, 32, 1, (100, 900)))
+
+
+def test_moe_prefill_2x1024_tiles():
+    # 8192 pairs on 32 experts: 256 per expert on average, so full and partly
+    # filled 256-row tiles both occur
+    run_moe_layer(synth.Workload(203, "moe_prefill_2x1024", MOE, 2, 1024, 0), repeat=True)
+
+
+def test_moe8_prefill_with_context():
+    run_moe_layer(synth.Workload(204, "moe8_prefill_3x200_ctx", MOE8, 3, 200, (30, 400)))
+
+
+def test_moe_mixed_chunk_and_decode():
+    mix = tuple([(1, 300)] * 12 + [(150, 200)] + [(1, 40)] * 4)
+    run_moe_layer(synth.Workload(205, "moe_mixed", MOE, len(mix), 0, mix=mix), repeat=True)
+
+
+def test_moe_decode_repeat_bitwise():
+    run_moe_layer(synth.Workload(206, "moe_decode_b64_repeat", MOE8, 64, 1, (10, 200)), repeat=True)
