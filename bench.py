@@ -7,7 +7,9 @@ KV write, paged attention, o_proj + residual, post_attention_layernorm,
 gate_up_proj + SiluAndMul, down_proj) over one batch of seeded synthetic
 inputs that are resident in HBM before timing starts.  Default workload: 32
 sequences decoding one token each after a 2048-token cached context (70B
-layer shapes, bf16).  Prints one JSON line.
+layer shapes, bf16).  The extra lines measure the 70B prefill, the
+Qwen3-MoE layer (the MLP replaced by the routed experts) and one GPU's TP = 8
+share of the 70B layer (no all-reduce: one GPU).  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -53,16 +55,24 @@ def counter_traffic(workload, kernel):
 
 def layer_flops(model, num_tokens, attn_pairs):
     H, I, Q = model.hidden_size, model.intermediate_size, model.q_size
-    proj = 2 * num_tokens * H * (model.qkv_size + Q + 2 * I) + 2 * num_tokens * I * H
-    return proj + 4 * model.num_attention_heads * model.head_dim * attn_pairs
+    attn = 2 * num_tokens * H * (model.qkv_size + Q) + 4 * model.num_attention_heads * model.head_dim * attn_pairs
+    if model.num_experts:  # router + each token's k experts (gate_up and down)
+        P, Ie = num_tokens * model.num_experts_per_tok, model.moe_intermediate_size
+        return attn + 2 * num_tokens * H * model.num_experts + 2 * P * H * 2 * Ie + 2 * P * Ie * H
+    return attn + 2 * num_tokens * H * 2 * I + 2 * num_tokens * I * H
 
 
-def kernel_bytes(model, name, T, kv_tokens):
+def kernel_bytes(model, name, T, kv_tokens, active_experts=0):
     """Algorithmic HBM bytes of one launch of kernel `name` (bf16): weights
-    read once, activations in and out once, KV read once."""
+    read once, activations in and out once, KV read once; an expert kernel
+    reads the weights of the experts that have tokens (`active_experts`)."""
     H, I, Q, QKV = model.hidden_size, model.intermediate_size, model.q_size, model.qkv_size
     e = 2
+    P, Ie = T * model.num_experts_per_tok, model.moe_intermediate_size
     return {
+        "gate_up": 2 * I * H * e + T * H * e,  # split-K partials, SiluAndMul in the reduce
+        "moe_gate_up_silu": active_experts * 2 * Ie * H * e + T * H * e + P * Ie * e,
+        "moe_down": active_experts * H * Ie * e + P * Ie * e + P * H * e,
         "gate_up_silu": 2 * I * H * e + T * H * e + T * I * e,
         "down_proj": H * I * e + T * I * e + T * H * e,
         "qkv_proj": QKV * H * e + T * H * e + T * QKV * e,
@@ -124,15 +134,20 @@ def measure(wl, steps, warmup):
             kt[name] = (a + tot, c + cnt)
         L.set_timing(False)
     kernel_avg_ms = {k: v[0] / v[1] for k, v in kt.items()}
+    active = 0
+    if model.num_experts:  # experts the batch routed tokens to (the same every step)
+        ids = layers[0].workspace_tensor(ws, "topk_ids", T, B, batch.max_seq_len)
+        active = int(torch.unique(ids).numel())
 
     kv_tokens = int(batch.seq_lens.sum())
     # causal (query, key) pairs: a sequence with c cached and n new rows
     attn_pairs = sum(n * c + n * (n + 1) // 2 for c, n in
                      ((batch.ctx_lens[b], batch.new_rows(b)) for b in range(B)))
-    dom = "gate_up_silu"
+    dom = "moe_gate_up_silu" if model.num_experts else ("gate_up_silu" if "gate_up_silu" in kernel_avg_ms
+                                                          else "gate_up")
     dur = kernel_avg_ms[dom] / 1e3
     if T == B:  # decode: one row per sequence, the step streams weights and KV
-        alg = kernel_bytes(model, dom, T, kv_tokens)
+        alg = kernel_bytes(model, dom, T, kv_tokens, active)
         roof = {"bound": "hbm", "kernel": dom, "achieved": alg / dur / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": alg / dur / 1e9 / PEAK_HBM_GBS,
                 "traffic": counter_traffic(wl.name, dom),
@@ -140,11 +155,16 @@ def measure(wl, steps, warmup):
     else:
         H, I = model.hidden_size, model.intermediate_size
         alg = 2 * T * H * 2 * I
+        if model.num_experts:
+            alg = 2 * T * model.num_experts_per_tok * H * 2 * model.moe_intermediate_size
         roof = {"bound": "mfma", "kernel": dom, "achieved": alg / dur / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": alg / dur / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
                 "algorithmic_flops_per_launch": alg, "avg_launch_us": dur * 1e6}
-    step_bytes = len(layers) * (sum(v.numel() * v.element_size() for v in per_layer[0]["weights"].values())
-                                + kv_tokens * 2 * model.kv_size * 2 + 4 * T * model.hidden_size * 2)
+    wbytes = sum(v.numel() * v.element_size() for k, v in per_layer[0]["weights"].items()
+                 if not k.startswith("experts_"))
+    if model.num_experts:  # only the routed-to experts' weights are read
+        wbytes += active * 3 * model.moe_intermediate_size * model.hidden_size * 2
+    step_bytes = len(layers) * (wbytes + kv_tokens * 2 * model.kv_size * 2 + 4 * T * model.hidden_size * 2)
     step_flops = len(layers) * layer_flops(model, T, attn_pairs)
     res = {
         "workload": wl.name, "value": round(T / (ms / 1e3), 2), "unit": "tokens/s", "ms_per_step": round(ms, 4),
@@ -153,6 +173,7 @@ def measure(wl, steps, warmup):
                           "mfma": step_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS},
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in sorted(kernel_avg_ms.items())},
         "wall_s_timed_region": round(wall, 3),
+        **({"experts_with_tokens": active} if model.num_experts else {}),
         "config": ({"workload": wl.name, "num_seqs": B, "q_len": wl.q_len,
                     "ctx_len": wl.ctx if not isinstance(wl.ctx, tuple) else list(wl.ctx),
                     "layers": len(layers), "parallelism": "single GPU"} if not wl.mixed else
@@ -241,7 +262,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama70b_decode_b32_ctx2048")
-    ap.add_argument("--extra", default="llama70b_prefill_4x2048",
+    ap.add_argument("--extra", default="llama70b_prefill_4x2048,qwen3moe_decode_b32_ctx2048,qwen3moe_prefill_4x2048,"
+                                       "llama70b_tp8shard_decode_b32_ctx2048,llama70b_tp8shard_prefill_4x2048",
                     help="comma-separated workloads measured after the main one ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=None,

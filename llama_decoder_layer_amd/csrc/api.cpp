@@ -103,7 +103,7 @@ struct Workspace {
   size_t h, qkv, attn, h2, act, part, gpart, tpart, tpart_bytes, seq_of, ntiles, tiles, total;
   int tile_cap;  // entries of the prefill tile table (mixed batches)
   // MoE routing and expert buffers (P = T * topk pairs)
-  size_t logits, ids, wts, seg, sorted, active, nactive, mtiles, mntiles, mact, mpart;
+  size_t rpart, logits, ids, wts, seg, sorted, active, nactive, mtiles, mntiles, mact, mpart;
   int moe_tile_cap;
   llk::AttnPlan plan;
   bool skinny;  // few tokens: weight-streaming projections with split-K partials
@@ -136,7 +136,14 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
     size_t n = (size_t)w.pq.splits * L->qkv_n;
     if ((size_t)w.po.splits * H > n) n = (size_t)w.po.splits * H;
     if (!L->E) {
+      // gate_up: unsplit (SiluAndMul in the epilogue) when its row tiles
+      // alone fill the CUs; a short weight (e.g. one GPU's tensor-parallel
+      // share) splits K into fp32 partials that a SiluAndMul reduce finishes
       w.pg = llk::skinny_plan(T, 2 * I, H, false, L->num_cus);
+      if (2 * I / (16 * w.pg.nt * w.pg.nw) < L->num_cus) {
+        w.pg = llk::skinny_plan(T, 2 * I, H, true, L->num_cus);
+        if ((size_t)w.pg.splits * 2 * I > n) n = (size_t)w.pg.splits * 2 * I;
+      }
       w.pd = llk::skinny_plan(T, H, I, true, L->num_cus);
       if ((size_t)w.pd.splits * H > n) n = (size_t)w.pd.splits * H;
     }
@@ -162,6 +169,7 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.tiles = take((size_t)w.tile_cap * sizeof(int4));
   const size_t P = L->E ? (size_t)T * L->topk : 0;
   w.moe_tile_cap = L->E ? (int)(P / llk::kMoeTileRows) + L->E + 1 : 0;
+  w.rpart = take(L->E ? (size_t)llk::moe_router_splits(T, H) * T * L->E * sizeof(float) : 0);
   w.logits = take((size_t)T * L->E * sizeof(float));
   w.ids = take(P * sizeof(int));
   w.wts = take(P * sizeof(float));
@@ -253,7 +261,7 @@ llama_status moe_block(llama_layer* L, const Workspace& w, char* ws, const void*
   r.wts = (float*)(ws + w.wts);
   int* ids = (int*)(ws + w.ids);
   hipError_t e = llk::launch_moe_route(h2, T, H, L->w_router, L->E, L->topk, L->cfg.norm_topk_prob != 0,
-                                       (float*)(ws + w.logits), ids, r.wts, s);
+                                       (float*)(ws + w.rpart), (float*)(ws + w.logits), ids, r.wts, s);
   if (e != hipSuccess) return hip_fail(e, "moe router");
   mk.mark("moe_router_topk");
   e = llk::launch_moe_align(ids, P, L->E, llk::kMoeTileRows, r, s);
@@ -581,9 +589,18 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
     if (e != hipSuccess) return hip_fail(e, "post_attention_layernorm");
     mk.mark("post_attention_layernorm");
     if (L->E) return moe_block(L, w, ws, h2, T, hidden_out, s, mk);
-    e = llk::launch_skinny(h2, L->w_gu, T, I, H, llk::kEpiSiluMul, w.pg, act, s, L->wlayout);
-    if (e != hipSuccess) return hip_fail(e, "gate_up_proj");
-    mk.mark("gate_up_silu");
+    if (w.pg.splits > 1) {
+      e = llk::launch_skinny(h2, L->w_gu, T, 2 * I, H, llk::kEpiPartial, w.pg, gp, s, L->wlayout);
+      if (e != hipSuccess) return hip_fail(e, "gate_up_proj");
+      mk.mark("gate_up");
+      e = llk::launch_silu_reduce(gp, w.pg.splits, T, 2 * I, act, s);
+      if (e != hipSuccess) return hip_fail(e, "gate_up SiluAndMul reduce");
+      mk.mark("gate_up_silu_reduce");
+    } else {
+      e = llk::launch_skinny(h2, L->w_gu, T, I, H, llk::kEpiSiluMul, w.pg, act, s, L->wlayout);
+      if (e != hipSuccess) return hip_fail(e, "gate_up_proj");
+      mk.mark("gate_up_silu");
+    }
     e = llk::launch_skinny(act, L->w_down, T, H, I, llk::kEpiPartial, w.pd, gp, s, L->wlayout);
     if (e != hipSuccess) return hip_fail(e, "down_proj");
     mk.mark("down_proj");

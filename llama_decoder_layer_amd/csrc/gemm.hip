@@ -427,6 +427,15 @@ hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, 
   }
 }
 
+hipError_t launch_silu_reduce(const float* part, int S, int M, int wrows, void* out, hipStream_t s) {
+  const size_t quads = (size_t)M * (wrows / 2) / 4;
+  if (quads == 0) return hipSuccess;
+  if (wrows % 32) return hipErrorInvalidValue;
+  tile_reduce_kernel<kEpiSiluMul><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(part, S, M, wrows, wrows / 2,
+                                                                                 (bf16*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_reorder_gate_up(const void* src, int inter, int K, void* dst, hipStream_t s) {
   reorder_gate_up_kernel<<<2 * inter, 256, 0, s>>>((const bf16*)src, inter, K, (bf16*)dst);
   return hipGetLastError();

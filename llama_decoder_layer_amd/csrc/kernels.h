@@ -49,6 +49,9 @@ struct TilePlan {
 };
 TilePlan tile_plan(int M, int wrows, int K, int num_cus);
 hipError_t launch_reorder_gate_up(const void* src, int inter, int K, void* dst, hipStream_t s);
+// out [M, wrows/2] bf16 = SiluAndMul of the sum of S fp32 partial planes
+// [S][M][wrows] of a re-ordered gate_up projection (split-K).
+hipError_t launch_silu_reduce(const float* part, int S, int M, int wrows, void* out, hipStream_t s);
 // Row-major bf16 [rows][K] -> kTiled16x32.  With inter > 0 the source is the
 // merged gate_up weight [2*inter][K] and the rows are re-ordered on the way
 // as launch_reorder_gate_up does (each 32-row group: 16 gate, 16 up rows).
@@ -134,7 +137,8 @@ hipError_t launch_prefill_attention_bf16(const void* q, int ldq, int T, const in
 
 // moe.hip: the sparse MoE block (bf16).  Pair p = t * topk + slot.
 // launch_moe_route: logits [T, E] fp32, ids and wts [T * topk] (E % 16 == 0,
-// E <= 256, H % 64 == 0, topk <= min(E, 64)).  launch_moe_align groups the
+// E <= 256, H % 64 == 0, topk <= min(E, 64)); part holds the router's
+// moe_router_splits(T, H) partial logit planes [S][T][E].  launch_moe_align groups the
 // pairs by expert (one workgroup) into the routing tables below, with tiles of
 // at most bm pair rows.  launch_moe_experts: act [P, I] (sorted rows) and part
 // [P, H] (pair rows, weighted) from the expert weights w13 [E][2I][H] (each
@@ -153,8 +157,9 @@ struct MoeRouting {
   float* wts = nullptr;     // [P] routing weight of each pair
 };
 bool moe_streaming(int T);
+int moe_router_splits(int T, int H);
 hipError_t launch_moe_route(const void* x, int T, int H, const void* router, int E, int topk, bool norm,
-                            float* logits, int* ids, float* wts, hipStream_t s);
+                            float* part, float* logits, int* ids, float* wts, hipStream_t s);
 hipError_t launch_moe_align(const int* ids, int P, int E, int bm, const MoeRouting& r, hipStream_t s);
 hipError_t launch_moe_experts(const void* x, int T, int H, int topk, const void* w13, const void* w2, int E, int I,
                               int layout, const MoeRouting& r, void* act, void* part, hipStream_t s,

@@ -12,7 +12,7 @@
 //
 // Kernels, in launch order:
 //   moe_router_kernel  logits [T, E] fp32 = x Wr^T on MFMA (one wave per 16
-//                      tokens x 16 experts, whole K);
+//                      tokens x all experts and one of S K ranges);
 //   moe_topk_kernel    one wave per token: softmax statistics, k rounds of a
 //                      wave arg-max (ties: lower expert), renormalisation;
 //                      ids [T*k] and weights [T*k], pair p = t*k + slot;
@@ -45,40 +45,58 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 
 // ------------------------------------------------------------- router -----
 
-// D[e][t] = Wr[e,:] . x[t,:]: the router row is the MFMA's A operand, the
-// token row its B operand; a lane ends with experts e0 + 4g .. +3 of token
-// t0 + r16.  Grid (ceil(T/16), ceil(E/64)), four waves of 16 experts.
-__global__ __launch_bounds__(256) void moe_router_kernel(const bf16* __restrict__ x, int T, int H,
-                                                         const bf16* __restrict__ wr, int E,
-                                                         float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// D[e][t] = Wr[e,:] . x[t,:]: router rows are the MFMA's A operand, token
+// rows its B operand.  One wave per workgroup computes 16 tokens x all E
+// experts (E/16 accumulator tiles) over one K range: grid (ceil(T/16), S).
+// A lane ends with experts 16i + 4g .. +3 of token t0 + r16; the S ranges'
+// partial logits [S][T][E] are summed in order by the top-k kernel.
+template <int NT>  // E / 16 accumulator tiles
+__global__ __launch_bounds__(64) void moe_router_kernel(const bf16* __restrict__ x, int T, int H, int kps,
+                                                        const bf16* __restrict__ wr, int E,
+                                                        float* __restrict__ part) {
+  const int lane = threadIdx.x;
   const int r16 = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * 16;
-  const int e0 = (blockIdx.y * 4 + wave) * 16;
-  if (e0 >= E) return;
+  const int k0 = blockIdx.y * kps;
   const int t = min(t0 + r16, T - 1);
-  const bf16* xa = x + (size_t)t * H + g * 8;
-  const bf16* wa = wr + (size_t)(e0 + r16) * H + g * 8;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k = 0; k < H; k += 64) {
-    const bf16x8 a0 = ld16<bf16x8>(wa + k), b0 = ld16<bf16x8>(xa + k);
-    const bf16x8 a1 = ld16<bf16x8>(wa + k + 32), b1 = ld16<bf16x8>(xa + k + 32);
-    acc0 = mfma16(a0, b0, acc0);
-    acc1 = mfma16(a1, b1, acc1);
+  const bf16* xa = x + (size_t)t * H + k0 + g * 8;
+  const bf16* wa = wr + (size_t)r16 * H + k0 + g * 8;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // loads run one 32-wide k step ahead of the MFMAs
+  bf16x8 b = ld16<bf16x8>(xa), a[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) a[i] = ld16<bf16x8>(wa + (size_t)i * 16 * H);
+  for (int k = 32; k <= kps; k += 32) {
+    bf16x8 bn = b, an[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) an[i] = a[i];
+    if (k < kps) {
+      bn = ld16<bf16x8>(xa + k);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) an[i] = ld16<bf16x8>(wa + (size_t)i * 16 * H + k);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = mfma16(a[i], b, acc[i]);
+    b = bn;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) a[i] = an[i];
   }
   if (t0 + r16 < T) {
-    f32x4 s;
+    float* dst = part + ((size_t)blockIdx.y * T + t0 + r16) * E + 4 * g;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = acc0[r] + acc1[r];
-    *reinterpret_cast<f32x4*>(logits + (size_t)(t0 + r16) * E + e0 + 4 * g) = s;
+    for (int i = 0; i < NT; ++i) *reinterpret_cast<f32x4*>(dst + 16 * i) = acc[i];
   }
 }
 
 // One wave per token; lane l holds experts l, l + 64, ... (EPL of them).
+// The logits are first summed over the router's S partial ranges (in order)
+// and stored to `logits`.
 template <int EPL>
-__global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                       int norm, int* __restrict__ ids, float* __restrict__ wts) {
+__global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ part, int S, int T, int E, int k,
+                                                       int norm, float* __restrict__ logits, int* __restrict__ ids,
+                                                       float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -86,7 +104,14 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+    v[j] = -INFINITY;
+    if (e < E) {
+      float a = part[(size_t)t * E + e];
+#pragma unroll 8
+      for (int sp = 1; sp < S; ++sp) a += part[((size_t)sp * T + t) * E + e];
+      v[j] = a;
+      logits[(size_t)t * E + e] = a;
+    }
   }
   float m = v[0];
 #pragma unroll
@@ -148,19 +173,49 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int* __restrict__
   __syncthreads();
   for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[min(max(ids[p], 0), E - 1)], 1);
   __syncthreads();
-  if (tid == 0) {
-    int run = 0, nt = 0, na = 0;
-    for (int e = 0; e < E; ++e) {
-      seg[e] = run;
-      cur[e] = run;
-      toff[e] = nt;
-      aidx[e] = cnt[e] > 0 ? na++ : -1;
-      run += cnt[e];
-      nt += (cnt[e] + bm - 1) / bm;
+  // exclusive scans of (pairs, tiles, active flag) over the experts in
+  // wave 0: lane l owns experts 4l .. 4l+3
+  if (tid < 64) {
+    int c[4], run = 0, nt = 0, na = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * tid + j;
+      c[j] = e < E ? cnt[e] : 0;
+      run += c[j];
+      nt += (c[j] + bm - 1) / bm;
+      na += c[j] > 0;
     }
-    seg[E] = run;
-    *nactive = na;
-    *ntiles = min(nt, tile_cap);
+    int ir = run, it = nt, ia = na;  // inclusive scans across lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int ur = __shfl_up(ir, o, kWave), ut = __shfl_up(it, o, kWave), ua = __shfl_up(ia, o, kWave);
+      if (tid >= o) {
+        ir += ur;
+        it += ut;
+        ia += ua;
+      }
+    }
+    run = ir - run;
+    nt = it - nt;
+    na = ia - na;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * tid + j;
+      if (e < E) {
+        seg[e] = run;
+        cur[e] = run;
+        toff[e] = nt;
+        aidx[e] = c[j] > 0 ? na : -1;
+      }
+      run += c[j];
+      nt += (c[j] + bm - 1) / bm;
+      na += c[j] > 0;
+    }
+    if (tid == 63) {
+      seg[E] = run;
+      *nactive = na;
+      *ntiles = min(nt, tile_cap);
+    }
   }
   __syncthreads();
   if (tid < E && cnt[tid] > 0) {
@@ -544,22 +599,41 @@ hipError_t launch_moe_stream(const bf16* x, int topk, const bf16* w, int wrows, 
 
 bool moe_streaming(int T) { return T <= kSkinnyMaxM; }
 
+int moe_router_splits(int T, int H) {
+  // about 1024 single-wave workgroups; each K range a multiple of 64
+  const int tiles = (T + 15) / 16;
+  int S = 1;
+  while (S < 16 && tiles * S * 2 <= 1024 && H % (64 * S * 2) == 0) S *= 2;
+  return S;
+}
+
 hipError_t launch_moe_route(const void* x, int T, int H, const void* router, int E, int topk, bool norm,
-                            float* logits, int* ids, float* wts, hipStream_t s) {
+                            float* part, float* logits, int* ids, float* wts, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (E <= 0 || E > kMaxExperts || E % 16 || H % 64 || topk < 1 || topk > 64 || topk > E)
-    return hipErrorInvalidValue;
-  moe_router_kernel<<<dim3((T + 15) / 16, (E + 63) / 64), 256, 0, s>>>((const bf16*)x, T, H, (const bf16*)router,
-                                                                        E, logits);
+  if (E <= 0 || E > 256 || E % 16 || H % 64 || topk < 1 || topk > 64 || topk > E) return hipErrorInvalidValue;
+  const int S = moe_router_splits(T, H);
+  const dim3 grid((T + 15) / 16, S);
+  const bf16* xb = (const bf16*)x;
+  const bf16* wb = (const bf16*)router;
+  switch (E / 16) {
+#define LLK_ROUTER_CASE(NT) \
+  case NT: moe_router_kernel<NT><<<grid, 64, 0, s>>>(xb, T, H, H / S, wb, E, part); break;
+    LLK_ROUTER_CASE(1) LLK_ROUTER_CASE(2) LLK_ROUTER_CASE(3) LLK_ROUTER_CASE(4) LLK_ROUTER_CASE(5)
+    LLK_ROUTER_CASE(6) LLK_ROUTER_CASE(7) LLK_ROUTER_CASE(8) LLK_ROUTER_CASE(9) LLK_ROUTER_CASE(10)
+    LLK_ROUTER_CASE(11) LLK_ROUTER_CASE(12) LLK_ROUTER_CASE(13) LLK_ROUTER_CASE(14) LLK_ROUTER_CASE(15)
+    LLK_ROUTER_CASE(16)
+#undef LLK_ROUTER_CASE
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned blocks = (unsigned)((T + 3) / 4);
   const int epl = (E + 63) / 64;
+  const int nm = norm ? 1 : 0;
   switch (epl) {
-    case 1: moe_topk_kernel<1><<<blocks, 256, 0, s>>>(logits, T, E, topk, norm ? 1 : 0, ids, wts); break;
-    case 2: moe_topk_kernel<2><<<blocks, 256, 0, s>>>(logits, T, E, topk, norm ? 1 : 0, ids, wts); break;
-    case 3: moe_topk_kernel<3><<<blocks, 256, 0, s>>>(logits, T, E, topk, norm ? 1 : 0, ids, wts); break;
-    default: moe_topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, topk, norm ? 1 : 0, ids, wts); break;
+    case 1: moe_topk_kernel<1><<<blocks, 256, 0, s>>>(part, S, T, E, topk, nm, logits, ids, wts); break;
+    case 2: moe_topk_kernel<2><<<blocks, 256, 0, s>>>(part, S, T, E, topk, nm, logits, ids, wts); break;
+    case 3: moe_topk_kernel<3><<<blocks, 256, 0, s>>>(part, S, T, E, topk, nm, logits, ids, wts); break;
+    default: moe_topk_kernel<4><<<blocks, 256, 0, s>>>(part, S, T, E, topk, nm, logits, ids, wts); break;
   }
   return hipGetLastError();
 }

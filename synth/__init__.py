@@ -112,6 +112,12 @@ LLAMA3_SCALING = {
 
 LLAMA70B = ModelShape(8192, 64, 8, 128, 28672, 1e-5, 500000.0, LLAMA3_SCALING, 131072, "bf16")
 TINY = ModelShape(256, 4, 2, 64, 688, 1e-5, 10000.0, None, 4096, "fp32")
+# one GPU's share of the 70B layer under the pages' tensor parallelism at
+# TP = 8: the column-parallel qkv and gate_up keep 8 query heads, 1 KV head
+# and 28672 / 8 intermediate features per GPU; the row-parallel o_proj and
+# down_proj read those shards (K = 1024 and 3584) and produce partial sums
+# that an all-reduce would complete
+LLAMA70B_TP8 = ModelShape(8192, 8, 1, 128, 3584, 1e-5, 500000.0, LLAMA3_SCALING, 131072, "bf16")
 # Qwen3-30B-A3B (config.json on the page "LLama", section
 # "Qwen3MoeForCausalLM"): every layer is sparse (decoder_sparse_step 1, no
 # mlp_only_layers), so intermediate_size (the dense width) is never used.
@@ -166,6 +172,9 @@ WORKLOADS = {
         # the Qwen3-MoE layer on the same two batch shapes as the 70B layer
         Workload(7, "qwen3moe_decode_b32_ctx2048", QWEN3MOE, 32, 1, 2048),
         Workload(8, "qwen3moe_prefill_4x2048", QWEN3MOE, 4, 2048, 0),
+        # one GPU's TP = 8 share of the 70B layer on the 70B batch shapes
+        Workload(9, "llama70b_tp8shard_decode_b32_ctx2048", LLAMA70B_TP8, 32, 1, 2048),
+        Workload(10, "llama70b_tp8shard_prefill_4x2048", LLAMA70B_TP8, 4, 2048, 0),
     ]
 }
 WORKLOAD_LIST = sorted(WORKLOADS.values(), key=lambda w: w.index)

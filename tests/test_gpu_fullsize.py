@@ -134,3 +134,38 @@ def test_mixed_chunk512_decode32_sampled_rows():
     # one call with 32 decode rows (context 2048) and a 512-row prefill chunk
     # on a 4096-token context: every decode row, sampled chunk rows
     _check_prefill("llama70b_mixed_chunk512_decode32", extra=(255, 256, 511))
+
+
+def test_qwen3moe_decode_b32_ctx2048_all_rows():
+    # the Qwen3-30B-A3B layer: 128 experts, top-8, q/k norm
+    from tests.test_gpu_moe import run_moe_layer
+    run_moe_layer(synth.WORKLOADS["qwen3moe_decode_b32_ctx2048"])
+
+
+@pytest.mark.timeout(600)
+def test_qwen3moe_prefill_4x2048_sampled_rows():
+    from tests.test_gpu_moe import run_moe_layer
+    wl = synth.WORKLOADS["qwen3moe_prefill_4x2048"]
+    batch = synth.build_batch(wl)
+    # each sequence's last row is sampled, so the oracle forms every new K/V
+    run_moe_layer(wl, want=_sample_rows(batch, (511, 512, 1023, 1024)), check_kv=True)
+
+
+def test_tp8_shard_decode_b32_ctx2048_all_rows():
+    # one GPU's TP = 8 share of the 70B layer: qkv N = 1280, o_proj K = 1024,
+    # gate_up N = 2 x 3584, down K = 3584, attention 8 query heads on 1 KV head
+    wl = synth.WORKLOADS["llama70b_tp8shard_decode_b32_ctx2048"]
+    batch = synth.build_batch(wl)
+    hidden, residual = synth.draw_activations(wl.model, batch.num_tokens, wl.index, DEV)
+    w, kp0, vp0, kp, vp, ho, ro = _forward(wl, batch, 0, hidden, residual)
+    seqs = oracle_seqs(wl.model, batch, kp0, vp0)
+    exact, rounded = run_oracle(wl.model, oracle_weights(w), hidden, residual, batch, seqs)
+    s1 = compare("hidden_out", np64(ho), exact["hidden_out"], rounded["hidden_out"])
+    s2 = compare("residual_out", np64(ro), exact["residual_out"], rounded["residual_out"])
+    print("hidden_out", s1, "residual_out", s2, flush=True)
+    _check_kv(wl.model, batch, kp0, vp0, kp, vp, exact, rounded)
+
+
+@pytest.mark.timeout(600)
+def test_tp8_shard_prefill_4x2048_sampled_rows():
+    _check_prefill("llama70b_tp8shard_prefill_4x2048", extra=(511, 512, 1023, 1024))
