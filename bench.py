@@ -30,6 +30,12 @@ METRIC = "70B-shape layer tokens/s (prefill, decode) + % MFMA/HBM peak, 1 MI355X
 # x 1.0 (factors from a plain 1 GiB copy; profiles/pmc_copy_calibration.md).  Reported only while
 # the kernel's source file is the one the counters were taken on.
 COUNTER_TRAFFIC = {
+    ("qwen3moe_decode_b32_ctx2048", "moe_gate_up_silu"): {
+        "bytes": 703207232,
+        "source": "llama_decoder_layer_amd/csrc/moe.hip",
+        "sha1": "7f7dd7d91c25bef44e73697aac3eda81087ad39a",
+        "summary": "profiles/moe_gate_up_silu_qwen3moe_decode_b32_ctx2048.md",
+    },
     ("llama70b_decode_b32_ctx2048", "gate_up_silu"): {
         "bytes": 945618555,
         "source": "llama_decoder_layer_amd/csrc/gemm_skinny.hip",
@@ -328,6 +334,7 @@ def main():
         "cpu_baseline": cpu,
         "step_fraction": main_res.get("step_fraction"),
         "kernel_avg_us": main_res.get("kernel_avg_us"),
+        **({"experts_with_tokens": main_res["experts_with_tokens"]} if "experts_with_tokens" in main_res else {}),
         "wall_s_timed_region": main_res["wall_s_timed_region"],
         "extra": extra,
     }

@@ -103,7 +103,7 @@ struct Workspace {
   size_t h, qkv, attn, h2, act, part, gpart, tpart, tpart_bytes, seq_of, ntiles, tiles, total;
   int tile_cap;  // entries of the prefill tile table (mixed batches)
   // MoE routing and expert buffers (P = T * topk pairs)
-  size_t rpart, logits, ids, wts, seg, sorted, active, nactive, mtiles, mntiles, mact, mpart;
+  size_t rpart, logits, ids, wts, seg, sorted, active, nactive, mtiles, mntiles, mchunk, mact, mpart;
   int moe_tile_cap;
   llk::AttnPlan plan;
   bool skinny;  // few tokens: weight-streaming projections with split-K partials
@@ -179,6 +179,7 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.nactive = take(L->E ? sizeof(int) : 0);
   w.mtiles = take((size_t)w.moe_tile_cap * sizeof(int4));
   w.mntiles = take(L->E ? sizeof(int) : 0);
+  w.mchunk = take((size_t)llk::moe_align_chunks((int)P) * L->E * sizeof(int));
   w.mact = take(P * L->moe_I * L->es);
   w.mpart = take(P * H * L->es);
   w.total = off;
@@ -259,6 +260,7 @@ llama_status moe_block(llama_layer* L, const Workspace& w, char* ws, const void*
   r.ntiles = (int*)(ws + w.mntiles);
   r.tile_cap = w.moe_tile_cap;
   r.wts = (float*)(ws + w.wts);
+  r.chunk = (int*)(ws + w.mchunk);
   int* ids = (int*)(ws + w.ids);
   hipError_t e = llk::launch_moe_route(h2, T, H, L->w_router, L->E, L->topk, L->cfg.norm_topk_prob != 0,
                                        (float*)(ws + w.rpart), (float*)(ws + w.logits), ids, r.wts, s);

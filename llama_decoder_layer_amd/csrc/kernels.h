@@ -155,7 +155,9 @@ struct MoeRouting {
   int* ntiles = nullptr;    // [1]
   int tile_cap = 0;         // >= P / bm + E
   float* wts = nullptr;     // [P] routing weight of each pair
+  int* chunk = nullptr;     // [moe_align_chunks(P)][E] grouping scratch (many pairs)
 };
+int moe_align_chunks(int P);  // 0: the grouping runs in one workgroup
 bool moe_streaming(int T);
 int moe_router_splits(int T, int H);
 hipError_t launch_moe_route(const void* x, int T, int H, const void* router, int E, int topk, bool norm,

@@ -13,12 +13,15 @@
 // Kernels, in launch order:
 //   moe_router_kernel  logits [T, E] fp32 = x Wr^T on MFMA (one wave per 16
 //                      tokens x all experts and one of S K ranges);
-//   moe_topk_kernel    one wave per token: softmax statistics, k rounds of a
-//                      wave arg-max (ties: lower expert), renormalisation;
+//   moe_topk_kernel    one wave per token: softmax statistics, each expert's
+//                      rank among the token's logits (ties: lower expert),
+//                      the k best written in rank order, renormalisation;
 //                      ids [T*k] and weights [T*k], pair p = t*k + slot;
-//   moe_align_kernel   one workgroup: per-expert counts, the pairs grouped by
-//                      expert ("sorted" positions), the active-expert list and
-//                      a table of row tiles (expert, first row, rows);
+//   moe_align_kernel   per-expert counts, the pairs grouped by expert
+//                      ("sorted" positions), the active-expert list and a
+//                      table of row tiles (expert, first row, rows): one
+//                      workgroup for few pairs, else count / scan / scatter
+//                      kernels over chunks of 4096 pairs;
 //   expert GEMMs       gate_up + SiluAndMul over each expert's gathered token
 //                      rows into act [P, I] (sorted order), then down with the
 //                      routing weight applied before the bf16 store, scattered
@@ -29,8 +32,6 @@
 //                      order, fp32 accumulation.
 // No atomics touch the results: the order of pairs inside an expert's group
 // (set by LDS atomics) changes which rows share a tile, never a row's value.
-#include <type_traits>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -92,27 +93,40 @@ __global__ __launch_bounds__(64) void moe_router_kernel(const bf16* __restrict__
 
 // One wave per token; lane l holds experts l, l + 64, ... (EPL of them).
 // The logits are first summed over the router's S partial ranges (in order)
-// and stored to `logits`.
+// and stored to `logits`.  Selection by rank: each logit becomes a 64-bit
+// key, its float bits mapped to an unsigned order above the complemented
+// expert index, so that larger keys are larger logits and, among equal ones,
+// lower experts.  Each lane counts the keys of the token above each of its
+// own -- all E keys read from LDS, which broadcasts -- and an expert whose
+// rank is below k writes slot `rank`.
 template <int EPL>
 __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ part, int S, int T, int E, int k,
                                                        int norm, float* __restrict__ logits, int* __restrict__ ids,
                                                        float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  __shared__ unsigned long long sk[4][64 * EPL];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + w;
+  const bool live = t < T;  // the wave's token exists (uniform)
   float v[EPL];
+  unsigned long long key[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
     v[j] = -INFINITY;
-    if (e < E) {
+    if (live && e < E) {
       float a = part[(size_t)t * E + e];
 #pragma unroll 8
       for (int sp = 1; sp < S; ++sp) a += part[((size_t)sp * T + t) * E + e];
       v[j] = a;
       logits[(size_t)t * E + e] = a;
     }
+    unsigned u = __float_as_uint(v[j] + 0.f);  // -0 -> +0
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    key[j] = ((unsigned long long)u << 32) | (unsigned)(0xFFFFu - e);
+    sk[w][e] = key[j];
   }
+  __syncthreads();
+  if (!live) return;
   float m = v[0];
 #pragma unroll
   for (int j = 1; j < EPL; ++j) m = fmaxf(m, v[j]);
@@ -122,46 +136,98 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
   for (int j = 0; j < EPL; ++j)
     if (lane + 64 * j < E) s += expf(v[j] - m);
   s = wave_sum(s);
-  int my_id = 0;
-  float my_p = 0.f;
-  for (int r = 0; r < k; ++r) {
-    float bv = v[0];
-    int bi = lane;
+  int rank[EPL];
 #pragma unroll
-    for (int j = 1; j < EPL; ++j)
-      if (v[j] > bv) {  // a later slot of this lane has a larger index: strict
-        bv = v[j];
-        bi = lane + 64 * j;
-      }
+  for (int j = 0; j < EPL; ++j) rank[j] = 0;
+#pragma unroll 8
+  for (int f = 0; f < E; ++f) {
+    const unsigned long long kf = sk[w][f];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (lane == r) {
-      my_id = bi;
-      my_p = expf(bv - m) / s;
-    }
-    // the owner drops the winner from later rounds
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (lane + 64 * j == bi) v[j] = -INFINITY;
+    for (int j = 0; j < EPL; ++j) rank[j] += kf > key[j];
   }
-  const float wsum = wave_sum(lane < k ? my_p : 0.f);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = min(max(my_id, 0), E - 1);
-    wts[(size_t)t * k + lane] = norm ? my_p / wsum : my_p;
+  float p[EPL], kept = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    p[j] = expf(v[j] - m) / s;
+    if (lane + 64 * j < E && rank[j] < k) kept += p[j];
   }
+  const float wsum = wave_sum(kept);
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (lane + 64 * j < E && rank[j] < k) {
+      ids[(size_t)t * k + rank[j]] = lane + 64 * j;
+      wts[(size_t)t * k + rank[j]] = norm ? p[j] / wsum : p[j];
+    }
 }
 
 // ---------------------------------------------------------- alignment -----
 
 constexpr int kMaxExperts = 256;
+constexpr int kAlignVec = 8;  // 16-byte id loads per thread per pass
 
+// Exclusive scans of (pairs, tiles, active flag) over the experts, by one
+// wave (lane l owns experts 4l .. 4l+3), from the per-expert counts in cnt:
+// writes seg[0..E], nactive, ntiles and the LDS arrays cur (= seg), toff
+// (first tile) and aidx (slot in the active list).  Called by wave 0.
+__device__ void align_scan(const int* cnt, int E, int bm, int tile_cap, int* seg, int* nactive, int* ntiles,
+                           int* cur, int* toff, int* aidx) {
+  const int lane = threadIdx.x & 63;
+  int c[4], run = 0, nt = 0, na = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;
+    c[j] = e < E ? cnt[e] : 0;
+    run += c[j];
+    nt += (c[j] + bm - 1) / bm;
+    na += c[j] > 0;
+  }
+  int ir = run, it = nt, ia = na;  // inclusive scans across lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ur = __shfl_up(ir, o, kWave), ut = __shfl_up(it, o, kWave), ua = __shfl_up(ia, o, kWave);
+    if (lane >= o) {
+      ir += ur;
+      it += ut;
+      ia += ua;
+    }
+  }
+  run = ir - run;
+  nt = it - nt;
+  na = ia - na;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;
+    if (e < E) {
+      seg[e] = run;
+      cur[e] = run;
+      toff[e] = nt;
+      aidx[e] = c[j] > 0 ? na : -1;
+    }
+    run += c[j];
+    nt += (c[j] + bm - 1) / bm;
+    na += c[j] > 0;
+  }
+  if (lane == 63) {
+    seg[E] = run;
+    *nactive = na;
+    *ntiles = min(nt, tile_cap);
+  }
+}
+
+// Thread e (< E): expert e's entry in the active list and its row tiles.
+__device__ void align_tiles(const int* cnt, int E, int bm, const int* cur, const int* toff, const int* aidx,
+                            int* active, int4* tiles, int tile_cap) {
+  const int e = threadIdx.x;
+  if (e >= E || cnt[e] == 0) return;
+  const int c = cnt[e];
+  active[aidx[e]] = e;
+  for (int i = 0; i * bm < c; ++i) {
+    const int idx = toff[e] + i;
+    if (idx < tile_cap) tiles[idx] = make_int4(e, cur[e] + i * bm, min(bm, c - i * bm), 0);
+  }
+}
+
+// Few pairs (decode): everything in one workgroup.
 __global__ __launch_bounds__(1024) void moe_align_kernel(const int* __restrict__ ids, int P, int E, int bm,
                                                          int* __restrict__ seg, int* __restrict__ sorted,
                                                          int* __restrict__ active, int* __restrict__ nactive,
@@ -171,66 +237,119 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int* __restrict__
   const int tid = threadIdx.x;
   if (tid < E) cnt[tid] = 0;
   __syncthreads();
-  for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[min(max(ids[p], 0), E - 1)], 1);
-  __syncthreads();
-  // exclusive scans of (pairs, tiles, active flag) over the experts in
-  // wave 0: lane l owns experts 4l .. 4l+3
-  if (tid < 64) {
-    int c[4], run = 0, nt = 0, na = 0;
+  // pairs are read 16 bytes at a time, kAlignVec per thread per pass, all
+  // loads of a pass in flight together (a strided loop of single loads would
+  // wait out one memory latency per pair)
+  auto load_pass = [&](int base, int (&v)[kAlignVec * 4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * tid + j;
-      c[j] = e < E ? cnt[e] : 0;
-      run += c[j];
-      nt += (c[j] + bm - 1) / bm;
-      na += c[j] > 0;
-    }
-    int ir = run, it = nt, ia = na;  // inclusive scans across lanes
+    for (int j = 0; j < kAlignVec; ++j) {
+      const int i = base + (j * 1024 + tid) * 4;
+      if (i + 3 < P) {
+        const int4 q = *reinterpret_cast<const int4*>(ids + i);
+        v[4 * j] = q.x;
+        v[4 * j + 1] = q.y;
+        v[4 * j + 2] = q.z;
+        v[4 * j + 3] = q.w;
+      } else {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int ur = __shfl_up(ir, o, kWave), ut = __shfl_up(it, o, kWave), ua = __shfl_up(ia, o, kWave);
-      if (tid >= o) {
-        ir += ur;
-        it += ut;
-        ia += ua;
+        for (int r = 0; r < 4; ++r) v[4 * j + r] = i + r < P ? ids[i + r] : -1;
       }
     }
-    run = ir - run;
-    nt = it - nt;
-    na = ia - na;
+  };
+  constexpr int kPass = 1024 * kAlignVec * 4;
+  for (int base = 0; base < P; base += kPass) {
+    int v[kAlignVec * 4];
+    load_pass(base, v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * tid + j;
-      if (e < E) {
-        seg[e] = run;
-        cur[e] = run;
-        toff[e] = nt;
-        aidx[e] = c[j] > 0 ? na : -1;
-      }
-      run += c[j];
-      nt += (c[j] + bm - 1) / bm;
-      na += c[j] > 0;
-    }
-    if (tid == 63) {
-      seg[E] = run;
-      *nactive = na;
-      *ntiles = min(nt, tile_cap);
-    }
+    for (int j = 0; j < kAlignVec * 4; ++j)
+      if (v[j] >= 0) atomicAdd(&cnt[min(v[j], E - 1)], 1);
   }
   __syncthreads();
-  if (tid < E && cnt[tid] > 0) {
-    const int e = tid, c = cnt[e];
-    active[aidx[e]] = e;
-    for (int i = 0; i * bm < c; ++i) {
-      const int idx = toff[e] + i;
-      if (idx < tile_cap) tiles[idx] = make_int4(e, cur[e] + i * bm, min(bm, c - i * bm), 0);
-    }
+  if (tid < 64) align_scan(cnt, E, bm, tile_cap, seg, nactive, ntiles, cur, toff, aidx);
+  __syncthreads();
+  align_tiles(cnt, E, bm, cur, toff, aidx, active, tiles, tile_cap);
+  __syncthreads();
+  for (int base = 0; base < P; base += kPass) {
+    int v[kAlignVec * 4];
+    load_pass(base, v);
+#pragma unroll
+    for (int j = 0; j < kAlignVec * 4; ++j)
+      if (v[j] >= 0) sorted[atomicAdd(&cur[min(v[j], E - 1)], 1)] = base + ((j >> 2) * 1024 + tid) * 4 + (j & 3);
+  }
+}
+
+// Many pairs (prefill): the same grouping over chunks of kAlignChunk pairs,
+// one workgroup each, so the LDS atomics spread over many CUs.  count: each
+// chunk's per-expert counts -> chunk[b][e]; scan (one workgroup): totals,
+// the tables, and chunk[b][e] := the first sorted position of chunk b's
+// pairs of expert e; scatter: each chunk places its pairs from there.
+constexpr int kAlignChunk = 4096;  // 4 pairs per thread
+
+__device__ __forceinline__ void load4_ids(const int* ids, int P, int i, int (&v)[4]) {
+  if (i + 3 < P) {
+    const int4 q = *reinterpret_cast<const int4*>(ids + i);
+    v[0] = q.x;
+    v[1] = q.y;
+    v[2] = q.z;
+    v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = i + r < P ? ids[i + r] : -1;
+  }
+}
+
+__global__ __launch_bounds__(1024) void moe_count_kernel(const int* __restrict__ ids, int P, int E,
+                                                         int* __restrict__ chunk) {
+  __shared__ int cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < E) cnt[tid] = 0;
+  __syncthreads();
+  int v[4];
+  load4_ids(ids, P, blockIdx.x * kAlignChunk + tid * 4, v);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (v[r] >= 0) atomicAdd(&cnt[min(v[r], E - 1)], 1);
+  __syncthreads();
+  if (tid < E) chunk[(size_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(256) void moe_scan_kernel(int nb, int E, int bm, int* __restrict__ chunk,
+                                                       int* __restrict__ seg, int* __restrict__ active,
+                                                       int* __restrict__ nactive, int4* __restrict__ tiles,
+                                                       int tile_cap, int* __restrict__ ntiles) {
+  __shared__ int cnt[kMaxExperts], cur[kMaxExperts], toff[kMaxExperts], aidx[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < E) {
+    int c = 0;
+    for (int b = 0; b < nb; ++b) c += chunk[(size_t)b * E + tid];
+    cnt[tid] = c;
   }
   __syncthreads();
-  for (int p = tid; p < P; p += 1024) {
-    const int e = min(max(ids[p], 0), E - 1);
-    sorted[atomicAdd(&cur[e], 1)] = p;
+  if (tid < 64) align_scan(cnt, E, bm, tile_cap, seg, nactive, ntiles, cur, toff, aidx);
+  __syncthreads();
+  align_tiles(cnt, E, bm, cur, toff, aidx, active, tiles, tile_cap);
+  if (tid < E) {
+    int run = cur[tid];
+    for (int b = 0; b < nb; ++b) {
+      const int c = chunk[(size_t)b * E + tid];
+      chunk[(size_t)b * E + tid] = run;
+      run += c;
+    }
   }
+}
+
+__global__ __launch_bounds__(1024) void moe_scatter_kernel(const int* __restrict__ ids, int P, int E,
+                                                           const int* __restrict__ chunk, int* __restrict__ sorted) {
+  __shared__ int cur[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < E) cur[tid] = chunk[(size_t)blockIdx.x * E + tid];
+  __syncthreads();
+  const int i = blockIdx.x * kAlignChunk + tid * 4;
+  int v[4];
+  load4_ids(ids, P, i, v);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (v[r] >= 0) sorted[atomicAdd(&cur[min(v[r], E - 1)], 1)] = i + r;
 }
 
 // ------------------------------------------------ expert GEMM: streaming --
@@ -383,10 +502,11 @@ constexpr int kEntriesPerChunk = 2;
 // memory into double-buffered XOR-swizzled LDS, as the dense tiled kernel.
 // Work order: chunks of kEntriesPerChunk entries x all weight tiles are
 // dealt to the 8 XCDs in turn, so that the weight tiles of one entry, which
-// share its gathered x rows, run together on one XCD.  Waves are numbered
-// with the weight-tile index fastest (SIMD = wave % 4 holds one wave of
-// each token half): a partly filled tile skips the MFMAs of its empty
-// 16-row sub-tiles and the saving spreads over all four SIMDs.
+// share its gathered x rows, run together on one XCD (chunks of 1 to 8
+// entries measured the same).  A partly filled tile computes all its rows
+// (rows past the entry repeat its last row and are not stored): skipping
+// the MFMAs of empty 16-row sub-tiles measured no faster, the kernel being
+// bound by feeding LDS rather than by MFMA issue.
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void moe_tile_kernel(const bf16* __restrict__ X, int topk,
                                                                 const bf16* __restrict__ W, int wrows, int K,
@@ -418,7 +538,7 @@ __global__ __launch_bounds__(64 * WM * WN) void moe_tile_kernel(const bf16* __re
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave % WM, wn = wave / WM;
   const int r16 = lane & 15, g = lane >> 4;
   const int prow = lane >> 3, pc = lane & 7;
 
@@ -451,52 +571,36 @@ __global__ __launch_bounds__(64 * WM * WN) void moe_tile_kernel(const bf16* __re
           (__attribute__((address_space(3))) void*)(sX + buf * BM * kTBK + (j * NW + wave) * 8 * kTBK), 16, 0, 0);
   };
 
-  // 16-row sub-tiles of this wave that hold pair rows (wave-uniform)
-  const int act_sub = min(SM, max(0, (rows - wm * TM + 15) / 16));
-
   f32x4 acc[SN][SM];
 #pragma unroll
   for (int i = 0; i < SN; ++i)
 #pragma unroll
     for (int j = 0; j < SM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one k stage of this wave's MFMAs over its first `nsub` 16-row sub-tiles
-  auto stage = [&](int buf, auto full) {
+  const int nk = K / kTBK;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) issue(buf ^ 1, kt + 1);
 #pragma unroll
     for (int s = 0; s < kTBK / 32; ++s) {
       const int c = s * 4 + g;
       bf16x8 b[SM];
 #pragma unroll
       for (int j = 0; j < SM; ++j)
-        if (decltype(full)::value || j < act_sub)
-          b[j] = *reinterpret_cast<const bf16x8*>(&sX[buf * BM * kTBK + swz(wm * TM + j * 16 + r16, c)]);
+        b[j] = *reinterpret_cast<const bf16x8*>(&sX[buf * BM * kTBK + swz(wm * TM + j * 16 + r16, c)]);
 #pragma unroll
       for (int i = 0; i < SN; ++i) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sW[buf * BN * kTBK + swz(wn * TN + i * 16 + r16, c)]);
 #pragma unroll
-        for (int j = 0; j < SM; ++j)
-          if (decltype(full)::value || j < act_sub) acc[i][j] = mfma16(a, b[j], acc[i][j]);
+        for (int j = 0; j < SM; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
       }
     }
-  };
-  const int nk = K / kTBK;
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (act_sub == SM) {
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) issue((kt & 1) ^ 1, kt + 1);
-      stage(kt & 1, std::true_type());
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-  } else {
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) issue((kt & 1) ^ 1, kt + 1);
-      if (act_sub > 0) stage(kt & 1, std::false_type());
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
+    // the next stage's loads have landed and every wave is done with this one
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
 #pragma unroll
@@ -603,7 +707,7 @@ int moe_router_splits(int T, int H) {
   // about 1024 single-wave workgroups; each K range a multiple of 64
   const int tiles = (T + 15) / 16;
   int S = 1;
-  while (S < 16 && tiles * S * 2 <= 1024 && H % (64 * S * 2) == 0) S *= 2;
+  while (S < 8 && tiles * S * 2 <= 1024 && H % (64 * S * 2) == 0) S *= 2;
   return S;
 }
 
@@ -638,11 +742,21 @@ hipError_t launch_moe_route(const void* x, int T, int H, const void* router, int
   return hipGetLastError();
 }
 
+int moe_align_chunks(int P) { return P > 2 * kAlignChunk ? (P + kAlignChunk - 1) / kAlignChunk : 0; }
+
 hipError_t launch_moe_align(const int* ids, int P, int E, int bm, const MoeRouting& r, hipStream_t s) {
   if (P <= 0) return hipSuccess;
   if (E <= 0 || E > kMaxExperts || bm <= 0) return hipErrorInvalidValue;
-  moe_align_kernel<<<1, 1024, 0, s>>>(ids, P, E, bm, r.seg, r.sorted, r.active, r.nactive, r.tiles, r.tile_cap,
-                                      r.ntiles);
+  const int nb = moe_align_chunks(P);
+  if (nb == 0) {
+    moe_align_kernel<<<1, 1024, 0, s>>>(ids, P, E, bm, r.seg, r.sorted, r.active, r.nactive, r.tiles, r.tile_cap,
+                                        r.ntiles);
+    return hipGetLastError();
+  }
+  if (!r.chunk) return hipErrorInvalidValue;
+  moe_count_kernel<<<nb, 1024, 0, s>>>(ids, P, E, r.chunk);
+  moe_scan_kernel<<<1, 256, 0, s>>>(nb, E, bm, r.chunk, r.seg, r.active, r.nactive, r.tiles, r.tile_cap, r.ntiles);
+  moe_scatter_kernel<<<nb, 1024, 0, s>>>(ids, P, E, r.chunk, r.sorted);
   return hipGetLastError();
 }
 

@@ -119,3 +119,9 @@ def test_moe_mixed_chunk_and_decode():
 
 def test_moe_decode_repeat_bitwise():
     run_moe_layer(synth.Workload(206, "moe_decode_b64_repeat", MOE8, 64, 1, (10, 200)), repeat=True)
+
+
+def test_moe_prefill_3x1000_chunked_grouping():
+    # 12000 pairs: more than 8192, so the grouping by expert runs as count /
+    # scan / scatter kernels over chunks of 4096 pairs (the last one ragged)
+    run_moe_layer(synth.Workload(207, "moe_prefill_3x1000", MOE, 3, 1000, 0), repeat=True)
