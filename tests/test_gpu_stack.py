@@ -1,6 +1,7 @@
 """GPU parity of the decoder stack (layers + the final RMSNorm,
 llama_stack_forward) against the oracle's model forward, and HIP-graph
-replays of a captured stack forward against eager runs."""
+replays of a captured stack forward against eager runs; also for stacks of
+Qwen3-MoE-structured layers."""
 import numpy as np
 import pytest
 import torch
@@ -82,5 +83,101 @@ def test_stack_graph_replays_match_eager():
         graph.launch(side)
         side.synchronize()
         assert torch.equal(out.view(torch.int16), ref2.view(torch.int16)), "replay on new input %d" % i
+    graph.close()
+    stack.close()
+
+
+def _moe_model():
+    from tests.test_gpu_moe import MOE
+    return MOE
+
+
+def test_moe_stack_equals_chained_layers_and_oracle():
+    """Three Qwen3-MoE-structured layers and the final norm: the stack is
+    bitwise the chain of single-layer forwards plus the norm op; against the
+    oracle's chain, rows whose expert choice differs in some layer (a near
+    tie, validated against that layer's oracle logits) are left out of the
+    output comparison, every other row is compared."""
+    model = _moe_model()
+    layers = 3
+    wl = synth.Workload(52, "moe_stack3_decode_b24", model, 24, 1, (30, 500))
+    batch, hidden, weights, pools, final = _stack_inputs(wl, layers)
+    pools0 = [(k.clone(), v.clone()) for k, v in pools]
+    cfg = model.config_dict()
+    pos, bt, sl = device_batch(batch, DEV)
+    T, B = batch.num_tokens, batch.num_seqs
+    # chained single layers, keeping each layer's routing
+    h, r, gpu_ids = hidden, None, []
+    for l in range(layers):
+        L = lda.Layer(cfg, weights[l])
+        ws = L.alloc_workspace(T, B, batch.max_seq_len)
+        h, r = L.forward(h, r, pos, pools[l][0], pools[l][1], bt, sl, batch.max_seq_len, workspace=ws)
+        torch.cuda.synchronize()
+        gpu_ids.append(L.workspace_tensor(ws, "topk_ids", T, B, batch.max_seq_len).cpu().numpy())
+        L.close()
+    chained, _ = lda.add_rmsnorm(h, r, final, model.rms_norm_eps, write_residual=False)
+    for l in range(layers):  # the stack rewrites the same K/V slots
+        pools[l][0].copy_(pools0[l][0])
+        pools[l][1].copy_(pools0[l][1])
+    stack = lda.Stack(cfg, weights, final)
+    out = stack.forward(hidden, pos, pools, bt, sl, batch.max_seq_len)
+    torch.cuda.synchronize()
+    stack.close()
+    assert torch.equal(out.view(torch.int16), chained.view(torch.int16))
+
+    wn = [oracle_weights(w) for w in weights]
+    seqs = [oracle_seqs(model, batch, k0, v0) for k0, v0 in pools0]
+    posn = batch.positions.numpy().astype(np.int64)
+    k = cfg["num_experts_per_tok"]
+    keep = np.ones(T, dtype=bool)
+    res = {}
+    for mode, rnd in (("exact", None), ("rounded", oracle.bf16_round)):
+        rr = rnd or (lambda x: x)
+        he, re_ = np64(hidden), None
+        for l in range(layers):
+            tr = {}
+            o = oracle.decoder_layer(cfg, wn[l], he, re_, posn, seqs[l], rnd=rnd, trace=tr)
+            logits = tr["router_logits"]
+            tol = 2e-2 * np.sqrt(np.mean(logits * logits))
+            margin = oracle.topk_margin(logits, k)
+            for t in range(T):
+                if set(gpu_ids[l][t]) != set(tr["topk_ids"][t]):
+                    assert margin[t] <= tol, ("clear expert choice differs", l, t, margin[t])
+                    kth = np.sort(logits[t])[::-1][k - 1]
+                    assert all(logits[t, e] >= kth - tol for e in gpu_ids[l][t])
+                    keep[t] = False
+            he, re_ = rr(o["hidden_out"]), rr(o["residual_out"])
+        res[mode], _ = oracle.fused_add_rms_norm(he, re_, np64(final), cfg["rms_norm_eps"], rnd=rr)
+    print("rows compared", int(keep.sum()), "of", T, flush=True)
+    assert keep.sum() >= T // 2
+    s = compare("moe_stack_out", np64(out)[keep], res["exact"][keep], res["rounded"][keep], "bf16",
+                depth=layers + 1)
+    print("moe stack out", s, flush=True)
+
+
+def test_moe_stack_graph_replays_match_eager():
+    model = _moe_model()
+    wl = synth.Workload(53, "moe_stack2_decode_b16", model, 16, 1, (5, 700))
+    batch, hidden, weights, pools, final = _stack_inputs(wl, 2)
+    stack = lda.Stack(model.config_dict(), weights, final)
+    pos, bt, sl = device_batch(batch, DEV)
+    T, B = batch.num_tokens, batch.num_seqs
+    ws = stack.alloc_workspace(T, B, batch.max_seq_len)
+    side = torch.cuda.Stream()
+    out_eager = torch.empty_like(hidden)
+    stack.forward(hidden, pos, pools, bt, sl, batch.max_seq_len, out=out_eager, workspace=ws, stream=side)
+    side.synchronize()
+    out = torch.zeros_like(hidden)
+    graph = stack.capture(hidden, pos, pools, bt, sl, batch.max_seq_len, out, ws, side)
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.launch(side)
+        side.synchronize()
+        assert torch.equal(out.view(torch.int16), out_eager.view(torch.int16)), "replay %d" % i
+        scratch = torch.empty_like(hidden)
+        stack.forward(hidden, pos, pools, bt, sl, batch.max_seq_len, out=scratch, workspace=ws, stream=side)
+        side.synchronize()
+        assert torch.equal(scratch.view(torch.int16), out_eager.view(torch.int16))
     graph.close()
     stack.close()
