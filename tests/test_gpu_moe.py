@@ -125,3 +125,25 @@ def test_moe_prefill_3x1000_chunked_grouping():
     # 12000 pairs: more than 8192, so the grouping by expert runs as count /
     # scan / scatter kernels over chunks of 4096 pairs (the last one ragged)
     run_moe_layer(synth.Workload(207, "moe_prefill_3x1000", MOE, 3, 1000, 0), repeat=True)
+
+
+# 48 experts (not a multiple of 64: the top-k wave leaves lanes 48..63 empty),
+# top-3 without renormalisation, head_dim 64 with 4 query heads per KV head
+MOE48 = synth.ModelShape(512, 8, 2, 64, 1408, 1e-6, 1e7, None, 32768, "bf16",
+                         num_experts=48, num_experts_per_tok=3, moe_intermediate_size=128,
+                         norm_topk_prob=False, qk_norm=True)
+# top-1 (every token's weight is exactly 1 after renormalising), no q/k norm
+MOE1 = synth.ModelShape(512, 8, 2, 64, 1408, 1e-6, 1e7, None, 32768, "bf16",
+                        num_experts=16, num_experts_per_tok=1, moe_intermediate_size=256,
+                        norm_topk_prob=True, qk_norm=False)
+
+
+def test_moe48_top3_unnormalised_decode_and_prefill():
+    run_moe_layer(synth.Workload(208, "moe48_decode_b40", MOE48, 40, 1, (10, 300)))
+    run_moe_layer(synth.Workload(209, "moe48_prefill_2x300", MOE48, 2, 300, (0, 64)))
+
+
+def test_moe_top1_decode_and_prefill():
+    _, _, ids = run_moe_layer(synth.Workload(210, "moe1_decode_b16", MOE1, 16, 1, (10, 300)))
+    assert ids.shape == (16, 1)
+    run_moe_layer(synth.Workload(211, "moe1_prefill_3x100", MOE1, 3, 100, 0))
