@@ -550,6 +550,15 @@ __global__ __launch_bounds__(64 * WM * WN) void moe_tile_kernel(const bf16* __re
     wsrc[j] = We + (size_t)(row & ~15) * K + (size_t)(row & 15) * ws.rs + (size_t)(ch >> 2) * ws.ks + (ch & 3) * 8;
   }
   const size_t wstage = (size_t)(kTBK / 32) * ws.ks;
+  auto issue_w = [&](int buf, int kt) {
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(wsrc[j] + kt * wstage),
+          (__attribute__((address_space(3))) void*)(sW + buf * BN * kTBK + (j * NW + wave) * 8 * kTBK), 16, 0, 0);
+  };
+  // the weights of the first stage need no pair list: on their way first
+  issue_w(0, 0);
   const bf16* xsrc[XJ];
 #pragma unroll
   for (int j = 0; j < XJ; ++j) {
@@ -558,18 +567,29 @@ __global__ __launch_bounds__(64 * WM * WN) void moe_tile_kernel(const bf16* __re
     const int src = EPI == kMoeGateUp ? sorted[r0 + i] / topk : r0 + i;
     xsrc[j] = X + (size_t)src * K + ((pc ^ (row & 7)) << 3);
   }
-  auto issue = [&](int buf, int kt) {
-#pragma unroll
-    for (int j = 0; j < WJ; ++j)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(wsrc[j] + kt * wstage),
-          (__attribute__((address_space(3))) void*)(sW + buf * BN * kTBK + (j * NW + wave) * 8 * kTBK), 16, 0, 0);
+  auto issue_x = [&](int buf, int kt) {
 #pragma unroll
     for (int j = 0; j < XJ; ++j)
       __builtin_amdgcn_global_load_lds(
           (const void*)(xsrc[j] + kt * kTBK),
           (__attribute__((address_space(3))) void*)(sX + buf * BM * kTBK + (j * NW + wave) * 8 * kTBK), 16, 0, 0);
   };
+  issue_x(0, 0);
+
+  // down: the pair row and routing weight of each output row, fetched now so
+  // that the epilogue does not wait out two dependent loads
+  int prow_out[SM];
+  float pwgt[SM];
+#pragma unroll
+  for (int j = 0; j < SM; ++j) {
+    prow_out[j] = 0;
+    pwgt[j] = 0.f;
+    const int m = wm * TM + j * 16 + r16;
+    if (EPI == kMoeDown && m < rows) {
+      prow_out[j] = sorted[r0 + m];
+      pwgt[j] = wts[prow_out[j]];
+    }
+  }
 
   f32x4 acc[SN][SM];
 #pragma unroll
@@ -578,12 +598,14 @@ __global__ __launch_bounds__(64 * WM * WN) void moe_tile_kernel(const bf16* __re
     for (int j = 0; j < SM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / kTBK;
-  issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) issue(buf ^ 1, kt + 1);
+    if (kt + 1 < nk) {
+      issue_w(buf ^ 1, kt + 1);
+      issue_x(buf ^ 1, kt + 1);
+    }
 #pragma unroll
     for (int s = 0; s < kTBK / 32; ++s) {
       const int c = s * 4 + g;
@@ -618,9 +640,8 @@ __global__ __launch_bounds__(64 * WM * WN) void moe_tile_kernel(const bf16* __re
         *reinterpret_cast<bf16x4*>(dst + f) = o;
       }
     } else {
-      const int p = sorted[r0 + m];
-      const float wgt = wts[p];
-      bf16* dst = out + (size_t)p * ldo;
+      const float wgt = pwgt[j];
+      bf16* dst = out + (size_t)prow_out[j] * ldo;
 #pragma unroll
       for (int i = 0; i < SN; ++i) {
         bf16x4 o;
