@@ -169,7 +169,7 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.tiles = take((size_t)w.tile_cap * sizeof(int4));
   const size_t P = L->E ? (size_t)T * L->topk : 0;
   w.moe_tile_cap = L->E ? (int)(P / llk::kMoeTileRows) + L->E + 1 : 0;
-  w.rpart = take(L->E ? (size_t)llk::moe_router_splits(T, H) * T * L->E * sizeof(float) : 0);
+  w.rpart = take(L->E ? (size_t)llk::moe_router_splits(T, H, L->E, L->num_cus) * T * L->E * sizeof(float) : 0);
   w.logits = take((size_t)T * L->E * sizeof(float));
   w.ids = take(P * sizeof(int));
   w.wts = take(P * sizeof(float));

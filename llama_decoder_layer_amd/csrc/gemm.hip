@@ -427,6 +427,19 @@ hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, 
   }
 }
 
+hipError_t launch_gemm_partials(const void* x, const void* w, int M, int wrows, int K, int layout, float* out,
+                                hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (wrows % 128 || K % kTBK) return hipErrorInvalidValue;
+  const TilePlan tp = tile_plan(M, wrows, K, device_cu_count());
+  const WStride ws = weight_stride(layout, K);
+  if (tp.big)
+    return launch_tile<256, 256, 2, 4, kEpiPartial>((const bf16*)x, M, (const bf16*)w, wrows, K, ws, out, wrows, s,
+                                                    tp.splits);
+  return launch_tile<128, 128, 2, 2, kEpiPartial>((const bf16*)x, M, (const bf16*)w, wrows, K, ws, out, wrows, s,
+                                                  tp.splits);
+}
+
 hipError_t launch_silu_reduce(const float* part, int S, int M, int wrows, void* out, hipStream_t s) {
   const size_t quads = (size_t)M * (wrows / 2) / 4;
   if (quads == 0) return hipSuccess;

@@ -49,6 +49,11 @@ struct TilePlan {
 };
 TilePlan tile_plan(int M, int wrows, int K, int num_cus);
 hipError_t launch_reorder_gate_up(const void* src, int inter, int K, void* dst, hipStream_t s);
+// fp32 partial products [tile_plan(M, wrows, K).splits][M][wrows] of x W^T on
+// the tiled kernel (bf16 x and W, wrows % 128 == 0, K % 64 == 0), for a
+// consumer that sums the planes in order.
+hipError_t launch_gemm_partials(const void* x, const void* w, int M, int wrows, int K, int layout, float* out,
+                                hipStream_t s);
 // out [M, wrows/2] bf16 = SiluAndMul of the sum of S fp32 partial planes
 // [S][M][wrows] of a re-ordered gate_up projection (split-K).
 hipError_t launch_silu_reduce(const float* part, int S, int M, int wrows, void* out, hipStream_t s);
@@ -159,9 +164,14 @@ struct MoeRouting {
 };
 int moe_align_chunks(int P);  // 0: the grouping runs in one workgroup
 bool moe_streaming(int T);
-int moe_router_splits(int T, int H);
+// K ranges of the router: many tokens with E % 128 == 0 run the router on the
+// tiled GEMM (its split-K plan), otherwise on moe_router_kernel
+int moe_router_splits(int T, int H, int E, int num_cus);
 hipError_t launch_moe_route(const void* x, int T, int H, const void* router, int E, int topk, bool norm,
                             float* part, float* logits, int* ids, float* wts, hipStream_t s);
+// top-k of each token from S partial logit planes [S][T][E] (summed in order)
+hipError_t launch_moe_topk(const float* part, int S, int T, int E, int topk, bool norm, float* logits, int* ids,
+                           float* wts, hipStream_t s);
 hipError_t launch_moe_align(const int* ids, int P, int E, int bm, const MoeRouting& r, hipStream_t s);
 hipError_t launch_moe_experts(const void* x, int T, int H, int topk, const void* w13, const void* w2, int E, int I,
                               int layout, const MoeRouting& r, void* act, void* part, hipStream_t s,

@@ -724,7 +724,12 @@ hipError_t launch_moe_stream(const bf16* x, int topk, const bf16* w, int wrows, 
 
 bool moe_streaming(int T) { return T <= kSkinnyMaxM; }
 
-int moe_router_splits(int T, int H) {
+namespace {
+bool router_on_gemm(int T, int E) { return T > kSkinnyMaxM && E % 128 == 0; }
+}  // namespace
+
+int moe_router_splits(int T, int H, int E, int num_cus) {
+  if (router_on_gemm(T, E)) return tile_plan(T, E, H, num_cus).splits;
   // about 1024 single-wave workgroups; each K range a multiple of 64
   const int tiles = (T + 15) / 16;
   int S = 1;
@@ -736,7 +741,13 @@ hipError_t launch_moe_route(const void* x, int T, int H, const void* router, int
                             float* part, float* logits, int* ids, float* wts, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (E <= 0 || E > 256 || E % 16 || H % 64 || topk < 1 || topk > 64 || topk > E) return hipErrorInvalidValue;
-  const int S = moe_router_splits(T, H);
+  const int S = moe_router_splits(T, H, E, device_cu_count());
+  hipError_t e = hipSuccess;
+  if (router_on_gemm(T, E)) {
+    e = launch_gemm_partials(x, router, T, E, H, kRowMajor, part, s);
+    if (e != hipSuccess) return e;
+    return launch_moe_topk(part, S, T, E, topk, norm, logits, ids, wts, s);
+  }
   const dim3 grid((T + 15) / 16, S);
   const bf16* xb = (const bf16*)x;
   const bf16* wb = (const bf16*)router;
@@ -749,8 +760,13 @@ hipError_t launch_moe_route(const void* x, int T, int H, const void* router, int
     LLK_ROUTER_CASE(16)
 #undef LLK_ROUTER_CASE
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_moe_topk(part, S, T, E, topk, norm, logits, ids, wts, s);
+}
+
+hipError_t launch_moe_topk(const float* part, int S, int T, int E, int topk, bool norm, float* logits, int* ids,
+                           float* wts, hipStream_t s) {
   const unsigned blocks = (unsigned)((T + 3) / 4);
   const int epl = (E + 63) / 64;
   const int nm = norm ? 1 : 0;

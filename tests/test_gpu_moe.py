@@ -147,3 +147,15 @@ def test_moe_top1_decode_and_prefill():
     _, _, ids = run_moe_layer(synth.Workload(210, "moe1_decode_b16", MOE1, 16, 1, (10, 300)))
     assert ids.shape == (16, 1)
     run_moe_layer(synth.Workload(211, "moe1_prefill_3x100", MOE1, 3, 100, 0))
+
+
+# 128 experts with more than 128 tokens: the router runs on the tiled GEMM
+# (split-K fp32 partials summed by the top-k kernel)
+MOE128 = synth.ModelShape(512, 8, 1, 128, 1408, 1e-6, 1e7, None, 32768, "bf16",
+                          num_experts=128, num_experts_per_tok=8, moe_intermediate_size=128,
+                          norm_topk_prob=True, qk_norm=True)
+
+
+def test_moe128_router_on_gemm_prefill():
+    run_moe_layer(synth.Workload(212, "moe128_prefill_2x150", MOE128, 2, 150, (0, 40)))
+    run_moe_layer(synth.Workload(213, "moe128_decode_b20", MOE128, 20, 1, (10, 200)))
