@@ -332,6 +332,16 @@ __global__ void reorder_gate_up_kernel(const bf16* __restrict__ src, int inter, 
   for (int c = threadIdx.x; c < K / 8; c += blockDim.x) d[c] = s[c];
 }
 
+// The tile shape a plan names: 256 or 192 token rows x 256 weight rows (8
+// waves), or 128 x 128 (4 waves).
+template <int EPI>
+hipError_t launch_planned(const TilePlan& tp, const bf16* x, int M, const bf16* w, int wrows, int K, WStride ws,
+                          void* out, int ldo, hipStream_t s, int splits) {
+  if (tp.bm == 256) return launch_tile<256, 256, 2, 4, EPI>(x, M, w, wrows, K, ws, out, ldo, s, splits);
+  if (tp.bm == 192) return launch_tile<192, 256, 2, 4, EPI>(x, M, w, wrows, K, ws, out, ldo, s, splits);
+  return launch_tile<128, 128, 2, 2, EPI>(x, M, w, wrows, K, ws, out, ldo, s, splits);
+}
+
 template <int EPI>
 hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* out, hipStream_t s, int layout,
                        float* part, size_t part_cap) {
@@ -342,15 +352,13 @@ hipError_t linear_bf16(const bf16* x, const bf16* w, int M, int N, int K, bf16* 
   const WStride ws = weight_stride(layout, K);
   const TilePlan tp = tile_plan(M, wrows, K, device_cu_count());
   if (tp.splits > 1 && part && tp.partial_bytes <= part_cap) {
-    hipError_t e = tp.big ? launch_tile<256, 256, 2, 4, kEpiPartial>(x, M, w, wrows, K, ws, part, wrows, s, tp.splits)
-                          : launch_tile<128, 128, 2, 2, kEpiPartial>(x, M, w, wrows, K, ws, part, wrows, s, tp.splits);
+    hipError_t e = launch_planned<kEpiPartial>(tp, x, M, w, wrows, K, ws, part, wrows, s, tp.splits);
     if (e != hipSuccess) return e;
     const size_t quads = (size_t)M * N / 4;
     tile_reduce_kernel<EPI><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(part, tp.splits, M, wrows, N, out);
     return hipGetLastError();
   }
-  if (tp.big) return launch_tile<256, 256, 2, 4, EPI>(x, M, w, wrows, K, ws, out, N, s);
-  return launch_tile<128, 128, 2, 2, EPI>(x, M, w, wrows, K, ws, out, N, s);
+  return launch_planned<EPI>(tp, x, M, w, wrows, K, ws, out, N, s, 1);
 }
 
 // one thread per 16-byte piece of the destination
@@ -378,9 +386,18 @@ hipError_t linear_f32(const float* x, const float* w, int M, int N, int K, float
 
 TilePlan tile_plan(int M, int wrows, int K, int num_cus) {
   TilePlan p;
-  p.big = M >= 256 && wrows % 256 == 0;
-  const int bm = p.big ? 256 : 128;
-  const int tiles = ((M + bm - 1) / bm) * (wrows / bm);
+  // 256-row weight tiles need wrows % 256 == 0.  Token tiles of 256 rows,
+  // or of 192 when those pad M by more than a ninth less (e.g. 544 tokens:
+  // 3 x 192 = 576 rows computed instead of 3 x 256 = 768); fewer than 256
+  // tokens take 128 x 128.
+  const bool wide = M >= 256 && wrows % 256 == 0;
+  p.bm = 128;
+  if (wide) {
+    const int pad256 = (M + 255) / 256 * 256, pad192 = (M + 191) / 192 * 192;
+    p.bm = pad256 * 9 <= pad192 * 10 ? 256 : 192;
+  }
+  const int bn = wide ? 256 : 128;
+  const int tiles = ((M + p.bm - 1) / p.bm) * (wrows / bn);
   const int cus = num_cus > 0 ? num_cus : 256;
   p.splits = 1;
   for (int s = 2; s <= 8 && tiles * p.splits < cus && K % (s * kTBK) == 0; s *= 2) p.splits = s;
@@ -433,11 +450,7 @@ hipError_t launch_gemm_partials(const void* x, const void* w, int M, int wrows, 
   if (wrows % 128 || K % kTBK) return hipErrorInvalidValue;
   const TilePlan tp = tile_plan(M, wrows, K, device_cu_count());
   const WStride ws = weight_stride(layout, K);
-  if (tp.big)
-    return launch_tile<256, 256, 2, 4, kEpiPartial>((const bf16*)x, M, (const bf16*)w, wrows, K, ws, out, wrows, s,
-                                                    tp.splits);
-  return launch_tile<128, 128, 2, 2, kEpiPartial>((const bf16*)x, M, (const bf16*)w, wrows, K, ws, out, wrows, s,
-                                                  tp.splits);
+  return launch_planned<kEpiPartial>(tp, (const bf16*)x, M, (const bf16*)w, wrows, K, ws, out, wrows, s, tp.splits);
 }
 
 hipError_t launch_silu_reduce(const float* part, int S, int M, int wrows, void* out, hipStream_t s) {

@@ -39,11 +39,12 @@ inline WStride weight_stride(int layout, int K) { return layout == kTiled16x32 ?
 hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, int K, int epi,
                          void* out, hipStream_t s, int layout = kRowMajor, float* part = nullptr,
                          size_t part_cap = 0);
-// Tiled-kernel plan for M > kSkinnyMaxM: 256 x 256 tiles from 256 tokens on
-// (else 128 x 128), and K split in 2, 4 or 8 while the tiles alone number
-// fewer than the CUs.
+// Tiled-kernel plan for M > kSkinnyMaxM: bm token rows x 256 weight rows
+// (bm = 256, or 192 where that pads M less; 128 x 128 tiles for few tokens or
+// weight rows not a multiple of 256), and K split in 2, 4 or 8 while the
+// tiles alone number fewer than the CUs.
 struct TilePlan {
-  bool big;
+  int bm;
   int splits;
   size_t partial_bytes;  // fp32 partials the split needs (0 unsplit)
 };

@@ -17,7 +17,8 @@ def _randn(shape, seed, dtype=torch.bfloat16, std=1.0, mean=0.0):
     return (torch.randn(shape, generator=g) * std + mean).to(dtype).to(DEV)
 
 
-@pytest.mark.parametrize("M", [1, 7, 16, 32, 33, 64, 65, 128, 300])
+# 300 and 544 tokens take 192-row token tiles (less padding than 256)
+@pytest.mark.parametrize("M", [1, 7, 16, 32, 33, 64, 65, 128, 300, 544, 1024])
 @pytest.mark.parametrize("N,K", [(256, 512), (1536, 1024)])
 def test_linear_store(M, N, K):
     print("linear_store", M, N, K, flush=True)
@@ -29,7 +30,7 @@ def test_linear_store(M, N, K):
     compare("linear", np64(y), ref, dtype="bf16")
 
 
-@pytest.mark.parametrize("M", [5, 32, 64, 100, 200])
+@pytest.mark.parametrize("M", [5, 32, 64, 100, 200, 544])
 def test_linear_add(M):
     print("linear_add", M, flush=True)
     N, K = 1024, 768
@@ -43,7 +44,7 @@ def test_linear_add(M):
     compare("linear_add", np64(out), exact, dtype="bf16")
 
 
-@pytest.mark.parametrize("M", [3, 32, 64, 100, 129])
+@pytest.mark.parametrize("M", [3, 32, 64, 100, 129, 300])
 def test_linear_silu_mul(M):
     print("linear_silu", M, flush=True)
     I, K = 384, 512
