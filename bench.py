@@ -30,6 +30,12 @@ METRIC = "70B-shape layer tokens/s (prefill, decode) + % MFMA/HBM peak, 1 MI355X
 # x 1.0 (factors from a plain 1 GiB copy; profiles/pmc_copy_calibration.md).  Reported only while
 # the kernel's source file is the one the counters were taken on.
 COUNTER_TRAFFIC = {
+    ("llama70b_prefill_4x2048", "gate_up_silu"): {
+        "bytes": 11743957635,
+        "source": "llama_decoder_layer_amd/csrc/gemm.hip",
+        "sha1": "b59e6a8385c5f8d8efa36a66f0e1b400cd7d33af",
+        "summary": "profiles/gate_up_silu_prefill_4x2048_counters.md",
+    },
     ("qwen3moe_decode_b32_ctx2048", "moe_gate_up_silu"): {
         "bytes": 703180197,
         "source": "llama_decoder_layer_amd/csrc/moe.hip",
@@ -164,8 +170,11 @@ def measure(wl, steps, warmup):
         if model.num_experts:
             alg = 2 * T * model.num_experts_per_tok * H * 2 * model.moe_intermediate_size
         roof = {"bound": "mfma", "kernel": dom, "achieved": alg / dur / 1e12, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": alg / dur / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": alg / dur / 1e12 / PEAK_BF16_TFLOPS,
+                "traffic": counter_traffic(wl.name, dom),
                 "algorithmic_flops_per_launch": alg, "avg_launch_us": dur * 1e6}
+        if roof["traffic"] is not None and not model.num_experts:  # HBM bytes a launch must move at least
+            roof["algorithmic_bytes_per_launch"] = kernel_bytes(model, dom, T, kv_tokens)
     wbytes = sum(v.numel() * v.element_size() for k, v in per_layer[0]["weights"].items()
                  if not k.startswith("experts_"))
     if model.num_experts:  # only the routed-to experts' weights are read
