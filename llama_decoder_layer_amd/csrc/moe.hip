@@ -11,11 +11,14 @@
 // when norm_topk_prob is set.
 //
 // Kernels, in launch order:
-//   moe_router_kernel  logits [T, E] fp32 = x Wr^T on MFMA (one wave per 16
-//                      tokens x all experts and one of S K ranges);
-//   moe_topk_kernel    one wave per token: softmax statistics, each expert's
-//                      rank among the token's logits (ties: lower expert),
-//                      the k best written in rank order, renormalisation;
+//   router             logits [T, E] fp32 = x Wr^T as S fp32 partial planes:
+//                      moe_router_kernel (one wave per 16 tokens x all
+//                      experts x one of S K ranges) for few tokens, the
+//                      tiled GEMM's split-K partials for many;
+//   moe_topk_kernel    one wave per token: the S planes summed in order,
+//                      softmax statistics, each expert's rank among the
+//                      token's logits (ties: lower expert), the k best
+//                      written in rank order, renormalisation;
 //                      ids [T*k] and weights [T*k], pair p = t*k + slot;
 //   moe_align_kernel   per-expert counts, the pairs grouped by expert
 //                      ("sorted" positions), the active-expert list and a
