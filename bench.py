@@ -37,9 +37,9 @@ COUNTER_TRAFFIC = {
         "summary": "profiles/gate_up_silu_prefill_4x2048_counters.md",
     },
     ("qwen3moe_decode_b32_ctx2048", "moe_gate_up_silu"): {
-        "bytes": 703180197,
+        "bytes": 703212909,
         "source": "llama_decoder_layer_amd/csrc/moe.hip",
-        "sha1": "c162e31148aed826d4c9b75818f09262a588d47c",
+        "sha1": "755722e27b7a0844d60c7110d6ebca39ad3481fe",
         "summary": "profiles/moe_gate_up_silu_qwen3moe_decode_b32_ctx2048.md",
     },
     ("llama70b_decode_b32_ctx2048", "gate_up_silu"): {
