@@ -100,7 +100,7 @@ struct llama_layer {
 namespace {
 
 struct Workspace {
-  size_t h, qkv, attn, h2, act, part, gpart, tpart, tpart_bytes, seq_of, ntiles, tiles, total;
+  size_t h, qkv, attn, h2, act, part, gpart, tpart, tpart_bytes, seq_of, ntiles, tiles, dec, ndec, row_parts, total;
   int tile_cap;  // entries of the prefill tile table (mixed batches)
   // MoE routing and expert buffers (P = T * topk pairs)
   size_t rpart, logits, ids, wts, seg, sorted, active, nactive, mtiles, mntiles, mchunk, mact, mpart;
@@ -110,11 +110,18 @@ struct Workspace {
   llk::SkinnyPlan pq, po, pg, pd;
 };
 
+// prefill attention runs on the matrix-core kernel (whose keys may be split)
+bool split_prefill(const llama_layer* L) {
+  const llama_layer_config& c = L->cfg;
+  return L->dtype == LLAMA_DTYPE_BF16 &&
+         llk::prefill_attention_supported(c.num_attention_heads, c.num_key_value_heads, c.head_dim);
+}
+
 Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   const llama_layer_config& c = L->cfg;
   Workspace w{};
-  w.plan = llk::attention_plan(T, c.num_attention_heads, c.num_key_value_heads, c.head_dim, T == B, max_seq_len,
-                              L->num_cus);
+  w.plan = llk::attention_plan(T, B, c.num_attention_heads, c.num_key_value_heads, c.head_dim, T == B,
+                              max_seq_len, L->num_cus, split_prefill(L));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -167,6 +174,11 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.seq_of = take((size_t)T * sizeof(int));
   w.ntiles = take(sizeof(int));
   w.tiles = take((size_t)w.tile_cap * sizeof(int4));
+  // the rows of single-row sequences (decode attention) and the key
+  // partitions of each row when prefill attention is split
+  w.dec = take((size_t)B * sizeof(int));
+  w.ndec = take(sizeof(int));
+  w.row_parts = take((size_t)T * sizeof(int));
   const size_t P = L->E ? (size_t)T * L->topk : 0;
   w.moe_tile_cap = L->E ? (int)(P / llk::kMoeTileRows) + L->E + 1 : 0;
   w.rpart = take(L->E ? (size_t)llk::moe_router_splits(T, H, L->E, L->num_cus) * T * L->E * sizeof(float) : 0);
@@ -543,8 +555,17 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
     map.tiles = (const int4*)(ws + w.tiles);
     map.ntiles = (const int*)(ws + w.ntiles);
     map.tile_cap = T / qw + B;
+    // with the matrix-core prefill kernel, sequences of one query row go to
+    // the decode kernel instead of a 1-row query tile
+    int* dec = nullptr;
+    if (split_prefill(L)) {
+      dec = (int*)(ws + w.dec);
+      map.dec = dec;
+      map.ndec = (const int*)(ws + w.ndec);
+      map.dec_cap = B;
+    }
     e = llk::launch_batch_map(query_start_loc, B, T, qw, (int*)(ws + w.seq_of), (int4*)(ws + w.tiles),
-                              w.tile_cap, (int*)(ws + w.ntiles), s);
+                              w.tile_cap, (int*)(ws + w.ntiles), dec, dec ? (int*)(ws + w.ndec) : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "batch_map");
     mk.mark("batch_map");
   }
@@ -576,7 +597,7 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   mk.mark("rope_kv_write");
   hipEvent_t mid = w.plan.parts > 1 ? mk.extra() : nullptr;
   e = llk::launch_attention(dt, qkv, L->qkv_n, T, positions, nq, nkv, d, kv->k, kv->v, block_table, max_blocks,
-                            map, decode, w.plan, part, attn, s, mid);
+                            map, decode, w.plan, part, (int*)(ws + w.row_parts), attn, s, mid);
   if (e != hipSuccess) return hip_fail(e, "attention");
   if (mid) mk.list->push_back({"attention", mid});
   mk.mark(w.plan.parts > 1 ? "attention_combine" : "attention");

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(
 
   const int out_per_thread = (G * D + kThreads - 1) / kThreads;  // <= 8 (G<=16, D<=128)
   if (k_begin >= k_end) {  // empty partition: only its max (-inf) is read
-    if (tid < G) partials[(((size_t)t * nq + g * G + tid) * parts + part) * (D + 2)] = -INFINITY;
+    if (tid < G) partials[(((size_t)t * nq + g * G + tid) * parts + part) * (D + kPartHead)] = -INFINITY;
     return;
   }
 
@@ -162,34 +162,60 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(
       if (parts == 1) {
         out[(size_t)t * nq * D + (size_t)qh * D + e] = from_f32<T>(acc[j] / s_l[h]);
       } else {
-        float* dst = partials + (((size_t)t * nq + qh) * parts + part) * (D + 2);
+        float* dst = partials + (((size_t)t * nq + qh) * parts + part) * (D + kPartHead);
         if (e == 0) {
           dst[0] = s_m[h];
           dst[1] = s_l[h];
         }
-        dst[2 + e] = acc[j];
+        dst[kPartHead + e] = acc[j];
       }
     }
   }
 }
 
+// Merges the key partitions of each (row, query head) with their
+// log-sum-exp weights, in partition order (deterministic).  One thread per 4
+// output components; grid (rows, ceil(heads * D / 4 / kCombineThreads)).
+// With row_parts, row t has row_parts[t] partitions; a row of one was
+// written by the attention kernel itself.
+constexpr int kCombineThreads = 256;
 template <typename T, int D>
-__global__ __launch_bounds__(D) void attention_combine_kernel(const float* __restrict__ partials, int nq,
-                                                              int parts, T* __restrict__ out) {
-  const int t = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
-  const float* src = partials + ((size_t)t * nq + h) * parts * (D + 2);
+__global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(const float* __restrict__ partials,
+                                                                            int nq, int parts,
+                                                                            const int* __restrict__ row_parts,
+                                                                            T* __restrict__ out) {
+  constexpr int R = D + kPartHead;  // floats per partition record
+  const int t = blockIdx.x;
+  int np = parts;
+  if (row_parts) {
+    np = min(row_parts[t], parts);
+    if (np <= 1) return;
+  }
+  const int i = blockIdx.y * kCombineThreads + threadIdx.x;
+  if (i >= nq * (D / 4)) return;
+  const int h = i / (D / 4), e = (i % (D / 4)) * 4;
+  const float* src = partials + ((size_t)t * nq + h) * parts * R;
   float M = -INFINITY;
-  for (int i = 0; i < parts; ++i) M = fmaxf(M, src[(size_t)i * (D + 2)]);
-  float L = 0.f, o = 0.f;
-  for (int i = 0; i < parts; ++i) {
-    const float* pp = src + (size_t)i * (D + 2);
+  for (int k = 0; k < np; ++k) M = fmaxf(M, src[(size_t)k * R]);
+  float L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < np; ++k) {
+    const float* pp = src + (size_t)k * R;
     const float m = pp[0];
     if (m == -INFINITY) continue;
     const float w = exp2f(m - M);
     L = fmaf(pp[1], w, L);
-    o = fmaf(pp[2 + e], w, o);
+    const float4 v = *reinterpret_cast<const float4*>(pp + kPartHead + e);
+    o.x = fmaf(v.x, w, o.x);
+    o.y = fmaf(v.y, w, o.y);
+    o.z = fmaf(v.z, w, o.z);
+    o.w = fmaf(v.w, w, o.w);
   }
-  out[(size_t)t * nq * D + (size_t)h * D + e] = from_f32<T>(o / L);
+  T* dst = out + ((size_t)t * nq + h) * D + e;
+  dst[0] = from_f32<T>(o.x / L);
+  dst[1] = from_f32<T>(o.y / L);
+  dst[2] = from_f32<T>(o.z / L);
+  dst[3] = from_f32<T>(o.w / L);
 }
 
 template <typename T, int D>
@@ -204,55 +230,112 @@ hipError_t attention_typed(const T* q, int ldq, int T_, const int* positions, in
 }
 
 template <typename T>
-hipError_t combine(int d, int T_, int nq, int parts, const float* partials, void* out, hipStream_t s) {
-  if (d == 128) attention_combine_kernel<T, 128><<<dim3(T_, nq), 128, 0, s>>>(partials, nq, parts, (T*)out);
-  else attention_combine_kernel<T, 64><<<dim3(T_, nq), 64, 0, s>>>(partials, nq, parts, (T*)out);
+hipError_t combine(int d, int T_, int nq, int parts, const float* partials, const int* row_parts, void* out,
+                   hipStream_t s) {
+  const int per_row = (nq * d / 4 + kCombineThreads - 1) / kCombineThreads;
+  if (d == 128)
+    attention_combine_kernel<T, 128><<<dim3(T_, per_row), kCombineThreads, 0, s>>>(partials, nq, parts, row_parts,
+                                                                                   (T*)out);
+  else
+    attention_combine_kernel<T, 64><<<dim3(T_, per_row), kCombineThreads, 0, s>>>(partials, nq, parts, row_parts,
+                                                                                  (T*)out);
   return hipGetLastError();
 }
 
 }  // namespace
 
-AttnPlan attention_plan(int T, int nq, int nkv, int d, bool decode, int max_seq_len, int num_cus) {
+namespace {
+
+// decode rows: long-running workgroups stream best, so the keys of a (row,
+// KV head) are split only as far as needed to give every compute unit a
+// workgroup, and no partition is longer than kMaxDecodePart keys so that one
+// long sequence in a ragged batch does not leave a single workgroup
+// streaming long after the rest have finished; partitions are multiples of
+// 64 keys (four waves x 16-slot blocks)
+int decode_part_len(long long groups, int max_seq_len, int cus) {
+  constexpr int kMaxDecodePart = 4096;
+  const long long want = (cus + groups - 1) / groups;
+  int len = (int)((max_seq_len + want - 1) / want);
+  len = (len + 63) / 64 * 64;
+  if (len > kMaxDecodePart) len = kMaxDecodePart;
+  return len < 64 ? 64 : len;
+}
+
+}  // namespace
+
+AttnPlan attention_plan(int T, int B, int nq, int nkv, int d, bool decode, int max_seq_len, int num_cus,
+                        bool split_prefill) {
   AttnPlan pl;
+  pl.tpp = 0;
+  pl.part_len = max_seq_len;
+  pl.parts = 1;
+  const int cus = num_cus > 0 ? num_cus : 256;
   if (decode) {
-    // decode: long-running workgroups stream best, so the keys of a
-    // (sequence, KV head) are split only as far as needed to give every
-    // compute unit a workgroup, and no partition is longer than
-    // kMaxDecodePart keys so that one long sequence in a ragged batch does
-    // not leave a single workgroup streaming long after the rest have
-    // finished; partitions are multiples of 64 keys (four waves x 16-slot
-    // blocks)
-    constexpr int kMaxDecodePart = 4096;
-    const int groups = T * nkv;
-    const int cus = num_cus > 0 ? num_cus : 256;
-    const int want = (cus + groups - 1) / groups;
-    int len = (max_seq_len + want - 1) / want;
-    len = (len + 63) / 64 * 64;
-    if (len > kMaxDecodePart) len = kMaxDecodePart;
-    pl.part_len = len < 64 ? 64 : len;
+    pl.part_len = decode_part_len((long long)T * nkv, max_seq_len, cus);
     pl.parts = (max_seq_len + pl.part_len - 1) / pl.part_len;
-  } else {
-    pl.part_len = max_seq_len;
-    pl.parts = 1;
+  } else if (split_prefill) {
+    // prefill on the matrix-core kernel: one workgroup per (query tile, KV
+    // head) walks the tile's whole key range, and the kernel's register use
+    // lets one workgroup run per CU.  A batch whose query tiles cannot fill
+    // the CUs once (a short chunk on a long context, a mixed batch) would
+    // leave CUs idle while a few workgroups walk thousands of keys: its keys
+    // are split into partitions of whole 64-key tiles, about two workgroups
+    // per CU (two rounds balance the unequal causal lengths better than
+    // one), none shorter than kMinPrefillPart keys since each split row
+    // costs partials written and read back.  ceil(T / tile rows) counts the
+    // query tiles as if the batch were one sequence.
+    constexpr int kMinPrefillPart = 512, kMaxPrefillParts = 8;
+    const int qw = prefill_tile_rows(nq, nkv, d);
+    const long long tiles = (long long)((T + qw - 1) / qw) * nkv;
+    if (tiles < cus) {
+      long long want = (2LL * cus + tiles - 1) / tiles;
+      if (want > kMaxPrefillParts) want = kMaxPrefillParts;
+      int len = (int)((max_seq_len + want - 1) / want);
+      len = (len + 63) / 64 * 64;
+      if (len < kMinPrefillPart) len = kMinPrefillPart;
+      const int parts = (max_seq_len + len - 1) / len;
+      if (parts > 1) {
+        pl.tpp = len / 64;
+        pl.parts = parts;
+        // the single-row sequences of a mixed batch (at most B) on the
+        // decode kernel: the decode rule, but never more partitions than
+        // the prefill tiles have (the partials hold `parts` per row)
+        const int dl = decode_part_len((long long)B * nkv, max_seq_len, cus);
+        pl.part_len = dl > len ? dl : len;
+      }
+    }
   }
-  if (pl.parts < 1) pl.parts = 1;
-  pl.ws_bytes = pl.parts > 1 ? (size_t)T * nq * pl.parts * (d + 2) * sizeof(float) : 0;
+  pl.ws_bytes = pl.parts > 1 ? (size_t)T * nq * pl.parts * (d + kPartHead) * sizeof(float) : 0;
   return pl;
 }
 
 hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
                             int nkv, int d, const void* k_cache, const void* v_cache,
                             const int* block_table, int max_blocks, const SeqMap& map, bool decode,
-                            const AttnPlan& plan, float* partials, void* out, hipStream_t s, hipEvent_t mid_event) {
+                            const AttnPlan& plan, float* partials, int* row_parts, void* out, hipStream_t s,
+                            hipEvent_t mid_event) {
   if (T <= 0) return hipSuccess;
   hipError_t e;
+  int* rp = nullptr;  // per-row partition counts for the combine
   if (dtype == kBF16 && decode) {
     // one query row per sequence: row t is sequence t
     e = launch_decode_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table,
                                      max_blocks, plan.part_len, plan.parts, partials, out, s);
-  } else if (dtype == kBF16 && plan.parts == 1 && prefill_attention_supported(nq, nkv, d)) {
-    return launch_prefill_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table,
-                                         max_blocks, map, out, s);
+  } else if (dtype == kBF16 && prefill_attention_supported(nq, nkv, d)) {
+    // the single-row sequences of a mixed batch on the decode kernel, the
+    // query tiles on the prefill kernel; with parts > 1 both record each
+    // row's partition count for the combine
+    if (plan.parts > 1) {
+      if (!row_parts || !partials) return hipErrorInvalidValue;
+      rp = row_parts;
+    }
+    if (map.dec) {
+      e = launch_decode_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table,
+                                       max_blocks, plan.part_len, plan.parts, partials, out, s, &map, rp);
+      if (e != hipSuccess) return e;
+    }
+    e = launch_prefill_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table, max_blocks,
+                                      map, out, s, plan.tpp, plan.parts, partials, rp);
   } else if (dtype == kBF16) {
     e = d == 128 ? attention_typed<bf16, 128>((const bf16*)q, ldq, T, positions, nq, nkv, (const bf16*)k_cache,
                                               (const bf16*)v_cache, block_table, max_blocks, map, plan,
@@ -273,8 +356,8 @@ hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int*
     e = hipEventRecord(mid_event, s);
     if (e != hipSuccess) return e;
   }
-  return dtype == kBF16 ? combine<bf16>(d, T, nq, plan.parts, partials, out, s)
-                        : combine<float>(d, T, nq, plan.parts, partials, out, s);
+  return dtype == kBF16 ? combine<bf16>(d, T, nq, plan.parts, partials, rp, out, s)
+                        : combine<float>(d, T, nq, plan.parts, partials, rp, out, s);
 }
 
 }  // namespace llk

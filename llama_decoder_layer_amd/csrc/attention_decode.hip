@@ -28,7 +28,8 @@
 // (including the unwritten tail of the last block) are masked in both S and
 // V, so stale or poisoned cache contents never reach the output.
 // With several partitions each workgroup leaves (max, sum, unnormalised o)
-// for the combine kernel in attention.hip.
+// for the combine kernel in attention.hip.  In a mixed batch the kernel
+// serves the sequences with a single query row from a list of their rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -50,24 +51,38 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
     const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
     const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
     int max_blocks, int part_len, int parts, float* __restrict__ partials,
-    bf16* __restrict__ out) {
+    bf16* __restrict__ out, const int* __restrict__ dec, const int* __restrict__ ndec,
+    const int* __restrict__ seq_of, int* __restrict__ row_parts) {
   constexpr int KS = D / 32;  // k-steps of S = K q^T
   constexpr int DT = D / 16;  // 16-wide output tiles of P V
   const int G = nq / nkv;
-  const int g = blockIdx.x % nkv, t = blockIdx.x / nkv, part = blockIdx.y;
+  const int g = blockIdx.x % nkv, part = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
+  int t, b;
+  if (dec) {  // the single-row sequences of a mixed batch
+    const int i = blockIdx.x / nkv;
+    if (i >= *ndec) return;
+    t = dec[i];
+    b = seq_of[t];
+  } else {    // one query row per sequence
+    t = blockIdx.x / nkv;
+    b = t;
+  }
   const int p = positions[t];
-  const int b = t;  // one query row per sequence
   const int k_begin = part * part_len;
   const int k_end = min(p + 1, k_begin + part_len);
 
   if (k_begin >= k_end) {  // empty partition: only its max (-inf) is read
-    if (threadIdx.x < G)
-      partials[(((size_t)t * nq + g * G + threadIdx.x) * parts + part) * (D + 2)] = -INFINITY;
+    if (!row_parts && threadIdx.x < G)
+      partials[(((size_t)t * nq + g * G + threadIdx.x) * parts + part) * (D + kPartHead)] = -INFINITY;
     return;
   }
+  // partitions that hold keys of this row; with row_parts a row of one
+  // partition is final here and the combine skips it
+  const int np = row_parts ? min(p / part_len + 1, parts) : parts;
+  if (row_parts && part == 0 && g == 0 && threadIdx.x == 0) row_parts[t] = np;
 
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
@@ -190,15 +205,15 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
       O = fmaf(s_o[w][h][e], f, O);
     }
     const int qh = g * G + h;
-    if (parts == 1) {
+    if (np == 1) {
       out[(size_t)t * nq * D + (size_t)qh * D + e] = static_cast<bf16>(O / L);
     } else {
-      float* dst = partials + (((size_t)t * nq + qh) * parts + part) * (D + 2);
+      float* dst = partials + (((size_t)t * nq + qh) * parts + part) * (D + kPartHead);
       if (e == 0) {
         dst[0] = M;
         dst[1] = L;
       }
-      dst[2 + e] = O;
+      dst[kPartHead + e] = O;
     }
   }
 }
@@ -206,11 +221,14 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
 template <int D>
 hipError_t launch_dec(const void* q, int ldq, int T, const int* positions, int nq, int nkv, const void* k_cache,
                       const void* v_cache, const int* block_table, int max_blocks, int part_len,
-                      int parts, float* partials, void* out, hipStream_t s) {
-  dim3 grid(T * nkv, parts);
+                      int parts, float* partials, void* out, hipStream_t s, const SeqMap* map, int* row_parts) {
+  const int rows = map ? map->dec_cap : T;
+  if (rows <= 0) return hipSuccess;
+  dim3 grid(rows * nkv, parts);
   decode_attention_mfma<D><<<grid, kWaves * kWave, 0, s>>>(
       (const bf16*)q, ldq, positions, nq, nkv, (const bf16*)k_cache, (const bf16*)v_cache, block_table,
-      max_blocks, part_len, parts, partials, (bf16*)out);
+      max_blocks, part_len, parts, partials, (bf16*)out, map ? map->dec : nullptr, map ? map->ndec : nullptr,
+      map ? map->seq_of : nullptr, row_parts);
   return hipGetLastError();
 }
 
@@ -219,12 +237,13 @@ hipError_t launch_dec(const void* q, int ldq, int T, const int* positions, int n
 hipError_t launch_decode_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
                                         int d, const void* k_cache, const void* v_cache, const int* block_table,
                                         int max_blocks, int part_len, int parts, float* partials,
-                                        void* out, hipStream_t s) {
+                                        void* out, hipStream_t s, const SeqMap* map, int* row_parts) {
+  if (map && (!map->dec || !map->ndec || !map->seq_of || (parts > 1 && !row_parts))) return hipErrorInvalidValue;
   if (d == 128)
     return launch_dec<128>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks,
-                           part_len, parts, partials, out, s);
+                           part_len, parts, partials, out, s, map, row_parts);
   return launch_dec<64>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, part_len,
-                        parts, partials, out, s);
+                        parts, partials, out, s, map, row_parts);
 }
 
 }  // namespace llk

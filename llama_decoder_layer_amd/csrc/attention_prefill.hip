@@ -27,7 +27,10 @@
 //       order that puts exactly those 8 keys side by side, so the operand is
 //       one 16-byte read (XOR-swizzled rows keep the reads conflict-free).
 // Keys past the sequence's last written slot are staged as zeros, never read
-// from the cache.
+// from the cache.  When few query tiles would leave CUs idle while each
+// walks a long context, the keys of a tile are split into partitions of
+// whole 64-key tiles (grid z), merged afterwards by the combine kernel in
+// attention.hip.
 #include "common.h"
 #include "kernels.h"
 
@@ -64,7 +67,8 @@ template <int D, int HPW, int QT, int NW>
 __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
     const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
     const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
-    int max_blocks, SeqMap map, int num_qtiles, bf16* __restrict__ out) {
+    int max_blocks, SeqMap map, int num_qtiles, bf16* __restrict__ out, int tpp, int parts,
+    float* __restrict__ partials, int* __restrict__ row_parts) {
   constexpr int KS = D / 32;        // d-steps of S^T
   constexpr int DT = D / 16;        // 16-wide d tiles of O
   constexpr int CH = D / 8;         // 16-byte chunks per K row
@@ -105,6 +109,20 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
   const int p_last = positions[t_begin + qn - 1];           // last written key of the sequence
   const int key_end = min(p0 + QW - 1, p_last) + 1;         // keys this tile needs
   const int ntiles = (key_end + kKT - 1) / kKT;
+  // key partition z = blockIdx.z: tiles [kt_begin, kt_end).  Partitions are
+  // cut only among the tiles that start at or before p0, and the last one
+  // also takes the (at most one) tile after those, so every query of the
+  // tile has at least one unmasked key in every partition.
+  int kt_begin = 0, kt_end = ntiles, np = 1;
+  if (tpp > 0) {
+    const int head = p0 / kKT + 1;
+    np = min((head + tpp - 1) / tpp, parts);
+    const int z = blockIdx.z;
+    if (z >= np) return;
+    kt_begin = z * tpp;
+    if (z < np - 1) kt_end = kt_begin + tpp;
+  }
+  if (row_parts && blockIdx.z == 0 && blockIdx.y == 0 && (int)threadIdx.x < nvalid) row_parts[t0 + threadIdx.x] = np;
   const int* bt = block_table + (size_t)b * max_blocks;
   const size_t head_off = (size_t)g * kKvBlock * D;
   const size_t blk_stride = (size_t)nkv * kKvBlock * D;
@@ -205,12 +223,12 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
       for (int i = 0; i < DT; ++i) o[hh][u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  gload(0);
-  sstore(0);
+  gload(kt_begin);
+  sstore(kt_begin & 1);
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
+    if (kt + 1 < kt_end) gload(kt + 1);
 
     // S^T (raw scores): 4 slices of 16 keys per (head, query tile)
     f32x4 s4[HPW][QT][4];
@@ -295,11 +313,13 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
           for (int u = 0; u < QT; ++u) o[hh][u][i] = mfma16(pa[hh][u][mh], vf, o[hh][u][i]);
       }
     }
-    if (kt + 1 < ntiles) sstore(buf ^ 1);
+    if (kt + 1 < kt_end) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  // normalise and store: lane holds O[query 16u + 4grp + r][d = 16i + l16]
+  // normalise and store: lane holds O[query 16u + 4grp + r][d = 16i + l16].
+  // Of a split tile, leave (max in log2 units, sum, unnormalised O) per
+  // (query, head, partition) for the combine kernel.
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
@@ -311,11 +331,23 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int qi = 16 * u + 4 * grp + r;
-        const float inv = 1.0f / __shfl(lt, 4 * grp + r, kWave);
+        const float lq = __shfl(lt, 4 * grp + r, kWave);
+        const float mq = __shfl(m_run[hh][u], 4 * grp + r, kWave);
         if (qi < nvalid) {
-          bf16* dst = out + (size_t)(t0 + qi) * nq * D + (size_t)h * D + l16;
+          if (np == 1) {
+            const float inv = 1.0f / lq;
+            bf16* dst = out + (size_t)(t0 + qi) * nq * D + (size_t)h * D + l16;
 #pragma unroll
-          for (int i = 0; i < DT; ++i) dst[16 * i] = static_cast<bf16>(o[hh][u][i][r] * inv);
+            for (int i = 0; i < DT; ++i) dst[16 * i] = static_cast<bf16>(o[hh][u][i][r] * inv);
+          } else {
+            float* dst = partials + (((size_t)(t0 + qi) * nq + h) * parts + blockIdx.z) * (D + kPartHead);
+            if (l16 == 0) {
+              dst[0] = mq * sc;
+              dst[1] = lq;
+            }
+#pragma unroll
+            for (int i = 0; i < DT; ++i) dst[kPartHead + 16 * i + l16] = o[hh][u][i][r];
+          }
         }
       }
     }
@@ -324,7 +356,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
 template <int D, int HPW, int QT, int NW>
 hipError_t launch_pf(const void* q, int ldq, int T, const int* positions, int nq, int nkv, const void* k_cache,
                      const void* v_cache, const int* block_table, int max_blocks, const SeqMap& map, void* out,
-                     hipStream_t s) {
+                     hipStream_t s, int tpp, int parts, float* partials, int* row_parts) {
   int nqt = 0, wgs;
   if (map.tiles) {
     wgs = map.tile_cap;
@@ -333,10 +365,10 @@ hipError_t launch_pf(const void* q, int ldq, int T, const int* positions, int nq
     wgs = T / map.q_len * nqt;
   }
   if (wgs <= 0) return hipSuccess;
-  dim3 grid(wgs, nkv);
+  dim3 grid(wgs, nkv, tpp > 0 ? parts : 1);
   prefill_attention_mfma<D, HPW, QT, NW><<<grid, NW * kWave, 0, s>>>(
       (const bf16*)q, ldq, positions, nq, nkv, (const bf16*)k_cache, (const bf16*)v_cache, block_table,
-      max_blocks, map, nqt, (bf16*)out);
+      max_blocks, map, nqt, (bf16*)out, tpp, parts, partials, row_parts);
   return hipGetLastError();
 }
 
@@ -365,12 +397,15 @@ int prefill_tile_rows(int nq, int nkv, int d) {
 
 hipError_t launch_prefill_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
                                          int d, const void* k_cache, const void* v_cache, const int* block_table,
-                                         int max_blocks, const SeqMap& map, void* out, hipStream_t s) {
+                                         int max_blocks, const SeqMap& map, void* out, hipStream_t s, int tpp,
+                                         int parts, float* partials, int* row_parts) {
   const int G = nq / nkv;
   if (!map.tiles && (map.q_len <= 0 || T % map.q_len != 0)) return hipErrorInvalidValue;
-#define LLK_PF_CASE(DD, GG, HH, QQ, WW) \
-  if (d == DD && G == GG)               \
-    return launch_pf<DD, HH, QQ, WW>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, map, out, s);
+  if ((tpp > 0 || parts > 1) && (parts < 2 || !partials || !row_parts)) return hipErrorInvalidValue;
+#define LLK_PF_CASE(DD, GG, HH, QQ, WW)                                                                      \
+  if (d == DD && G == GG)                                                                                    \
+    return launch_pf<DD, HH, QQ, WW>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, \
+                                     map, out, s, tpp, parts, partials, row_parts);
   LLK_PF_CONFIGS(LLK_PF_CASE)
 #undef LLK_PF_CASE
   return hipErrorInvalidValue;

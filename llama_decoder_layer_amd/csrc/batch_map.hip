@@ -1,4 +1,5 @@
-// Row -> sequence map and prefill query-tile table of a mixed batch, built
+// Row -> sequence map, prefill query-tile table and the list of single-row
+// sequences (served by the decode attention kernel) of a mixed batch, built
 // on the device from query_start_loc (the per-sequence query counts that
 // vLLM's attention metadata carries with a paged batch: page
 // "模型库与算子层 — 代码走读", vllm-learning.pages.dev, section "Attention
@@ -48,7 +49,8 @@ __device__ __forceinline__ int last_le(const int* a, int n, int x) {
 
 __global__ __launch_bounds__(kThreads) void batch_map_kernel(const int* __restrict__ qsl, int B, int T, int qw,
                                                               int* __restrict__ seq_of, int4* __restrict__ tiles,
-                                                              int tile_cap, int* __restrict__ ntiles) {
+                                                              int tile_cap, int* __restrict__ ntiles,
+                                                              int* __restrict__ dec, int* __restrict__ ndec) {
   __shared__ int s_row[kMaxMappedSeqs + 1];   // clamped first row of each sequence, then T
   __shared__ int s_tile[kMaxMappedSeqs + 1];  // first tile of each sequence, then the tile count
   __shared__ int s_wave[kThreads / kWave];
@@ -57,16 +59,28 @@ __global__ __launch_bounds__(kThreads) void batch_map_kernel(const int* __restri
   for (int b = tid; b < B; b += kThreads) s_row[b] = min(max(qsl[b], 0), T);
   if (tid == 0) s_row[B] = T;
   __syncthreads();
-  int base = 0;
+  int base = 0, dbase = 0;
   for (int c0 = 0; c0 < B; c0 += kThreads) {
     const int b = c0 + tid;
-    const int n = b < B ? (max(s_row[b + 1] - s_row[b], 0) + qw - 1) / qw : 0;
+    const int rows = b < B ? max(s_row[b + 1] - s_row[b], 0) : 0;
+    const bool single = dec && rows == 1;  // served by the decode kernel
+    const int n = single ? 0 : (rows + qw - 1) / qw;
     const int incl = block_scan(n, s_wave, &s_total);
     if (b < B) s_tile[b] = base + incl - n;
     base += s_total;
     __syncthreads();
+    if (dec) {
+      const int f = single ? 1 : 0;
+      const int di = block_scan(f, s_wave, &s_total) - f;
+      if (single) dec[dbase + di] = s_row[b];
+      dbase += s_total;
+      __syncthreads();
+    }
   }
-  if (tid == 0) s_tile[B] = base;
+  if (tid == 0) {
+    s_tile[B] = base;
+    if (dec) *ndec = dbase;
+  }
   __syncthreads();
   const int total = min(base, tile_cap);
   if (tid == 0) *ntiles = total;
@@ -86,9 +100,9 @@ __global__ __launch_bounds__(kThreads) void batch_map_kernel(const int* __restri
 }  // namespace
 
 hipError_t launch_batch_map(const int* query_start_loc, int B, int T, int qw, int* seq_of, int4* tiles,
-                            int tile_cap, int* ntiles, hipStream_t s) {
-  if (B <= 0 || B > kMaxMappedSeqs || T <= 0 || qw <= 0) return hipErrorInvalidValue;
-  batch_map_kernel<<<1, kThreads, 0, s>>>(query_start_loc, B, T, qw, seq_of, tiles, tile_cap, ntiles);
+                            int tile_cap, int* ntiles, int* dec, int* ndec, hipStream_t s) {
+  if (B <= 0 || B > kMaxMappedSeqs || T <= 0 || qw <= 0 || (dec && !ndec)) return hipErrorInvalidValue;
+  batch_map_kernel<<<1, kThreads, 0, s>>>(query_start_loc, B, T, qw, seq_of, tiles, tile_cap, ntiles, dec, ndec);
   return hipGetLastError();
 }
 

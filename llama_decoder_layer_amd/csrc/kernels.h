@@ -87,16 +87,21 @@ struct SeqMap {
   const int4* tiles = nullptr;   // (sequence, tile, first row, rows) per entry
   const int* ntiles = nullptr;   // valid entries in tiles
   int tile_cap = 0;              // capacity of tiles: the prefill grid bound
+  const int* dec = nullptr;      // rows of the single-row sequences (decode attention), or NULL
+  const int* ndec = nullptr;     // valid entries in dec
+  int dec_cap = 0;               // capacity of dec: the decode grid bound
   __device__ __forceinline__ int seq(int t) const { return seq_of ? seq_of[t] : t / q_len; }
 };
 
 // batch_map.hip.  One workgroup.  Row starts are clamped to [0, T] and rows
 // that no sequence claims map to sequence 0, so a malformed query_start_loc
 // gives wrong rows but no out-of-range access.  Tiles hold qw query rows;
-// a sequence's tiles are listed longest (last) first.
+// a sequence's tiles are listed longest (last) first.  With dec != NULL the
+// sequences with exactly one query row get no tile: their rows are listed
+// in dec (sequence order, *ndec of them) for the decode attention kernel.
 constexpr int kMaxMappedSeqs = 4096;
 hipError_t launch_batch_map(const int* query_start_loc, int B, int T, int qw, int* seq_of, int4* tiles,
-                            int tile_cap, int* ntiles, hipStream_t s);
+                            int tile_cap, int* ntiles, int* dec, int* ndec, hipStream_t s);
 
 // rope_kv.hip.  With part != NULL (bf16 only) the projection row is first
 // formed as the bf16 rounding of the sum of S fp32 partial rows and stored
@@ -112,34 +117,53 @@ hipError_t launch_rope_kv(int dtype, void* qkv, int T, const int* positions, con
                           void* k_cache, void* v_cache, hipStream_t s, const float* part = nullptr,
                           int S = 0, const QkNorm& qkn = QkNorm());
 
-// attention.hip
+// attention.hip.  A key partition's partial result for one (row, query
+// head) is a record of D + kPartHead floats: the running max (log2 units),
+// the sum of exponentials, two pad floats, then the unnormalised output
+// (16-byte aligned for the combine kernel's vector loads).
+constexpr int kPartHead = 4;
 struct AttnPlan {
-  int parts;        // key partitions per query (1 = no split)
-  int part_len;     // keys per partition
+  int parts;        // key partitions per query (1 = no split): partial records per row
+  int part_len;     // keys per partition of the decode kernel's rows
+  int tpp;          // prefill kernel: 64-key tiles per partition (0 = no split)
   size_t ws_bytes;  // fp32 partial results
 };
-// decode: every sequence has exactly one query row this call
-AttnPlan attention_plan(int T, int nq, int nkv, int d, bool decode, int max_seq_len, int num_cus);
+// decode: every sequence has exactly one query row this call.  split_prefill:
+// a prefill batch runs on the matrix-core prefill kernel (bf16, supported
+// group size), whose long key ranges may be split.
+AttnPlan attention_plan(int T, int B, int nq, int nkv, int d, bool decode, int max_seq_len, int num_cus,
+                        bool split_prefill);
+// row_parts: [T] ints, used when a prefill batch's keys are split
 hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
                             int nkv, int d, const void* k_cache, const void* v_cache,
                             const int* block_table, int max_blocks, const SeqMap& map, bool decode,
-                            const AttnPlan& plan, float* partials, void* out, hipStream_t s,
+                            const AttnPlan& plan, float* partials, int* row_parts, void* out, hipStream_t s,
                             hipEvent_t mid_event);
 
-// attention_decode.hip (bf16, one query token per sequence)
+// attention_decode.hip (bf16, one query token per row).  Without map.dec row
+// t of T is sequence t and every partition leaves partials (empty ones a max
+// of -inf).  With map.dec the rows are map.dec[0 .. *map.ndec) of sequences
+// map.seq_of[row]; a row whose keys fit one partition is written to out
+// directly, a longer one leaves partials in its first row_parts[row]
+// partitions.
 hipError_t launch_decode_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
                                         int d, const void* k_cache, const void* v_cache, const int* block_table,
                                         int max_blocks, int part_len, int parts, float* partials,
-                                        void* out, hipStream_t s);
+                                        void* out, hipStream_t s, const SeqMap* map = nullptr,
+                                        int* row_parts = nullptr);
 
 // attention_prefill.hip (bf16, G in {4, 8, 16}).  A uniform batch launches
 // one workgroup per (sequence, query tile, KV head); a mixed batch one per
-// entry of map.tiles, whose tiles must hold prefill_tile_rows() rows.
+// entry of map.tiles, whose tiles must hold prefill_tile_rows() rows.  With
+// tpp > 0 each query tile's keys are split into partitions of tpp 64-key
+// tiles (grid z = parts): a tile with one partition is written to out, a
+// longer one leaves partials and records its partition count in row_parts.
 bool prefill_attention_supported(int nq, int nkv, int d);
 int prefill_tile_rows(int nq, int nkv, int d);
 hipError_t launch_prefill_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
                                          int d, const void* k_cache, const void* v_cache, const int* block_table,
-                                         int max_blocks, const SeqMap& map, void* out, hipStream_t s);
+                                         int max_blocks, const SeqMap& map, void* out, hipStream_t s, int tpp = 0,
+                                         int parts = 1, float* partials = nullptr, int* row_parts = nullptr);
 
 // moe.hip: the sparse MoE block (bf16).  Pair p = t * topk + slot.
 // launch_moe_route: logits [T, E] fp32, ids and wts [T * topk] (E % 16 == 0,

@@ -189,11 +189,45 @@ def test_mid8_mixed_few_rows():
     # 24 rows: the weight-streaming projections with a mixed attention batch
     mix = ((1, 100), (1, 1500), (17, 40), (5, 0))
     _run(synth.Workload(33, "mid8_mixed_4seq", MID8, len(mix), 0, mix=mix))
+    # short contexts: no key partitions, decode rows written directly
+    mix = ((1, 30), (20, 10), (1, 5))
+    _run(synth.Workload(47, "mid8_mixed_short", MID8, len(mix), 0, mix=mix))
 
 
 def test_mid64_mixed():
     mix = ((33, 10), (1, 500), (2, 700))
     _run(synth.Workload(34, "mid64_mixed_3seq", MID64, len(mix), 0, mix=mix))
+
+
+def test_mid8_mixed_long_context_key_partitions():
+    # few query tiles on long contexts: the prefill kernel splits each tile's
+    # keys into partitions (cut at or before the tile's first query position,
+    # so a tile starting mid-way through a 64-key tile spans two), the single-
+    # row sequences run on the decode kernel with the same partitions (one
+    # partition: written directly; a row at position 0: one key), and the
+    # combine merges only the rows that were split
+    mix = ((1, 100), (64, 3000), (1, 1500), (40, 1000), (1, 2999), (1, 0), (3, 511))
+    _run(synth.Workload(41, "mid8_mixed_long_ctx", MID8, len(mix), 0, mix=mix), repeat=True)
+
+
+def test_mid64_mixed_key_partitions():
+    mix = ((1, 1800), (48, 1500), (1, 900), (2, 1023))
+    _run(synth.Workload(42, "mid64_mixed_long_ctx", MID64, len(mix), 0, mix=mix))
+
+
+# 16 query heads per KV head: one wave serves two heads over 16-row tiles
+MID16 = synth.ModelShape(1024, 16, 1, 64, 2816, 1e-5, 500000.0, synth.LLAMA3_SCALING, 131072, "bf16")
+
+
+def test_mid16_mixed_and_prefill_key_partitions():
+    mix = ((1, 700), (40, 1100), (3, 50), (1, 1))
+    _run(synth.Workload(43, "mid16_mixed", MID16, len(mix), 0, mix=mix))
+    _run(synth.Workload(44, "mid16_prefill_1x48_ctx1500", MID16, 1, 48, 1500))
+
+
+def test_mid8_uniform_prefill_split_keys():
+    # a uniform (no query_start_loc) chunk on a long context splits too
+    _run(synth.Workload(45, "mid8_prefill_1x64_ctx2000", MID8, 1, 64, 2000), repeat=True)
 
 
 def test_tiny_fp32_mixed():
@@ -206,7 +240,9 @@ def test_explicit_query_start_loc_matches_uniform():
     # a uniform batch given its query_start_loc takes the tile-table path (and
     # a decode batch the decode path): results are bit-identical to NULL
     for wl, ctx in [(synth.Workload(36, "mid8_prefill_2x100_q", MID8, 2, 100, 0), [0, 33]),
-                    (synth.Workload(37, "mid_decode_b7_q", MID, 7, 1, 0), [3, 15, 16, 17, 400, 1000, 2500])]:
+                    (synth.Workload(37, "mid_decode_b7_q", MID, 7, 1, 0), [3, 15, 16, 17, 400, 1000, 2500]),
+                    # split key ranges: the same partitions either way
+                    (synth.Workload(46, "mid8_prefill_2x64_q", MID8, 2, 64, 0), [1500, 2000])]:
         batch = synth.build_batch(wl, ctx)
         qsl = torch.arange(0, batch.num_tokens + 1, wl.q_len, dtype=torch.int32, device=DEV)
         a = _run(wl, ctx_lens=ctx, check_kv=False)
