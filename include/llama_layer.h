@@ -221,9 +221,13 @@ LLAMA_API size_t llama_layer_workspace_bytes(const llama_layer* layer, int32_t n
  * The call writes only hidden_out, residual_out, the new tokens' KV slots and
  * the workspace.  Preconditions on device data (block ids < num_blocks,
  * positions < max_position_embeddings and consistent with seq_lens, the
- * query_start_loc conditions above) are not checked on the device; a
- * query_start_loc that breaks them gives wrong rows, but the row map stays
- * inside [0, T) and [0, num_seqs).
+ * query_start_loc conditions above) are not checked on the device by
+ * default; a query_start_loc that breaks them gives wrong rows, but the row
+ * map stays inside [0, T) and [0, num_seqs).  With the environment variable
+ * LLAMA_DEBUG=1 (read at each call) the call first checks them with one
+ * kernel and synchronises the stream: a broken condition returns
+ * INVALID_ARGUMENT naming it, before anything is written.  The check is
+ * skipped while the stream is being captured into a graph.
  * Errors: INVALID_ARGUMENT (NULL pointer; T % num_seqs != 0 with
  * query_start_loc NULL; T < num_seqs; T/num_seqs > max_seq_len; max_seq_len >
  * max_position_embeddings or > 16 * max_blocks_per_seq; aliasing outputs),

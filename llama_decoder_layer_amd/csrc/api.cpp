@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <string>
@@ -100,7 +101,8 @@ struct llama_layer {
 namespace {
 
 struct Workspace {
-  size_t h, qkv, attn, h2, act, part, gpart, tpart, tpart_bytes, seq_of, ntiles, tiles, dec, ndec, row_parts, total;
+  size_t h, qkv, attn, h2, act, part, gpart, tpart, tpart_bytes, seq_of, ntiles, tiles, dec, ndec, row_parts, check,
+      total;
   int tile_cap;  // entries of the prefill tile table (mixed batches)
   // MoE routing and expert buffers (P = T * topk pairs)
   size_t rpart, logits, ids, wts, seg, sorted, active, nactive, mtiles, mntiles, mchunk, mact, mpart;
@@ -179,6 +181,7 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   w.dec = take((size_t)B * sizeof(int));
   w.ndec = take(sizeof(int));
   w.row_parts = take((size_t)T * sizeof(int));
+  w.check = take(llk::kCheckFlags * sizeof(int));  // flags of the debug-mode metadata check
   const size_t P = L->E ? (size_t)T * L->topk : 0;
   w.moe_tile_cap = L->E ? (int)(P / llk::kMoeTileRows) + L->E + 1 : 0;
   w.rpart = take(L->E ? (size_t)llk::moe_router_splits(T, H, L->E, L->num_cus) * T * L->E * sizeof(float) : 0);
@@ -260,6 +263,44 @@ void free_layer(llama_layer* L) {
 // The sparse MoE block on the post-attention norm output h2 [T, H]: router +
 // top-k, grouping of the (token, expert) pairs by expert, the expert GEMMs,
 // and the weighted sum into out.
+// Debug mode: the environment variable LLAMA_DEBUG=1, read at each call.
+bool debug_checks() {
+  const char* v = std::getenv("LLAMA_DEBUG");
+  return v && std::strcmp(v, "1") == 0;
+}
+
+// Checks the call's device metadata (block ids, positions, row ranges,
+// KV lengths) on the device and waits for the answer.  Skipped while the
+// stream is being captured: a capture cannot wait.
+llama_status check_metadata(const llama_layer* L, const Workspace& w, char* ws, const int* positions, int T,
+                            const llama_kv_cache* kv, const int* block_table, int max_blocks, const int* seq_lens,
+                            const int* qsl, int B, int max_seq_len, hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone) return LLAMA_OK;
+  int* flags = (int*)(ws + w.check);
+  e = hipMemsetAsync(flags, 0, llk::kCheckFlags * sizeof(int), s);
+  if (e != hipSuccess) return hip_fail(e, "metadata check");
+  e = llk::launch_validate_batch(positions, T, block_table, max_blocks, seq_lens, qsl, B, kv->num_blocks,
+                                 L->cfg.max_position_embeddings, max_seq_len, flags, s);
+  if (e != hipSuccess) return hip_fail(e, "metadata check");
+  int host[llk::kCheckFlags] = {};
+  e = hipMemcpyAsync(host, flags, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "metadata check");
+  static const char* what[llk::kCheckFlags] = {
+      "query_start_loc is not 0 = q[0] < q[1] < ... < q[num_seqs] = num_tokens",
+      "a seq_lens entry is below the sequence's rows or 1, or above max_seq_len",
+      "a block_table entry covering positions below seq_lens is outside [0, kv_cache.num_blocks)",
+      "a position is outside [0, max_position_embeddings) or not seq_lens[b] - rows_b + its index in the run"};
+  std::string msg;
+  for (int k = 0; k < llk::kCheckFlags; ++k)
+    if (host[k]) msg += std::string(msg.empty() ? "" : "; ") + what[k];
+  if (!msg.empty()) return fail(LLAMA_ERR_INVALID_ARGUMENT, "metadata check (LLAMA_DEBUG=1): %s", msg.c_str());
+  return LLAMA_OK;
+}
+
 llama_status moe_block(llama_layer* L, const Workspace& w, char* ws, const void* h2, int T, void* out,
                        hipStream_t s, Marker& mk) {
   const int H = L->cfg.hidden_size, P = T * L->topk;
@@ -533,6 +574,11 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   hipStream_t s = (hipStream_t)stream;
   const Workspace w = carve(L, T, B, max_seq_len);
   char* ws = (char*)workspace;
+  if (debug_checks()) {
+    const llama_status st = check_metadata(L, w, ws, positions, T, kv, block_table, max_blocks, seq_lens,
+                                           decode ? nullptr : query_start_loc, B, max_seq_len, s);
+    if (st != LLAMA_OK) return st;
+  }
   void* h = ws + w.h;
   void* qkv = ws + w.qkv;
   void* attn = ws + w.attn;

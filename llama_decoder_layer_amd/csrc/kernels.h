@@ -103,6 +103,19 @@ constexpr int kMaxMappedSeqs = 4096;
 hipError_t launch_batch_map(const int* query_start_loc, int B, int T, int qw, int* seq_of, int4* tiles,
                             int tile_cap, int* ntiles, int* dec, int* ndec, hipStream_t s);
 
+// validate.hip (debug mode).  Raises flags[k] = 1 for each broken condition
+// k of the call's metadata; the caller zeroes kCheckFlags ints first.
+enum CheckFlag {
+  kCheckRowRanges = 0,  // query_start_loc not 0 = q[0] < q[1] < ... < q[B] = T
+  kCheckSeqLens,        // a seq_lens[b] outside [max(1, rows of b), max_seq_len]
+  kCheckBlockIds,       // a block id of positions < seq_lens[b] outside [0, num_blocks)
+  kCheckPositions,      // a position outside [0, max_pos) or not seq_lens[b] - rows + index
+  kCheckFlags
+};
+hipError_t launch_validate_batch(const int* positions, int T, const int* block_table, int max_blocks,
+                                 const int* seq_lens, const int* query_start_loc, int B, int num_blocks, int max_pos,
+                                 int max_seq_len, int* flags, hipStream_t s);
+
 // rope_kv.hip.  With part != NULL (bf16 only) the projection row is first
 // formed as the bf16 rounding of the sum of S fp32 partial rows and stored
 // into qkv.  A QkNorm with weights set (Qwen3) RMS-normalises each q and k

@@ -276,3 +276,74 @@ def test_mid_decode_b128_and_b129():
     # 128 rows: the largest weight-streaming batch (8 token tiles); 129: tiled
     _run(synth.Workload(39, "mid_decode_b128", MID, 128, 1, (1, 600)))
     _run(synth.Workload(40, "mid_decode_b129", MID, 129, 1, (1, 600)))
+
+
+def test_debug_mode_metadata_checks(monkeypatch):
+    # LLAMA_DEBUG=1: one kernel checks block ids, positions, KV lengths and
+    # row ranges before anything runs, and a broken condition is rejected
+    # with nothing written.  Every broken input below stays inside allocated
+    # memory (block ids point into spare pool blocks the call is not told
+    # of), so the layer could not fault even if the check missed one.
+    model = MID8
+    wl = synth.Workload(48, "mid8_debug_b4", model, 4, 1, (20, 100))
+    batch = synth.build_batch(wl)
+    print("case", wl.name, "ctx", batch.ctx_lens, flush=True)
+    hidden, residual = synth.draw_activations(model, batch.num_tokens, wl.index, DEV)
+    pos, bt, sl = device_batch(batch, DEV)
+    w = synth.draw_weights(model, wl.index, 0, DEV)
+    kp, vp = synth.build_kv_pool(wl, batch, 0, DEV)
+    n = kp.shape[0]
+    kbig = torch.cat([kp, kp[:4]])  # 4 spare blocks past the declared pool
+    vbig = torch.cat([vp, vp[:4]])
+    layer = lda.Layer(model.config_dict(), w)
+    try:
+        ho_ref, ro_ref = layer.forward(hidden, residual, pos, kbig[:n].clone(), vbig[:n].clone(), bt, sl,
+                                       batch.max_seq_len)
+        monkeypatch.setenv("LLAMA_DEBUG", "1")
+        ho, ro = layer.forward(hidden, residual, pos, kbig[:n].clone(), vbig[:n].clone(), bt, sl, batch.max_seq_len)
+        torch.cuda.synchronize()
+        assert torch.equal(ho.view(torch.int16), ho_ref.view(torch.int16))
+        assert torch.equal(ro.view(torch.int16), ro_ref.view(torch.int16))
+
+        def rejected(match, pos_=pos, bt_=bt, sl_=sl, qsl=None, rows=None, msl=batch.max_seq_len):
+            h_, r_ = (hidden, residual) if rows is None else rows
+            k0, v0 = kbig.clone(), vbig.clone()
+            hout = torch.full_like(h_, 7.0)
+            rout = torch.full_like(r_, 7.0)
+            with pytest.raises(lda.LlamaError, match=match) as ei:
+                layer.forward(h_, r_, pos_, kbig[:n], vbig[:n], bt_, sl_, msl, hidden_out=hout,
+                              residual_out=rout, query_start_loc=qsl)
+            assert ei.value.status == lda.Status.INVALID_ARGUMENT
+            torch.cuda.synchronize()
+            assert bool((hout == 7.0).all()) and bool((rout == 7.0).all())
+            assert torch.equal(kbig.view(torch.int16), k0.view(torch.int16))
+            assert torch.equal(vbig.view(torch.int16), v0.view(torch.int16))
+
+        bad = bt.clone()
+        bad[1, 0] = n + 1  # allocated, but past kv_cache.num_blocks
+        rejected("block_table", bt_=bad)
+        bad = bt.clone()
+        bad[0, 5] = n + 3  # sequence 0's last block (KV length 89), where its new token goes
+        rejected("block_table", bt_=bad)
+        p2 = pos.clone()
+        p2[1] -= 1  # no longer seq_lens - 1
+        rejected("position", pos_=p2)
+        s2 = sl.clone()
+        s2[0] = batch.max_seq_len + 1
+        rejected("seq_lens", sl_=s2)
+
+        # a mixed batch: row ranges out of order
+        mix = ((1, 30), (5, 10), (1, 7))
+        wm = synth.Workload(49, "mid8_debug_mixed", model, len(mix), 0, mix=mix)
+        bm = synth.build_batch(wm)
+        hm, rm = synth.draw_activations(model, bm.num_tokens, wm.index, DEV)
+        pm, btm, slm = device_batch(bm, DEV)
+        qsl = device_qsl(bm, DEV)
+        assert bm.num_blocks <= n
+        layer.forward(hm, rm, pm, kbig[:n].clone(), vbig[:n].clone(), btm, slm, bm.max_seq_len,
+                      query_start_loc=qsl)
+        q2 = torch.tensor([0, 6, 1, 7], dtype=torch.int32, device=DEV)  # rows of 1 and 5 swapped
+        assert qsl.tolist() == [0, 1, 6, 7]
+        rejected("query_start_loc", pos_=pm, bt_=btm, sl_=slm, qsl=q2, rows=(hm, rm), msl=bm.max_seq_len)
+    finally:
+        layer.close()
