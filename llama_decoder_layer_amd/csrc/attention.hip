@@ -174,12 +174,14 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(
 }
 
 // Merges the key partitions of each (row, query head) with their
-// log-sum-exp weights, in partition order (deterministic).  One thread per 4
-// output components; grid (rows, ceil(heads * D / 4 / kCombineThreads)).
-// With row_parts, row t has row_parts[t] partitions; a row of one was
-// written by the attention kernel itself.
+// log-sum-exp weights, in partition order (deterministic).  One thread per
+// VEC output components; grid (rows, ceil(heads * D / VEC / kCombineThreads)).
+// The partition loops are unrolled so that their loads are in flight
+// together.  With row_parts, row t has row_parts[t] partitions; a row of one
+// was written by the attention kernel itself.
 constexpr int kCombineThreads = 256;
-template <typename T, int D>
+constexpr int kCombineVec = 4;
+template <typename T, int D, int VEC>
 __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(const float* __restrict__ partials,
                                                                             int nq, int parts,
                                                                             const int* __restrict__ row_parts,
@@ -192,30 +194,38 @@ __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(cons
     if (np <= 1) return;
   }
   const int i = blockIdx.y * kCombineThreads + threadIdx.x;
-  if (i >= nq * (D / 4)) return;
-  const int h = i / (D / 4), e = (i % (D / 4)) * 4;
+  if (i >= nq * (D / VEC)) return;
+  const int h = i / (D / VEC), e = (i % (D / VEC)) * VEC;
   const float* src = partials + ((size_t)t * nq + h) * parts * R;
   float M = -INFINITY;
+#pragma unroll 4
   for (int k = 0; k < np; ++k) M = fmaxf(M, src[(size_t)k * R]);
   float L = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float o[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) o[c] = 0.f;
+#pragma unroll 4
   for (int k = 0; k < np; ++k) {
     const float* pp = src + (size_t)k * R;
     const float m = pp[0];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    L = fmaf(pp[1], w, L);
-    const float4 v = *reinterpret_cast<const float4*>(pp + kPartHead + e);
-    o.x = fmaf(v.x, w, o.x);
-    o.y = fmaf(v.y, w, o.y);
-    o.z = fmaf(v.z, w, o.z);
-    o.w = fmaf(v.w, w, o.w);
+    if (m != -INFINITY) {  // an empty partition's other fields are not written
+      const float w = exp2f(m - M);
+      L = fmaf(pp[1], w, L);
+      float v[VEC];
+      if constexpr (VEC == 4) {
+        const float4 x = *reinterpret_cast<const float4*>(pp + kPartHead + e);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      } else {
+        const float2 x = *reinterpret_cast<const float2*>(pp + kPartHead + e);
+        v[0] = x.x; v[1] = x.y;
+      }
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) o[c] = fmaf(v[c], w, o[c]);
+    }
   }
   T* dst = out + ((size_t)t * nq + h) * D + e;
-  dst[0] = from_f32<T>(o.x / L);
-  dst[1] = from_f32<T>(o.y / L);
-  dst[2] = from_f32<T>(o.z / L);
-  dst[3] = from_f32<T>(o.w / L);
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) dst[c] = from_f32<T>(o[c] / L);
 }
 
 template <typename T, int D>
@@ -232,13 +242,13 @@ hipError_t attention_typed(const T* q, int ldq, int T_, const int* positions, in
 template <typename T>
 hipError_t combine(int d, int T_, int nq, int parts, const float* partials, const int* row_parts, void* out,
                    hipStream_t s) {
-  const int per_row = (nq * d / 4 + kCombineThreads - 1) / kCombineThreads;
+  const int per_row = (nq * d / kCombineVec + kCombineThreads - 1) / kCombineThreads;
   if (d == 128)
-    attention_combine_kernel<T, 128><<<dim3(T_, per_row), kCombineThreads, 0, s>>>(partials, nq, parts, row_parts,
-                                                                                   (T*)out);
+    attention_combine_kernel<T, 128, kCombineVec><<<dim3(T_, per_row), kCombineThreads, 0, s>>>(
+        partials, nq, parts, row_parts, (T*)out);
   else
-    attention_combine_kernel<T, 64><<<dim3(T_, per_row), kCombineThreads, 0, s>>>(partials, nq, parts, row_parts,
-                                                                                  (T*)out);
+    attention_combine_kernel<T, 64, kCombineVec><<<dim3(T_, per_row), kCombineThreads, 0, s>>>(
+        partials, nq, parts, row_parts, (T*)out);
   return hipGetLastError();
 }
 
