@@ -14,6 +14,8 @@ from tests.parity import compare, device_batch, device_qsl, np64, oracle_seqs, o
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 MID = synth.ModelShape(1024, 8, 2, 128, 2816, 1e-5, 500000.0, synth.LLAMA3_SCALING, 131072, "bf16")
+# 8 query heads per KV head, one KV head: few query tiles, so long contexts split
+MID8 = synth.ModelShape(1024, 8, 1, 128, 2816, 1e-5, 500000.0, synth.LLAMA3_SCALING, 131072, "bf16")
 
 
 def _stack_inputs(wl, layers):
@@ -83,6 +85,41 @@ def test_stack_graph_replays_match_eager():
         graph.launch(side)
         side.synchronize()
         assert torch.equal(out.view(torch.int16), ref2.view(torch.int16)), "replay on new input %d" % i
+    graph.close()
+    stack.close()
+
+
+def test_stack_graph_mixed_batch_split_attention_replays():
+    # a mixed batch whose prefill tiles split their keys and whose decode rows
+    # run on the decode kernel (row map, partition counts, combine), captured
+    # once and replayed: every replay bit-identical to the eager forward
+    layers = 2
+    mix = ((1, 1500), (40, 1000), (1, 300), (3, 700))
+    wl = synth.Workload(52, "mid8_stack2_mixed_split", MID8, len(mix), 0, mix=mix)
+    batch, hidden, weights, pools, final = _stack_inputs(wl, layers)
+    stack = lda.Stack(MID8.config_dict(), weights, final)
+    pos, bt, sl = device_batch(batch, DEV)
+    qsl = device_qsl(batch, DEV)
+    T, B = batch.num_tokens, batch.num_seqs
+    ws = stack.alloc_workspace(T, B, batch.max_seq_len)
+    side = torch.cuda.Stream()
+    out_eager = torch.empty_like(hidden)
+    stack.forward(hidden, pos, pools, bt, sl, batch.max_seq_len, out=out_eager, workspace=ws, stream=side,
+                  query_start_loc=qsl)
+    side.synchronize()
+    out = torch.zeros_like(hidden)
+    graph = stack.capture(hidden, pos, pools, bt, sl, batch.max_seq_len, out, ws, side, query_start_loc=qsl)
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.launch(side)
+        side.synchronize()
+        assert torch.equal(out.view(torch.int16), out_eager.view(torch.int16)), "replay %d" % i
+        scratch = torch.empty_like(hidden)
+        stack.forward(hidden, pos, pools, bt, sl, batch.max_seq_len, out=scratch, workspace=ws, stream=side,
+                      query_start_loc=qsl)
+        side.synchronize()
+        assert torch.equal(scratch.view(torch.int16), out_eager.view(torch.int16))
     graph.close()
     stack.close()
 
