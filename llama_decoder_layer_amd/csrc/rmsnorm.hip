@@ -20,12 +20,17 @@ namespace llk {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxChunks = 8;  // 16-byte chunks per thread -> H <= 256*8*VEC
+// A batch of few rows (decode) runs kWideThreads threads per row: with one
+// workgroup per row, 256 threads cannot keep enough loads in flight to
+// stream the row (and its split-K partials) at a useful rate.
+constexpr int kWideThreads = 1024;
+constexpr int kWideMaxRows = 256;
 
 // S > 0: the input row is the sum of S fp32 partial rows xpart[s][row][:]
-// (a split-K projection's output), added in split order.
-template <typename T, int S>
-__global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const T* __restrict__ x,
+// (a split-K projection's output), added in split order.  NT threads, each
+// with at most kMaxChunks 16-byte chunks: H <= NT * kMaxChunks * (16 / sizeof(T)).
+template <typename T, int S, int NT>
+__global__ __launch_bounds__(NT) void add_rmsnorm_kernel(const T* __restrict__ x,
                                                                const T* res,
                                                                const T* __restrict__ w, float eps,
                                                                int H, T* __restrict__ normed,
@@ -33,6 +38,8 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const T* __restri
                                                                int rows) {
   using V = typename Vec16<T>::type;
   constexpr int VN = Vec16<T>::N;
+  constexpr int kThreads = NT;
+  constexpr int kMaxChunks = 2048 / NT;
   const int row = blockIdx.x;
   const int nchunk = H / VN;
   const size_t base = (size_t)row * H;
@@ -124,17 +131,23 @@ hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* res, const v
     const bf16* wb = (const bf16*)w;
     bf16* n = (bf16*)normed;
     bf16* ro = (bf16*)res_out;
-#define LLK_NORM(SS, XX) add_rmsnorm_kernel<bf16, SS><<<rows, kThreads, 0, s>>>((const bf16*)(XX), r, wb, eps, hidden, n, ro, xpart, rows)
-    if (!xpart) LLK_NORM(0, x);
-    else if (S == 1) LLK_NORM(1, nullptr);
-    else if (S == 2) LLK_NORM(2, nullptr);
-    else if (S == 4) LLK_NORM(4, nullptr);
-    else if (S == 8) LLK_NORM(8, nullptr);
+    const bool wide = rows <= kWideMaxRows && hidden >= 8 * kWideThreads;
+#define LLK_NORM_NT(SS, XX, NT) \
+  add_rmsnorm_kernel<bf16, SS, NT><<<rows, NT, 0, s>>>((const bf16*)(XX), r, wb, eps, hidden, n, ro, xpart, rows)
+#define LLK_NORM(SS, XX)                \
+  if (wide) LLK_NORM_NT(SS, XX, kWideThreads); \
+  else LLK_NORM_NT(SS, XX, kThreads)
+    if (!xpart) { LLK_NORM(0, x); }
+    else if (S == 1) { LLK_NORM(1, nullptr); }
+    else if (S == 2) { LLK_NORM(2, nullptr); }
+    else if (S == 4) { LLK_NORM(4, nullptr); }
+    else if (S == 8) { LLK_NORM(8, nullptr); }
     else return hipErrorInvalidValue;
 #undef LLK_NORM
+#undef LLK_NORM_NT
   } else {
     if (xpart) return hipErrorInvalidValue;
-    add_rmsnorm_kernel<float, 0><<<rows, kThreads, 0, s>>>(
+    add_rmsnorm_kernel<float, 0, kThreads><<<rows, kThreads, 0, s>>>(
         (const float*)x, (const float*)res, (const float*)w, eps, hidden, (float*)normed, (float*)res_out,
         nullptr, rows);
   }

@@ -84,7 +84,7 @@ def test_linear_fp32(dtype, M, N, K):
     compare("silu_f32", np64(y2), oracle.silu_and_mul(oracle.linear(np64(x), np64(w2))), dtype="fp32")
 
 
-@pytest.mark.parametrize("rows,H", [(1, 128), (7, 1024), (33, 8192), (5, 16384)])
+@pytest.mark.parametrize("rows,H", [(1, 128), (7, 1024), (33, 8192), (5, 16384), (257, 8192)])
 def test_add_rmsnorm_bf16(rows, H):
     print("rmsnorm", rows, H, flush=True)
     x = _randn((rows, H), 41)
