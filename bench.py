@@ -30,6 +30,24 @@ METRIC = "70B-shape layer tokens/s (prefill, decode) + % MFMA/HBM peak, 1 MI355X
 # x 1.0 (factors from a plain 1 GiB copy; profiles/pmc_copy_calibration.md).  Reported only while
 # the kernel's source file is the one the counters were taken on.
 COUNTER_TRAFFIC = {
+    ("qwen3moe_prefill_4x2048", "moe_gate_up_silu"): {
+        "bytes": 1979509634,
+        "source": "llama_decoder_layer_amd/csrc/moe.hip",
+        "sha1": "755722e27b7a0844d60c7110d6ebca39ad3481fe",
+        "summary": "profiles/moe_gate_up_silu_qwen3moe_prefill_4x2048_counters.md",
+    },
+    ("llama70b_tp8shard_prefill_4x2048", "gate_up_silu"): {
+        "bytes": 1535327477,
+        "source": "llama_decoder_layer_amd/csrc/gemm.hip",
+        "sha1": "b59e6a8385c5f8d8efa36a66f0e1b400cd7d33af",
+        "summary": "profiles/gate_up_silu_tp8shard_prefill_4x2048_counters.md",
+    },
+    ("llama70b_tp8shard_decode_b32_ctx2048", "gate_up"): {
+        "bytes": 129054497,
+        "source": "llama_decoder_layer_amd/csrc/gemm_skinny.hip",
+        "sha1": "3433ede963efa27c5b31834bf3b204ea1bf66cca",
+        "summary": "profiles/gate_up_tp8shard_decode_b32_ctx2048_counters.md",
+    },
     ("llama70b_prefill_4x2048", "gate_up_silu"): {
         "bytes": 11743957635,
         "source": "llama_decoder_layer_amd/csrc/gemm.hip",
