@@ -76,8 +76,15 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
   constexpr int SPL = BCH / kWave;        // chunks per lane when one wave stages one block
   constexpr int QW = kQ * QT;             // queries per workgroup
   constexpr int BPT = kKT / kKvBlock;     // cache blocks per key tile (4)
+  // With 8 waves, each SIMD holds one staging wave (0..3), which runs every
+  // tile's S, softmax and P.V in order, and one deferred wave (4..7), which
+  // runs the previous tile's P.V first and then this tile's S and softmax:
+  // the two waves' softmax phases then fall against each other's MFMAs.  The
+  // deferred P.V reads the previous tile's V, so V has three buffers.
+  constexpr bool PP = NW == 8;
+  constexpr int VB = PP ? 3 : 2;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][kKT * D];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][D * kKT];
+  __shared__ __attribute__((aligned(16))) bf16 sV[VB][D * kKT];
 
   const int G = nq / nkv;
   // this workgroup's query tile: qt of sequence b, whose rows are
@@ -186,19 +193,20 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int kt) {  // tile kt's K into sK[kt % 2], V into sV[kt % VB]
     if (!stager) return;
+    const int kb = kt & 1, vb = kt % VB;
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
-      *reinterpret_cast<bf16x8*>(&sK[buf][k_dst[i]]) = kst[i];
+      *reinterpret_cast<bf16x8*>(&sK[kb][k_dst[i]]) = kst[i];
       bf16x4 lo, hi;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         lo[r] = vst[i][r];
         hi[r] = vst[i][4 + r];
       }
-      *reinterpret_cast<bf16x4*>(&sV[buf][v_dst[i][0]]) = lo;
-      *reinterpret_cast<bf16x4*>(&sV[buf][v_dst[i][1]]) = hi;
+      *reinterpret_cast<bf16x4*>(&sV[vb][v_dst[i][0]]) = lo;
+      *reinterpret_cast<bf16x4*>(&sV[vb][v_dst[i][1]]) = hi;
     }
   };
 
@@ -223,15 +231,11 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
       for (int i = 0; i < DT; ++i) o[hh][u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  gload(kt_begin);
-  sstore(kt_begin & 1);
-  __syncthreads();
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
+  // S^T (raw scores) of tile kt: 4 slices of 16 keys per (head, query tile),
+  // masked where keys pass a query's position (only the tiles that reach the
+  // tile's first query position, or hold unwritten slots, have such keys)
+  auto scores = [&](int kt, f32x4 (&s4)[HPW][QT][4]) {
     const int buf = kt & 1;
-    if (kt + 1 < kt_end) gload(kt + 1);
-
-    // S^T (raw scores): 4 slices of 16 keys per (head, query tile)
-    f32x4 s4[HPW][QT][4];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
@@ -249,8 +253,6 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
           for (int u = 0; u < QT; ++u) s4[hh][u][j] = mfma16(kf, qf[hh][u][s], s4[hh][u][j]);
       }
     }
-    // keys past a query's position exist only in the tiles that reach the
-    // tile's first query position (or hold unwritten slots)
     if (kt * kKT + kKT - 1 > p0) {
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
@@ -264,7 +266,10 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
               if (kt * kKT + 16 * j + 4 * grp + r > pq) s4[hh][u][j][r] = -INFINITY;
       }
     }
-    bf16x8 pa[HPW][QT][2];
+  };
+  // online softmax of one tile's scores: P (bf16) for P.V, the running max
+  // and sum, and O rescaled where a query's max moved
+  auto softmax = [&](const f32x4 (&s4)[HPW][QT][4], bf16x8 (&pa)[HPW][QT][2]) {
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
@@ -301,20 +306,50 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
         }
         m_run[hh][u] = m_new;
       }
-    // O += P V : two 32-key halves, DT d-tiles
+  };
+  // O += P V of tile kt: two 32-key halves, DT d-tiles
+  auto pv = [&](int kt, const bf16x8 (&pa)[HPW][QT][2]) {
+    const int vb = kt % VB;
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][v_rd[mh] + 16 * kKT * i]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[vb][v_rd[mh] + 16 * kKT * i]);
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
           for (int u = 0; u < QT; ++u) o[hh][u][i] = mfma16(pa[hh][u][mh], vf, o[hh][u][i]);
       }
     }
-    if (kt + 1 < kt_end) sstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // One barrier per tile in either order.  A V buffer is rewritten (tile
+  // kt + 1, during tile kt) only after the barrier that follows its last
+  // reader: the deferred P.V of tile kt - 2, run during tile kt - 1.
+  gload(kt_begin);
+  sstore(kt_begin);
+  __syncthreads();
+  if (!PP || stager) {
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      if (kt + 1 < kt_end) gload(kt + 1);
+      f32x4 s4[HPW][QT][4];
+      scores(kt, s4);
+      bf16x8 pa[HPW][QT][2];
+      softmax(s4, pa);
+      pv(kt, pa);
+      if (kt + 1 < kt_end) sstore(kt + 1);
+      __syncthreads();
+    }
+  } else {
+    bf16x8 pa[HPW][QT][2];
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      if (kt > kt_begin) pv(kt - 1, pa);
+      f32x4 s4[HPW][QT][4];
+      scores(kt, s4);
+      softmax(s4, pa);
+      __syncthreads();
+    }
+    pv(kt_end - 1, pa);
   }
 
   // normalise and store: lane holds O[query 16u + 4grp + r][d = 16i + l16].
