@@ -124,6 +124,34 @@ def test_stack_graph_mixed_batch_split_attention_replays():
     stack.close()
 
 
+def test_stack_graph_capture_with_debug_checks_on(monkeypatch):
+    # LLAMA_DEBUG=1 makes an eager forward check its metadata and wait for the
+    # answer; under capture the check is skipped (a capture cannot wait), so
+    # capturing still works and the replays match the (checked) eager forward
+    monkeypatch.setenv("LLAMA_DEBUG", "1")
+    layers = 2
+    wl = synth.Workload(53, "mid_stack2_decode_b4_debug", MID, 4, 1, (5, 300))
+    batch, hidden, weights, pools, final = _stack_inputs(wl, layers)
+    stack = lda.Stack(MID.config_dict(), weights, final)
+    pos, bt, sl = device_batch(batch, DEV)
+    T, B = batch.num_tokens, batch.num_seqs
+    ws = stack.alloc_workspace(T, B, batch.max_seq_len)
+    side = torch.cuda.Stream()
+    out_eager = torch.empty_like(hidden)
+    stack.forward(hidden, pos, pools, bt, sl, batch.max_seq_len, out=out_eager, workspace=ws, stream=side)
+    side.synchronize()
+    out = torch.zeros_like(hidden)
+    graph = stack.capture(hidden, pos, pools, bt, sl, batch.max_seq_len, out, ws, side)
+    for i in range(2):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.launch(side)
+        side.synchronize()
+        assert torch.equal(out.view(torch.int16), out_eager.view(torch.int16)), "replay %d" % i
+    graph.close()
+    stack.close()
+
+
 def _moe_model():
     from tests.test_gpu_moe import MOE
     return MOE
