@@ -110,6 +110,7 @@ struct Workspace {
   llk::AttnPlan plan;
   bool skinny;  // few tokens: weight-streaming projections with split-K partials
   llk::SkinnyPlan pq, po, pg, pd;
+  bool o_wsplit, d_wsplit;  // o_proj / down_proj split K inside the workgroup (final rows, no partials)
 };
 
 // prefill attention runs on the matrix-core kernel (whose keys may be split)
@@ -142,8 +143,10 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
   if (w.skinny) {
     w.pq = llk::skinny_plan(T, L->qkv_n, H, true, L->num_cus);
     w.po = llk::skinny_plan(T, H, Q, true, L->num_cus);
+    w.o_wsplit = llk::skinny_wave_split_ok(T, H, Q, L->num_cus);
+    w.d_wsplit = !L->E && llk::skinny_wave_split_ok(T, H, I, L->num_cus);
     size_t n = (size_t)w.pq.splits * L->qkv_n;
-    if ((size_t)w.po.splits * H > n) n = (size_t)w.po.splits * H;
+    if (!w.o_wsplit && (size_t)w.po.splits * H > n) n = (size_t)w.po.splits * H;
     if (!L->E) {
       // gate_up: unsplit (SiluAndMul in the epilogue) when its row tiles
       // alone fill the CUs; a short weight (e.g. one GPU's tensor-parallel
@@ -154,7 +157,7 @@ Workspace carve(const llama_layer* L, int T, int B, int max_seq_len) {
         if ((size_t)w.pg.splits * 2 * I > n) n = (size_t)w.pg.splits * 2 * I;
       }
       w.pd = llk::skinny_plan(T, H, I, true, L->num_cus);
-      if ((size_t)w.pd.splits * H > n) n = (size_t)w.pd.splits * H;
+      if (!w.d_wsplit && (size_t)w.pd.splits * H > n) n = (size_t)w.pd.splits * H;
     }
     gpart = n * T * sizeof(float);
   }
@@ -648,13 +651,22 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   if (mid) mk.list->push_back({"attention", mid});
   mk.mark(w.plan.parts > 1 ? "attention_combine" : "attention");
   if (w.skinny) {
-    // o_proj as split-K partials; the post-attention norm kernel sums them,
-    // adds the residual and stores the new residual before normalising
-    e = llk::launch_skinny(attn, L->w_o, T, H, nq * d, llk::kEpiPartial, w.po, gp, s, L->wlayout);
-    if (e != hipSuccess) return hip_fail(e, "o_proj");
-    mk.mark("o_proj");
-    e = llk::launch_add_rmsnorm(dt, nullptr, residual_out, L->w_post, c.rms_norm_eps, T, H, h2, residual_out, s,
-                                gp, w.po.splits);
+    if (w.o_wsplit) {
+      // o_proj adds its final rows to the residual stream in place; then a
+      // plain norm of the new residual
+      e = llk::launch_skinny_wave_split(attn, L->w_o, T, H, nq * d, llk::kEpiAdd, residual_out, s, L->wlayout);
+      if (e != hipSuccess) return hip_fail(e, "o_proj");
+      mk.mark("o_proj_residual");
+      e = llk::launch_add_rmsnorm(dt, residual_out, nullptr, L->w_post, c.rms_norm_eps, T, H, h2, nullptr, s);
+    } else {
+      // o_proj as split-K partials; the post-attention norm kernel sums them,
+      // adds the residual and stores the new residual before normalising
+      e = llk::launch_skinny(attn, L->w_o, T, H, nq * d, llk::kEpiPartial, w.po, gp, s, L->wlayout);
+      if (e != hipSuccess) return hip_fail(e, "o_proj");
+      mk.mark("o_proj");
+      e = llk::launch_add_rmsnorm(dt, nullptr, residual_out, L->w_post, c.rms_norm_eps, T, H, h2, residual_out, s,
+                                  gp, w.po.splits);
+    }
     if (e != hipSuccess) return hip_fail(e, "post_attention_layernorm");
     mk.mark("post_attention_layernorm");
     if (L->E) return moe_block(L, w, ws, h2, T, hidden_out, s, mk);
@@ -669,6 +681,12 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
       e = llk::launch_skinny(h2, L->w_gu, T, I, H, llk::kEpiSiluMul, w.pg, act, s, L->wlayout);
       if (e != hipSuccess) return hip_fail(e, "gate_up_proj");
       mk.mark("gate_up_silu");
+    }
+    if (w.d_wsplit) {
+      e = llk::launch_skinny_wave_split(act, L->w_down, T, H, I, llk::kEpiStore, hidden_out, s, L->wlayout);
+      if (e != hipSuccess) return hip_fail(e, "down_proj");
+      mk.mark("down_proj");
+      return LLAMA_OK;
     }
     e = llk::launch_skinny(act, L->w_down, T, H, I, llk::kEpiPartial, w.pd, gp, s, L->wlayout);
     if (e != hipSuccess) return hip_fail(e, "down_proj");

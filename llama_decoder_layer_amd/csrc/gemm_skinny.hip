@@ -178,6 +178,126 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<bf16x4*>(out + i) = o;
 }
 
+// In-workgroup split-K for weights of many rows and a short K (o_proj and
+// down_proj of one GPU's tensor-parallel share of the 70B layer: 8192 rows =
+// 256 CUs x 32, K = 1024 and 3584): a workgroup of kWaveSplit waves
+// owns 32 weight rows, each wave one K slice, with both operands loaded
+// straight into MFMA registers one chunk ahead (x rows come from L2).  The
+// waves' sums are added in wave order through LDS and wave 0 writes the
+// final rows (plain store or residual add): no fp32 partial planes and no
+// separate reduce.
+constexpr int kWaveSplit = 8;
+constexpr int kWsRows = 32;
+constexpr int kWsKc = 64;
+template <int MT, int EPI>
+__global__ __launch_bounds__(kWaveSplit * 64) void gemm_skinny_wsplit(const bf16* __restrict__ X, int M,
+                                                                      const bf16* __restrict__ W, int K,
+                                                                      WStride ws, bf16* __restrict__ out, int N) {
+  constexpr int NT = kWsRows / 16, SPC = kWsKc / 32;
+  __shared__ f32x4 red[kWaveSplit - 1][NT * MT][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * kWsRows;
+  const int kslice = K / kWaveSplit;
+  const int k0 = wave * kslice;
+  const int nchunk = kslice / kWsKc;
+
+  const bf16* wr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    wr[t] = W + (size_t)(n0 + 16 * t) * K + (size_t)r16 * ws.rs + (size_t)(k0 / 32) * ws.ks + g * 8;
+  const bf16* xr[MT];  // rows past M read row M-1; their outputs are never stored
+#pragma unroll
+  for (int u = 0; u < MT; ++u) xr[u] = X + (size_t)min(16 * u + r16, M - 1) * K + k0 + g * 8;
+  bf16x8 wn[SPC][NT], xn[SPC][MT];
+  auto load = [&](int kc) {
+#pragma unroll
+    for (int s = 0; s < SPC; ++s) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wn[s][t] = ld16<bf16x8>(wr[t] + (size_t)(kc / 32 + s) * ws.ks);
+#pragma unroll
+      for (int u = 0; u < MT; ++u) xn[s][u] = ld16<bf16x8>(xr[u] + kc + 32 * s);
+    }
+  };
+
+  f32x4 acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int c = 0; c < nchunk; ++c) {
+    bf16x8 wc[SPC][NT], xc[SPC][MT];
+#pragma unroll
+    for (int s = 0; s < SPC; ++s) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wc[s][t] = wn[s][t];
+#pragma unroll
+      for (int u = 0; u < MT; ++u) xc[s][u] = xn[s][u];
+    }
+    if (c + 1 < nchunk) load((c + 1) * kWsKc);
+#pragma unroll
+    for (int s = 0; s < SPC; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int u = 0; u < MT; ++u) acc[t][u] = mfma16(wc[s][t], xc[s][u], acc[t][u]);
+  }
+
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) red[wave - 1][t * MT + u][lane] = acc[t][u];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kWaveSplit - 1; ++w)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) {
+        const f32x4 v = red[w][t * MT + u][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][u][r] += v[r];
+      }
+
+  // lane holds features n0 + 16t + 4g + (0..3) of token 16u + r16
+#pragma unroll
+  for (int u = 0; u < MT; ++u) {
+    const int m = 16 * u + r16;
+    if (m >= M) continue;
+    bf16* dst = out + (size_t)m * N;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bf16x4* p = reinterpret_cast<bf16x4*>(dst + n0 + 16 * t + 4 * g);
+      bf16x4 o;
+      if (EPI == kEpiAdd) {
+        const bf16x4 prev = *p;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[t][u][r] + static_cast<float>(prev[r]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[t][u][r]);
+      }
+      *p = o;
+    }
+  }
+}
+
+template <int MT>
+hipError_t launch_wsplit(const bf16* x, int M, const bf16* w, int K, WStride ws, int epi, bf16* out, int N,
+                         hipStream_t s) {
+  const dim3 grid(N / kWsRows);
+  if (epi == kEpiAdd)
+    gemm_skinny_wsplit<MT, kEpiAdd><<<grid, kWaveSplit * 64, 0, s>>>(x, M, w, K, ws, out, N);
+  else
+    gemm_skinny_wsplit<MT, kEpiStore><<<grid, kWaveSplit * 64, 0, s>>>(x, M, w, K, ws, out, N);
+  return hipGetLastError();
+}
+
 template <int MT, int NT, int KC, int NW>
 hipError_t launch3(const bf16* x, int M, const bf16* w, int K, int kps, WStride ws, int epi, void* out, int N,
                    dim3 grid, hipStream_t s) {
@@ -282,6 +402,33 @@ hipError_t launch_skinny(const void* x, const void* w, int M, int N, int K, int 
   dim3 grid(wrows / rows_per_wg, p.splits);
   return launch_shape(p, (const bf16*)x, M, (const bf16*)w, K, K / p.splits, weight_stride(layout, K), epi, out,
                       N, grid, s);
+}
+
+// Only for short K: each wave then streams few bytes, and the partial planes
+// and their reduce that this form saves are a large share of the time (the
+// TP = 8 share's o_proj, K = 1024, and down_proj, K = 3584: decode 0.091 ->
+// 0.085 ms).  For long K (the 70B o_proj, K = 8192, and down_proj, K =
+// 28672) the split across workgroups streams faster: there the x chunk is
+// shared through LDS by the waves, where here every wave fetches its own x
+// slice from L2 (0.389 -> 0.405 ms with this form).
+constexpr int kWsMaxK = 4096;
+bool skinny_wave_split_ok(int M, int N, int K, int num_cus) {
+  return M > 0 && M <= 64 && N % kWsRows == 0 && num_cus > 0 && N / kWsRows >= num_cus &&
+         K % (kWaveSplit * kWsKc) == 0 && K <= kWsMaxK;
+}
+
+hipError_t launch_skinny_wave_split(const void* x, const void* w, int M, int N, int K, int epi, void* out,
+                                    hipStream_t s, int layout) {
+  if (M <= 0) return hipSuccess;
+  if (M > 64 || N % kWsRows != 0 || K % (kWaveSplit * kWsKc) != 0 || (epi != kEpiStore && epi != kEpiAdd))
+    return hipErrorInvalidValue;
+  const WStride ws = weight_stride(layout, K);
+  const bf16* xb = (const bf16*)x;
+  const bf16* wb = (const bf16*)w;
+  bf16* ob = (bf16*)out;
+  if (M <= 16) return launch_wsplit<1>(xb, M, wb, K, ws, epi, ob, N, s);
+  if (M <= 32) return launch_wsplit<2>(xb, M, wb, K, ws, epi, ob, N, s);
+  return launch_wsplit<4>(xb, M, wb, K, ws, epi, ob, N, s);
 }
 
 hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, void* out, hipStream_t s) {

@@ -75,6 +75,12 @@ int device_cu_count();
 hipError_t launch_skinny(const void* x, const void* w, int M, int N, int K, int epi, const SkinnyPlan& p,
                          void* out, hipStream_t s, int layout = kRowMajor);
 hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, void* out, hipStream_t s);
+// In-workgroup split-K (bf16, M <= 64, N % 32 == 0, at least one 32-row
+// workgroup per CU, K % 512 == 0 and K <= 4096): the final rows with a plain
+// store or a residual add, without partial planes.
+bool skinny_wave_split_ok(int M, int N, int K, int num_cus);
+hipError_t launch_skinny_wave_split(const void* x, const void* w, int M, int N, int K, int epi, void* out,
+                                    hipStream_t s, int layout);
 
 // Token rows -> sequences.  A uniform batch (query_start_loc NULL) has q_len
 // consecutive rows per sequence, so row t belongs to sequence t / q_len.  A

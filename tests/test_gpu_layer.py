@@ -347,3 +347,16 @@ def test_debug_mode_metadata_checks(monkeypatch):
         rejected("query_start_loc", pos_=pm, bt_=btm, sl_=slm, qsl=q2, rows=(hm, rm), msl=bm.max_seq_len)
     finally:
         layer.close()
+
+
+# hidden 8192 with a narrow attention (32 query heads on 8 KV heads, K = 4096
+# for o_proj) and MLP (K = 1024 for down_proj): at decode both projections
+# have 8192 output rows, one 32-row workgroup per CU, and a short K, so they
+# split K inside the workgroup and write their final rows (o_proj with the
+# residual add) instead of partial planes
+WIDE = synth.ModelShape(8192, 32, 8, 128, 1024, 1e-5, 500000.0, synth.LLAMA3_SCALING, 131072, "bf16")
+
+
+def test_wide_decode_in_workgroup_split_k():
+    for idx, b in ((54, 8), (55, 32), (56, 64)):  # 1, 2 and 4 token tiles
+        _run(synth.Workload(idx, "wide_decode_b%d" % b, WIDE, b, 1, (10, 300)))
