@@ -38,6 +38,7 @@ namespace llk {
 namespace {
 
 constexpr int kQ = 16;         // query tokens per MFMA row tile
+constexpr float kLazyLog2 = 8.0f;  // reference-max slack of the online softmax, log2 units
 constexpr int kKT = 64;        // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -276,25 +277,43 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
       for (int u = 0; u < QT; ++u) {
         float bm = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bm = fmaxf(bm, fmaxf(fmaxf(s4[hh][u][j][0], s4[hh][u][j][1]), fmaxf(s4[hh][u][j][2], s4[hh][u][j][3])));
+        for (int j = 0; j < 4; ++j) {  // pairs fold into three-input maxima
+          bm = fmaxf(fmaxf(bm, s4[hh][u][j][0]), s4[hh][u][j][1]);
+          bm = fmaxf(fmaxf(bm, s4[hh][u][j][2]), s4[hh][u][j][3]);
+        }
         bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
         bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-        const float m_new = fmaxf(m_run[hh][u], bm);
+        // The reference max m_run only has to bound the scores closely
+        // enough that exp2 stays in range: softmax is unchanged by the
+        // choice, as long as O and the sum share it.  It moves (and O is
+        // rescaled) only when some query's tile max exceeds it by more than
+        // kLazyLog2 in log2 units, so P <= 2^kLazyLog2 (exact in bf16's
+        // exponent range) and most tiles skip the rescale.
+        const float m_old = m_run[hh][u];
+        const bool keep = __all(bm * sc <= m_old * sc + kLazyLog2);
+        const float m_new = keep ? m_old : fmaxf(m_old, bm);
         const float ms = m_new * sc;
-        float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s4[hh][u][j][r], sc, -ms));
-            ps += pv;
-            pa[hh][u][j >> 1][4 * (j & 1) + r] = static_cast<bf16>(pv);
-          }
-        if (__all(m_new == m_run[hh][u])) {
-          l_run[hh][u] += ps;  // no query's max moved: O needs no rescale
+          for (int r = 0; r < 4; ++r)
+            pa[hh][u][j >> 1][4 * (j & 1) + r] =
+                static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s4[hh][u][j][r], sc, -ms)));
+        // the sum takes the rounded probabilities that P.V applies, two per
+        // instruction (v_dot2 against ones)
+        const bf16x2 one2 = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+        float ps = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pa[hh][u][c], pa[hh][u][c], 0, 1), one2, ps, false);
+          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pa[hh][u][c], pa[hh][u][c], 2, 3), one2, ps, false);
+          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pa[hh][u][c], pa[hh][u][c], 4, 5), one2, ps, false);
+          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pa[hh][u][c], pa[hh][u][c], 6, 7), one2, ps, false);
+        }
+        if (keep) {
+          l_run[hh][u] += ps;  // reference max kept: O needs no rescale
         } else {
-          const float alpha = __builtin_amdgcn_exp2f((m_run[hh][u] - m_new) * sc);
+          const float alpha = __builtin_amdgcn_exp2f((m_old - m_new) * sc);
           l_run[hh][u] = l_run[hh][u] * alpha + ps;
           float ah[4];
 #pragma unroll
