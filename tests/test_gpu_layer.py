@@ -25,9 +25,10 @@ MID8 = synth.ModelShape(1024, 8, 1, 128, 2816, 1e-5, 500000.0, synth.LLAMA3_SCAL
 MID64 = synth.ModelShape(512, 16, 4, 64, 1408, 1e-5, 10000.0, None, 8192, "bf16")
 
 
-def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False, qsl=None):
+def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False, qsl=None, kv_hook=None):
     """qsl: "auto" = query_start_loc of a mixed batch (None otherwise); a
-    tensor to pass one explicitly (e.g. for a uniform batch)."""
+    tensor to pass one explicitly (e.g. for a uniform batch).  kv_hook(batch,
+    k_pool, v_pool) may reshape the drawn cached context in place."""
     model = workload.model
     batch = synth.build_batch(workload, ctx_lens)
     print("case", workload.name, "ctx", batch.ctx_lens[:8], "T", batch.num_tokens, flush=True)
@@ -43,6 +44,8 @@ def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False, qsl=Non
     for l in range(layers):
         w = synth.draw_weights(model, workload.index, l, DEV)
         kp, vp = synth.build_kv_pool(workload, batch, l, DEV)
+        if kv_hook is not None:
+            kv_hook(batch, kp, vp)
         kp0, vp0 = kp.clone(), vp.clone()
         layer = lda.Layer(model.config_dict(), w)
         ws = layer.alloc_workspace(batch.num_tokens, batch.num_seqs, batch.max_seq_len)
@@ -228,6 +231,33 @@ def test_mid16_mixed_and_prefill_key_partitions():
 def test_mid8_uniform_prefill_split_keys():
     # a uniform (no query_start_loc) chunk on a long context splits too
     _run(synth.Workload(45, "mid8_prefill_1x64_ctx2000", MID8, 1, 64, 2000), repeat=True)
+
+
+def _ramp_keys(scale_per_key):
+    """kv_hook: cached key at position p multiplied by 1 + p * scale_per_key,
+    so scores grow along the context and each new tile's max keeps rising."""
+    def hook(batch, kp, vp):
+        for b, c in enumerate(batch.ctx_lens):
+            if c == 0:
+                continue
+            x = synth.gather_context(kp, batch, b, c).float()
+            ramp = 1.0 + scale_per_key * torch.arange(c, device=x.device, dtype=torch.float32)
+            synth.scatter_context(kp, batch, b, (x * ramp[:, None, None]).to(kp.dtype))
+    return hook
+
+
+def test_mid8_prefill_rising_scores_move_reference_max():
+    # The online softmax keeps its reference max until a tile's max exceeds
+    # it by 8 (log2 units).  With keys growing 1 + p/250 along the context
+    # the reference moves on about a sixth of the later (wave, tile) steps
+    # of the first case (127 of 736, counted on the CPU from the same inputs)
+    # and is kept with P above 1 on the rest; with 1 + p/40 it moves on most
+    # of them.  Cases: a chunk on a long context (split keys merged by the
+    # combine), two chunks on a short one, and a mixed batch with decode rows.
+    _run(synth.Workload(70, "mid8_prefill_1x64_ctx1500_ramp", MID8, 1, 64, 1500), kv_hook=_ramp_keys(1 / 250))
+    _run(synth.Workload(71, "mid8_prefill_2x150_ctx300_ramp", MID8, 2, 150, 300), kv_hook=_ramp_keys(1 / 40))
+    mix = ((1, 1200), (48, 900), (1, 64))
+    _run(synth.Workload(72, "mid8_mixed_ramp", MID8, len(mix), 0, mix=mix), kv_hook=_ramp_keys(1 / 250))
 
 
 def test_tiny_fp32_mixed():
