@@ -5,6 +5,8 @@ cached context, decode at several batch sizes, the fp32 tiny workload, and
 the first-layer (no residual) path.  Also: the KV cache is written exactly at
 the new tokens' slots and nowhere else, and repeated calls are bitwise
 identical."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -298,6 +300,58 @@ def test_query_start_loc_host_checks():
             # two rows for three sequences
             layer.forward(hidden[:2], residual[:2], pos[:2], kp, vp, bt, sl, batch.max_seq_len,
                           query_start_loc=torch.tensor([0, 1, 1, 2], dtype=torch.int32, device=DEV))
+    finally:
+        layer.close()
+
+
+def test_forward_host_checks_write_nothing():
+    # Host-side rejections of llama_layer_forward: each returns an error
+    # before any launch, so the outputs and the KV cache keep their contents.
+    model = MID
+    wl = synth.Workload(73, "mid_decode_checks", model, 3, 1, (20, 90))
+    batch = synth.build_batch(wl)
+    hidden, residual = synth.draw_activations(model, batch.num_tokens, wl.index, DEV)
+    pos, bt, sl = device_batch(batch, DEV)
+    w = synth.draw_weights(model, wl.index, 0, DEV)
+    kp, vp = synth.build_kv_pool(wl, batch, 0, DEV)
+    kp0, vp0 = kp.clone(), vp.clone()
+    T, H = hidden.shape
+    ho = torch.full_like(hidden, 7.0)
+    ro = torch.full_like(hidden, -7.0)
+    L = lda.lib()
+    layer = lda.Layer(model.config_dict(), w)
+    ws = layer.alloc_workspace(T, batch.num_seqs, batch.max_seq_len)
+
+    def call(h=hidden, T_=T, B=batch.num_seqs, msl=batch.max_seq_len, hout=ho, rout=ro):
+        kv = lda.KvCache(kp.data_ptr(), vp.data_ptr(), kp.shape[0])
+        return L.llama_layer_forward(layer._h, h.data_ptr(), residual.data_ptr(), pos.data_ptr(), T_,
+                                     ctypes.byref(kv), bt.data_ptr(), bt.shape[1], sl.data_ptr(), None, B, msl,
+                                     hout.data_ptr(), rout.data_ptr(), ws.data_ptr(), None)
+
+    try:
+        flat = torch.empty(T * H + 1, dtype=hidden.dtype, device=DEV)
+        misaligned = flat[1:].view(T, H)
+        misaligned.copy_(hidden)
+        cases = [
+            (dict(T_=0), "must be positive"),                                    # empty batch
+            (dict(B=0), "must be positive"),                                     # no sequences
+            (dict(T_=2), "multiple of num_seqs"),                                # ragged uniform batch
+            (dict(msl=bt.shape[1] * 16 + 1), "cannot hold"),                     # table too short
+            (dict(rout=ho), "aliases"),                                          # outputs alias
+            (dict(h=misaligned), "16-byte aligned"),                             # misaligned activations
+        ]
+        for kw, msg in cases:
+            st = call(**kw)
+            assert st == lda.Status.INVALID_ARGUMENT, (kw, st)
+            assert msg in L.llama_layer_last_error().decode(), (kw, L.llama_layer_last_error())
+        torch.cuda.synchronize()
+        assert bool((ho == 7.0).all()) and bool((ro == -7.0).all())
+        assert torch.equal(kp.view(torch.int16), kp0.view(torch.int16))
+        assert torch.equal(vp.view(torch.int16), vp0.view(torch.int16))
+        # and the same call with valid arguments runs
+        assert call() == lda.Status.OK
+        torch.cuda.synchronize()
+        assert not bool((ho == 7.0).all())
     finally:
         layer.close()
 
