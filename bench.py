@@ -43,9 +43,9 @@ COUNTER_TRAFFIC = {
         "summary": "profiles/gate_up_silu_tp8shard_prefill_4x2048_counters.md",
     },
     ("llama70b_tp8shard_decode_b32_ctx2048", "gate_up"): {
-        "bytes": 129081877,
+        "bytes": 129033522,
         "source": "llama_decoder_layer_amd/csrc/gemm_skinny.hip",
-        "sha1": "10d9f67562a7e350ade60795651003248d3c0740",
+        "sha1": "ee8feba85821bd1f610cc90ce33abda82a193c67",
         "summary": "profiles/gate_up_tp8shard_decode_b32_ctx2048_counters.md",
     },
     ("llama70b_prefill_4x2048", "gate_up_silu"): {
@@ -61,9 +61,9 @@ COUNTER_TRAFFIC = {
         "summary": "profiles/moe_gate_up_silu_qwen3moe_decode_b32_ctx2048.md",
     },
     ("llama70b_decode_b32_ctx2048", "gate_up_silu"): {
-        "bytes": 945614009,
+        "bytes": 945630302,
         "source": "llama_decoder_layer_amd/csrc/gemm_skinny.hip",
-        "sha1": "10d9f67562a7e350ade60795651003248d3c0740",
+        "sha1": "ee8feba85821bd1f610cc90ce33abda82a193c67",
         "summary": "profiles/gate_up_silu_decode_b32_ctx2048.md",
     },
 }

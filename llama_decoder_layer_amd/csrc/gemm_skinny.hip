@@ -359,13 +359,15 @@ SkinnyPlan skinny_plan(int M, int wrows, int K, bool allow_split, int num_cus) {
   // of the CU count (every CU streams the same number of workgroups; a
   // half-filled last round costs up to a fifth of the time).  The 4-wave
   // candidate suits 8192-row weights, the 5-wave one 10240-row weights.
-  // K chunks for 32 tokens, measured on the 70B decode: 128 for the 4-wave
-  // form (o_proj 35 -> 33 us, down_proj 86 -> 84 us against 64; 256 no
-  // better), 64 for the 5-wave one (qkv_proj 35 us; 37 at 128, 39.5 at 256).
+  // K chunks, measured on the 70B decode: 128 for the 4-wave form (32
+  // tokens: o_proj 35 -> 33 us, down_proj 86 -> 84 us against 64, 256 no
+  // better; 64 tokens: o_proj 37 -> 33 us, down_proj 94 -> 89 us against
+  // 256), 64 for the 5-wave one at 32 tokens (qkv_proj 35 us; 37 at 128,
+  // 39.5 at 256).
   if (allow_split && num_cus > 0 && p.mt >= 2) {
     struct Cand { int nt, nw, kc, splits; };
     static const Cand c2[] = {{2, 4, 128, 8}, {2, 5, 64, 8}};
-    static const Cand c4[] = {{2, 4, 256, 8}, {1, 5, 128, 4}};
+    static const Cand c4[] = {{2, 4, 128, 8}, {1, 5, 128, 4}};
     static const Cand c8[] = {{2, 4, 128, 8}, {1, 5, 128, 4}};
     const Cand* c = p.mt == 2 ? c2 : (p.mt == 4 ? c4 : c8);
     for (int i = 0; i < 2; ++i) {
