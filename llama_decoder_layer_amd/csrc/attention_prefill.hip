@@ -281,8 +281,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
           bm = fmaxf(fmaxf(bm, s4[hh][u][j][0]), s4[hh][u][j][1]);
           bm = fmaxf(fmaxf(bm, s4[hh][u][j][2]), s4[hh][u][j][3]);
         }
-        bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+        bm = row_group_max(bm);
         // The reference max m_run only has to bound the scores closely
         // enough that exp2 stays in range: softmax is unchanged by the
         // choice, as long as O and the sum share it.  It moves (and O is
@@ -379,8 +378,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
       float lt = l_run[hh][u];
-      lt += __shfl_xor(lt, 16, kWave);
-      lt += __shfl_xor(lt, 32, kWave);
+      lt = row_group_sum(lt);
       const int h = g * G + wave * HPW + hh;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

@@ -45,6 +45,25 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Max / sum over the four 16-lane rows of a wave: lanes l, l^16, l^32 and
+// l^48 all end with the same value.  gfx950's v_permlane16_swap and
+// v_permlane32_swap, given one value for both operands, hand each lane the
+// pair {x[l], x[l^16]} (resp. {x[l], x[l^32]}), in VALU without a trip
+// through LDS.  Both orders of a pair add to the same fp32 sum.
+__device__ __forceinline__ float row_group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float row_group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Sum over a group of `W` consecutive lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
