@@ -24,10 +24,13 @@
 //       the B operand is the matching four slots of one V component, a single
 //       8-byte load from the V plane's slot-contiguous layout.
 // Scores, max and sums are fp32 with exp2 on log2(e)/sqrt(d)-scaled scores;
-// P enters the P.V product rounded to bf16.  Slots past the token's position
+// P enters the P.V product rounded to bf16.  The running reference max moves
+// only when a block's max exceeds it by more than 2^8 (so P <= 2^8), which
+// spares most blocks the rescale of o and the sum; softmax is the same for
+// any reference that o and the sum share.  Slots past the token's position
 // (including the unwritten tail of the last block) are masked in both S and
 // V, so stale or poisoned cache contents never reach the output.
-// With several partitions each workgroup leaves (max, sum, unnormalised o)
+// With several partitions each workgroup leaves (reference max, sum, unnormalised o)
 // for the combine kernel in attention.hip.  In a mixed batch the kernel
 // serves the sequences with a single query row from a list of their rows.
 #include "common.h"

@@ -15,7 +15,8 @@
 // tile is staged in LDS once for all G heads, and two waves share each SIMD
 // (one wave's softmax overlaps another's MFMAs).  The key loop walks 64-key tiles (four
 // 16-slot cache blocks) with an online softmax in fp32 (exp2 of
-// log2(e)/sqrt(d)-scaled scores), only up to the tile's last query position
+// log2(e)/sqrt(d)-scaled scores; the reference max moves only when a tile's
+// max exceeds it by more than 2^8), only up to the tile's last query position
 // (causal tile skipping); the diagonal tiles mask key > query position.
 // With v_mfma_f32_16x16x32_bf16:
 //   S^T = K Q^T : A = 16 keys x 32 d from LDS, B = the 16 queries' q from
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
   }
 
   // normalise and store: lane holds O[query 16u + 4grp + r][d = 16i + l16].
-  // Of a split tile, leave (max in log2 units, sum, unnormalised O) per
+  // Of a split tile, leave (reference max in log2 units, sum, unnormalised O) per
   // (query, head, partition) for the combine kernel.
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
