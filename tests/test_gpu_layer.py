@@ -255,11 +255,16 @@ def test_mid8_prefill_rising_scores_move_reference_max():
     # of the first case (127 of 736, counted on the CPU from the same inputs)
     # and is kept with P above 1 on the rest; with 1 + p/40 it moves on most
     # of them.  Cases: a chunk on a long context (split keys merged by the
-    # combine), two chunks on a short one, and a mixed batch with decode rows.
+    # combine), two chunks on a short one, a mixed batch with decode rows, and
+    # a decode batch.
     _run(synth.Workload(70, "mid8_prefill_1x64_ctx1500_ramp", MID8, 1, 64, 1500), kv_hook=_ramp_keys(1 / 250))
     _run(synth.Workload(71, "mid8_prefill_2x150_ctx300_ramp", MID8, 2, 150, 300), kv_hook=_ramp_keys(1 / 40))
     mix = ((1, 1200), (48, 900), (1, 64))
     _run(synth.Workload(72, "mid8_mixed_ramp", MID8, len(mix), 0, mix=mix), kv_hook=_ramp_keys(1 / 250))
+    # decode kernel: 6 sequences on one KV head split their keys into many
+    # short partitions, each with its own reference max for the combine
+    _run(synth.Workload(74, "mid8_decode_b6_ramp", MID8, 6, 1, 0), ctx_lens=[17, 300, 1000, 1999, 2500, 64],
+         kv_hook=_ramp_keys(1 / 250))
 
 
 def test_tiny_fp32_mixed():
