@@ -19,12 +19,17 @@
 //       16 with zeros).  Lane (head = l%16, grp = l/16) receives the scores
 //       of keys 4*grp .. 4*grp+3.
 //   O += P V      : the k index of this product runs over keys.  Each lane
-//       supplies, as its 8 k-slots, its own four keys followed by four zero
-//       slots -- so P goes in straight from the lane that computed it, and
-//       the B operand is the matching four slots of one V component, a single
-//       8-byte load from the V plane's slot-contiguous layout.
-// Scores, max and sums are fp32 with exp2 on log2(e)/sqrt(d)-scaled scores;
-// P enters the P.V product rounded to bf16.  The running reference max moves
+//       supplies, as its 8 k-slots, its own four keys twice -- P rounded to
+//       bf16 in the first four, the bf16 rounding of what that leaves in the
+//       other four -- so P goes in straight from the lane that computed it,
+//       and the B operand is the matching four slots of one V component (a
+//       single 8-byte load from the V plane's slot-contiguous layout) taken
+//       twice.  The one product thus applies P to about 16 significant bits
+//       at no extra cost: a bf16 P alone (8 bits) flips the bf16 rounding of
+//       about 40% of the attention outputs, and those flips reach the
+//       residual stream and the MLP.
+// Scores, max and sums are fp32 with exp2 on log2(e)/sqrt(d)-scaled scores.
+// The running reference max moves
 // only when a block's max exceeds it by more than 2^8 (so P <= 2^8), which
 // spares most blocks the rescale of o and the sum; softmax is the same for
 // any reference that o and the sum share.  Slots past the token's position
@@ -162,12 +167,14 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
     const bool keep = __all(bm <= m_run + kLazyLog2);
     const float m_new = keep ? m_run : fmaxf(m_run, bm);
     float ps = 0.f;
-    bf16x8 pa = zero8;
+    bf16x8 pa;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float pv = __builtin_amdgcn_exp2f(sv[r] - m_new);
       ps += pv;
-      pa[r] = static_cast<bf16>(pv);
+      const bf16 hi = static_cast<bf16>(pv);
+      pa[r] = hi;
+      pa[r + 4] = static_cast<bf16>(pv - static_cast<float>(hi));  // exact difference, then rounded
     }
     if (keep) {
       l_run += ps;
@@ -187,9 +194,13 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
 
 #pragma unroll
     for (int i = 0; i < DT; ++i) {
-      bf16x8 vb = zero8;
+      bf16x8 vb;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vb[r] = valid[r] ? vcur[i][r] : static_cast<bf16>(0.f);
+      for (int r = 0; r < 4; ++r) {
+        const bf16 v = valid[r] ? vcur[i][r] : static_cast<bf16>(0.f);
+        vb[r] = v;
+        vb[r + 4] = v;
+      }
       o[i] = mfma16(pa, vb, o[i]);
     }
   }

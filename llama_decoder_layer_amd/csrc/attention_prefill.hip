@@ -27,6 +27,10 @@
 //       copy of the V tile stores each component's 64 keys in the permuted
 //       order that puts exactly those 8 keys side by side, so the operand is
 //       one 16-byte read (XOR-swizzled rows keep the reads conflict-free).
+//       P enters as two bf16 parts, its rounding and the rounding of what
+//       that leaves, each multiplied by the same V operand: about 16
+//       significant bits of P instead of bf16's 8, whose rounding alone moved
+//       attention outputs by more than 1e-2 of their RMS.
 // Keys past the sequence's last written slot are staged as zeros, never read
 // from the cache.  When few query tiles would leave CUs idle while each
 // walks a long context, the keys of a tile are split into partitions of
@@ -269,9 +273,10 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
       }
     }
   };
-  // online softmax of one tile's scores: P (bf16) for P.V, the running max
-  // and sum, and O rescaled where a query's max moved
-  auto softmax = [&](const f32x4 (&s4)[HPW][QT][4], bf16x8 (&pa)[HPW][QT][2]) {
+  // online softmax of one tile's scores: P for P.V (two bf16 parts: the
+  // rounding of P and the rounding of the remainder), the running max and
+  // sum, and O rescaled where a query's max moved
+  auto softmax = [&](const f32x4 (&s4)[HPW][QT][4], bf16x8 (&pa)[HPW][QT][2], bf16x8 (&pl)[HPW][QT][2]) {
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
@@ -293,23 +298,17 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
         const bool keep = __all(bm * sc <= m_old * sc + kLazyLog2);
         const float m_new = keep ? m_old : fmaxf(m_old, bm);
         const float ms = m_new * sc;
+        float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            pa[hh][u][j >> 1][4 * (j & 1) + r] =
-                static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s4[hh][u][j][r], sc, -ms)));
-        // the sum takes the rounded probabilities that P.V applies, two per
-        // instruction (v_dot2 against ones)
-        const bf16x2 one2 = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
-        float ps = 0.f;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pa[hh][u][c], pa[hh][u][c], 0, 1), one2, ps, false);
-          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pa[hh][u][c], pa[hh][u][c], 2, 3), one2, ps, false);
-          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pa[hh][u][c], pa[hh][u][c], 4, 5), one2, ps, false);
-          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pa[hh][u][c], pa[hh][u][c], 6, 7), one2, ps, false);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const float pf = __builtin_amdgcn_exp2f(fmaf(s4[hh][u][j][r], sc, -ms));
+            const bf16 hi = static_cast<bf16>(pf);
+            pa[hh][u][j >> 1][4 * (j & 1) + r] = hi;
+            pl[hh][u][j >> 1][4 * (j & 1) + r] = static_cast<bf16>(pf - static_cast<float>(hi));
+            ps += pf;
+          }
         if (keep) {
           l_run[hh][u] += ps;  // reference max kept: O needs no rescale
         } else {
@@ -326,8 +325,9 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
         m_run[hh][u] = m_new;
       }
   };
-  // O += P V of tile kt: two 32-key halves, DT d-tiles
-  auto pv = [&](int kt, const bf16x8 (&pa)[HPW][QT][2]) {
+  // O += P V of tile kt: two 32-key halves, DT d-tiles, each V operand
+  // applied to both parts of P
+  auto pv = [&](int kt, const bf16x8 (&pa)[HPW][QT][2], const bf16x8 (&pl)[HPW][QT][2]) {
     const int vb = kt % VB;
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
@@ -337,7 +337,10 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-          for (int u = 0; u < QT; ++u) o[hh][u][i] = mfma16(pa[hh][u][mh], vf, o[hh][u][i]);
+          for (int u = 0; u < QT; ++u) {
+            o[hh][u][i] = mfma16(pa[hh][u][mh], vf, o[hh][u][i]);
+            o[hh][u][i] = mfma16(pl[hh][u][mh], vf, o[hh][u][i]);
+          }
       }
     }
   };
@@ -353,22 +356,22 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
       if (kt + 1 < kt_end) gload(kt + 1);
       f32x4 s4[HPW][QT][4];
       scores(kt, s4);
-      bf16x8 pa[HPW][QT][2];
-      softmax(s4, pa);
-      pv(kt, pa);
+      bf16x8 pa[HPW][QT][2], pl[HPW][QT][2];
+      softmax(s4, pa, pl);
+      pv(kt, pa, pl);
       if (kt + 1 < kt_end) sstore(kt + 1);
       __syncthreads();
     }
   } else {
-    bf16x8 pa[HPW][QT][2];
+    bf16x8 pa[HPW][QT][2], pl[HPW][QT][2];
     for (int kt = kt_begin; kt < kt_end; ++kt) {
-      if (kt > kt_begin) pv(kt - 1, pa);
+      if (kt > kt_begin) pv(kt - 1, pa, pl);
       f32x4 s4[HPW][QT][4];
       scores(kt, s4);
-      softmax(s4, pa);
+      softmax(s4, pa, pl);
       __syncthreads();
     }
-    pv(kt_end - 1, pa);
+    pv(kt_end - 1, pa, pl);
   }
 
   // normalise and store: lane holds O[query 16u + 4grp + r][d = 16i + l16].
