@@ -315,10 +315,29 @@ LLAMA_API void llama_graph_destroy(llama_graph* graph);
  *   "act"  [T, I]          SiluAndMul output (dense layers)
  *   "router_logits" [T, E] float32, "topk_ids" [T, k] int32 (best first),
  *   "topk_weights" [T, k] float32   the MoE routing (MoE layers)
+ *   "moe_sorted" [T*k] int32  the (token, expert) pair p = t*k + slot held by
+ *                          each row of moe_act (pairs grouped by expert)
+ *   "moe_act"  [T*k, moe_intermediate_size]  each pair's SiluAndMul output,
+ *                          in moe_sorted's row order
+ *   "moe_part" [T*k, H]    each pair's expert output times its routing
+ *                          weight, rounded to the layer dtype, row p = pair p;
+ *                          hidden_out[t] is the sum over t's k slots
  * Returns INVALID_ARGUMENT for an unknown name or one the layer lacks. */
 LLAMA_API llama_status llama_layer_workspace_tensor(const llama_layer* layer, int32_t num_tokens,
                                           int32_t num_seqs, int32_t max_seq_len, const char* name,
                                           size_t* offset, size_t* bytes);
+
+/* The layer's RoPE table, read-only device memory the layer owns (valid
+ * until destroy): table[p * pairs + i] = {cos, sin} (two floats) of the
+ * angle p * w_i, angle and cosine/sine computed in double precision and
+ * rounded once to float, for p < *num_positions (max_position_embeddings) and
+ * pair i < *pairs (head_dim / 2).  The RoPE kernel rotates the pair
+ * (x0, x1) = (x_i, x_{i + head_dim/2}) of a head at position p with it as
+ *   y0 = fmaf(x0, cos, -(x1 * sin)),  y1 = fmaf(x1, cos, x0 * sin)
+ * in float, each rounded once to the layer dtype; the K written to the cache
+ * is exactly that.  Errors: INVALID_ARGUMENT for NULL arguments. */
+LLAMA_API llama_status llama_layer_rope_table(const llama_layer* layer, const void** table, int32_t* num_positions,
+                                              int32_t* pairs);
 
 /* Per-kernel timing.  While enabled, every launch of a forward is bracketed
  * by HIP events on the forward's stream.  llama_layer_timing_read waits for

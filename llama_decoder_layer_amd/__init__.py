@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
     L.llama_layer_workspace_tensor.restype = st
     L.llama_layer_workspace_tensor.argtypes = [vp, i32, i32, i32, ctypes.c_char_p,
                                                ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    L.llama_layer_rope_table.restype = st
+    L.llama_layer_rope_table.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.llama_layer_set_timing.restype = st
     L.llama_layer_set_timing.argtypes = [vp, i32]
     L.llama_layer_timing_read.restype = i32
@@ -140,10 +142,24 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ["llama_layer_config_validate", "llama_layer_create", "llama_layer_workspace_bytes",
             "llama_layer_forward", "llama_layer_destroy", "llama_layer_last_error",
-            "llama_layer_workspace_tensor", "llama_layer_set_timing", "llama_layer_timing_read",
+            "llama_layer_workspace_tensor", "llama_layer_rope_table", "llama_layer_set_timing", "llama_layer_timing_read",
             "llama_op_linear", "llama_op_reorder_gate_up", "llama_op_add_rmsnorm",
             "llama_stack_create", "llama_stack_workspace_bytes", "llama_stack_forward", "llama_stack_destroy",
             "llama_stack_graph_create", "llama_graph_launch", "llama_graph_destroy"]
+
+
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime torch already loaded (for plain copies of memory the
+    library owns)."""
+    global _hip_rt
+    if _hip_rt is None:
+        _hip_rt = ctypes.CDLL("libamdhip64.so")
+        _hip_rt.hipMemcpy.restype = ctypes.c_int
+        _hip_rt.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    return _hip_rt
 
 
 def _check(status: int) -> None:
@@ -167,6 +183,31 @@ def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _torch_stream(stream):
+    """The torch stream object of `stream` (None: torch's current stream)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _alloc_on(stream, make):
+    """A tensor the library will use on `stream`: allocated while that stream
+    is torch's current one, so torch's caching allocator ties the memory to it
+    and never hands it out again while work queued there may still use it."""
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        t = make()
+    t.record_stream(ts)
+    return t
+
+
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
@@ -229,7 +270,8 @@ class Layer:
 
     WEIGHT_NAMES = tuple(n for n, _ in Weights._fields_)
     # workspace tensors that are not in the layer dtype
-    _WS_DTYPES = {"router_logits": torch.float32, "topk_ids": torch.int32, "topk_weights": torch.float32}
+    _WS_DTYPES = {"router_logits": torch.float32, "topk_ids": torch.int32, "topk_weights": torch.float32,
+                  "moe_sorted": torch.int32}
 
     def __init__(self, cfg: dict, weights: dict, stream=None):
         self.cfg = dict(cfg)
@@ -261,26 +303,41 @@ class Layer:
 
     def forward(self, hidden, residual, positions, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,
                 hidden_out=None, residual_out=None, workspace=None, stream=None, query_start_loc=None):
-        T = hidden.shape[0]
-        B = seq_lens.shape[0]
         _dev(hidden, "hidden", self.dtype)
+        if hidden.dim() != 2 or hidden.shape[1] != self.cfg["hidden_size"]:
+            raise ValueError("hidden must be [num_tokens, hidden_size]")
+        T = hidden.shape[0]
+        _dev(seq_lens, "seq_lens", torch.int32)
+        if seq_lens.dim() != 1:
+            raise ValueError("seq_lens must be [num_seqs]")
+        B = seq_lens.shape[0]
         if residual is not None:
             _dev(residual, "residual", self.dtype)
+            _shape(residual, "residual", hidden.shape)
         _dev(positions, "positions", torch.int32)
+        _shape(positions, "positions", (T,))
         _dev(block_table, "block_table", torch.int32)
-        _dev(seq_lens, "seq_lens", torch.int32)
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
         _dev(k_cache, "k_cache", self.dtype)
         _dev(v_cache, "v_cache", self.dtype)
+        nb, nkv, d = k_cache.shape[0], self.cfg["num_key_value_heads"], self.cfg.get(
+            "head_dim", self.cfg["hidden_size"] // self.cfg["num_attention_heads"])
+        _shape(k_cache, "k_cache", (nb, nkv, 16, d))
+        _shape(v_cache, "v_cache", (nb, nkv, d, 16))
         if query_start_loc is not None:
             _dev(query_start_loc, "query_start_loc", torch.int32)
             if tuple(query_start_loc.shape) != (B + 1,):
                 raise ValueError("query_start_loc must have num_seqs + 1 entries")
         if hidden_out is None:
-            hidden_out = torch.empty_like(hidden)
+            hidden_out = _alloc_on(stream, lambda: torch.empty_like(hidden))
         if residual_out is None:
-            residual_out = torch.empty_like(hidden)
+            residual_out = _alloc_on(stream, lambda: torch.empty_like(hidden))
+        for name, t in (("hidden_out", hidden_out), ("residual_out", residual_out)):
+            _dev(t, name, self.dtype)
+            _shape(t, name, hidden.shape)
         if workspace is None:
-            workspace = self.alloc_workspace(T, B, max_seq_len, hidden.device)
+            workspace = _alloc_on(stream, lambda: self.alloc_workspace(T, B, max_seq_len, hidden.device))
         elif workspace.numel() < self.workspace_bytes(T, B, max_seq_len):
             raise ValueError("workspace too small")
         kv = KvCache(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[0])
@@ -297,6 +354,20 @@ class Layer:
                                                   ctypes.byref(off), ctypes.byref(nb)))
         raw = workspace[off.value: off.value + nb.value]
         return raw.view(self._WS_DTYPES.get(name, self.dtype)).view(num_tokens, -1)
+
+    def rope_table(self):
+        """A host copy of the layer's RoPE table, numpy float32
+        [max_position_embeddings, head_dim/2, 2] of (cos, sin)
+        (llama_layer_rope_table)."""
+        import numpy as np
+        p, n, pairs = ctypes.c_void_p(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().llama_layer_rope_table(self._h, ctypes.byref(p), ctypes.byref(n), ctypes.byref(pairs)))
+        out = np.empty((n.value, pairs.value, 2), dtype=np.float32)
+        torch.cuda.synchronize()
+        rc = _hip().hipMemcpy(ctypes.c_void_p(out.ctypes.data), p, ctypes.c_size_t(out.nbytes), 2)  # device to host
+        if rc != 0:
+            raise RuntimeError("hipMemcpy of the RoPE table failed (%d)" % rc)
+        return out
 
     def set_timing(self, enable: bool) -> None:
         _check(lib().llama_layer_set_timing(self._h, int(bool(enable))))
@@ -353,8 +424,13 @@ class Stack:
               query_start_loc):
         T, B = hidden.shape[0], seq_lens.shape[0]
         _dev(hidden, "hidden", self.dtype)
+        if hidden.dim() != 2 or hidden.shape[1] != self.cfg["hidden_size"]:
+            raise ValueError("hidden must be [num_tokens, hidden_size]")
         _dev(positions, "positions", torch.int32)
+        _shape(positions, "positions", (T,))
         _dev(block_table, "block_table", torch.int32)
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
         _dev(seq_lens, "seq_lens", torch.int32)
         if len(kv_caches) != self.num_layers:
             raise ValueError("one (k, v) cache pair per layer")
@@ -368,6 +444,7 @@ class Stack:
             if tuple(query_start_loc.shape) != (B + 1,):
                 raise ValueError("query_start_loc must have num_seqs + 1 entries")
         _dev(out, "out", self.dtype)
+        _shape(out, "out", hidden.shape)
         if workspace.numel() < self.workspace_bytes(T, B, max_seq_len):
             raise ValueError("workspace too small")
         self._kvs = kvs  # kept alive: a graph reads the array only at capture, a forward during the call
@@ -378,9 +455,10 @@ class Stack:
                 workspace=None, stream=None, query_start_loc=None):
         """kv_caches: list of (k_cache, v_cache), one per layer.  Returns out."""
         if out is None:
-            out = torch.empty_like(hidden)
+            out = _alloc_on(stream, lambda: torch.empty_like(hidden))
         if workspace is None:
-            workspace = self.alloc_workspace(hidden.shape[0], seq_lens.shape[0], max_seq_len, hidden.device)
+            workspace = _alloc_on(stream, lambda: self.alloc_workspace(hidden.shape[0], seq_lens.shape[0],
+                                                                         max_seq_len, hidden.device))
         a = self._args(hidden, positions, kv_caches, block_table, seq_lens, max_seq_len, out, workspace,
                        query_start_loc)
         _check(lib().llama_stack_forward(*a, _stream(stream)))

@@ -528,6 +528,9 @@ llama_status llama_layer_workspace_tensor(const llama_layer* L, int32_t T, int32
       {"router_logits", w.logits, (size_t)T * L->E * sizeof(float)},
       {"topk_ids", w.ids, (size_t)T * L->topk * sizeof(int)},
       {"topk_weights", w.wts, (size_t)T * L->topk * sizeof(float)},
+      {"moe_sorted", w.sorted, (size_t)T * L->topk * sizeof(int)},
+      {"moe_act", w.mact, (size_t)T * L->topk * L->moe_I * L->es},
+      {"moe_part", w.mpart, (size_t)T * L->topk * c.hidden_size * L->es},
   };
   for (auto& x : t)
     if (std::strcmp(x.n, name) == 0 && x.sz > 0) {
@@ -536,6 +539,15 @@ llama_status llama_layer_workspace_tensor(const llama_layer* L, int32_t T, int32
       return LLAMA_OK;
     }
   return fail(LLAMA_ERR_INVALID_ARGUMENT, "unknown workspace tensor %s", name);
+}
+
+llama_status llama_layer_rope_table(const llama_layer* L, const void** table, int32_t* num_positions,
+                                    int32_t* pairs) {
+  if (!L || !table || !num_positions || !pairs) return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  *table = L->rope;
+  *num_positions = L->cfg.max_position_embeddings;
+  *pairs = L->cfg.head_dim / 2;
+  return LLAMA_OK;
 }
 
 llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void* residual,

@@ -4,23 +4,31 @@ the library consumed, and compare under the stated tolerance.
 Tolerance, per output tensor (bf16 layers).  `exact` is the float64 oracle
 with nothing rounded; `R` is the same oracle storing every tensor in bf16 at
 the points where a bf16 model stores it (the pages fix the model dtype as
-bfloat16), its output rounded to bf16 as the GPU's is.  R's distance from
-`exact` is what bf16 storage by itself costs; the GPU, which stores at the
-same points but makes its own rounding decisions, may differ from `exact` by
-that much plus the stated arithmetic budget:
-  * cosine(gpu, exact) >= 0.9999;
-  * max|gpu - exact| <= max|R - exact| + 1e-2 * RMS(exact);
-  * RMS(gpu - exact) <= 2 * RMS(R - exact) + 1e-3 * RMS(exact)  (a guard
-    against small systematic errors that the max would hide).
-In a chain of layers the budget is per layer: the output of the l-th layer
-(l = 0, 1, ...) carries the arithmetic of l+1 layers and is allowed
-(l+1) * 1e-2 * RMS (and (l+1) * 1e-3 in the RMS guard) on top of R's distance.
+bfloat16), its returned outputs left unrounded.  The GPU stores at the same
+points but makes its own rounding decisions and then rounds its outputs:
+  * cosine(gpu, exact) >= 0.9999, literally;
+  * max|gpu - exact| <= max|bf16(R) - exact| + 1e-2 * RMS(exact): no worse
+    than what bf16 storage itself costs, plus the arithmetic budget;
+  * RMS(gpu - exact) <= 2 * RMS(bf16(R) - exact) + 1e-3 * RMS(exact) (a
+    guard against small systematic errors that the max would hide);
+  * reported: max_i (|gpu_i - R_i| - ulp_bf16(R_i)/2) / RMS(exact).
+The arithmetic itself is bounded stage by stage (tests/stages.py): each
+stored tensor against the oracle's step computed from the GPU's own input to
+that step, max(|gpu - ref| - ulp/2) <= 1e-2 * RMS(ref).  End to end that
+statistic also carries the bf16 rounding flips that two bf16 pipelines make
+at different elements (fp32 against float64 sums), which the layer amplifies
+through the residual stream and the MLP; measured, it reaches 1.1e-2 on the
+70B decode and up to 2.6e-2 on the mixture-of-experts layers, while every
+stage stays far inside 1e-2.
+Every layer is checked with the oracle fed the GPU's own bf16 inputs to that
+layer (teacher forcing), so the budget never grows with depth; chained layers
+add an end-to-end cosine against the oracle chained on itself.
 With no R (a single kernel whose only storage point is its own output) the
 max criterion is max(|gpu - exact| - ulp_bf16/2) <= 1e-2 * RMS(exact).
 A literal max|gpu - exact| <= 1e-2 * RMS cannot hold for bf16 outputs of this
 size: the output rounding alone reaches ~1.5e-2 RMS, and independent 1-ulp
 rounding decisions at the internal storage points propagate to ~1e-2 RMS.
-The literal figure and the distance to R are reported alongside.
+The literal figure is reported alongside.
 fp32 layers: max|gpu - exact| <= 1e-2 * RMS(exact) and cosine >= 0.9999,
 unchanged, plus a tighter 1e-4 check.
 """
@@ -54,8 +62,10 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
 
 
 def compare(name: str, gpu: np.ndarray, ref_exact: np.ndarray, ref_r: np.ndarray = None,
-            dtype: str = "bf16", depth: int = 1) -> dict:
-    """Asserts the tolerance; returns the statistics."""
+            dtype: str = "bf16", extra_ulp_of: np.ndarray = None) -> dict:
+    """Asserts the tolerance; returns the statistics.  extra_ulp_of (no-R
+    comparisons): magnitudes whose bf16 ulp is allowed on top of the half ulp
+    of the output, for a stage that stores an intermediate too."""
     gpu = np.asarray(gpu, np.float64)
     assert gpu.shape == ref_exact.shape, (name, gpu.shape, ref_exact.shape)
     assert np.all(np.isfinite(gpu)), "%s: non-finite values" % name
@@ -71,6 +81,8 @@ def compare(name: str, gpu: np.ndarray, ref_exact: np.ndarray, ref_r: np.ndarray
         return stat
     if ref_r is None:
         excess = err - 0.5 * ulp_bf16(np.maximum(np.abs(ref_exact), np.abs(gpu)))
+        if extra_ulp_of is not None:
+            excess = excess - ulp_bf16(np.abs(extra_ulp_of))
         stat["max_excess_rel"] = float(excess.max()) / rms
         assert stat["max_excess_rel"] <= MAX_REL, (name, stat)
         return stat
@@ -79,8 +91,10 @@ def compare(name: str, gpu: np.ndarray, ref_exact: np.ndarray, ref_r: np.ndarray
     stat["bf16_oracle_rms_err_rel"] = math.sqrt(float(np.mean(rerr * rerr))) / rms
     d = np.abs(gpu - ref_r)
     stat["max_rel_vs_bf16_oracle"] = float(d.max()) / rms
-    assert stat["max_rel"] <= stat["bf16_oracle_max_rel"] + depth * MAX_REL, (name, stat)
-    assert stat["rms_err_rel"] <= 2 * stat["bf16_oracle_rms_err_rel"] + depth * 1e-3, (name, stat)
+    excess = d - 0.5 * ulp_bf16(np.maximum(np.abs(ref_r), np.abs(gpu)))
+    stat["max_excess_vs_bf16_oracle"] = float(excess.max()) / rms
+    assert stat["max_rel"] <= stat["bf16_oracle_max_rel"] + MAX_REL, (name, stat)
+    assert stat["rms_err_rel"] <= 2 * stat["bf16_oracle_rms_err_rel"] + 1e-3, (name, stat)
     return stat
 
 
@@ -106,6 +120,9 @@ def run_oracle(model, weights_np, hidden, residual, batch, seqs, want=None, both
     cfg = model.config_dict()
     h = np64(hidden)
     r = None if residual is None else np64(residual)
+    assert np.all(np.isfinite(h)) and (r is None or np.all(np.isfinite(r))), "non-finite oracle input (hidden/residual)"
+    for i, sq in enumerate(seqs):
+        assert np.all(np.isfinite(sq.k_ctx)) and np.all(np.isfinite(sq.v_ctx)), ("non-finite cached context", i)
     pos = batch.positions.numpy().astype(np.int64)
     exact = oracle.decoder_layer(cfg, weights_np, h, r, pos, seqs, rnd=None, want=want)
     rounded = None
@@ -174,3 +191,22 @@ def moe_check_weights(cfg: dict, trace: dict, gpu_ids: np.ndarray, gpu_w: np.nda
     # best first
     g = np.take_along_axis(gpu_logits, gpu_ids.astype(np.int64), axis=1)
     assert np.all(np.diff(g, axis=1) <= 0), "experts not listed best first"
+    check_topk_of_own_logits(gpu_ids, gpu_logits)
+
+
+def check_topk_of_own_logits(ids: np.ndarray, logits: np.ndarray) -> None:
+    """Each row's chosen experts are a top-k of that row's logits as the GPU
+    computed them: no expert left out has a larger logit than a chosen one,
+    and at an exact tie the lower expert index is the one chosen."""
+    ids = ids.astype(np.int64)
+    for i in range(ids.shape[0]):
+        chosen = set(int(e) for e in ids[i])
+        assert len(chosen) == ids.shape[1], ("repeated expert", i, ids[i])
+        low = min(float(logits[i, e]) for e in chosen)
+        for e in range(logits.shape[1]):
+            if e in chosen:
+                continue
+            v = float(logits[i, e])
+            assert v <= low, ("an expert left out beats a chosen one", i, e, v, low)
+            if v == low:
+                assert all(c < e for c in chosen if float(logits[i, c]) == low), ("tie order", i, e)

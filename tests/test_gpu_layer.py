@@ -13,7 +13,11 @@ import torch
 
 import llama_decoder_layer_amd as lda
 import synth
-from tests.parity import compare, device_batch, device_qsl, np64, oracle_seqs, oracle_weights, run_oracle
+import oracle
+from tests import stages
+from tests.kvbits import check_kv_bits
+from tests.parity import (COS_MIN, compare, cosine, device_batch, device_qsl, np64, oracle_seqs, oracle_weights,
+                          run_oracle)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -30,7 +34,11 @@ MID64 = synth.ModelShape(512, 16, 4, 64, 1408, 1e-5, 10000.0, None, 8192, "bf16"
 def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False, qsl=None, kv_hook=None):
     """qsl: "auto" = query_start_loc of a mixed batch (None otherwise); a
     tensor to pass one explicitly (e.g. for a uniform batch).  kv_hook(batch,
-    k_pool, v_pool) may reshape the drawn cached context in place."""
+    k_pool, v_pool) may reshape the drawn cached context in place.
+
+    Every layer is checked against the oracle fed the GPU's own inputs to that
+    layer (teacher forcing); a chain of layers is also compared end to end
+    (cosine) with the oracle chained on itself."""
     model = workload.model
     batch = synth.build_batch(workload, ctx_lens)
     print("case", workload.name, "ctx", batch.ctx_lens[:8], "T", batch.num_tokens, flush=True)
@@ -39,10 +47,10 @@ def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False, qsl=Non
     pos, bt, sl = device_batch(batch, DEV)
     if qsl is None:
         qsl = device_qsl(batch, DEV)
+    meta0 = [t.clone() for t in (pos, bt, sl) + ((qsl,) if qsl is not None else ())]
     h, r = hidden, residual
-    ref_h = None
     results = []
-    oracle_in_h, oracle_in_r = hidden, residual
+    T, B = batch.num_tokens, batch.num_seqs
     for l in range(layers):
         w = synth.draw_weights(model, workload.index, l, DEV)
         kp, vp = synth.build_kv_pool(workload, batch, l, DEV)
@@ -50,9 +58,12 @@ def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False, qsl=Non
             kv_hook(batch, kp, vp)
         kp0, vp0 = kp.clone(), vp.clone()
         layer = lda.Layer(model.config_dict(), w)
-        ws = layer.alloc_workspace(batch.num_tokens, batch.num_seqs, batch.max_seq_len)
+        ws = layer.alloc_workspace(T, B, batch.max_seq_len)
         ho, ro = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws, query_start_loc=qsl)
         torch.cuda.synchronize()
+        qkv = layer.workspace_tensor(ws, "qkv", T, B, batch.max_seq_len).clone()
+        table = layer.rope_table()
+        wst = stages.workspace(layer, ws, T, B, batch.max_seq_len)
         if repeat:
             kp1, vp1 = kp.clone(), vp.clone()
             ho2, ro2 = layer.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws,
@@ -62,35 +73,48 @@ def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False, qsl=Non
             assert torch.equal(ro.view(torch.int16), ro2.view(torch.int16))
             assert torch.equal(kp.view(torch.int16), kp1.view(torch.int16))
             assert torch.equal(vp.view(torch.int16), vp1.view(torch.int16))
-        results.append((w, kp0, vp0, kp, vp, ho, ro))
+        _check_metadata_unchanged(meta0, pos, bt, sl, qsl)
+        results.append((w, kp0, vp0, kp, vp, h, r, ho, ro, qkv, table, wst))
         h, r = ho, ro
         layer.close()
 
-    # oracle: chained on its own (never fed the GPU's outputs)
-    cfg_np_h = oracle_in_h
     dtype = model.dtype
-    hx = hr_ = None
-    for l, (w, kp0, vp0, kp, vp, ho, ro) in enumerate(results):
+    cfg = model.config_dict()
+    posn = batch.positions.numpy().astype(np.int64)
+    chained = None
+    for l, (w, kp0, vp0, kp, vp, hin, rin, ho, ro, qkv, table, wst) in enumerate(results):
         seqs = oracle_seqs(model, batch, kp0, vp0)
-        if l == 0:
-            exact, rounded = run_oracle(model, oracle_weights(w), oracle_in_h, oracle_in_r, batch, seqs)
-        else:
-            import oracle as orc
-            cfg = model.config_dict()
-            posn = batch.positions.numpy().astype(np.int64)
-            exact = orc.decoder_layer(cfg, oracle_weights(w), prev_exact["hidden_out"], prev_exact["residual_out"],
-                                      posn, seqs)
-            rounded = orc.decoder_layer(cfg, oracle_weights(w), orc.bf16_round(prev_r["hidden_out"]),
-                                        orc.bf16_round(prev_r["residual_out"]), posn, seqs, rnd=orc.bf16_round)
-        prev_exact, prev_r = exact, rounded
+        wn = oracle_weights(w)
+        # teacher forcing: the oracle takes the GPU's own (bf16) inputs to this layer
+        exact, rounded = run_oracle(model, wn, hin, rin, batch, seqs)
         s1 = compare("hidden_out[%d]" % l, np64(ho), exact["hidden_out"],
-                     None if rounded is None else rounded["hidden_out"], dtype, depth=l + 1)
+                     None if rounded is None else rounded["hidden_out"], dtype)
         s2 = compare("residual_out[%d]" % l, np64(ro), exact["residual_out"],
-                     None if rounded is None else rounded["residual_out"], dtype, depth=l + 1)
+                     None if rounded is None else rounded["residual_out"], dtype)
         print("layer", l, "hidden_out", s1, "residual_out", s2, flush=True)
+        print("layer", l, stages.summary(stages.check_stages(model, wn, batch, hin, rin, kp, vp, wst, ho, ro)),
+              flush=True)
         if check_kv:
-            _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded, depth=l + 1)
-    return [(ho, ro, kp, vp) for (_, _, _, kp, vp, ho, ro) in results]
+            _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded, qkv=qkv, table=table)
+        if layers > 1:
+            # the oracle chained on its own exact outputs, for an end-to-end cosine
+            ch = chained if chained is not None else (np64(hidden), None if residual is None else np64(residual))
+            ce = oracle.decoder_layer(cfg, wn, ch[0], ch[1], posn, seqs)
+            chained = (ce["hidden_out"], ce["residual_out"])
+    if layers > 1:
+        for name, got, ref in (("hidden_out", results[-1][7], chained[0]), ("residual_out", results[-1][8], chained[1])):
+            cos = cosine(np64(got), ref)
+            print("chained %d layers %s cos %.7f" % (layers, name, cos), flush=True)
+            assert cos >= COS_MIN, (name, cos)
+    return [(ho, ro, kp, vp) for (_, _, _, kp, vp, _, _, ho, ro, _, _, _) in results]
+
+
+def _check_metadata_unchanged(meta0, pos, bt, sl, qsl):
+    """The forward reads positions, block_table, seq_lens and query_start_loc
+    and never writes them."""
+    now = (pos, bt, sl) + ((qsl,) if qsl is not None else ())
+    for a, b in zip(meta0, now):
+        assert torch.equal(a, b), "forward changed its metadata input"
 
 
 def _new_slot_mask(batch):
@@ -114,8 +138,16 @@ def _check_placement(model, batch, kp0, vp0, kp, vp):
     assert not torch.isnan(kp[mk].float()).any() and not torch.isnan(vp[mv].float()).any()
 
 
-def _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded, depth=1):
+def _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded, qkv=None, table=None):
+    """Placement bit-exact over the whole pool; with the workspace's qkv and
+    the layer's RoPE table, the new slots' values bit-exact too (V a copy of
+    the projection's v, K the kernel's documented float32 rotation of its k;
+    K only without the q/k norm, whose reciprocal square root has no exact
+    host emulation); and against the oracle under the tolerance."""
     _check_placement(model, batch, kp0, vp0, kp, vp)
+    if qkv is not None:
+        n = check_kv_bits(model, batch, kp, vp, qkv, table, check_k=not model.qk_norm)
+        print("KV slots bit-exact:", n, "(K and V)" if not model.qk_norm else "(V)", flush=True)
     ks, vs, kref, vref, kr, vr = [], [], [], [], [], []
     for b in range(batch.num_seqs):
         c, n = batch.ctx_lens[b], int(batch.seq_lens[b])
@@ -126,10 +158,8 @@ def _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded, depth=1):
         if rounded is not None:
             kr.append(rounded["k_new"][b])
             vr.append(rounded["v_new"][b])
-    compare("k_cache", np.concatenate(ks), np.concatenate(kref), np.concatenate(kr) if kr else None, model.dtype,
-            depth)
-    compare("v_cache", np.concatenate(vs), np.concatenate(vref), np.concatenate(vr) if vr else None, model.dtype,
-            depth)
+    compare("k_cache", np.concatenate(ks), np.concatenate(kref), np.concatenate(kr) if kr else None, model.dtype)
+    compare("v_cache", np.concatenate(vs), np.concatenate(vref), np.concatenate(vr) if vr else None, model.dtype)
 
 
 def test_tiny_fp32_prefill():

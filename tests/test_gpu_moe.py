@@ -13,7 +13,8 @@ import oracle
 import synth
 from tests.parity import (compare, device_batch, device_qsl, moe_check_weights, moe_fix_routing, np64,
                           oracle_seqs, oracle_weights)
-from tests.test_gpu_layer import _check_kv
+from tests import stages
+from tests.test_gpu_layer import _check_kv, _check_metadata_unchanged
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -50,12 +51,17 @@ def run_moe_layer(workload, ctx_lens=None, repeat=False, want=None, check_kv=Non
     w = synth.draw_weights(model, workload.index, 0, DEV)
     kp, vp = synth.build_kv_pool(workload, batch, 0, DEV)
     kp0, vp0 = kp.clone(), vp.clone()
+    meta0 = [t.clone() for t in (pos, bt, sl) + ((qsl,) if qsl is not None else ())]
     layer = lda.Layer(model.config_dict(), w)
     ws = layer.alloc_workspace(T, B, batch.max_seq_len)
     ho, ro = layer.forward(hidden, residual, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws,
                            query_start_loc=qsl)
     torch.cuda.synchronize()
+    _check_metadata_unchanged(meta0, pos, bt, sl, qsl)
     ids, wts, logits = _routing(layer, ws, T, B, batch.max_seq_len)
+    qkv = layer.workspace_tensor(ws, "qkv", T, B, batch.max_seq_len).clone()
+    table = layer.rope_table()
+    wst = {n: t.clone() for n, t in stages.workspace(layer, ws, T, B, batch.max_seq_len).items()}
     if repeat:
         ho1, ro1 = ho.clone(), ro.clone()
         kp.copy_(kp0)
@@ -83,8 +89,10 @@ def run_moe_layer(workload, ctx_lens=None, repeat=False, want=None, check_kv=Non
     s1 = compare("hidden_out", np64(ho)[rows], exact["hidden_out"], rounded["hidden_out"])
     s2 = compare("residual_out", np64(ro)[rows], exact["residual_out"], rounded["residual_out"])
     print("rows with a near-tie expert choice", n_fix, n_fix_r, "hidden_out", s1, "residual_out", s2, flush=True)
+    print(stages.summary(stages.check_stages(model, w_np, batch, hidden, residual, kp, vp, wst, ho, ro, rows)),
+          flush=True)
     if (want is None) if check_kv is None else check_kv:
-        _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded)
+        _check_kv(model, batch, kp0, vp0, kp, vp, exact, rounded, qkv=qkv, table=table)
     return ho, ro, ids
 
 

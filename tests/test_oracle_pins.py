@@ -187,6 +187,29 @@ def test_llama3_factor_one_is_plain_rope():
                                oracle.rope_frequencies(128, 5e5, None), rtol=1e-15)
 
 
+def test_llama3_interior_pairs_match_fixture():
+    """The six pairs between the wavelength edges: their scaled frequencies,
+    read back as blend weights s = (w'/w - 1/8) / (1 - 1/8), equal the
+    hand-evaluated weights of tests/golden/llama3_interior.json (4 decimals).
+    A blend harmonic in the factor, or one linear in the wavelength instead of
+    in its inverse, moves every s by more than 0.1."""
+    with open(os.path.join(GOLDEN, "llama3_interior.json")) as f:
+        g = json.load(f)
+    d, theta = g["head_dim"], g["theta"]
+    base = oracle.rope_frequencies(d, theta, None)
+    f = oracle.rope_frequencies(d, theta, synth.LLAMA3_SCALING)
+    factor = synth.LLAMA3_SCALING["factor"]
+    ratio = f / base
+    interior = [i for i in range(d // 2) if not (np.isclose(ratio[i], 1.0, rtol=1e-15, atol=0)
+                                                 or np.isclose(ratio[i], 1 / factor, rtol=1e-15, atol=0))]
+    assert interior == g["pairs"]
+    s = (ratio[interior] - 1 / factor) / (1 - 1 / factor)
+    np.testing.assert_allclose(s, g["s"], rtol=0, atol=5.1e-5)
+    np.testing.assert_allclose(2 * math.pi / base[interior], g["wavelength"], rtol=0, atol=0.051)
+    assert int(np.sum(np.isclose(ratio, 1.0, rtol=1e-15, atol=0))) == g["unchanged_pairs"]
+    assert int(np.sum(np.isclose(ratio, 1 / factor, rtol=1e-15, atol=0))) == g["divided_pairs"]
+
+
 # ------------------------------------------------------------- attention --
 
 def _sdpa_causal(q, k, v, q_pos):
@@ -433,6 +456,66 @@ def test_bf16_storage_mode_close_to_exact():
     z = oracle.decoder_layer(cfg, w, hb, np.zeros_like(hb), np.arange(12), seq, rnd=oracle.bf16_round)
     np.testing.assert_array_equal(c["residual_out"], z["residual_out"])
     np.testing.assert_array_equal(c["hidden_out"], z["hidden_out"])
+
+
+def _layer_bf16_storage_torch(cfg, w, hidden, residual, positions, k_ctx, v_ctx, freqs):
+    """The layer as a bf16 model stores it, written with torch routines in
+    float64 and torch's own bfloat16 conversion at each storage point: the
+    residual r, the normed h, the q/k/v projections, rotated q and k, the
+    attention output, the post-attention residual r2, its normed h2 and the
+    SiluAndMul output.  Returns (hidden_out, residual_out) before their own
+    final rounding."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    bf = lambda x: x.to(torch.bfloat16).to(torch.float64)
+    H, nq, nkv, d, I = (cfg["hidden_size"], cfg["num_attention_heads"], cfg["num_key_value_heads"],
+                        cfg["head_dim"], cfg["intermediate_size"])
+    eps = cfg["rms_norm_eps"]
+    wqkv = t(w["qkv_proj"])
+    wq, wk, wv = wqkv[: nq * d], wqkv[nq * d: (nq + nkv) * d], wqkv[(nq + nkv) * d:]
+    r = bf(t(hidden) + t(residual))
+    h = bf(F.rms_norm(r, (H,), weight=t(w["input_layernorm"]), eps=eps))
+    q = bf(F.linear(h, wq)).reshape(-1, nq, d).numpy()
+    k = bf(F.linear(h, wk)).reshape(-1, nkv, d).numpy()
+    v = bf(F.linear(h, wv)).reshape(-1, nkv, d).numpy()
+    q = bf(t(_rope_complex(q, positions, freqs))).numpy()
+    k = bf(t(_rope_complex(k, positions, freqs))).numpy()
+    a = _sdpa_causal(q, np.concatenate([k_ctx, k]), np.concatenate([v_ctx, v]), positions)
+    a = bf(t(a.reshape(-1, nq * d)))
+    r2 = F.linear(a, t(w["o_proj"])) + r
+    h2 = bf(F.rms_norm(bf(r2), (H,), weight=t(w["post_attention_layernorm"]), eps=eps))
+    gu = F.linear(h2, t(w["gate_up_proj"]))
+    act = bf(F.silu(gu[:, :I]) * gu[:, I:])
+    return F.linear(act, t(w["down_proj"])).numpy(), r2.numpy()
+
+
+@pytest.mark.parametrize("scaling,ctx", [(None, 0), (synth.LLAMA3_SCALING, 7)])
+def test_bf16_storage_points_match_torch_bf16_pipeline(scaling, ctx):
+    """The oracle's bf16-storage mode rounds exactly where a bf16 model stores
+    a tensor.  Against a torch pipeline with torch's bf16 conversion at the
+    same points, the returned residual agrees to float64 rounding and the
+    returned hidden state to far below one bf16 ulp.  A storage point dropped
+    or added (say r2 left unrounded before its norm) moves h2 by up to half
+    an ulp and flips a large share of its roundings, which this fails."""
+    cfg = _cfg(H=128, d=32, I=192, theta=5e5 if scaling else 1e4, scaling=scaling)
+    rng = np.random.default_rng(17)
+    w = {k: oracle.bf16_round(v) for k, v in _weights(cfg, rng).items()}
+    T = 9
+    nkv, d = cfg["num_key_value_heads"], cfg["head_dim"]
+    k_ctx = oracle.bf16_round(rng.standard_normal((ctx, nkv, d)))
+    v_ctx = oracle.bf16_round(rng.standard_normal((ctx, nkv, d)))
+    hidden = oracle.bf16_round(rng.standard_normal((T, cfg["hidden_size"])))
+    residual = oracle.bf16_round(rng.standard_normal((T, cfg["hidden_size"])))
+    pos = np.arange(ctx, ctx + T)
+    out = oracle.decoder_layer(cfg, w, hidden, residual, pos, [oracle.Seq(range(T), k_ctx, v_ctx)],
+                               rnd=oracle.bf16_round)
+    freqs = oracle.rope_frequencies(d, cfg["rope_theta"], scaling)
+    ref_h, ref_r = _layer_bf16_storage_torch(cfg, w, hidden, residual, pos, k_ctx, v_ctx, freqs)
+    np.testing.assert_allclose(out["residual_out"], ref_r, rtol=1e-12, atol=1e-12)
+    rms = float(np.sqrt(np.mean(ref_h ** 2)))
+    assert float(np.abs(out["hidden_out"] - ref_h).max()) <= 1e-9 * rms
+    # the unrounded oracle is a different function: its distance is bf16-sized
+    exact = oracle.decoder_layer(cfg, w, hidden, residual, pos, [oracle.Seq(range(T), k_ctx, v_ctx)])
+    assert float(np.abs(exact["hidden_out"] - ref_h).max()) > 1e-4 * rms
 
 
 def test_stack_hands_pair_on():
