@@ -240,6 +240,28 @@ LLAMA_API llama_status llama_layer_forward(llama_layer* layer, const void* hidde
                                  int32_t max_seq_len, void* hidden_out, void* residual_out,
                                  void* workspace, void* stream);
 
+/* llama_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Arguments, results and errors as llama_layer_forward, without
+ * the workspace: the forward's intermediate tensors live in a device array
+ * of 64 MiB that the library holds on each GPU it runs on, from module load
+ * until the process ends (enough for decode batches of up to 64 sequences at
+ * 32768-token contexts on the 70B layer).  The call makes no allocation of
+ * any kind.  Every call on one GPU shares that GPU's array, so calls that
+ * overlap on one GPU (other streams, other threads) race; the caller
+ * serialises them.  Extra errors: INVALID_ARGUMENT when the call would need
+ * more than 64 MiB (llama_layer_workspace_bytes tells; use
+ * llama_layer_forward with a workspace then), when per-kernel timing is on,
+ * or when the current device is not the layer's; HIP when the array's
+ * address could not be looked up at create. */
+LLAMA_API llama_status llama_layer_forward_noalloc(llama_layer* layer, const void* hidden, const void* residual,
+                                                   const int32_t* positions, int32_t num_tokens,
+                                                   const llama_kv_cache* kv_cache, const int32_t* block_table,
+                                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                                   const int32_t* query_start_loc, int32_t num_seqs,
+                                                   int32_t max_seq_len, void* hidden_out, void* residual_out,
+                                                   void* stream);
+
 /* Frees the layer's device memory (synchronises the device first). */
 LLAMA_API void llama_layer_destroy(llama_layer* layer);
 

@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
     L.llama_layer_forward.restype = st
     L.llama_layer_forward.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(KvCache), vp, i32, vp, vp, i32, i32,
                                       vp, vp, vp, vp]
+    L.llama_layer_forward_noalloc.restype = st
+    L.llama_layer_forward_noalloc.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(KvCache), vp, i32, vp, vp, i32, i32,
+                                              vp, vp, vp]
     L.llama_layer_destroy.restype = None
     L.llama_layer_destroy.argtypes = [vp]
     L.llama_layer_workspace_tensor.restype = st
@@ -141,7 +144,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ["llama_layer_config_validate", "llama_layer_create", "llama_layer_workspace_bytes",
-            "llama_layer_forward", "llama_layer_destroy", "llama_layer_last_error",
+            "llama_layer_forward", "llama_layer_forward_noalloc", "llama_layer_destroy", "llama_layer_last_error",
             "llama_layer_workspace_tensor", "llama_layer_rope_table", "llama_layer_set_timing", "llama_layer_timing_read",
             "llama_op_linear", "llama_op_reorder_gate_up", "llama_op_add_rmsnorm",
             "llama_stack_create", "llama_stack_workspace_bytes", "llama_stack_forward", "llama_stack_destroy",
@@ -303,6 +306,36 @@ class Layer:
 
     def forward(self, hidden, residual, positions, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,
                 hidden_out=None, residual_out=None, workspace=None, stream=None, query_start_loc=None):
+        hidden_out, residual_out, kv, T, B = self._check(hidden, residual, positions, k_cache, v_cache, block_table,
+                                                          seq_lens, hidden_out, residual_out, stream, query_start_loc)
+        if workspace is None:
+            workspace = _alloc_on(stream, lambda: self.alloc_workspace(T, B, max_seq_len, hidden.device))
+        elif workspace.numel() < self.workspace_bytes(T, B, max_seq_len):
+            raise ValueError("workspace too small")
+        _check(lib().llama_layer_forward(
+            self._h, _ptr(hidden), _ptr(residual), _ptr(positions), T, ctypes.byref(kv), _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), _ptr(query_start_loc), B, int(max_seq_len), _ptr(hidden_out),
+            _ptr(residual_out), _ptr(workspace), _stream(stream)))
+        return hidden_out, residual_out
+
+    def forward_noalloc(self, hidden, residual, positions, k_cache, v_cache, block_table, seq_lens,
+                        max_seq_len: int, hidden_out, residual_out, stream=None, query_start_loc=None):
+        """llama_layer_forward_noalloc: the forward with the library's own
+        scratch instead of a workspace; the caller supplies the outputs."""
+        if hidden_out is None or residual_out is None:
+            raise ValueError("the no-allocation forward writes into caller-supplied outputs")
+        hidden_out, residual_out, kv, T, B = self._check(hidden, residual, positions, k_cache, v_cache, block_table,
+                                                          seq_lens, hidden_out, residual_out, stream, query_start_loc)
+        _check(lib().llama_layer_forward_noalloc(
+            self._h, _ptr(hidden), _ptr(residual), _ptr(positions), T, ctypes.byref(kv), _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), _ptr(query_start_loc), B, int(max_seq_len), _ptr(hidden_out),
+            _ptr(residual_out), _stream(stream)))
+        return hidden_out, residual_out
+
+    def _check(self, hidden, residual, positions, k_cache, v_cache, block_table, seq_lens, hidden_out, residual_out,
+               stream, query_start_loc):
+        """Argument checks shared by the forwards; allocates missing outputs
+        on the call's stream.  Returns (hidden_out, residual_out, KvCache, T, B)."""
         _dev(hidden, "hidden", self.dtype)
         if hidden.dim() != 2 or hidden.shape[1] != self.cfg["hidden_size"]:
             raise ValueError("hidden must be [num_tokens, hidden_size]")
@@ -336,16 +369,8 @@ class Layer:
         for name, t in (("hidden_out", hidden_out), ("residual_out", residual_out)):
             _dev(t, name, self.dtype)
             _shape(t, name, hidden.shape)
-        if workspace is None:
-            workspace = _alloc_on(stream, lambda: self.alloc_workspace(T, B, max_seq_len, hidden.device))
-        elif workspace.numel() < self.workspace_bytes(T, B, max_seq_len):
-            raise ValueError("workspace too small")
         kv = KvCache(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[0])
-        _check(lib().llama_layer_forward(
-            self._h, _ptr(hidden), _ptr(residual), _ptr(positions), T, ctypes.byref(kv), _ptr(block_table),
-            block_table.shape[1], _ptr(seq_lens), _ptr(query_start_loc), B, int(max_seq_len), _ptr(hidden_out),
-            _ptr(residual_out), _ptr(workspace), _stream(stream)))
-        return hidden_out, residual_out
+        return hidden_out, residual_out, kv, T, B
 
     def workspace_tensor(self, workspace: torch.Tensor, name: str, num_tokens: int, num_seqs: int,
                          max_seq_len: int) -> torch.Tensor:

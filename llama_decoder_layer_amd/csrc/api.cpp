@@ -78,6 +78,8 @@ struct llama_layer {
   int qkv_n = 0;
   int num_cus = 0;  // compute units of the device the layer was created on
   int wlayout = 0;  // llk::WeightLayout of the projection weights
+  int device = -1;  // HIP device the layer lives on
+  hipError_t scratch_err = hipSuccess;  // setup of that device's no-allocation scratch
   void* w_in = nullptr;
   void* w_qkv = nullptr;
   void* w_o = nullptr;
@@ -421,6 +423,12 @@ llama_status llama_layer_create(const llama_layer_config* config, const llama_la
   L->dtype = config->dtype;
   L->es = elem_size(config->dtype);
   L->num_cus = llk::device_cu_count();
+  if (hipGetDevice(&L->device) != hipSuccess) {
+    delete L;
+    return fail(LLAMA_ERR_HIP, "hipGetDevice failed");
+  }
+  // the device's scratch for llama_layer_forward_noalloc, looked up once
+  L->scratch_err = llk::noalloc_scratch_setup(L->device);
   const llama_layer_config& c = L->cfg;
   const size_t H = c.hidden_size, I = c.intermediate_size, Q = (size_t)c.num_attention_heads * c.head_dim;
   L->qkv_n = (c.num_attention_heads + 2 * c.num_key_value_heads) * c.head_dim;
@@ -550,11 +558,15 @@ llama_status llama_layer_rope_table(const llama_layer* L, const void** table, in
   return LLAMA_OK;
 }
 
-llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void* residual,
-                                 const int32_t* positions, int32_t T, const llama_kv_cache* kv,
-                                 const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
-                                 const int32_t* query_start_loc, int32_t B, int32_t max_seq_len,
-                                 void* hidden_out, void* residual_out, void* workspace, void* stream) {
+}  // extern "C"
+
+namespace {
+
+llama_status forward_impl(llama_layer* L, const void* hidden, const void* residual, const int32_t* positions,
+                          int32_t T, const llama_kv_cache* kv, const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* seq_lens, const int32_t* query_start_loc, int32_t B,
+                          int32_t max_seq_len, void* hidden_out, void* residual_out, void* workspace,
+                          void* stream) {
   if (!L) return fail(LLAMA_ERR_INVALID_ARGUMENT, "layer is NULL");
   if (!hidden || !positions || !kv || !kv->k || !kv->v || !block_table || !seq_lens || !hidden_out ||
       !residual_out || !workspace)
@@ -724,6 +736,46 @@ llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void*
   if (e != hipSuccess) return hip_fail(e, "down_proj");
   mk.mark("down_proj");
   return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+llama_status llama_layer_forward(llama_layer* L, const void* hidden, const void* residual,
+                                 const int32_t* positions, int32_t T, const llama_kv_cache* kv,
+                                 const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                 const int32_t* query_start_loc, int32_t B, int32_t max_seq_len,
+                                 void* hidden_out, void* residual_out, void* workspace, void* stream) {
+  return forward_impl(L, hidden, residual, positions, T, kv, block_table, max_blocks, seq_lens, query_start_loc, B,
+                      max_seq_len, hidden_out, residual_out, workspace, stream);
+}
+
+llama_status llama_layer_forward_noalloc(llama_layer* L, const void* hidden, const void* residual,
+                                         const int32_t* positions, int32_t T, const llama_kv_cache* kv,
+                                         const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                         const int32_t* query_start_loc, int32_t B, int32_t max_seq_len,
+                                         void* hidden_out, void* residual_out, void* stream) {
+  if (!L) return fail(LLAMA_ERR_INVALID_ARGUMENT, "layer is NULL");
+  if (T <= 0 || B <= 0 || max_seq_len <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_tokens, num_seqs and max_seq_len must be positive");
+  if (L->timing) return fail(LLAMA_ERR_INVALID_ARGUMENT, "per-kernel timing must be off (it creates events)");
+  const size_t need = carve(L, T, B, max_seq_len).total;
+  if (need > llk::kNoAllocScratchBytes)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT,
+                "this call needs %zu bytes of workspace; the no-allocation forward holds at most %zu "
+                "(use llama_layer_forward with a workspace)",
+                need, llk::kNoAllocScratchBytes);
+  if (L->scratch_err != hipSuccess) return hip_fail(L->scratch_err, "no-allocation scratch lookup");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != L->device)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "current device %d is not the layer's device %d", dev, L->device);
+  void* scratch = llk::noalloc_scratch(L->device);
+  if (!scratch) return fail(LLAMA_ERR_HIP, "no-allocation scratch of device %d not set up", L->device);
+  return forward_impl(L, hidden, residual, positions, T, kv, block_table, max_blocks, seq_lens, query_start_loc, B,
+                      max_seq_len, hidden_out, residual_out, scratch, stream);
 }
 
 void llama_layer_destroy(llama_layer* L) {

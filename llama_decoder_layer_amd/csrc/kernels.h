@@ -222,4 +222,12 @@ hipError_t launch_moe_experts(const void* x, int T, int H, int topk, const void*
                               hipEvent_t mid = nullptr);  // recorded between the two GEMMs
 hipError_t launch_moe_sum(const void* part, int T, int topk, int H, void* out, hipStream_t s);
 
+// noalloc.hip: the device array that holds the workspace of the forward
+// entry point that allocates nothing.  setup looks up a device's address
+// once (that device current), at layer create; scratch returns it (NULL
+// before setup or after a failed one).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch_setup(int device);
+void* noalloc_scratch(int device);
+
 }  // namespace llk
