@@ -1,21 +1,36 @@
 """Throughput of the Llama-70B-shape decoder-layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra A,B,..]
+                    [--no-cpu-baseline] [--cpu-seconds S]
 
 A step is one forward of the whole layer (input_layernorm, qkv_proj, RoPE +
 KV write, paged attention, o_proj + residual, post_attention_layernorm,
-gate_up_proj + SiluAndMul, down_proj) over one batch of seeded synthetic
-inputs that are resident in HBM before timing starts.  Default workload: 32
-sequences decoding one token each after a 2048-token cached context (70B
-layer shapes, bf16).  The extra lines measure the 70B prefill, the
-Qwen3-MoE layer (the MLP replaced by the routed experts) and one GPU's TP = 8
-share of the 70B layer (no all-reduce: one GPU).  Prints one JSON line.
+gate_up_proj + SiluAndMul, down_proj) -- through every layer of a stacked
+workload -- over one batch of seeded synthetic inputs that are resident in HBM
+before timing starts.  The main line is the 70B decode (32 sequences, one new
+token each after a 2048-token context); the extra lines are the 70B prefills
+(4 x 2048 and 1 x 32768), the 70B ragged decode through 4 layers, the
+Qwen3-MoE layer and one GPU's TP = 8 share of the 70B layer.  Prints one
+JSON line.
+
+Per workload:
+  * value / ms_per_step: K steps back to back between two events, with a
+    device synchronisation on both sides;
+  * per_call_flushed: each of N further steps between its own events, with
+    1 GiB written to a scratch buffer before each (outside the events) so the
+    256 MB last-level cache holds nothing of the step's inputs; median, min;
+  * kernel_avg_us: the library's own per-kernel events over K more steps;
+    the roofline names the kernel with the largest time per step and divides
+    its algorithmic work per launch by its average launch time;
+  * cpu_baseline: the oracle (float64 numpy, as it stands) on a bounded
+    sample of the same step, its weights widened before the timed region.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -25,59 +40,38 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "70B-shape layer tokens/s (prefill, decode) + % MFMA/HBM peak, 1 MI355X"
+FLUSH_BYTES = 1 << 30
+DEFAULT_EXTRA = ("llama70b_prefill_4x2048,llama70b_prefill_1x32768,llama70b_ragged_decode_b64_4layer,"
+                 "qwen3moe_decode_b32_ctx2048,qwen3moe_prefill_4x2048,llama70b_tp8shard_decode_b32_ctx2048,"
+                 "llama70b_tp8shard_prefill_4x2048")
+# timed calls with a cache flush between them, per workload (the rest: 10)
+FLUSHED_CALLS = {"llama70b_decode_b32_ctx2048": 20, "llama70b_ragged_decode_b64_4layer": 20,
+                 "llama70b_prefill_4x2048": 10, "llama70b_prefill_1x32768": 5}
 
-# HBM bytes per launch of a dominant kernel from rocprofv3 counters: FETCH_SIZE x 2.0 + WRITE_SIZE
-# x 1.0 (factors from a plain 1 GiB copy; profiles/pmc_copy_calibration.md).  Reported only while
-# the kernel's source file is the one the counters were taken on.
-COUNTER_TRAFFIC = {
-    ("qwen3moe_prefill_4x2048", "moe_gate_up_silu"): {
-        "bytes": 1979509634,
-        "source": "llama_decoder_layer_amd/csrc/moe.hip",
-        "sha1": "755722e27b7a0844d60c7110d6ebca39ad3481fe",
-        "summary": "profiles/moe_gate_up_silu_qwen3moe_prefill_4x2048_counters.md",
-    },
-    ("llama70b_tp8shard_prefill_4x2048", "gate_up_silu"): {
-        "bytes": 1535327477,
-        "source": "llama_decoder_layer_amd/csrc/gemm.hip",
-        "sha1": "b59e6a8385c5f8d8efa36a66f0e1b400cd7d33af",
-        "summary": "profiles/gate_up_silu_tp8shard_prefill_4x2048_counters.md",
-    },
-    ("llama70b_tp8shard_decode_b32_ctx2048", "gate_up"): {
-        "bytes": 129033522,
-        "source": "llama_decoder_layer_amd/csrc/gemm_skinny.hip",
-        "sha1": "ee8feba85821bd1f610cc90ce33abda82a193c67",
-        "summary": "profiles/gate_up_tp8shard_decode_b32_ctx2048_counters.md",
-    },
-    ("llama70b_prefill_4x2048", "gate_up_silu"): {
-        "bytes": 11743957635,
-        "source": "llama_decoder_layer_amd/csrc/gemm.hip",
-        "sha1": "b59e6a8385c5f8d8efa36a66f0e1b400cd7d33af",
-        "summary": "profiles/gate_up_silu_prefill_4x2048_counters.md",
-    },
-    ("qwen3moe_decode_b32_ctx2048", "moe_gate_up_silu"): {
-        "bytes": 703212909,
-        "source": "llama_decoder_layer_amd/csrc/moe.hip",
-        "sha1": "755722e27b7a0844d60c7110d6ebca39ad3481fe",
-        "summary": "profiles/moe_gate_up_silu_qwen3moe_decode_b32_ctx2048.md",
-    },
-    ("llama70b_decode_b32_ctx2048", "gate_up_silu"): {
-        "bytes": 945630302,
-        "source": "llama_decoder_layer_amd/csrc/gemm_skinny.hip",
-        "sha1": "ee8feba85821bd1f610cc90ce33abda82a193c67",
-        "summary": "profiles/gate_up_silu_decode_b32_ctx2048.md",
-    },
-}
+# HBM bytes per launch of a kernel from rocprofv3 counters: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
+# (factors from a plain 1 GiB copy; profiles/pmc_copy_calibration.md).  Reported only while every
+# source the kernel's code and launch plan come from is the one the counters were taken on.
+PLAN_SOURCES = ("llama_decoder_layer_amd/csrc/common.h", "llama_decoder_layer_amd/csrc/kernels.h",
+                "llama_decoder_layer_amd/csrc/api.cpp")
+COUNTER_TRAFFIC = {}
+
+
+def sources_sha1(paths):
+    import hashlib
+    h = hashlib.sha1()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def counter_traffic(workload, kernel):
-    import hashlib
     rec = COUNTER_TRAFFIC.get((workload, kernel))
     if rec is None:
         return None
     try:
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            if hashlib.sha1(f.read()).hexdigest() != rec["sha1"]:
-                return None
+        if sources_sha1((rec["source"],) + PLAN_SOURCES) != rec["sha1"]:
+            return None
     except OSError:
         return None
     return rec["bytes"]
@@ -94,26 +88,47 @@ def layer_flops(model, num_tokens, attn_pairs):
 
 def kernel_bytes(model, name, T, kv_tokens, active_experts=0):
     """Algorithmic HBM bytes of one launch of kernel `name` (bf16): weights
-    read once, activations in and out once, KV read once; an expert kernel
-    reads the weights of the experts that have tokens (`active_experts`)."""
+    read once, activations in and out once, K/V read once; an expert kernel
+    reads the weights of the experts that have tokens."""
     H, I, Q, QKV = model.hidden_size, model.intermediate_size, model.q_size, model.qkv_size
     e = 2
     P, Ie = T * model.num_experts_per_tok, model.moe_intermediate_size
     return {
         "gate_up": 2 * I * H * e + T * H * e,  # split-K partials, SiluAndMul in the reduce
-        "moe_gate_up_silu": active_experts * 2 * Ie * H * e + T * H * e + P * Ie * e,
-        "moe_down": active_experts * H * Ie * e + P * Ie * e + P * H * e,
         "gate_up_silu": 2 * I * H * e + T * H * e + T * I * e,
         "down_proj": H * I * e + T * I * e + T * H * e,
         "qkv_proj": QKV * H * e + T * H * e + T * QKV * e,
+        "o_proj": H * Q * e + T * Q * e + T * H * e,
         "o_proj_residual": H * Q * e + T * Q * e + 2 * T * H * e,
-        "attention": kv_tokens * 2 * model.kv_size * e + T * Q * e,
+        "attention": kv_tokens * 2 * model.kv_size * e + 2 * T * Q * e,
+        "moe_gate_up_silu": active_experts * 2 * Ie * H * e + T * H * e + P * Ie * e,
+        "moe_down": active_experts * H * Ie * e + P * Ie * e + P * H * e,
     }.get(name)
 
 
-def measure(wl, steps, warmup):
-    """Times `steps` forwards (after `warmup`) of workload `wl`, then the same
-    number again with the library's per-kernel HIP events on."""
+def kernel_flops(model, name, T, attn_pairs):
+    """Algorithmic FLOPs of one launch of kernel `name`."""
+    H, I, Q, QKV = model.hidden_size, model.intermediate_size, model.q_size, model.qkv_size
+    P, Ie = T * model.num_experts_per_tok, model.moe_intermediate_size
+    return {
+        "gate_up_silu": 2 * T * H * 2 * I,
+        "down_proj": 2 * T * I * H,
+        "qkv_proj": 2 * T * H * QKV,
+        "o_proj_residual": 2 * T * Q * H,
+        "attention": 4 * model.num_attention_heads * model.head_dim * attn_pairs,
+        "moe_gate_up_silu": 2 * P * H * 2 * Ie,
+        "moe_down": 2 * P * Ie * H,
+    }.get(name)
+
+
+def _flush(buf):
+    buf.add_(1)  # reads and writes all of it: 2 GiB of traffic evicts the 256 MB cache
+
+
+def measure(wl, steps, warmup, flushed_calls, flush_buf):
+    """Times `steps` forwards (after `warmup`) of workload `wl` back to back,
+    then `flushed_calls` forwards one at a time after a cache flush, then
+    `steps` more with the library's per-kernel HIP events on."""
     import torch
 
     import llama_decoder_layer_amd as lda
@@ -151,6 +166,18 @@ def measure(wl, steps, warmup):
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / steps
 
+    # one call at a time, each after a cache flush outside its events
+    per_call = []
+    for _ in range(flushed_calls):
+        _flush(flush_buf)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        per_call.append(a.elapsed_time(b))
+
     # per-kernel durations: HIP events the library records on its stream
     for L in layers:
         L.set_timing(True)
@@ -160,10 +187,11 @@ def measure(wl, steps, warmup):
     kt = {}
     for L in layers:
         for name, (tot, cnt) in L.timing_read().items():
-            a, c = kt.get(name, (0.0, 0))
-            kt[name] = (a + tot, c + cnt)
+            a_, c_ = kt.get(name, (0.0, 0))
+            kt[name] = (a_ + tot, c_ + cnt)
         L.set_timing(False)
     kernel_avg_ms = {k: v[0] / v[1] for k, v in kt.items()}
+    kernel_step_ms = {k: v[0] / steps for k, v in kt.items()}
     active = 0
     if model.num_experts:  # experts the batch routed tokens to (the same every step)
         ids = layers[0].workspace_tensor(ws, "topk_ids", T, B, batch.max_seq_len)
@@ -173,25 +201,25 @@ def measure(wl, steps, warmup):
     # causal (query, key) pairs: a sequence with c cached and n new rows
     attn_pairs = sum(n * c + n * (n + 1) // 2 for c, n in
                      ((batch.ctx_lens[b], batch.new_rows(b)) for b in range(B)))
-    dom = "moe_gate_up_silu" if model.num_experts else ("gate_up_silu" if "gate_up_silu" in kernel_avg_ms
-                                                          else "gate_up")
+    decode = T == B
+    work = ((lambda k: kernel_bytes(model, k, T, kv_tokens, active)) if decode
+            else (lambda k: kernel_flops(model, k, T, attn_pairs)))
+    # the kernel with the largest time per step (among those with a work figure)
+    cands = [k for k in kernel_step_ms if work(k) is not None]
+    dom = max(cands, key=lambda k: kernel_step_ms[k])
     dur = kernel_avg_ms[dom] / 1e3
-    if T == B:  # decode: one row per sequence, the step streams weights and KV
-        alg = kernel_bytes(model, dom, T, kv_tokens, active)
+    alg = work(dom)
+    if decode:
         roof = {"bound": "hbm", "kernel": dom, "achieved": alg / dur / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": alg / dur / 1e9 / PEAK_HBM_GBS,
-                "traffic": counter_traffic(wl.name, dom),
-                "algorithmic_bytes_per_launch": alg, "avg_launch_us": dur * 1e6}
+                "unit": "GB/s", "frac": alg / dur / 1e9 / PEAK_HBM_GBS, "traffic": counter_traffic(wl.name, dom),
+                "algorithmic_bytes_per_launch": alg, "avg_launch_us": dur * 1e6,
+                "share_of_step": kernel_step_ms[dom] / ms}
     else:
-        H, I = model.hidden_size, model.intermediate_size
-        alg = 2 * T * H * 2 * I
-        if model.num_experts:
-            alg = 2 * T * model.num_experts_per_tok * H * 2 * model.moe_intermediate_size
         roof = {"bound": "mfma", "kernel": dom, "achieved": alg / dur / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": alg / dur / 1e12 / PEAK_BF16_TFLOPS,
-                "traffic": counter_traffic(wl.name, dom),
-                "algorithmic_flops_per_launch": alg, "avg_launch_us": dur * 1e6}
-        if roof["traffic"] is not None and not model.num_experts:  # HBM bytes a launch must move at least
+                "traffic": counter_traffic(wl.name, dom), "algorithmic_flops_per_launch": alg,
+                "avg_launch_us": dur * 1e6, "share_of_step": kernel_step_ms[dom] / ms}
+        if roof["traffic"] is not None and kernel_bytes(model, dom, T, kv_tokens) is not None:
             roof["algorithmic_bytes_per_launch"] = kernel_bytes(model, dom, T, kv_tokens)
     wbytes = sum(v.numel() * v.element_size() for k, v in per_layer[0]["weights"].items()
                  if not k.startswith("experts_"))
@@ -204,7 +232,13 @@ def measure(wl, steps, warmup):
         "roofline": roof,
         "step_fraction": {"hbm": step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
                           "mfma": step_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS},
+        "per_call_flushed": {"calls": len(per_call), "flush_bytes_written": FLUSH_BYTES,
+                             "median_ms": round(statistics.median(per_call), 4) if per_call else None,
+                             "min_ms": round(min(per_call), 4) if per_call else None,
+                             "tokens_per_s_at_median": round(T / (statistics.median(per_call) / 1e3), 2)
+                             if per_call else None},
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in sorted(kernel_avg_ms.items())},
+        "kernel_us_per_step": {k: round(v * 1e3, 2) for k, v in sorted(kernel_step_ms.items())},
         "wall_s_timed_region": round(wall, 3),
         **({"experts_with_tokens": active} if model.num_experts else {}),
         "config": ({"workload": wl.name, "num_seqs": B, "q_len": wl.q_len,
@@ -215,6 +249,9 @@ def measure(wl, steps, warmup):
                         sum(1 for q, _ in wl.mix if q == 1), wl.mix[0][1], wl.mix[-1][0], wl.mix[-1][1]),
                     "layers": len(layers), "parallelism": "single GPU"}),
     }
+    for L in layers:
+        L.close()
+    del ws, bufs
     ctx = (batch, hidden, residual, per_layer)
     return res, ctx
 
@@ -222,7 +259,7 @@ def measure(wl, steps, warmup):
 STACK_SOURCE_LAYERS = 8
 
 
-def measure_stack(wl, steps, warmup, graph=True):
+def measure_stack(wl, steps, warmup, flushed_calls, flush_buf, graph=True):
     """A whole layer stack plus the final norm (llama_stack_forward), replayed
     from one captured HIP graph.  Weights are drawn for STACK_SOURCE_LAYERS
     layers and reused cyclically as the sources of the stack's copies: every
@@ -269,6 +306,17 @@ def measure_stack(wl, steps, warmup, graph=True):
     side.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / steps
+    per_call = []
+    for _ in range(flushed_calls):
+        with torch.cuda.stream(side):
+            _flush(flush_buf)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(side)
+        step()
+        b.record(side)
+        side.synchronize()
+        per_call.append(a.elapsed_time(b))
     kv_tokens = int(batch.seq_lens.sum())
     step_bytes = wl.layers * (weight_bytes + kv_tokens * 2 * model.kv_size * 2 + 4 * T * model.hidden_size * 2)
     achieved = step_bytes / (ms / 1e3) / 1e9
@@ -277,6 +325,9 @@ def measure_stack(wl, steps, warmup, graph=True):
         "roofline": {"bound": "hbm", "kernel": "whole step (%d layers + final norm)" % wl.layers,
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": None, "algorithmic_bytes_per_step": step_bytes},
+        "per_call_flushed": {"calls": len(per_call), "flush_bytes_written": FLUSH_BYTES,
+                             "median_ms": round(statistics.median(per_call), 4) if per_call else None,
+                             "min_ms": round(min(per_call), 4) if per_call else None},
         "wall_s_timed_region": round(wall, 3),
         "config": {"workload": wl.name, "num_seqs": B, "q_len": wl.q_len, "ctx_len": wl.ctx, "layers": wl.layers,
                    "final_norm": True, "hip_graph": bool(graph),
@@ -289,31 +340,155 @@ def measure_stack(wl, steps, warmup, graph=True):
     return res, None
 
 
+def hbm_read_ceiling(steps=10):
+    """The read-only streaming kernel over the bytes and in the launch shape
+    of the decode step's largest kernel (the 70B gate_up weight, one
+    workgroup of 7 waves per CU), and over 1 GiB with many small workgroups."""
+    import torch
+
+    import llama_decoder_layer_amd as lda
+    import synth
+
+    m = synth.LLAMA70B
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {}
+    for name, nbytes, wgs, threads in (("gate_up_shape", 2 * m.intermediate_size * m.hidden_size * 2, cus, 448),
+                                       ("1GiB_4096x256", 1 << 30, 4096, 256)):
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        sink = torch.empty(wgs * threads, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            lda.stream_read(src, wgs, threads, sink)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            lda.stream_read(src, wgs, threads, sink)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        out[name] = {"bytes": nbytes, "workgroups": wgs, "threads": threads, "avg_us": round(us, 2),
+                     "GB_per_s": round(nbytes / (us / 1e6) / 1e9, 1),
+                     "frac_of_peak": round(nbytes / (us / 1e6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del src, sink
+    return out
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    threads = affinity
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [affinity])
+    except Exception:
+        pass
+    return model, affinity, threads
+
+
+def cpu_baseline(wl, batch, hidden, residual, per_layer, min_seconds):
+    """The oracle (float64 numpy, as it stands) on a bounded sample of the
+    same step, its inputs and weights widened before the timed region.
+    Decode: every row of the step (the ragged batch: its first 4 sequences),
+    through every layer (the ragged batch: through layer 0, the time scaled
+    by its 4 layers).  Prefill: the first 256 token rows of the step.
+    Repeated until about `min_seconds` of CPU work have run."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    f64 = lambda t: t.detach().to("cpu", torch_f64()).numpy()
+    model = wl.model
+    T = batch.num_tokens
+    decode = T == batch.num_seqs
+    rows = (4 if len(per_layer) > 1 else T) if decode else min(256, T)
+    use_layers = per_layer[:1] if (decode and len(per_layer) > 1) else per_layer
+    scale = len(per_layer) / len(use_layers)
+    rows_list = list(range(rows))
+    seq_of = batch.seq_of_row()
+    seq_ids = sorted({seq_of[r] for r in rows_list})
+    cfg = model.config_dict()
+    pos = batch.positions.numpy().astype(np.int64)
+    h0 = f64(hidden)
+    r0 = None if residual is None else f64(residual)
+    prepared = []
+    for p in use_layers:
+        w = {k: f64(v) for k, v in p["weights"].items()}
+        seqs = [oracle.Seq(list(batch.rows(b)), f64(synth.gather_context(p["k_pool"], batch, b, batch.ctx_lens[b])),
+                           f64(synth.gather_context(p["v_pool"], batch, b, batch.ctx_lens[b], "v"))) for b in seq_ids]
+        prepared.append((w, seqs))
+    iters, t0 = 0, time.perf_counter()
+    while True:
+        h, r = h0, r0
+        for w, seqs in prepared:
+            o = oracle.decoder_layer(cfg, w, h, r, pos, seqs, want=rows_list)
+            h = h.copy()
+            r = np.zeros_like(h) if r is None else r.copy()
+            h[rows_list] = o["hidden_out"]
+            r[rows_list] = o["residual_out"]
+        iters += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = (time.perf_counter() - t0) * scale
+    cpu_model, affinity, threads = cpu_info()
+    return {"value": round(rows * iters / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d token rows of the step through %d of %d layer(s)%s, %d repetition(s); float64 numpy "
+                      "oracle, weights and inputs widened before timing" % (
+                          rows, T, len(use_layers), len(per_layer),
+                          " (time scaled by %d layers)" % len(per_layer) if scale != 1 else "", iters),
+            "seconds": round(time.perf_counter() - t0, 2), "cpu_model": cpu_model, "affinity_cores": affinity,
+            "blas_threads": threads}
+
+
+def torch_f64():
+    import torch
+    return torch.float64
+
+
+def run_workload(name, steps, warmup, flushed_calls, flush_buf, cpu_seconds):
+    import torch
+
+    import synth
+
+    wl = synth.WORKLOADS[name]
+    run = measure_stack if wl.layers > 4 else measure
+    res, ctx = run(wl, steps, warmup, flushed_calls, flush_buf)
+    if ctx is not None and cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, *ctx, min_seconds=cpu_seconds)
+    del ctx
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama70b_decode_b32_ctx2048")
-    ap.add_argument("--extra", default="llama70b_prefill_4x2048,qwen3moe_decode_b32_ctx2048,qwen3moe_prefill_4x2048,"
-                                       "llama70b_tp8shard_decode_b32_ctx2048,llama70b_tp8shard_prefill_4x2048",
+    ap.add_argument("--extra", default=DEFAULT_EXTRA,
                     help="comma-separated workloads measured after the main one ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=None,
-                    help="tokens of the step the oracle runs (default: all of a decode step, 256 of a prefill)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work per oracle baseline")
+    ap.add_argument("--flushed-calls", type=int, default=None, help="override the per-workload flushed call counts")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes, 3 times (a reference for "
                          "the HBM byte counters of a profiler), and exit")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="only run the read-only streaming kernel (the HBM read ceiling) and exit")
     args = ap.parse_args()
-    if args.calibrate_copy:
-        import torch
-        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "launches": 3}))
-        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sequences shard across GPUs with no exchange inside the layer)", file=sys.stderr)
@@ -324,25 +499,29 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
-    wl = synth.WORKLOADS[args.workload]
-    run = measure_stack if wl.layers > 4 else measure
-    main_res, ctx = run(wl, args.steps, args.warmup)
-    cpu = None
-    if not args.no_cpu_baseline and ctx is not None:
-        batch, hidden, residual, per_layer = ctx
-        rows = args.cpu_sample_rows or (batch.num_tokens if batch.num_tokens == batch.num_seqs else 256)
-        cpu = cpu_baseline(wl, batch, hidden, residual, per_layer, rows)
-    del ctx
-    torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "launches": 3}))
+        return
+    if args.ceiling_only:
+        print(json.dumps({"hbm_read_ceiling": hbm_read_ceiling()}))
+        return
+
+    flush_buf = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    calls = lambda n: args.flushed_calls if args.flushed_calls is not None else FLUSHED_CALLS.get(n, 10)
+    main_res = run_workload(args.workload, args.steps, args.warmup, calls(args.workload), flush_buf, cpu_s)
     extra = []
     if args.extra and args.extra != "none":
         for name in args.extra.split(","):
-            xw = synth.WORKLOADS[name]
-            r, c = (measure_stack if xw.layers > 4 else measure)(xw, max(3, args.steps // 4), min(args.warmup, 2))
-            del c
-            torch.cuda.empty_cache()
-            extra.append(r)
-
+            extra.append(run_workload(name, max(3, args.steps // 4), min(args.warmup, 2), calls(name), flush_buf,
+                                      cpu_s / 2))
+    ceiling = hbm_read_ceiling()
+    wl = synth.WORKLOADS[args.workload]
     out = {
         "metric": METRIC,
         "value": main_res["value"],
@@ -358,65 +537,17 @@ def main():
         "data": "synthetic (seeded N(0,1) activations and KV context, N(0,0.02) weights)",
         "config": main_res["config"],
         "roofline": main_res["roofline"],
-        "cpu_baseline": cpu,
+        "cpu_baseline": main_res.get("cpu_baseline"),
         "step_fraction": main_res.get("step_fraction"),
+        "per_call_flushed": main_res.get("per_call_flushed"),
         "kernel_avg_us": main_res.get("kernel_avg_us"),
+        "kernel_us_per_step": main_res.get("kernel_us_per_step"),
         **({"experts_with_tokens": main_res["experts_with_tokens"]} if "experts_with_tokens" in main_res else {}),
         "wall_s_timed_region": main_res["wall_s_timed_region"],
+        "hbm_read_ceiling": ceiling,
         "extra": extra,
     }
     print(json.dumps(out))
-
-
-def cpu_baseline(wl, batch, hidden, residual, per_layer, rows, min_seconds=10.0):
-    """The oracle (float64 numpy, as it stands) on a bounded sample of the
-    same step -- the first `rows` tokens of the batch through every layer --
-    repeated until about `min_seconds` of CPU work have run."""
-    import numpy as np
-    import torch
-
-    import oracle
-    import synth
-
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:
-        cores = os.cpu_count()
-    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
-    model = wl.model
-    rows = min(rows, batch.num_tokens)
-    rows_list = list(range(rows))
-    seq_of = batch.seq_of_row()
-    seq_ids = sorted({seq_of[r] for r in rows_list})
-    cfg = model.config_dict()
-    pos = batch.positions.numpy().astype(np.int64)
-    h0 = f64(hidden)
-    r0 = None if residual is None else f64(residual)
-    ctx = []
-    for p in per_layer:
-        ctx.append([(b, f64(synth.gather_context(p["k_pool"], batch, b, batch.ctx_lens[b])),
-                     f64(synth.gather_context(p["v_pool"], batch, b, batch.ctx_lens[b], "v"))) for b in seq_ids])
-    weights = [p["weights"] for p in per_layer]
-    iters, t0 = 0, time.perf_counter()
-    while True:
-        h, r = h0, r0
-        for w_t, c in zip(weights, ctx):
-            w = {k: f64(v) for k, v in w_t.items()}
-            seqs = [oracle.Seq(list(batch.rows(b)), kc, vc) for b, kc, vc in c]
-            o = oracle.decoder_layer(cfg, w, h, r, pos, seqs, want=rows_list)
-            h = h.copy()
-            r = np.zeros_like(h) if r is None else r.copy()
-            h[rows_list] = o["hidden_out"]
-            r[rows_list] = o["residual_out"]
-        iters += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(rows * iters / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of %d tokens of the step through %d layer(s), %d repetition(s); float64 numpy "
-                      "oracle including its weight widening" % (rows, batch.num_tokens, len(per_layer), iters),
-            "seconds": round(dt, 2)}
 
 
 if __name__ == "__main__":

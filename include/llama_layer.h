@@ -152,7 +152,9 @@ typedef struct {
  * slot p % 16.  K is stored after RoPE.  The V plane keeps the 16 slots of a
  * component together so that attention reads V as the key-major operand of
  * its P.V product with whole-vector loads (the layout vLLM's paged attention
- * uses for V).                                                              */
+ * uses for V).  It replaces a V plane ordered like K ([blocks][kv_heads][16]
+ * [head_dim]), which would make every P.V operand a gather of 2-byte values
+ * from 16 different slot rows.                                              */
 typedef struct {
   void* k;
   void* v;
@@ -405,6 +407,18 @@ LLAMA_API llama_status llama_op_reorder_gate_up(const void* src, int32_t interme
 LLAMA_API llama_status llama_op_add_rmsnorm(int32_t dtype, const void* x, const void* residual, const void* w,
                                   float eps, int32_t rows, int32_t hidden, void* normed,
                                   void* residual_out, void* stream);
+
+/* ---- measurement ------------------------------------------------------ */
+
+/* Reads `bytes` of device memory at src (a multiple of 16, 16-byte aligned)
+ * and nothing else: each of `workgroups` workgroups of `threads` threads (a
+ * multiple of 64, at most 1024) streams one contiguous region with 16-byte
+ * loads, several in flight per lane, and writes one 32-bit word per thread to
+ * sink [workgroups * threads] (device) so the loads are kept.  Its rate is
+ * the HBM read ceiling the streaming kernels of the decode path are measured
+ * against.  Errors: INVALID_ARGUMENT, HIP. */
+LLAMA_API llama_status llama_diag_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t threads,
+                                              void* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -118,6 +118,8 @@ def lib() -> ctypes.CDLL:
     L.llama_layer_timing_read.restype = i32
     L.llama_layer_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64), i32]
+    L.llama_diag_stream_read.restype = st
+    L.llama_diag_stream_read.argtypes = [vp, ctypes.c_size_t, i32, i32, vp, vp]
     L.llama_op_linear.restype = st
     L.llama_op_linear.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, vp]
     L.llama_op_reorder_gate_up.restype = st
@@ -148,7 +150,7 @@ EXPORTED = ["llama_layer_config_validate", "llama_layer_create", "llama_layer_wo
             "llama_layer_workspace_tensor", "llama_layer_rope_table", "llama_layer_set_timing", "llama_layer_timing_read",
             "llama_op_linear", "llama_op_reorder_gate_up", "llama_op_add_rmsnorm",
             "llama_stack_create", "llama_stack_workspace_bytes", "llama_stack_forward", "llama_stack_destroy",
-            "llama_stack_graph_create", "llama_graph_launch", "llama_graph_destroy"]
+            "llama_stack_graph_create", "llama_graph_launch", "llama_graph_destroy", "llama_diag_stream_read"]
 
 
 _hip_rt = None
@@ -519,6 +521,17 @@ class Graph:
             self.close()
         except Exception:
             pass
+
+
+def stream_read(src: torch.Tensor, workgroups: int, threads: int, sink: torch.Tensor, stream=None) -> None:
+    """llama_diag_stream_read: reads all of src (device, contiguous) and
+    nothing else; sink holds workgroups * threads int32."""
+    _dev(src, "src")
+    _dev(sink, "sink")
+    if sink.numel() * sink.element_size() < workgroups * threads * 4:
+        raise ValueError("sink too small")
+    _check(lib().llama_diag_stream_read(_ptr(src), src.numel() * src.element_size(), workgroups, threads, _ptr(sink),
+                                        _stream(stream)))
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, epilogue: Epilogue = Epilogue.STORE, out=None, stream=None):

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build", "llama_layer")
 LIB = os.path.join(HERE, "libllama_layer.so")
 
 SOURCES = ["api.cpp", "rmsnorm.hip", "gemm.hip", "rope_kv.hip", "attention.hip", "attention_decode.hip", "gemm_skinny.hip",
-           "attention_prefill.hip", "batch_map.hip", "moe.hip", "validate.hip", "noalloc.hip"]
+           "attention_prefill.hip", "batch_map.hip", "moe.hip", "validate.hip", "noalloc.hip", "diag.hip"]
 ARCH = "gfx950"
 
 

@@ -222,6 +222,13 @@ hipError_t launch_moe_experts(const void* x, int T, int H, int topk, const void*
                               hipEvent_t mid = nullptr);  // recorded between the two GEMMs
 hipError_t launch_moe_sum(const void* part, int T, int topk, int H, void* out, hipStream_t s);
 
+// diag.hip: a read-only stream of `bytes` (a multiple of 16) from src, each
+// of `workgroups` workgroups of `threads` threads reading one contiguous
+// region with 16-byte loads; one word per thread goes to sink
+// [workgroups * threads] so that the loads are not dropped.
+hipError_t launch_stream_read(const void* src, size_t bytes, int workgroups, int threads, void* sink,
+                              hipStream_t s);
+
 // noalloc.hip: the device array that holds the workspace of the forward
 // entry point that allocates nothing.  setup looks up a device's address
 // once (that device current), at layer create; scratch returns it (NULL
