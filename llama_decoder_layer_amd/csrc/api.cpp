@@ -93,6 +93,7 @@ struct llama_layer {
   void* w_e2 = nullptr;
   int E = 0, topk = 0, moe_I = 0;
   float2* rope = nullptr;
+  bool owns_rope = true;  // false: the table belongs to another layer of the same stack
 
   bool timing = false;
   std::vector<std::vector<TimingMark>> marks;  // one list per forward
@@ -256,7 +257,8 @@ hipError_t alloc_weight(void** p, size_t bytes) {
 void free_layer(llama_layer* L) {
   if (!L) return;
   void* bufs[] = {L->w_in,  L->w_qkv,    L->w_o,   L->w_post, L->w_gu,          L->w_down,
-                  L->w_qn,  L->w_kn,     L->w_router, L->w_e13, L->w_e2, (void*)L->rope};
+                  L->w_qn,  L->w_kn,     L->w_router, L->w_e13, L->w_e2,
+                  L->owns_rope ? (void*)L->rope : nullptr};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   for (auto& list : L->marks)
@@ -401,8 +403,14 @@ llama_status llama_layer_config_validate(const llama_layer_config* c) {
   return LLAMA_OK;
 }
 
-llama_status llama_layer_create(const llama_layer_config* config, const llama_layer_weights* w,
-                                void* stream, llama_layer** out) {
+}  // extern "C"
+
+namespace {
+
+// A layer; with shared_rope the RoPE table of another layer of the same
+// configuration (a stack builds it once), else its own.
+llama_status create_layer(const llama_layer_config* config, const llama_layer_weights* w, void* stream,
+                          float2* shared_rope, llama_layer** out) {
   llama_status st = llama_layer_config_validate(config);
   if (st != LLAMA_OK) return st;
   if (!w || !out || !w->input_layernorm || !w->qkv_proj || !w->o_proj || !w->post_attention_layernorm)
@@ -487,6 +495,17 @@ llama_status llama_layer_create(const llama_layer_config* config, const llama_la
     }
   }
 
+  if (shared_rope) {
+    L->rope = shared_rope;
+    L->owns_rope = false;
+    e = hipStreamSynchronize(s);  // the weight copies read the caller's buffers
+    if (e != hipSuccess) {
+      free_layer(L);
+      return hip_fail(e, "weight copy");
+    }
+    *out = L;
+    return LLAMA_OK;
+  }
   // RoPE table: angles and cos/sin in double precision, stored as float
   const int half = c.head_dim / 2;
   const size_t n = (size_t)c.max_position_embeddings * half;
@@ -510,6 +529,15 @@ llama_status llama_layer_create(const llama_layer_config* config, const llama_la
   }
   *out = L;
   return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+llama_status llama_layer_create(const llama_layer_config* config, const llama_layer_weights* w,
+                                void* stream, llama_layer** out) {
+  return create_layer(config, w, stream, nullptr, out);
 }
 
 size_t llama_layer_workspace_bytes(const llama_layer* L, int32_t num_tokens, int32_t num_seqs,
@@ -562,11 +590,23 @@ llama_status llama_layer_rope_table(const llama_layer* L, const void** table, in
 
 namespace {
 
+// Hand-over between the layers of a stack: the input hidden state may arrive
+// as the previous layer's down_proj split-K partials (fp32 planes in the
+// workspace, summed and rounded by this layer's input norm exactly as the
+// previous layer's reduce would have), and the layer may leave its own
+// down_proj partials there instead of reducing them into hidden_out.
+struct StackLink {
+  const float* in_part = nullptr;  // S fp32 planes [in_S][T][H], or NULL: read `hidden`
+  int in_S = 0;
+  bool keep_down_part = false;     // leave down_proj's partials (when it makes them)
+  int out_S = 0;                   // set: planes left (0: hidden_out was written)
+};
+
 llama_status forward_impl(llama_layer* L, const void* hidden, const void* residual, const int32_t* positions,
                           int32_t T, const llama_kv_cache* kv, const int32_t* block_table, int32_t max_blocks,
                           const int32_t* seq_lens, const int32_t* query_start_loc, int32_t B,
                           int32_t max_seq_len, void* hidden_out, void* residual_out, void* workspace,
-                          void* stream) {
+                          void* stream, StackLink* link = nullptr) {
   if (!L) return fail(LLAMA_ERR_INVALID_ARGUMENT, "layer is NULL");
   if (!hidden || !positions || !kv || !kv->k || !kv->v || !block_table || !seq_lens || !hidden_out ||
       !residual_out || !workspace)
@@ -642,7 +682,14 @@ llama_status forward_impl(llama_layer* L, const void* hidden, const void* residu
     if (e != hipSuccess) return hip_fail(e, "batch_map");
     mk.mark("batch_map");
   }
-  e = llk::launch_add_rmsnorm(dt, hidden, residual, L->w_in, c.rms_norm_eps, T, H, h, residual_out, s);
+  if (link) link->out_S = 0;
+  if (link && link->in_part) {
+    if (!residual) return fail(LLAMA_ERR_INVALID_ARGUMENT, "a hidden state passed as partials needs a residual");
+    e = llk::launch_add_rmsnorm(dt, nullptr, residual, L->w_in, c.rms_norm_eps, T, H, h, residual_out, s,
+                                link->in_part, link->in_S, true);
+  } else {
+    e = llk::launch_add_rmsnorm(dt, hidden, residual, L->w_in, c.rms_norm_eps, T, H, h, residual_out, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "input_layernorm");
   mk.mark("input_layernorm");
   float* gp = (float*)(ws + w.gpart);
@@ -715,6 +762,10 @@ llama_status forward_impl(llama_layer* L, const void* hidden, const void* residu
     e = llk::launch_skinny(act, L->w_down, T, H, I, llk::kEpiPartial, w.pd, gp, s, L->wlayout);
     if (e != hipSuccess) return hip_fail(e, "down_proj");
     mk.mark("down_proj");
+    if (link && link->keep_down_part) {  // the next layer's input norm (or the final norm) sums them
+      link->out_S = w.pd.splits;
+      return LLAMA_OK;
+    }
     e = llk::launch_splitk_reduce(gp, w.pd.splits, T, H, hidden_out, s);
     if (e != hipSuccess) return hip_fail(e, "down_proj reduce");
     mk.mark("down_proj_reduce");
@@ -944,7 +995,8 @@ llama_status llama_stack_create(const llama_layer_config* config, int32_t num_la
   S->eps = config->rms_norm_eps;
   for (int l = 0; l < num_layers; ++l) {
     llama_layer* L = nullptr;
-    st = llama_layer_create(config, &weights[l], stream, &L);
+    // one RoPE table for the whole stack (the first layer builds it)
+    st = create_layer(config, &weights[l], stream, l == 0 ? nullptr : S->layers[0]->rope, &L);
     if (st != LLAMA_OK) {
       free_stack(S);
       return st;
@@ -984,18 +1036,30 @@ llama_status llama_stack_forward(llama_stack* S, const void* hidden, const int32
   char* ws = (char*)workspace;
   void* h = ws + w.h;
   void* r = ws + w.r;
+  // a layer's down_proj split-K partials (decode) stay in the layer workspace
+  // and the next layer's input norm -- or the final norm -- sums them: the
+  // same sums, rounded the same way, one launch fewer per layer
+  const float* part = (const float*)(ws + w.layer + carve(S->layers[0], T, B, max_seq_len).gpart);
+  int part_S = 0;
   for (size_t l = 0; l < S->layers.size(); ++l) {
     // layer 0 reads the input with no residual; later layers update (h, r) in place
     const void* hin = l == 0 ? hidden : h;
     const void* rin = l == 0 ? nullptr : r;
-    const llama_status st = llama_layer_forward(S->layers[l], hin, rin, positions, T, &kv_caches[l], block_table,
-                                                max_blocks, seq_lens, query_start_loc, B, max_seq_len, h, r,
-                                                ws + w.layer, stream);
+    StackLink link;
+    link.in_part = part_S > 0 ? part : nullptr;
+    link.in_S = part_S;
+    link.keep_down_part = true;
+    const llama_status st = forward_impl(S->layers[l], hin, rin, positions, T, &kv_caches[l], block_table,
+                                         max_blocks, seq_lens, query_start_loc, B, max_seq_len, h, r, ws + w.layer,
+                                         stream, &link);
     if (st != LLAMA_OK) return st;
+    part_S = link.out_S;
   }
   // final norm of hidden + residual
-  hipError_t e = llk::launch_add_rmsnorm(S->dtype, h, r, S->w_final, S->eps, T, S->H, out, nullptr,
-                                         (hipStream_t)stream);
+  hipError_t e = part_S > 0 ? llk::launch_add_rmsnorm(S->dtype, nullptr, r, S->w_final, S->eps, T, S->H, out, nullptr,
+                                                      (hipStream_t)stream, part, part_S, true)
+                            : llk::launch_add_rmsnorm(S->dtype, h, r, S->w_final, S->eps, T, S->H, out, nullptr,
+                                                      (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "final norm");
   return LLAMA_OK;
 }

@@ -10,10 +10,11 @@ enum Dtype { kBF16 = 0, kFP32 = 1 };
 enum Epi { kEpiStore = 0, kEpiAdd = 1, kEpiSiluMul = 2, kEpiPartial = 3 };
 
 // rmsnorm.hip.  With xpart != NULL (bf16 only) the input row is the sum of
-// S fp32 partial rows xpart[s][row][:] instead of x.
+// S fp32 partial rows xpart[s][row][:] instead of x, rounded to bf16 first
+// when round_part (the value a projection storing its output would pass on).
 hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* res, const void* w, float eps,
                               int rows, int hidden, void* normed, void* res_out, hipStream_t s,
-                              const float* xpart = nullptr, int S = 0);
+                              const float* xpart = nullptr, int S = 0, bool round_part = false);
 
 // Layouts of a bf16 weight [rows][K] that the GEMMs read.  Element (r, k)
 // sits at (r/16)*16*K + (r%16)*rs + (k/32)*ks + k%32:

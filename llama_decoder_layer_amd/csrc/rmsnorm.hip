@@ -27,9 +27,11 @@ constexpr int kWideThreads = 1024;
 constexpr int kWideMaxRows = 256;
 
 // S > 0: the input row is the sum of S fp32 partial rows xpart[s][row][:]
-// (a split-K projection's output), added in split order.  NT threads, each
-// with at most kMaxChunks 16-byte chunks: H <= NT * kMaxChunks * (16 / sizeof(T)).
-template <typename T, int S, int NT>
+// (a split-K projection's output), added in split order; with RX that sum is
+// first rounded to T, exactly as if the projection had stored its output and
+// this kernel read it back.  NT threads, each with at most kMaxChunks 16-byte
+// chunks: H <= NT * kMaxChunks * (16 / sizeof(T)).
+template <typename T, int S, int NT, bool RX>
 __global__ __launch_bounds__(NT) void add_rmsnorm_kernel(const T* __restrict__ x,
                                                                const T* res,
                                                                const T* __restrict__ w, float eps,
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(NT) void add_rmsnorm_kernel(const T* __restrict__ x
 #pragma unroll
             for (int q = 0; q < 4; ++q) a[q] += v[sp][q];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) xf[e + q] = a[q];
+          for (int q = 0; q < 4; ++q) xf[e + q] = RX ? to_f32(from_f32<T>(a[q])) : a[q];
         }
       } else {
         xv = ld16<V>(x + base + (size_t)ci * VN);
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(NT) void add_rmsnorm_kernel(const T* __restrict__ x
 
 hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* res, const void* w, float eps,
                               int rows, int hidden, void* normed, void* res_out, hipStream_t s,
-                              const float* xpart, int S) {
+                              const float* xpart, int S, bool round_part) {
   if (rows <= 0) return hipSuccess;
   if (dtype == kBF16) {
     const bf16* r = (const bf16*)res;
@@ -132,22 +134,27 @@ hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* res, const v
     bf16* n = (bf16*)normed;
     bf16* ro = (bf16*)res_out;
     const bool wide = rows <= kWideMaxRows && hidden >= 8 * kWideThreads;
-#define LLK_NORM_NT(SS, XX, NT) \
-  add_rmsnorm_kernel<bf16, SS, NT><<<rows, NT, 0, s>>>((const bf16*)(XX), r, wb, eps, hidden, n, ro, xpart, rows)
-#define LLK_NORM(SS, XX)                \
-  if (wide) LLK_NORM_NT(SS, XX, kWideThreads); \
-  else LLK_NORM_NT(SS, XX, kThreads)
-    if (!xpart) { LLK_NORM(0, x); }
+#define LLK_NORM_NT(SS, XX, NT, RR)                                                                      \
+  add_rmsnorm_kernel<bf16, SS, NT, RR><<<rows, NT, 0, s>>>((const bf16*)(XX), r, wb, eps, hidden, n, ro, xpart, \
+                                                           rows)
+#define LLK_NORM_R(SS, XX, RR)                       \
+  if (wide) LLK_NORM_NT(SS, XX, kWideThreads, RR); \
+  else LLK_NORM_NT(SS, XX, kThreads, RR)
+#define LLK_NORM(SS, XX)              \
+  if (round_part) { LLK_NORM_R(SS, XX, true); } \
+  else { LLK_NORM_R(SS, XX, false); }
+    if (!xpart) { LLK_NORM_R(0, x, false); }
     else if (S == 1) { LLK_NORM(1, nullptr); }
     else if (S == 2) { LLK_NORM(2, nullptr); }
     else if (S == 4) { LLK_NORM(4, nullptr); }
     else if (S == 8) { LLK_NORM(8, nullptr); }
     else return hipErrorInvalidValue;
 #undef LLK_NORM
+#undef LLK_NORM_R
 #undef LLK_NORM_NT
   } else {
     if (xpart) return hipErrorInvalidValue;
-    add_rmsnorm_kernel<float, 0, kThreads><<<rows, kThreads, 0, s>>>(
+    add_rmsnorm_kernel<float, 0, kThreads, false><<<rows, kThreads, 0, s>>>(
         (const float*)x, (const float*)res, (const float*)w, eps, hidden, (float*)normed, (float*)res_out,
         nullptr, rows);
   }

@@ -163,3 +163,19 @@ def workspace(layer, ws, T, B, max_seq_len) -> dict:
     names = ("h", "qkv", "attn", "h2") + (("topk_ids", "topk_weights", "moe_sorted", "moe_act", "moe_part")
                                           if moe else ("act",))
     return {n: layer.workspace_tensor(ws, n, T, B, max_seq_len) for n in names}
+
+
+def nan_report(ws: dict, outputs: dict) -> str:
+    """Where non-finite values sit: for each workspace tensor (in the order
+    the layer writes them) and output, the rows holding any.  Called only when
+    an output is non-finite, so it adds no synchronisation to a good run."""
+    parts = []
+    for n in ("h", "qkv", "attn", "h2", "act"):
+        if n in ws:
+            bad = (~torch.isfinite(ws[n].float())).any(dim=1).nonzero().flatten().tolist()
+            parts.append("%s rows %s" % (n, bad[:12] if bad else "none"))
+    for n, t in outputs.items():
+        bad = (~torch.isfinite(t.float())).any(dim=1).nonzero().flatten().tolist()
+        parts.append("%s rows %s" % (n, bad[:12] if bad else "none"))
+    return "non-finite values: " + "; ".join(parts)
+

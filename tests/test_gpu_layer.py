@@ -74,6 +74,8 @@ def _run(workload, ctx_lens=None, layers=1, check_kv=True, repeat=False, qsl=Non
             assert torch.equal(kp.view(torch.int16), kp1.view(torch.int16))
             assert torch.equal(vp.view(torch.int16), vp1.view(torch.int16))
         _check_metadata_unchanged(meta0, pos, bt, sl, qsl)
+        if not (torch.isfinite(ho.float()).all() and torch.isfinite(ro.float()).all()):
+            raise AssertionError("layer %d: %s" % (l, stages.nan_report(wst, {"hidden_out": ho, "residual_out": ro})))
         results.append((w, kp0, vp0, kp, vp, h, r, ho, ro, qkv, table, wst))
         h, r = ho, ro
         layer.close()

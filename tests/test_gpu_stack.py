@@ -9,6 +9,7 @@ import torch
 import llama_decoder_layer_amd as lda
 import oracle
 import synth
+from tests import stages
 from tests.parity import (COS_MIN, compare, cosine, device_batch, device_qsl, moe_check_weights, moe_fix_routing,
                           np64, oracle_seqs, oracle_weights, run_oracle)
 
@@ -57,16 +58,24 @@ def test_mid_stack_mixed_batch_vs_oracle():
     stack.close()
     cfg = MID.config_dict()
     # the same layers one at a time on fresh copies of the pools
-    h, r, ins, outs = hidden, None, [], []
+    h, r, ins, outs, wss = hidden, None, [], [], []
+    T, B = batch.num_tokens, batch.num_seqs
     for l in range(layers):
         kp, vp = pools0[l][0].clone(), pools0[l][1].clone()
         L = lda.Layer(cfg, weights[l])
-        ho, ro = L.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, query_start_loc=qsl)
+        ws = L.alloc_workspace(T, B, batch.max_seq_len)
+        ho, ro = L.forward(h, r, pos, kp, vp, bt, sl, batch.max_seq_len, workspace=ws, query_start_loc=qsl)
         torch.cuda.synchronize()
+        wss.append(stages.workspace(L, ws, T, B, batch.max_seq_len))
         L.close()
         ins.append((h, r))
         outs.append((ho, ro))
         h, r = ho, ro
+    for l in range(layers):
+        ho, ro = outs[l]
+        if not (torch.isfinite(ho.float()).all() and torch.isfinite(ro.float()).all()):
+            raise AssertionError("chained layer %d: %s" % (l, stages.nan_report(wss[l], {"hidden_out": ho,
+                                                                                        "residual_out": ro})))
     chained, _ = lda.add_rmsnorm(h, r, final, MID.rms_norm_eps, write_residual=False)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), chained.view(torch.int16))
