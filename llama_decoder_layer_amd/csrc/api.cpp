@@ -700,12 +700,25 @@ llama_status forward_impl(llama_layer* L, const void* hidden, const void* residu
     qkn.k = L->w_kn;
     qkn.eps = c.rms_norm_eps;
   }
+  // a decode batch on the matrix-core decode kernel: its workgroups form
+  // their rows' q, k, v from the projection's partials, rotate them and
+  // write the cache slot themselves (no separate RoPE / KV-write launch)
+  llk::DecodeRope fuse;
+  const bool fused_rope = w.skinny && decode && dt == LLAMA_DTYPE_BF16;
   if (w.skinny) {
     e = llk::launch_skinny(h, L->w_qkv, T, L->qkv_n, H, llk::kEpiPartial, w.pq, gp, s, L->wlayout);
     if (e != hipSuccess) return hip_fail(e, "qkv_proj");
     mk.mark("qkv_proj");
-    e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, map, kv->k,
-                            kv->v, s, gp, w.pq.splits, qkn);
+    if (fused_rope) {
+      fuse.part = gp;
+      fuse.S = w.pq.splits;
+      fuse.table = L->rope;
+      fuse.qkv = qkv;
+      fuse.qkn = qkn;
+    } else {
+      e = llk::launch_rope_kv(dt, qkv, T, positions, L->rope, nq, nkv, d, block_table, max_blocks, map, kv->k,
+                              kv->v, s, gp, w.pq.splits, qkn);
+    }
   } else {
     e = llk::launch_linear(dt, h, L->w_qkv, T, L->qkv_n, H, llk::kEpiStore, qkv, s, L->wlayout, tp, w.tpart_bytes);
     if (e != hipSuccess) return hip_fail(e, "qkv_proj");
@@ -714,10 +727,11 @@ llama_status forward_impl(llama_layer* L, const void* hidden, const void* residu
                             kv->v, s, nullptr, 0, qkn);
   }
   if (e != hipSuccess) return hip_fail(e, "rope_kv_write");
-  mk.mark("rope_kv_write");
+  if (!fused_rope) mk.mark("rope_kv_write");
   hipEvent_t mid = w.plan.parts > 1 ? mk.extra() : nullptr;
   e = llk::launch_attention(dt, qkv, L->qkv_n, T, positions, nq, nkv, d, kv->k, kv->v, block_table, max_blocks,
-                            map, decode, w.plan, part, (int*)(ws + w.row_parts), attn, s, mid);
+                            map, decode, w.plan, part, (int*)(ws + w.row_parts), attn, s, mid,
+                            fused_rope ? &fuse : nullptr);
   if (e != hipSuccess) return hip_fail(e, "attention");
   if (mid) mk.list->push_back({"attention", mid});
   mk.mark(w.plan.parts > 1 ? "attention_combine" : "attention");

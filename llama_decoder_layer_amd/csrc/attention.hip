@@ -320,17 +320,19 @@ AttnPlan attention_plan(int T, int B, int nq, int nkv, int d, bool decode, int m
 }
 
 hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
-                            int nkv, int d, const void* k_cache, const void* v_cache,
+                            int nkv, int d, void* k_cache, void* v_cache,
                             const int* block_table, int max_blocks, const SeqMap& map, bool decode,
                             const AttnPlan& plan, float* partials, int* row_parts, void* out, hipStream_t s,
-                            hipEvent_t mid_event) {
+                            hipEvent_t mid_event, const DecodeRope* rope) {
   if (T <= 0) return hipSuccess;
+  if (rope && !(dtype == kBF16 && decode)) return hipErrorInvalidValue;
   hipError_t e;
   int* rp = nullptr;  // per-row partition counts for the combine
   if (dtype == kBF16 && decode) {
     // one query row per sequence: row t is sequence t
     e = launch_decode_attention_bf16(q, ldq, T, positions, nq, nkv, d, k_cache, v_cache, block_table,
-                                     max_blocks, plan.part_len, plan.parts, partials, out, s);
+                                     max_blocks, plan.part_len, plan.parts, partials, out, s, nullptr, nullptr,
+                                     rope);
   } else if (dtype == kBF16 && prefill_attention_supported(nq, nkv, d)) {
     // the single-row sequences of a mixed batch on the decode kernel, the
     // query tiles on the prefill kernel; with parts > 1 both record each

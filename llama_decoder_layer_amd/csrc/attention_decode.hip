@@ -38,6 +38,21 @@
 // With several partitions each workgroup leaves (reference max, sum, unnormalised o)
 // for the combine kernel in attention.hip.  In a mixed batch the kernel
 // serves the sequences with a single query row from a list of their rows.
+//
+// Decode after a split-K qkv projection (SP > 0 partial planes): the
+// workgroup of (token t, KV head g) first forms what it needs of the
+// projection row itself -- the G query heads of its group, its k and v head
+// -- as the bf16 rounding of the SP fp32 partials summed in split order,
+// applies the q/k norm when the model has one, rotates q and k (page "LLama",
+// section "4 LlamaAttention": rotary_emb on q and k only; cos/sin from the
+// layer's table, y0 = fmaf(x0, c, -(x1 * s)), y1 = fmaf(x1, c, x0 * s), each
+// rounded once), and -- the workgroup whose key partition holds the token's
+// own position -- writes k_rot and v into the token's cache slot before any
+// wave reads that block ("模型库与算子层 — 代码走读", section "Attention 层":
+// the new K/V are in the cache before attention reads it), and leaves q_rot,
+// k and v in the qkv workspace row.  The arithmetic is the RoPE kernel's
+// (rope_kv.hip), term for term, so the cache and workspace bits are the same
+// as with that kernel in between; the step saves its launch.
 #include "common.h"
 #include "kernels.h"
 
@@ -52,16 +67,26 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// The fused projection reduce + RoPE + cache write of a decode row (SP > 0).
+struct DecFuse {
+  const float* part = nullptr;   // [SP][T][ld] fp32 partial planes of the qkv projection
+  const float2* table = nullptr; // RoPE (cos, sin) [max_position][D/2]
+  bf16* qkv = nullptr;           // [T][ld] workspace row: q_rot, k (before RoPE), v
+  const bf16* qn = nullptr;      // q/k norm weights [D], or NULL
+  const bf16* kn = nullptr;
+  float eps = 0.f;
+};
+
 // Grid: (token * KV heads + KV head, partition).  The KV heads of a token
 // are adjacent in launch order, so the workgroups that run together walk the same
 // scattered cache blocks (the heads of a block are contiguous in the pool).
-template <int D>
+template <int D, int SP>
 __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
     const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
-    const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
+    bf16* __restrict__ kc, bf16* __restrict__ vc, const int* __restrict__ block_table,
     int max_blocks, int part_len, int parts, float* __restrict__ partials,
     bf16* __restrict__ out, const int* __restrict__ dec, const int* __restrict__ ndec,
-    const int* __restrict__ seq_of, int* __restrict__ row_parts) {
+    const int* __restrict__ seq_of, int* __restrict__ row_parts, DecFuse fz, int T) {
   constexpr int KS = D / 32;  // k-steps of S = K q^T
   constexpr int DT = D / 16;  // 16-wide output tiles of P V
   const int G = nq / nkv;
@@ -100,13 +125,6 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
   const bf16x8 zero8 = {};
   const bf16x4 zero4 = {};
   bf16x8 qf[KS];
-  {
-    const bool hv = l16 < G;
-    const bf16* qrow = q + (size_t)t * ldq + (size_t)(g * G + (hv ? l16 : 0)) * D + 8 * grp;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = hv ? ld16<bf16x8>(qrow + 32 * s) : zero8;
-  }
-
   const float sc = kLog2e / sqrtf((float)D);
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[DT];
@@ -131,7 +149,111 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
   };
 
   int j = jb + wave;
-  if (j < je) load(j);
+  // with the fused RoPE, this wave's first block is fetched while the
+  // projection row is formed -- unless it holds the new key, which the
+  // prologue writes first
+  bool pre = false;
+  if constexpr (SP > 0) {
+    pre = j < je && j != p / kKvBlock;
+    if (pre) load(j);
+    // ---- this row's q heads of group g, its k and v head: partials summed
+    // in split order and rounded (the projection's stored value) ...
+    __shared__ float sx[18 * D];                        // (G + 2) heads, G <= 16
+    __shared__ __attribute__((aligned(16))) bf16 sq[16][D];  // q_rot of the group
+    const int half = D / 2;
+    const int nel = (G + 2) * D;
+    const bool owner = part == p / part_len;            // the partition holding the new key
+    auto col = [&](int e) {                             // element e of (q heads, k, v) -> qkv column
+      const int h = e / D, c = e - h * D;
+      return h < G ? (g * G + h) * D + c : (h == G ? (nq + g) * D + c : (nq + nkv + g) * D + c);
+    };
+    // two 4-element items per thread in flight at once (G + 2 heads of D
+    // make at most 2.25 passes of the workgroup for G <= 16)
+    constexpr int kStride = kWaves * kWave * 4;
+    for (int e0 = threadIdx.x * 4; e0 < nel; e0 += 2 * kStride) {
+      f32x4 v[2][SP];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e4 = e0 + u * kStride;
+        if (e4 < nel) {
+          const int c0 = col(e4);  // 4 consecutive elements of one head
+#pragma unroll
+          for (int sp = 0; sp < SP; ++sp)
+            v[u][sp] = *reinterpret_cast<const f32x4*>(fz.part + ((size_t)sp * T + t) * ldq + c0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e4 = e0 + u * kStride;
+        if (e4 >= nel) continue;
+        f32x4 a = v[u][0];
+#pragma unroll
+        for (int sp = 1; sp < SP; ++sp)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) a[k] += v[u][sp][k];
+        bf16x4 r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          r[k] = static_cast<bf16>(a[k]);
+          sx[e4 + k] = static_cast<float>(r[k]);
+        }
+        if (owner && e4 >= G * D) *reinterpret_cast<bf16x4*>(fz.qkv + (size_t)t * ldq + col(e4)) = r;  // k, v
+      }
+    }
+    __syncthreads();
+    // ---- ... the q/k norm, RoPE of the G q heads and the k head, and the
+    // new token's k_rot and v into its cache slot
+    const int blk = block_table[(size_t)b * max_blocks + p / kKvBlock];
+    const int slot = p % kKvBlock;
+    const float2* cs = fz.table + (size_t)p * half;
+    for (int idx = threadIdx.x; idx < (G + 1) * half; idx += kWaves * kWave) {
+      const int h = idx / half, i = idx - h * half;  // h == G: the k head
+      float x0 = sx[h * D + i], x1 = sx[h * D + i + half];
+      if (fz.qn) {
+        // the `half` lanes of one head are consecutive and aligned (a whole
+        // wave for D = 128, half a wave for D = 64)
+        float ss = x0 * x0 + x1 * x1;
+        ss = half == 64 ? group_sum<64>(ss) : group_sum<32>(ss);
+        const float inv = rsqrtf(ss / (float)D + fz.eps);
+        const bf16* wn = h < G ? fz.qn : fz.kn;
+        x0 = to_f32(static_cast<bf16>(x0 * inv * to_f32(wn[i])));
+        x1 = to_f32(static_cast<bf16>(x1 * inv * to_f32(wn[i + half])));
+      }
+      const float2 c = cs[i];
+      const bf16 y0 = static_cast<bf16>(fmaf(x0, c.x, -(x1 * c.y)));
+      const bf16 y1 = static_cast<bf16>(fmaf(x1, c.x, x0 * c.y));
+      if (h < G) {
+        sq[h][i] = y0;
+        sq[h][i + half] = y1;
+        if (owner) {
+          bf16* qo = fz.qkv + (size_t)t * ldq + (size_t)(g * G + h) * D;
+          qo[i] = y0;
+          qo[i + half] = y1;
+        }
+      } else if (owner) {
+        bf16* dst = kc + (((size_t)blk * nkv + g) * kKvBlock + slot) * D;
+        dst[i] = y0;
+        dst[i + half] = y1;
+      }
+    }
+    if (owner) {  // v: a copy into the slot-contiguous V plane
+      bf16* dst = vc + ((size_t)blk * nkv + g) * D * kKvBlock + slot;
+      for (int e = threadIdx.x; e < D; e += kWaves * kWave)
+        dst[(size_t)e * kKvBlock] = static_cast<bf16>(sx[(G + 1) * D + e]);
+    }
+    __syncthreads();  // the slot is written before any wave loads its block
+    const bool hv = l16 < G;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = hv ? *reinterpret_cast<const bf16x8*>(&sq[l16][8 * grp + 32 * s]) : zero8;
+  } else {
+    const bool hv = l16 < G;
+    const bf16* qrow = q + (size_t)t * ldq + (size_t)(g * G + (hv ? l16 : 0)) * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = hv ? ld16<bf16x8>(qrow + 32 * s) : zero8;
+  }
+
+  if (j < je && !pre) load(j);
   for (; j < je; j += kWaves) {
     bf16x8 kcur[KS];
     bf16x4 vcur[DT];
@@ -246,32 +368,58 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
   }
 }
 
-template <int D>
-hipError_t launch_dec(const void* q, int ldq, int T, const int* positions, int nq, int nkv, const void* k_cache,
-                      const void* v_cache, const int* block_table, int max_blocks, int part_len,
-                      int parts, float* partials, void* out, hipStream_t s, const SeqMap* map, int* row_parts) {
+template <int D, int SP>
+hipError_t launch_dec(const void* q, int ldq, int T, const int* positions, int nq, int nkv, void* k_cache,
+                      void* v_cache, const int* block_table, int max_blocks, int part_len, int parts, float* partials,
+                      void* out, hipStream_t s, const SeqMap* map, int* row_parts, const DecFuse& fz) {
   const int rows = map ? map->dec_cap : T;
   if (rows <= 0) return hipSuccess;
   dim3 grid(rows * nkv, parts);
-  decode_attention_mfma<D><<<grid, kWaves * kWave, 0, s>>>(
-      (const bf16*)q, ldq, positions, nq, nkv, (const bf16*)k_cache, (const bf16*)v_cache, block_table,
-      max_blocks, part_len, parts, partials, (bf16*)out, map ? map->dec : nullptr, map ? map->ndec : nullptr,
-      map ? map->seq_of : nullptr, row_parts);
+  decode_attention_mfma<D, SP><<<grid, kWaves * kWave, 0, s>>>(
+      (const bf16*)q, ldq, positions, nq, nkv, (bf16*)k_cache, (bf16*)v_cache, block_table, max_blocks, part_len,
+      parts, partials, (bf16*)out, map ? map->dec : nullptr, map ? map->ndec : nullptr, map ? map->seq_of : nullptr,
+      row_parts, fz, T);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
-                                        int d, const void* k_cache, const void* v_cache, const int* block_table,
+                                        int d, void* k_cache, void* v_cache, const int* block_table,
                                         int max_blocks, int part_len, int parts, float* partials,
-                                        void* out, hipStream_t s, const SeqMap* map, int* row_parts) {
+                                        void* out, hipStream_t s, const SeqMap* map, int* row_parts,
+                                        const DecodeRope* rope) {
   if (map && (!map->dec || !map->ndec || !map->seq_of || (parts > 1 && !row_parts))) return hipErrorInvalidValue;
-  if (d == 128)
-    return launch_dec<128>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks,
-                           part_len, parts, partials, out, s, map, row_parts);
-  return launch_dec<64>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, part_len,
-                        parts, partials, out, s, map, row_parts);
+  DecFuse fz;
+  int SP = 0;
+  if (rope) {
+    // one (token, KV head) row per workgroup forms its own projection slice
+    if (map || !rope->part || !rope->table || !rope->qkv || nq / nkv > 16) return hipErrorInvalidValue;
+    if (rope->qkn.q && (d != 64 && d != 128)) return hipErrorInvalidValue;
+    SP = rope->S;
+    fz.part = rope->part;
+    fz.table = rope->table;
+    fz.qkv = (bf16*)rope->qkv;
+    fz.qn = (const bf16*)rope->qkn.q;
+    fz.kn = (const bf16*)rope->qkn.k;
+    fz.eps = rope->qkn.eps;
+  }
+#define LLK_DEC(DD, SS) \
+  return launch_dec<DD, SS>(q, ldq, T, positions, nq, nkv, k_cache, v_cache, block_table, max_blocks, part_len, \
+                            parts, partials, out, s, map, row_parts, fz)
+#define LLK_DEC_S(DD)                \
+  switch (SP) {                      \
+    case 0: LLK_DEC(DD, 0);          \
+    case 1: LLK_DEC(DD, 1);          \
+    case 2: LLK_DEC(DD, 2);          \
+    case 4: LLK_DEC(DD, 4);          \
+    case 8: LLK_DEC(DD, 8);          \
+    default: return hipErrorInvalidValue; \
+  }
+  if (d == 128) { LLK_DEC_S(128) }
+  LLK_DEC_S(64)
+#undef LLK_DEC_S
+#undef LLK_DEC
 }
 
 }  // namespace llk

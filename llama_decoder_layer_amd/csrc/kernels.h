@@ -137,6 +137,17 @@ hipError_t launch_rope_kv(int dtype, void* qkv, int T, const int* positions, con
                           void* k_cache, void* v_cache, hipStream_t s, const float* part = nullptr,
                           int S = 0, const QkNorm& qkn = QkNorm());
 
+// The decode attention kernel's own RoPE / KV write (attention_decode.hip):
+// the qkv projection's S fp32 partial planes, the RoPE table, the qkv
+// workspace row it leaves q_rot, k and v in, and the q/k norm.
+struct DecodeRope {
+  const float* part = nullptr;
+  int S = 0;
+  const float2* table = nullptr;
+  void* qkv = nullptr;
+  QkNorm qkn;
+};
+
 // attention.hip.  A key partition's partial result for one (row, query
 // head) is a record of D + kPartHead floats: the running max (log2 units),
 // the sum of exponentials, two pad floats, then the unnormalised output
@@ -155,22 +166,26 @@ AttnPlan attention_plan(int T, int B, int nq, int nkv, int d, bool decode, int m
                         bool split_prefill);
 // row_parts: [T] ints, used when a prefill batch's keys are split
 hipError_t launch_attention(int dtype, const void* q, int ldq, int T, const int* positions, int nq,
-                            int nkv, int d, const void* k_cache, const void* v_cache,
+                            int nkv, int d, void* k_cache, void* v_cache,
                             const int* block_table, int max_blocks, const SeqMap& map, bool decode,
                             const AttnPlan& plan, float* partials, int* row_parts, void* out, hipStream_t s,
-                            hipEvent_t mid_event);
+                            hipEvent_t mid_event, const DecodeRope* rope = nullptr);
 
 // attention_decode.hip (bf16, one query token per row).  Without map.dec row
 // t of T is sequence t and every partition leaves partials (empty ones a max
 // of -inf).  With map.dec the rows are map.dec[0 .. *map.ndec) of sequences
 // map.seq_of[row]; a row whose keys fit one partition is written to out
 // directly, a longer one leaves partials in its first row_parts[row]
-// partitions.
+// partitions.  With rope (rows of the uniform decode batch only) the qkv
+// projection arrives as S fp32 partial planes [S][T][ldq]: each workgroup
+// sums and rounds its own q, k, v heads, applies the q/k norm and RoPE,
+// writes the new k_rot / v into the cache slot and q_rot, k, v into the qkv
+// row (`q` is then not read) -- the work of launch_rope_kv with partials.
 hipError_t launch_decode_attention_bf16(const void* q, int ldq, int T, const int* positions, int nq, int nkv,
-                                        int d, const void* k_cache, const void* v_cache, const int* block_table,
+                                        int d, void* k_cache, void* v_cache, const int* block_table,
                                         int max_blocks, int part_len, int parts, float* partials,
                                         void* out, hipStream_t s, const SeqMap* map = nullptr,
-                                        int* row_parts = nullptr);
+                                        int* row_parts = nullptr, const DecodeRope* rope = nullptr);
 
 // attention_prefill.hip (bf16, G in {4, 8, 16}).  A uniform batch launches
 // one workgroup per (sequence, query tile, KV head); a mixed batch one per
