@@ -13,29 +13,41 @@
 // One workgroup = (sequence, KV head g, 32 consecutive query tokens); its
 // waves each take one query head of the group (two for G = 16), so every K/V
 // tile is staged in LDS once for all G heads, and two waves share each SIMD
-// (one wave's softmax overlaps another's MFMAs).  The key loop walks 64-key tiles (four
-// 16-slot cache blocks) with an online softmax in fp32 (exp2 of
+// (one wave's softmax overlaps another's MFMAs).  The key loop walks 64-key
+// tiles (four 16-slot cache blocks) with an online softmax in fp32 (exp2 of
 // log2(e)/sqrt(d)-scaled scores; the reference max moves only when a tile's
 // max exceeds it by more than 2^8), only up to the tile's last query position
 // (causal tile skipping); the diagonal tiles mask key > query position.
+//
+// Staging: every wave copies whole cache blocks into LDS with direct
+// global->LDS loads (global_load_lds_dwordx4: no registers, no LDS store
+// instructions).  Such a load writes 64 consecutive 16-byte LDS slots, so the
+// bank-spreading swizzles below are made by choosing which 16-byte chunk of
+// the block each lane fetches.  K keeps the cache's [16 slots][D] rows, V the
+// cache's [D][16 slots] block layout.
+//
 // With v_mfma_f32_16x16x32_bf16:
 //   S^T = K Q^T : A = 16 keys x 32 d from LDS, B = the 16 queries' q from
-//       registers.  Lane (query = l%16, grp = l/16) receives keys
-//       4*grp .. 4*grp+3 of each 16-key slice.
-//   O += P V    : A = P: lane (query, grp) supplies as its 8 k-slots its own
-//       keys of two 16-key slices -- no data movement for P.  B = V: the LDS
-//       copy of the V tile stores each component's 64 keys in the permuted
-//       order that puts exactly those 8 keys side by side, so the operand is
-//       one 16-byte read (XOR-swizzled rows keep the reads conflict-free).
-//       P enters as two bf16 parts, its rounding and the rounding of what
-//       that leaves, each multiplied by the same V operand: about 16
-//       significant bits of P instead of bf16's 8, whose rounding alone moved
-//       attention outputs by more than 1e-2 of their RMS.
-// Keys past the sequence's last written slot are staged as zeros, never read
-// from the cache.  When few query tiles would leave CUs idle while each
-// walks a long context, the keys of a tile are split into partitions of
+//       registers.  Row m = 4 grp + r of 16-key slice j holds key
+//       32 (j >> 1) + 8 grp + 4 (j & 1) + r, so lane (query = l % 16,
+//       grp = l / 16) ends up with 8 consecutive keys, 32 mh + 8 grp .. +7,
+//       of each 32-key half mh.
+//   O += P V    : A = P: lane (query, grp) supplies those 8 keys as its 8
+//       k-slots -- no data movement for P.  B = V: lane (component, grp)
+//       reads the same 8 keys of its component, which the block layout keeps
+//       side by side: one 16-byte LDS read.  P enters as two bf16 parts, its
+//       rounding and the rounding of what that leaves, each multiplied by the
+//       same V operand: about 16 significant bits of P instead of bf16's 8,
+//       whose rounding alone moves attention outputs by up to 2e-2 of their
+//       RMS.
+// Keys past the tile's last query (among them any slot past the sequence's
+// last written one) enter P.V with V zeroed in registers, never as what the
+// cache or LDS holds there.  When few query tiles would leave CUs idle while
+// each walks a long context, the keys of a tile are split into partitions of
 // whole 64-key tiles (grid z), merged afterwards by the combine kernel in
 // attention.hip.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -46,25 +58,37 @@ constexpr int kQ = 16;         // query tokens per MFMA row tile
 constexpr float kLazyLog2 = 8.0f;  // reference-max slack of the online softmax, log2 units
 constexpr int kKT = 64;        // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// K tile in LDS: [64 keys][D] bf16, 16-byte chunks XOR-swizzled by key.
+// LDS banks: a 16-byte read (ds_read_b128) is served eight lanes at a time,
+// and is conflict-free when each group of eight consecutive lanes reads
+// eight distinct 16-byte columns of a 128-byte line (measured on gfx950:
+// column = (byte address / 16) % 8).
+//
+// K tile in LDS: [64 keys][D] bf16 in 16-byte chunks; key row `key` keeps its
+// chunk c in slot c ^ ksw(key).  One S^T operand read takes one chunk from
+// each of the 16 keys r0 + {0..3, 8..11, 16..19, 24..27}, eight lanes from
+// r0 + {0..3, 8..11} and eight from r0 + 16 + {0..3, 8..11}; ksw is distinct
+// on each of those eight.
+template <int D>
+__device__ __forceinline__ int ksw(int key) {
+  return (key & 3) | (((key >> 3) & 1) << 2);
+}
 template <int D>
 __device__ __forceinline__ int k_off(int key, int c) {
-  constexpr int CH = D / 8;  // chunks per key row
-  return key * D + ((c ^ (key & (CH - 1))) << 3);
+  return key * D + ((c ^ ksw<D>(key)) << 3);
 }
-// V tile in LDS: [D][64] bf16; key k = 32m + 16h + 4grp + r sits at
-// position 32m + 8grp + 4h + r; 16-byte chunks XOR-swizzled by component.
-__device__ __forceinline__ int v_pos(int key) {
-  const int m = key >> 5, h = (key >> 4) & 1, grp = (key >> 2) & 3, r = key & 3;
-  return 32 * m + 8 * grp + 4 * h + r;
-}
-__device__ __forceinline__ int v_off(int d, int pos) {
-  return d * kKT + ((((pos >> 3) ^ (d & 7)) << 3) | (pos & 7));
+// V tile in LDS: the tile's four cache blocks as the cache stores them,
+// [block][D][16 slots]; the two 8-slot halves of component d trade places
+// when bit 2 of d is set, so eight consecutive components' reads of one half
+// hit eight distinct columns.
+template <int D>
+__device__ __forceinline__ int v_off(int b, int d, int h) {
+  return ((b * D + d) * 2 + (h ^ ((d >> 2) & 1))) << 3;
 }
 
 // D head dim, HPW query heads per wave, QT 16-query tiles per workgroup,
@@ -75,43 +99,54 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
     const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
     int max_blocks, SeqMap map, int num_qtiles, bf16* __restrict__ out, int tpp, int parts,
     float* __restrict__ partials, int* __restrict__ row_parts) {
+  constexpr int U = HPW * QT;       // (head, 16-query tile) units per wave
   constexpr int KS = D / 32;        // d-steps of S^T
   constexpr int DT = D / 16;        // 16-wide d tiles of O
   constexpr int CH = D / 8;         // 16-byte chunks per K row
-  constexpr int BCH = kKvBlock * D / 8;   // 16-byte chunks per cache block (K or V)
-  constexpr int SPL = BCH / kWave;        // chunks per lane when one wave stages one block
-  constexpr int QW = kQ * QT;             // queries per workgroup
-  constexpr int BPT = kKT / kKvBlock;     // cache blocks per key tile (4)
-  // With 8 waves, each SIMD holds one staging wave (0..3), which runs every
-  // tile's S, softmax and P.V in order, and one deferred wave (4..7), which
-  // runs the previous tile's P.V first and then this tile's S and softmax:
-  // the two waves' softmax phases then fall against each other's MFMAs.  The
-  // deferred P.V reads the previous tile's V, so V has three buffers.
+  constexpr int QW = kQ * QT;       // queries per workgroup
+  constexpr int BPT = kKT / kKvBlock;             // cache blocks per key tile (4)
+  constexpr int IPB = kKvBlock * D / 8 / kWave;   // 16-byte chunks per lane when one wave copies a block
+  constexpr int BE = kKvBlock * D;                // elements of one cache block (K or V)
+  // With 8 waves, each SIMD holds one wave (0..3) that runs every tile's S,
+  // softmax and P.V in order, and one deferred wave (4..7) that runs the
+  // previous tile's P.V first and then this tile's S and softmax: the two
+  // waves' softmax phases then fall against each other's MFMAs.  The
+  // deferred P.V reads the previous tile's V while the next tile's is being
+  // copied in, so V has four buffers (two without deferred waves).
   constexpr bool PP = NW == 8;
-  constexpr int VB = PP ? 3 : 2;
+  constexpr int VB = PP ? 4 : 2;
+  static_assert(NW == 4 || NW == 8, "two or one cache blocks per wave and tile");
   __shared__ __attribute__((aligned(16))) bf16 sK[2][kKT * D];
-  __shared__ __attribute__((aligned(16))) bf16 sV[VB][D * kKT];
+  __shared__ __attribute__((aligned(16))) bf16 sV[VB][kKT * D];
 
   const int G = nq / nkv;
-  // this workgroup's query tile: qt of sequence b, whose rows are
+  // Workgroup x is KV head x % nkv of query tile x / nkv: the heads of one
+  // query tile are consecutive, so the longest tiles of every head start
+  // first (the causal lengths are unequal: longest-first keeps the tail
+  // short), and with 8 KV heads each XCD (workgroups go round-robin over
+  // the 8) serves one head, whose K/V stay in that XCD's L2.
+  // This workgroup's query tile: qt of sequence b, whose rows are
   // t_begin .. t_begin+qn-1.  Uniform batch: from the grid, longest tiles
-  // first; mixed batch: from the tile table (a bound-sized grid; workgroups
-  // past the table's length have nothing to do).
+  // first over all sequences; mixed batch: from the tile table (a
+  // bound-sized grid; workgroups past the table's length have nothing to
+  // do).
+  const int g = (int)blockIdx.x % nkv;
+  const int wx = (int)blockIdx.x / nkv;
   int b, qt, t_begin, qn;
   if (map.tiles) {
-    if ((int)blockIdx.x >= *map.ntiles) return;
-    const int4 e = map.tiles[blockIdx.x];
+    if (wx >= *map.ntiles) return;
+    const int4 e = map.tiles[wx];
     b = e.x;
     qt = e.y;
     t_begin = e.z;
     qn = e.w;
   } else {
-    qt = num_qtiles - 1 - (int)(blockIdx.x % num_qtiles);
-    b = blockIdx.x / num_qtiles;
+    const int nseq = (int)gridDim.x / nkv / num_qtiles;
+    qt = num_qtiles - 1 - wx / nseq;
+    b = wx % nseq;
     t_begin = b * map.q_len;
     qn = map.q_len;
   }
-  const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
@@ -135,13 +170,15 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
     kt_begin = z * tpp;
     if (z < np - 1) kt_end = kt_begin + tpp;
   }
-  if (row_parts && blockIdx.z == 0 && blockIdx.y == 0 && (int)threadIdx.x < nvalid) row_parts[t0 + threadIdx.x] = np;
+  if (row_parts && blockIdx.z == 0 && g == 0 && (int)threadIdx.x < nvalid) row_parts[t0 + threadIdx.x] = np;
   const int* bt = block_table + (size_t)b * max_blocks;
-  const size_t head_off = (size_t)g * kKvBlock * D;
-  const size_t blk_stride = (size_t)nkv * kKvBlock * D;
+  const size_t head_off = (size_t)g * BE;
+  const size_t blk_stride = (size_t)nkv * BE;
 
   const bf16x8 zero8 = {};
-  bf16x8 qf[HPW][QT][KS];
+  // q fragments of unit uu = (head hh, query tile u): lane (query l16,
+  // grp) holds components 32 s + 8 grp .. +7
+  bf16x8 qf[U][KS];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
@@ -151,250 +188,278 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
       const bool ok = qi < nvalid;
       const bf16* src = q + (size_t)(t0 + (ok ? qi : 0)) * ldq + (size_t)h * D + 8 * grp;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[hh][u][s] = ok ? ld16<bf16x8>(src + 32 * s) : zero8;
+      for (int s = 0; s < KS; ++s) qf[hh * QT + u][s] = ok ? ld16<bf16x8>(src + 32 * s) : zero8;
     }
 
-  // ---- staging: the 4 cache blocks of a 64-key tile, one wave per block
-  // (waves 4.. of an 8-wave workgroup take no part in staging).
-  // K block: 16 rows of D, chunk c = lane + 64 i -> row c / CH, chunk c % CH
-  // V block: D components of 16 slots, chunk c -> component c / 2, slots
-  //          8*(c%2) .. +7, stored as two 4-key pieces at permuted positions
-  const bool stager = wave < BPT;
-  int k_dst[SPL], v_dst[SPL][2];
+  // ---- staging: tile kt's 4 K and 4 V cache blocks; wave w copies block
+  // w (K of block w for w < 4, V of block w - 4 otherwise) with 8 waves,
+  // K and V of block w with 4.  Lane chunk i (0 .. IPB-1) fills LDS slot
+  // 64 i + lane of the block, from the block's chunk that the swizzle puts
+  // there.
+  const int kblk = wave % BPT;  // the block this wave copies
+  // source chunk offsets (elements) of this lane's chunks: K rows for k_src,
+  // V components for v_src; with 8 waves a wave copies only K or only V, and
+  // k_src holds the offsets of whichever it copies
+  int k_src[IPB], v_src[IPB];
 #pragma unroll
-  for (int i = 0; i < SPL; ++i) {
-    const int c = lane + kWave * i;
-    const int key = (wave % BPT) * kKvBlock + c / CH;
-    k_dst[i] = k_off<D>(key, c % CH);
-    const int d = c >> 1, key0 = (wave % BPT) * kKvBlock + 8 * (c & 1);
-    v_dst[i][0] = v_off(d, v_pos(key0));
-    v_dst[i][1] = v_off(d, v_pos(key0 + 4));
+  for (int i = 0; i < IPB; ++i) {
+    const int c = kWave * i + lane;
+    const int row = c / CH;                      // slot of the block = key row
+    const int ko = row * D + (((c % CH) ^ ksw<D>(kblk * kKvBlock + row)) << 3);
+    const int d = c >> 1;                        // V: component, half
+    const int vo = d * kKvBlock + (((c & 1) ^ ((d >> 2) & 1)) << 3);
+    k_src[i] = (NW == 8 && wave >= BPT) ? vo : ko;
+    v_src[i] = vo;
   }
-  bf16x8 kst[SPL], vst[SPL];
-  auto gload = [&](int kt) {
-    if (!stager) return;
-    const int first = kt * kKT + wave * kKvBlock;  // first key of this wave's block
-    if (first >= key_end) {
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) kst[i] = vst[i] = zero8;
-      return;
-    }
+  // one block of tile kt from cache plane `plane` into LDS at dst
+  auto stage_block = [&](int kt, bf16* dst, const bf16* plane, const int (&off)[IPB]) {
+    const int first = kt * kKT + kblk * kKvBlock;  // first key of the block
+    // a block wholly past the tile's last key is not copied (its
+    // block-table entry may not exist): its keys are masked in S and its V
+    // is replaced by zeros in P.V
+    if (first >= key_end) return;
     const int blk = __builtin_amdgcn_readfirstlane(bt[first / kKvBlock]);
-    const bf16* kb = kc + (size_t)blk * blk_stride + head_off;
-    const bf16* vb = vc + (size_t)blk * blk_stride + head_off;
+    const bf16* src = plane + (size_t)blk * blk_stride + head_off;
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-      kst[i] = ld16<bf16x8>(kb + (size_t)(lane + kWave * i) * 8);
-      vst[i] = ld16<bf16x8>(vb + (size_t)(lane + kWave * i) * 8);
-    }
-    if (first + kKvBlock > key_end) {  // the sequence's last, partly written block
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) {
-        const int c = lane + kWave * i;
-        if (first + c / CH >= key_end) kst[i] = zero8;
-        const int s0 = first + 8 * (c & 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (s0 + e >= key_end) vst[i][e] = static_cast<bf16>(0.f);
-      }
-    }
+    for (int i = 0; i < IPB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + off[i]),
+                                       (__attribute__((address_space(3))) void*)(dst + kWave * 8 * i), 16, 0, 0);
   };
-  auto sstore = [&](int kt) {  // tile kt's K into sK[kt % 2], V into sV[kt % VB]
-    if (!stager) return;
-    const int kb = kt & 1, vb = kt % VB;
-#pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-      *reinterpret_cast<bf16x8*>(&sK[kb][k_dst[i]]) = kst[i];
-      bf16x4 lo, hi;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        lo[r] = vst[i][r];
-        hi[r] = vst[i][4 + r];
-      }
-      *reinterpret_cast<bf16x4*>(&sV[vb][v_dst[i][0]]) = lo;
-      *reinterpret_cast<bf16x4*>(&sV[vb][v_dst[i][1]]) = hi;
+  // tile kt into K buffer kb and V buffer vb
+  auto stage = [&](int kt, int kb, int vb) {
+    if (NW == 8) {
+      const bool is_v = wave >= BPT;
+      stage_block(kt, is_v ? &sV[vb][kblk * BE] : &sK[kb][kblk * BE], is_v ? vc : kc, k_src);
+    } else {
+      stage_block(kt, &sK[kb][kblk * BE], kc, k_src);
+      stage_block(kt, &sV[vb][kblk * BE], vc, v_src);
     }
   };
 
   // ---- per-lane operand offsets in LDS (the same for every tile) ---------
-  int k_rd[KS];  // key 16j + l16 (j added below), chunk 4s + grp
+  // S^T operand of slice j: key 32 (j >> 1) + 4 (j & 1) + kr0, chunk 4 s + grp
+  // (ksw does not see bits 2 and 5 of the key, so the slice adds a constant)
+  const int kr0 = 8 * (l16 >> 2) + (l16 & 3);
+  int k_rd[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) k_rd[s] = k_off<D>(l16, 4 * s + grp);
-  int v_rd[2];   // component 16i + l16 (i added below), positions 32mh + 8grp
+  for (int s = 0; s < KS; ++s) k_rd[s] = k_off<D>(kr0, 4 * s + grp);
+  // P.V operand of half mh: keys 32 mh + 8 grp .. +7 of component l16
+  // (+16 i for d tile i)
+  int v_rd[2];
 #pragma unroll
-  for (int mh = 0; mh < 2; ++mh) v_rd[mh] = v_off(l16, 32 * mh + 8 * grp);
+  for (int mh = 0; mh < 2; ++mh) v_rd[mh] = v_off<D>(2 * mh + (grp >> 1), l16, grp & 1);
 
   const float sc = kLog2e / sqrtf((float)D);
-  float m_run[HPW][QT], l_run[HPW][QT];
-  f32x4 o[HPW][QT][DT];
+  float m_run[U], l_run[U];
+  f32x4 o[U][DT];
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
+  for (int uu = 0; uu < U; ++uu) {
+    m_run[uu] = -INFINITY;
+    l_run[uu] = 0.f;
 #pragma unroll
-    for (int u = 0; u < QT; ++u) {
-      m_run[hh][u] = -INFINITY;
-      l_run[hh][u] = 0.f;
-#pragma unroll
-      for (int i = 0; i < DT; ++i) o[hh][u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int i = 0; i < DT; ++i) o[uu][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // S^T (raw scores) of tile kt: 4 slices of 16 keys per (head, query tile),
-  // masked where keys pass a query's position (only the tiles that reach the
-  // tile's first query position, or hold unwritten slots, have such keys)
-  auto scores = [&](int kt, f32x4 (&s4)[HPW][QT][4]) {
-    const int buf = kt & 1;
+  // S^T (raw scores) of tile kt: 4 slices of 16 keys per unit, masked where
+  // keys pass a query's position (only the tiles that reach the tile's first
+  // query position, or hold unwritten slots, have such keys)
+  auto scores = [&](int kt, const bf16* K, f32x4 (&s4)[U][4]) {
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
+    for (int uu = 0; uu < U; ++uu)
 #pragma unroll
-      for (int u = 0; u < QT; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s4[hh][u][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) s4[uu][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][k_rd[s] + 16 * D * j]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&K[k_rd[s] + (32 * (j >> 1) + 4 * (j & 1)) * D]);
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-          for (int u = 0; u < QT; ++u) s4[hh][u][j] = mfma16(kf, qf[hh][u][s], s4[hh][u][j]);
+        for (int uu = 0; uu < U; ++uu) s4[uu][j] = mfma16(kf, qf[uu][s], s4[uu][j]);
       }
     }
     if (kt * kKT + kKT - 1 > p0) {
 #pragma unroll
-      for (int u = 0; u < QT; ++u) {
-        const int pq = p0 + 16 * u + l16;
+      for (int uu = 0; uu < U; ++uu) {
+        const int pq = p0 + 16 * (uu % QT) + l16;
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (kt * kKT + 16 * j + 4 * grp + r > pq) s4[hh][u][j][r] = -INFINITY;
+          for (int r = 0; r < 4; ++r)
+            if (kt * kKT + 32 * (j >> 1) + 8 * grp + 4 * (j & 1) + r > pq) s4[uu][j][r] = -INFINITY;
       }
     }
   };
   // online softmax of one tile's scores: P for P.V (two bf16 parts: the
-  // rounding of P and the rounding of the remainder), the running max and
-  // sum, and O rescaled where a query's max moved
-  auto softmax = [&](const f32x4 (&s4)[HPW][QT][4], bf16x8 (&pa)[HPW][QT][2], bf16x8 (&pl)[HPW][QT][2]) {
+  // rounding of P and the rounding of the remainder), the running reference
+  // max and sum, and O rescaled where the max moved
+  auto softmax = [&](const f32x4 (&s4)[U][4], bf16x8 (&pa)[U][2], bf16x8 (&pl)[U][2]) {
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
+    for (int uu = 0; uu < U; ++uu) {
+      float bm = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < QT; ++u) {
-        float bm = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {  // pairs fold into three-input maxima
-          bm = fmaxf(fmaxf(bm, s4[hh][u][j][0]), s4[hh][u][j][1]);
-          bm = fmaxf(fmaxf(bm, s4[hh][u][j][2]), s4[hh][u][j][3]);
-        }
-        bm = row_group_max(bm);
-        // The reference max m_run only has to bound the scores closely
-        // enough that exp2 stays in range: softmax is unchanged by the
-        // choice, as long as O and the sum share it.  It moves (and O is
-        // rescaled) only when some query's tile max exceeds it by more than
-        // kLazyLog2 in log2 units, so P <= 2^kLazyLog2 (exact in bf16's
-        // exponent range) and most tiles skip the rescale.
-        const float m_old = m_run[hh][u];
-        const bool keep = __all(bm * sc <= m_old * sc + kLazyLog2);
-        const float m_new = keep ? m_old : fmaxf(m_old, bm);
-        const float ms = m_new * sc;
-        float ps = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pf = __builtin_amdgcn_exp2f(fmaf(s4[hh][u][j][r], sc, -ms));
-            const bf16 hi = static_cast<bf16>(pf);
-            pa[hh][u][j >> 1][4 * (j & 1) + r] = hi;
-            pl[hh][u][j >> 1][4 * (j & 1) + r] = static_cast<bf16>(pf - static_cast<float>(hi));
-            ps += pf;
-          }
-        if (keep) {
-          l_run[hh][u] += ps;  // reference max kept: O needs no rescale
-        } else {
-          const float alpha = __builtin_amdgcn_exp2f((m_old - m_new) * sc);
-          l_run[hh][u] = l_run[hh][u] * alpha + ps;
-          float ah[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ah[r] = __shfl(alpha, 4 * grp + r, kWave);
-#pragma unroll
-          for (int i = 0; i < DT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[hh][u][i][r] *= ah[r];
-        }
-        m_run[hh][u] = m_new;
+      for (int j = 0; j < 4; ++j) {  // pairs fold into three-input maxima
+        bm = fmaxf(fmaxf(bm, s4[uu][j][0]), s4[uu][j][1]);
+        bm = fmaxf(fmaxf(bm, s4[uu][j][2]), s4[uu][j][3]);
       }
+      bm = row_group_max(bm);
+      // The reference max m_run only has to bound the scores closely
+      // enough that exp2 stays in range: softmax is unchanged by the
+      // choice, as long as O and the sum share it.  It moves (and O is
+      // rescaled) only when some query's tile max exceeds it by more than
+      // kLazyLog2 in log2 units, so P <= 2^kLazyLog2 (exact in bf16's
+      // exponent range) and most tiles skip the rescale.
+      const float m_old = m_run[uu];
+      const bool keep = __all(bm * sc <= m_old * sc + kLazyLog2);
+      const float m_new = keep ? m_old : fmaxf(m_old, bm);
+      const float ms = m_new * sc;
+      // two scores at a time: one conversion rounds both to bf16 (hi), the
+      // packed pair gives both back as floats by a shift and a mask, and one
+      // more conversion rounds both remainders (lo)
+      float ps = 0.f;
+      uint32_t hw[2][4], lw[2][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int rp = 0; rp < 2; ++rp) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s4[uu][j][2 * rp], sc, -ms));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s4[uu][j][2 * rp + 1], sc, -ms));
+          const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+          const float h0 = __uint_as_float(h << 16), h1 = __uint_as_float(h & 0xffff0000u);
+          hw[j >> 1][2 * (j & 1) + rp] = h;
+          lw[j >> 1][2 * (j & 1) + rp] =
+              __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0 - h0, p1 - h1}, bf16x2));
+          ps += p0;
+          ps += p1;
+        }
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh) {
+        pa[uu][mh] = __builtin_bit_cast(bf16x8, (uint4){hw[mh][0], hw[mh][1], hw[mh][2], hw[mh][3]});
+        pl[uu][mh] = __builtin_bit_cast(bf16x8, (uint4){lw[mh][0], lw[mh][1], lw[mh][2], lw[mh][3]});
+      }
+      if (keep) {
+        l_run[uu] += ps;  // reference max kept: O needs no rescale
+      } else {
+        const float alpha = __builtin_amdgcn_exp2f((m_old - m_new) * sc);
+        l_run[uu] = l_run[uu] * alpha + ps;
+        float ah[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ah[r] = __shfl(alpha, 4 * grp + r, kWave);
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[uu][i][r] *= ah[r];
+      }
+      m_run[uu] = m_new;
+    }
   };
   // O += P V of tile kt: two 32-key halves, DT d-tiles, each V operand
-  // applied to both parts of P
-  auto pv = [&](int kt, const bf16x8 (&pa)[HPW][QT][2], const bf16x8 (&pl)[HPW][QT][2]) {
-    const int vb = kt % VB;
+  // applied to both parts of P.  On the tile that reaches past key_end, the
+  // V operand's keys at or past it (unwritten cache slots or blocks not
+  // copied, weighted by P = 0) are zeroed in registers: 0 times whatever bits
+  // they hold could be NaN.
+  auto pv_tile = [&](const bf16* V, const bf16x8 (&pa)[U][2], const bf16x8 (&pl)[U][2], auto masked_c, int kt) {
+    constexpr bool masked = decltype(masked_c)::value;
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
+      // 16-bit elements kept: the first nv of this lane's 8 keys
+      uint4 keepm = {~0u, ~0u, ~0u, ~0u};
+      if constexpr (masked) {
+        const int nv = key_end - (kt * kKT + 32 * mh + 8 * grp);
+        keepm.x = nv >= 2 ? ~0u : (nv == 1 ? 0xffffu : 0u);
+        keepm.y = nv >= 4 ? ~0u : (nv == 3 ? 0xffffu : 0u);
+        keepm.z = nv >= 6 ? ~0u : (nv == 5 ? 0xffffu : 0u);
+        keepm.w = nv >= 8 ? ~0u : (nv == 7 ? 0xffffu : 0u);
+      }
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[vb][v_rd[mh] + 16 * kKT * i]);
+        bf16x8 vf = *reinterpret_cast<const bf16x8*>(&V[v_rd[mh] + 256 * i]);
+        if constexpr (masked) {
+          uint4 w = __builtin_bit_cast(uint4, vf);
+          w.x &= keepm.x;
+          w.y &= keepm.y;
+          w.z &= keepm.z;
+          w.w &= keepm.w;
+          vf = __builtin_bit_cast(bf16x8, w);
+        }
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-          for (int u = 0; u < QT; ++u) {
-            o[hh][u][i] = mfma16(pa[hh][u][mh], vf, o[hh][u][i]);
-            o[hh][u][i] = mfma16(pl[hh][u][mh], vf, o[hh][u][i]);
-          }
+        for (int uu = 0; uu < U; ++uu) {
+          o[uu][i] = mfma16(pa[uu][mh], vf, o[uu][i]);
+          o[uu][i] = mfma16(pl[uu][mh], vf, o[uu][i]);
+        }
       }
     }
   };
+  auto pv = [&](const bf16* V, const bf16x8 (&pa)[U][2], const bf16x8 (&pl)[U][2], int kt) {
+    if (kt * kKT + kKT > key_end)
+      pv_tile(V, pa, pl, std::true_type(), kt);
+    else
+      pv_tile(V, pa, pl, std::false_type(), kt);
+  };
 
-  // One barrier per tile in either order.  A V buffer is rewritten (tile
-  // kt + 1, during tile kt) only after the barrier that follows its last
-  // reader: the deferred P.V of tile kt - 2, run during tile kt - 1.
-  gload(kt_begin);
-  sstore(kt_begin);
+  // Buffer indices: K kt & 1, V kt & (VB - 1).  The index a copy writes is
+  // formed as an XOR of the index read in the same tile (K: kb ^ 1; V of a
+  // deferred wave: (kt - 1) & 3 ^ 2 = (kt + 1) & 3), so the compiler can see
+  // that the copies in flight never write what the wave reads, and waits for
+  // them only at the tile's barrier.
+  // Only the range's last tile can reach past key_end, so it is peeled off
+  // the loop: the loop's P.V never masks.
+  stage(kt_begin, kt_begin & 1, kt_begin & (VB - 1));
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (!PP || stager) {
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      if (kt + 1 < kt_end) gload(kt + 1);
-      f32x4 s4[HPW][QT][4];
-      scores(kt, s4);
-      bf16x8 pa[HPW][QT][2], pl[HPW][QT][2];
+  const int kt_last = kt_end - 1;
+  if (!PP || wave < BPT) {
+    for (int kt = kt_begin; kt < kt_last; ++kt) {
+      const int kb = kt & 1, vb = kt & (VB - 1);
+      stage(kt + 1, kb ^ 1, VB == 2 ? vb ^ 1 : (kt + 1) & (VB - 1));
+      f32x4 s4[U][4];
+      scores(kt, sK[kb], s4);
+      bf16x8 pa[U][2], pl[U][2];
       softmax(s4, pa, pl);
-      pv(kt, pa, pl);
-      if (kt + 1 < kt_end) sstore(kt + 1);
+      pv_tile(sV[vb], pa, pl, std::false_type(), kt);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
+    f32x4 s4[U][4];
+    scores(kt_last, sK[kt_last & 1], s4);
+    bf16x8 pa[U][2], pl[U][2];
+    softmax(s4, pa, pl);
+    pv(sV[kt_last & (VB - 1)], pa, pl, kt_last);
   } else {
-    bf16x8 pa[HPW][QT][2], pl[HPW][QT][2];
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      if (kt > kt_begin) pv(kt - 1, pa, pl);
-      f32x4 s4[HPW][QT][4];
-      scores(kt, s4);
+    bf16x8 pa[U][2], pl[U][2];
+    for (int kt = kt_begin; kt <= kt_last; ++kt) {
+      const int kb = kt & 1, vprev = (kt - 1) & 3;
+      if (kt > kt_begin) pv_tile(sV[vprev], pa, pl, std::false_type(), kt - 1);
+      if (kt < kt_last) stage(kt + 1, kb ^ 1, vprev ^ 2);
+      f32x4 s4[U][4];
+      scores(kt, sK[kb], s4);
       softmax(s4, pa, pl);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    pv(kt_end - 1, pa, pl);
+    pv(sV[kt_last & 3], pa, pl, kt_last);
   }
 
   // normalise and store: lane holds O[query 16u + 4grp + r][d = 16i + l16].
-  // Of a split tile, leave (reference max in log2 units, sum, unnormalised O) per
-  // (query, head, partition) for the combine kernel.
+  // Of a split tile, leave (reference max in log2 units, sum, unnormalised
+  // O) per (query, head, partition) for the combine kernel.
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
-      float lt = l_run[hh][u];
-      lt = row_group_sum(lt);
+      const int uu = hh * QT + u;
       const int h = g * G + wave * HPW + hh;
+      const float lt = row_group_sum(l_run[uu]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int qi = 16 * u + 4 * grp + r;
         const float lq = __shfl(lt, 4 * grp + r, kWave);
-        const float mq = __shfl(m_run[hh][u], 4 * grp + r, kWave);
+        const float mq = __shfl(m_run[uu], 4 * grp + r, kWave);
         if (qi < nvalid) {
           if (np == 1) {
             const float inv = 1.0f / lq;
             bf16* dst = out + (size_t)(t0 + qi) * nq * D + (size_t)h * D + l16;
 #pragma unroll
-            for (int i = 0; i < DT; ++i) dst[16 * i] = static_cast<bf16>(o[hh][u][i][r] * inv);
+            for (int i = 0; i < DT; ++i) dst[16 * i] = static_cast<bf16>(o[uu][i][r] * inv);
           } else {
             float* dst = partials + (((size_t)(t0 + qi) * nq + h) * parts + blockIdx.z) * (D + kPartHead);
             if (l16 == 0) {
@@ -402,7 +467,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
               dst[1] = lq;
             }
 #pragma unroll
-            for (int i = 0; i < DT; ++i) dst[kPartHead + 16 * i + l16] = o[hh][u][i][r];
+            for (int i = 0; i < DT; ++i) dst[kPartHead + 16 * i + l16] = o[uu][i][r];
           }
         }
       }
@@ -421,7 +486,7 @@ hipError_t launch_pf(const void* q, int ldq, int T, const int* positions, int nq
     wgs = T / map.q_len * nqt;
   }
   if (wgs <= 0) return hipSuccess;
-  dim3 grid(wgs, nkv, tpp > 0 ? parts : 1);
+  dim3 grid(wgs * nkv, 1, tpp > 0 ? parts : 1);
   prefill_attention_mfma<D, HPW, QT, NW><<<grid, NW * kWave, 0, s>>>(
       (const bf16*)q, ldq, positions, nq, nkv, (const bf16*)k_cache, (const bf16*)v_cache, block_table,
       max_blocks, map, nqt, (bf16*)out, tpp, parts, partials, row_parts);
