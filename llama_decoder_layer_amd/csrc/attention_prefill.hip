@@ -92,9 +92,11 @@ __device__ __forceinline__ int v_off(int b, int d, int h) {
 }
 
 // D head dim, HPW query heads per wave, QT 16-query tiles per workgroup,
-// NW waves (NW * HPW = G heads).
+// NW waves; the G heads of a KV group take G / (NW * HPW) workgroups.  With
+// 4 waves a workgroup stays within 256 registers a lane, so two workgroups
+// share each CU: their waves pair up on the SIMDs without a common barrier.
 template <int D, int HPW, int QT, int NW>
-__global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
+__global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void prefill_attention_mfma(
     const bf16* __restrict__ q, int ldq, const int* __restrict__ positions, int nq, int nkv,
     const bf16* __restrict__ kc, const bf16* __restrict__ vc, const int* __restrict__ block_table,
     int max_blocks, SeqMap map, int num_qtiles, bf16* __restrict__ out, int tpp, int parts,
@@ -120,18 +122,21 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
   __shared__ __attribute__((aligned(16))) bf16 sV[VB][kKT * D];
 
   const int G = nq / nkv;
-  // Workgroup x is KV head x % nkv of query tile x / nkv: the heads of one
-  // query tile are consecutive, so the longest tiles of every head start
-  // first (the causal lengths are unequal: longest-first keeps the tail
-  // short), and with 8 KV heads each XCD (workgroups go round-robin over
-  // the 8) serves one head, whose K/V stay in that XCD's L2.
+  // Workgroup x is KV head x % nkv, head group x / nkv % HG, of query tile
+  // x / nkv / HG: the heads of one query tile are consecutive, so the
+  // longest tiles of every head start first (the causal lengths are
+  // unequal: longest-first keeps the tail short), and with 8 KV heads each
+  // XCD (workgroups go round-robin over the 8) serves one KV head, whose
+  // K/V stay in that XCD's L2.
   // This workgroup's query tile: qt of sequence b, whose rows are
   // t_begin .. t_begin+qn-1.  Uniform batch: from the grid, longest tiles
   // first over all sequences; mixed batch: from the tile table (a
   // bound-sized grid; workgroups past the table's length have nothing to
   // do).
+  const int HG = G / (NW * HPW);  // workgroups per (query tile, KV head)
   const int g = (int)blockIdx.x % nkv;
-  const int wx = (int)blockIdx.x / nkv;
+  const int hgi = (int)blockIdx.x / nkv % HG;  // which heads of the group
+  const int wx = (int)blockIdx.x / nkv / HG;
   int b, qt, t_begin, qn;
   if (map.tiles) {
     if (wx >= *map.ntiles) return;
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
     t_begin = e.z;
     qn = e.w;
   } else {
-    const int nseq = (int)gridDim.x / nkv / num_qtiles;
+    const int nseq = (int)gridDim.x / nkv / HG / num_qtiles;
     qt = num_qtiles - 1 - wx / nseq;
     b = wx % nseq;
     t_begin = b * map.q_len;
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
     kt_begin = z * tpp;
     if (z < np - 1) kt_end = kt_begin + tpp;
   }
-  if (row_parts && blockIdx.z == 0 && g == 0 && (int)threadIdx.x < nvalid) row_parts[t0 + threadIdx.x] = np;
+  if (row_parts && blockIdx.z == 0 && g == 0 && hgi == 0 && (int)threadIdx.x < nvalid) row_parts[t0 + threadIdx.x] = np;
   const int* bt = block_table + (size_t)b * max_blocks;
   const size_t head_off = (size_t)g * BE;
   const size_t blk_stride = (size_t)nkv * BE;
@@ -183,7 +188,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
-      const int h = g * G + wave * HPW + hh;
+      const int h = g * G + (hgi * NW + wave) * HPW + hh;
       const int qi = 16 * u + l16;
       const bool ok = qi < nvalid;
       const bf16* src = q + (size_t)(t0 + (ok ? qi : 0)) * ldq + (size_t)h * D + 8 * grp;
@@ -447,7 +452,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_attention_mfma(
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
       const int uu = hh * QT + u;
-      const int h = g * G + wave * HPW + hh;
+      const int h = g * G + (hgi * NW + wave) * HPW + hh;
       const float lt = row_group_sum(l_run[uu]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -486,7 +491,8 @@ hipError_t launch_pf(const void* q, int ldq, int T, const int* positions, int nq
     wgs = T / map.q_len * nqt;
   }
   if (wgs <= 0) return hipSuccess;
-  dim3 grid(wgs * nkv, 1, tpp > 0 ? parts : 1);
+  const int hg = nq / nkv / (NW * HPW);
+  dim3 grid(wgs * nkv * hg, 1, tpp > 0 ? parts : 1);
   prefill_attention_mfma<D, HPW, QT, NW><<<grid, NW * kWave, 0, s>>>(
       (const bf16*)q, ldq, positions, nq, nkv, (const bf16*)k_cache, (const bf16*)v_cache, block_table,
       max_blocks, map, nqt, (bf16*)out, tpp, parts, partials, row_parts);
