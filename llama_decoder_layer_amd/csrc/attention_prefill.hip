@@ -403,8 +403,9 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void prefill_attention
 
   // Buffer indices: K kt & 1, V kt & (VB - 1).  The index a copy writes is
   // formed as an XOR of the index read in the same tile (K: kb ^ 1; V of a
-  // deferred wave: (kt - 1) & 3 ^ 2 = (kt + 1) & 3), so the compiler can see
-  // that the copies in flight never write what the wave reads, and waits for
+  // deferred wave: (kt - 1) & 3 ^ 2 = (kt + 1) & 3), and a deferred wave
+  // issues its V copy after its P.V reads: the compiler then sees that the
+  // copies in flight never write what the wave still reads, and waits for
   // them only at the tile's barrier.
   // Only the range's last tile can reach past key_end, so it is peeled off
   // the loop: the loop's P.V never masks.
