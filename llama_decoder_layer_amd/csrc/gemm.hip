@@ -77,7 +77,8 @@ constexpr int kGroupM = 8;  // token tiles per group in the XCD-local tile order
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __restrict__ X, int M,
                                                                const bf16* __restrict__ W, int N, int K,
-                                                               WStride ws, void* out, int ldo, int group_m, int kps) {
+                                                               WStride ws, void* out, int ldo, int group_m, int cw,
+                                                               int kps) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;     // wave tile: tokens x weight rows
   constexpr int SM = TM / 16, SN = TN / 16;     // 16x16 MFMA tiles per wave
@@ -95,21 +96,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_bf16(const bf16* __res
 
   // Workgroups are dispatched round-robin over the 8 XCDs, and the ones an
   // XCD runs together share its L2.  With group_m > 0 (the launcher checks
-  // that the weight tiles divide by 8) XCD x owns weight tiles
-  // [x*nn, (x+1)*nn) for every token tile, and walks them in groups of
-  // group_m token tiles: for each weight tile the group's token tiles run
-  // back to back.  Co-resident workgroups then form a group_m x (32/group_m)
-  // block of tiles, so each x panel and each W panel they stream is fetched
-  // into L2 once for several of them.  group_m = 0: token tiles fastest.
+  // that the weight tiles divide by 8) the weight tiles are taken cw at a
+  // time; within such a chunk XCD x owns nn = cw / 8 of them for every token
+  // tile, and walks them in groups of group_m token tiles: for each weight
+  // tile the group's token tiles run back to back.  Co-resident workgroups
+  // then form a group_m x (32/group_m) block of tiles, so each x panel and
+  // each W panel they stream is fetched into L2 once for several of them.
+  // group_m = 0: token tiles fastest.
   const int num_m = (M + BM - 1) / BM;
   int m_t, n_t;
+  //
+  // The weight tiles go in chunks of cw (cw / 8 per XCD), each chunk over
+  // every token tile before the next: a chunk small enough to stay in the
+  // 256 MB MALL while the token tiles stream past is read from HBM once,
+  // where walking all weight tiles per token group re-reads the whole
+  // weight from HBM once per group (32768 x 57344 x 8192: 23.7 -> 22.8 ms).
   if (group_m > 0) {
-    const int nn = N / BN / 8;
+    const int nn = cw / 8;
     const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
-    const int gsz = group_m * nn, grp = i / gsz, r = i - grp * gsz;
+    const int per_chunk = nn * num_m;
+    const int c = i / per_chunk, ic = i - c * per_chunk;
+    const int gsz = group_m * nn, grp = ic / gsz, r = ic - grp * gsz;
     const int gm = min(group_m, num_m - grp * group_m);
     m_t = grp * group_m + r % gm;
-    n_t = xcd * nn + r / gm;
+    n_t = c * cw + xcd * nn + r / gm;
   } else {
     m_t = blockIdx.x % num_m;
     n_t = blockIdx.x / num_m;
@@ -239,7 +249,10 @@ hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, WS
   // beyond that, grouped order (26.9 -> 25.8 ms on 32768 x 57344 x 8192).
   const int num_m = (M + BM - 1) / BM;
   const int group_m = num_m > 32 && (wrows / BN) % 8 == 0 ? kGroupM : 0;
-  fn<<<dim3(nb, splits), 64 * WM * WN, lds, s>>>(x, M, w, wrows, K, ws, out, ldo, group_m, K / splits);
+  // weight chunks of 32 tiles where 32 tiles of this K fit in 160 MB
+  const int ntot = wrows / BN;
+  const int cw = ntot % 32 == 0 && (size_t)32 * BN * K * sizeof(bf16) <= ((size_t)160 << 20) ? 32 : ntot;
+  fn<<<dim3(nb, splits), 64 * WM * WN, lds, s>>>(x, M, w, wrows, K, ws, out, ldo, group_m, cw, K / splits);
   return hipGetLastError();
 }
 

@@ -30,6 +30,21 @@ def test_linear_store(M, N, K):
     compare("linear", np64(y), ref, dtype="bf16")
 
 
+@pytest.mark.timeout(300)
+def test_linear_store_chunked_tile_order():
+    # more than 32 token tiles (34, the last one partial) over 64 weight tiles
+    # of 256 rows: the tiled kernel's XCD-grouped order, walking the weight
+    # tiles in two chunks of 32
+    M, N, K = 8500, 16384, 128
+    print("linear_store chunked order", M, N, K, flush=True)
+    x = _randn((M, K), 31)
+    w = _randn((N, K), 32, std=0.05)
+    y = lda.linear(x, w)
+    torch.cuda.synchronize()
+    ref = oracle.linear(np64(x), np64(w))
+    compare("linear chunked order", np64(y), ref, dtype="bf16")
+
+
 @pytest.mark.parametrize("M", [5, 32, 64, 100, 200, 544])
 def test_linear_add(M):
     print("linear_add", M, flush=True)
