@@ -70,7 +70,7 @@ def counter_traffic(workload, kernel):
     if rec is None:
         return None
     try:
-        if sources_sha1((rec["source"],) + PLAN_SOURCES) != rec["sha1"]:
+        if sources_sha1(tuple(rec["sources"]) + PLAN_SOURCES) != rec["sha1"]:
             return None
     except OSError:
         return None
@@ -343,7 +343,9 @@ def measure_stack(wl, steps, warmup, flushed_calls, flush_buf, graph=True):
 def hbm_read_ceiling(steps=10):
     """The read-only streaming kernel over the bytes and in the launch shape
     of the decode step's largest kernel (the 70B gate_up weight, one
-    workgroup of 7 waves per CU), and over 1 GiB with many small workgroups."""
+    workgroup of 7 waves per CU), and over 4 GiB in 256 workgroups of 256
+    threads; each with plain loads and with the nontemporal hint the decode
+    path's weight and KV streams use."""
     import torch
 
     import llama_decoder_layer_amd as lda
@@ -353,23 +355,25 @@ def hbm_read_ceiling(steps=10):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = {}
     for name, nbytes, wgs, threads in (("gate_up_shape", 2 * m.intermediate_size * m.hidden_size * 2, cus, 448),
-                                       ("1GiB_4096x256", 1 << 30, 4096, 256)):
+                                       ("4GiB_256x256", 4 << 30, 256, 256)):
         src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
         sink = torch.empty(wgs * threads, dtype=torch.int32, device="cuda")
-        for _ in range(3):
-            lda.stream_read(src, wgs, threads, sink)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(steps):
-            lda.stream_read(src, wgs, threads, sink)
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) / steps * 1e3
-        out[name] = {"bytes": nbytes, "workgroups": wgs, "threads": threads, "avg_us": round(us, 2),
-                     "GB_per_s": round(nbytes / (us / 1e6) / 1e9, 1),
-                     "frac_of_peak": round(nbytes / (us / 1e6) / 1e9 / PEAK_HBM_GBS, 4)}
+        for nt in (False, True):
+            for _ in range(3):
+                lda.stream_read(src, wgs, threads, sink, nontemporal=nt)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(steps):
+                lda.stream_read(src, wgs, threads, sink, nontemporal=nt)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / steps * 1e3
+            out[name + ("_nontemporal" if nt else "")] = {
+                "bytes": nbytes, "workgroups": wgs, "threads": threads, "avg_us": round(us, 2),
+                "GB_per_s": round(nbytes / (us / 1e6) / 1e9, 1),
+                "frac_of_peak": round(nbytes / (us / 1e6) / 1e9 / PEAK_HBM_GBS, 4)}
         del src, sink
     return out
 

@@ -414,11 +414,13 @@ LLAMA_API llama_status llama_op_add_rmsnorm(int32_t dtype, const void* x, const 
  * and nothing else: each of `workgroups` workgroups of `threads` threads (a
  * multiple of 64, at most 1024) streams one contiguous region with 16-byte
  * loads, several in flight per lane, and writes one 32-bit word per thread to
- * sink [workgroups * threads] (device) so the loads are kept.  Its rate is
- * the HBM read ceiling the streaming kernels of the decode path are measured
- * against.  Errors: INVALID_ARGUMENT, HIP. */
+ * sink [workgroups * threads] (device) so the loads are kept.  nontemporal
+ * != 0 gives the loads the nontemporal hint, as the decode path's weight and
+ * KV streams carry it.  Its rate is the HBM read ceiling the streaming
+ * kernels of the decode path are measured against.  Errors:
+ * INVALID_ARGUMENT, HIP. */
 LLAMA_API llama_status llama_diag_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t threads,
-                                              void* sink, void* stream);
+                                              int32_t nontemporal, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

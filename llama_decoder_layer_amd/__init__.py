@@ -119,7 +119,7 @@ def lib() -> ctypes.CDLL:
     L.llama_layer_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64), i32]
     L.llama_diag_stream_read.restype = st
-    L.llama_diag_stream_read.argtypes = [vp, ctypes.c_size_t, i32, i32, vp, vp]
+    L.llama_diag_stream_read.argtypes = [vp, ctypes.c_size_t, i32, i32, i32, vp, vp]
     L.llama_op_linear.restype = st
     L.llama_op_linear.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, vp]
     L.llama_op_reorder_gate_up.restype = st
@@ -523,15 +523,17 @@ class Graph:
             pass
 
 
-def stream_read(src: torch.Tensor, workgroups: int, threads: int, sink: torch.Tensor, stream=None) -> None:
+def stream_read(src: torch.Tensor, workgroups: int, threads: int, sink: torch.Tensor, nontemporal: bool = False,
+                stream=None) -> None:
     """llama_diag_stream_read: reads all of src (device, contiguous) and
-    nothing else; sink holds workgroups * threads int32."""
+    nothing else, with or without the nontemporal load hint; sink holds
+    workgroups * threads int32."""
     _dev(src, "src")
     _dev(sink, "sink")
     if sink.numel() * sink.element_size() < workgroups * threads * 4:
         raise ValueError("sink too small")
-    _check(lib().llama_diag_stream_read(_ptr(src), src.numel() * src.element_size(), workgroups, threads, _ptr(sink),
-                                        _stream(stream)))
+    _check(lib().llama_diag_stream_read(_ptr(src), src.numel() * src.element_size(), workgroups, threads,
+                                        int(bool(nontemporal)), _ptr(sink), _stream(stream)))
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, epilogue: Epilogue = Epilogue.STORE, out=None, stream=None):

@@ -907,14 +907,14 @@ llama_status llama_op_linear(int32_t dtype, const void* x, const void* w, int32_
   return LLAMA_OK;
 }
 
-llama_status llama_diag_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t threads, void* sink,
-                                    void* stream) {
+llama_status llama_diag_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t threads,
+                                    int32_t nontemporal, void* sink, void* stream) {
   if (!src || !sink) return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer");
   if (bytes == 0 || bytes % 16 || !aligned16(src))
     return fail(LLAMA_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16 and src 16-byte aligned");
   if (workgroups <= 0 || workgroups > (1 << 20) || threads < 64 || threads > 1024 || threads % 64)
     return fail(LLAMA_ERR_INVALID_ARGUMENT, "workgroups in [1, 2^20], threads a multiple of 64 in [64, 1024]");
-  hipError_t e = llk::launch_stream_read(src, bytes, workgroups, threads, sink, (hipStream_t)stream);
+  hipError_t e = llk::launch_stream_read(src, bytes, workgroups, threads, sink, nontemporal != 0, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "stream_read");
   return LLAMA_OK;
 }

@@ -143,9 +143,9 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
     const bf16* kb = kc + ((size_t)blk * nkv + g) * head_stride + (size_t)l16 * D + 8 * grp;
     const bf16* vb = vc + ((size_t)blk * nkv + g) * head_stride + (size_t)l16 * kKvBlock + 4 * grp;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = ld16<bf16x8>(kb + 32 * s);
+    for (int s = 0; s < KS; ++s) kf[s] = ld16_nt<bf16x8>(kb + 32 * s);
 #pragma unroll
-    for (int i = 0; i < DT; ++i) vf[i] = *reinterpret_cast<const bf16x4*>(vb + (size_t)i * 16 * kKvBlock);
+    for (int i = 0; i < DT; ++i) vf[i] = ld8_nt<bf16x4>(vb + (size_t)i * 16 * kKvBlock);
   };
 
   int j = jb + wave;

@@ -1,9 +1,9 @@
 // A read-only streaming kernel: the measured HBM read ceiling that the
 // weight- and KV-streaming kernels of the decode path are compared against.
 // It reads the same bytes the way they do -- each workgroup one contiguous
-// region, 16-byte loads, several in flight per lane -- and does nothing else
-// with them but fold them into one word per lane, so that its time is the
-// memory system's alone.
+// region, 16-byte loads, several in flight per lane, with or without the
+// nontemporal hint -- and does nothing else with them but fold them into one
+// word per lane, so that its time is the memory system's alone.
 #include "common.h"
 #include "kernels.h"
 
@@ -12,6 +12,9 @@ namespace {
 
 constexpr int kUnroll = 8;
 
+// NT: the loads carry the nontemporal hint (as the decode path's weight and
+// KV streams do)
+template <bool NT>
 __global__ void stream_read_kernel(const uint4* __restrict__ src, size_t n16, unsigned* __restrict__ sink) {
   const size_t per_wg = (n16 + gridDim.x - 1) / gridDim.x;
   const size_t begin = (size_t)blockIdx.x * per_wg;
@@ -22,7 +25,7 @@ __global__ void stream_read_kernel(const uint4* __restrict__ src, size_t n16, un
   for (; i + (kUnroll - 1) * step < end; i += kUnroll * step) {
     uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * step];
+    for (int u = 0; u < kUnroll; ++u) v[u] = NT ? ld16_nt<uint4>(&src[i + u * step]) : src[i + u * step];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
@@ -36,9 +39,12 @@ __global__ void stream_read_kernel(const uint4* __restrict__ src, size_t n16, un
 }  // namespace
 
 hipError_t launch_stream_read(const void* src, size_t bytes, int workgroups, int threads, void* sink,
-                              hipStream_t s) {
+                              bool nontemporal, hipStream_t s) {
   if (bytes == 0) return hipSuccess;
-  stream_read_kernel<<<workgroups, threads, 0, s>>>((const uint4*)src, bytes / 16, (unsigned*)sink);
+  if (nontemporal)
+    stream_read_kernel<true><<<workgroups, threads, 0, s>>>((const uint4*)src, bytes / 16, (unsigned*)sink);
+  else
+    stream_read_kernel<false><<<workgroups, threads, 0, s>>>((const uint4*)src, bytes / 16, (unsigned*)sink);
   return hipGetLastError();
 }
 

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(const bf16* __restri
 #pragma unroll
     for (int s = 0; s < SPC; ++s)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) wn[s][t] = ld16<bf16x8>(wr[t] + (size_t)(kc / 32 + s) * ws.ks);
+      for (int t = 0; t < NT; ++t) wn[s][t] = ld16_nt<bf16x8>(wr[t] + (size_t)(kc / 32 + s) * ws.ks);
   };
 
   f32x4 acc[NT][MT];
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kWaveSplit * 64) void gemm_skinny_wsplit(const bf16
 #pragma unroll
     for (int s = 0; s < SPC; ++s) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) wn[s][t] = ld16<bf16x8>(wr[t] + (size_t)(kc / 32 + s) * ws.ks);
+      for (int t = 0; t < NT; ++t) wn[s][t] = ld16_nt<bf16x8>(wr[t] + (size_t)(kc / 32 + s) * ws.ks);
 #pragma unroll
       for (int u = 0; u < MT; ++u) xn[s][u] = ld16<bf16x8>(xr[u] + kc + 32 * s);
     }

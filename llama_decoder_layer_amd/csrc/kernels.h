@@ -242,7 +242,7 @@ hipError_t launch_moe_sum(const void* part, int T, int topk, int H, void* out, h
 // of `workgroups` workgroups of `threads` threads reading one contiguous
 // region with 16-byte loads; one word per thread goes to sink
 // [workgroups * threads] so that the loads are not dropped.
-hipError_t launch_stream_read(const void* src, size_t bytes, int workgroups, int threads, void* sink,
+hipError_t launch_stream_read(const void* src, size_t bytes, int workgroups, int threads, void* sink, bool nontemporal,
                               hipStream_t s);
 
 // noalloc.hip: the device array that holds the workspace of the forward

@@ -427,7 +427,7 @@ __global__ __launch_bounds__(NW * 64) void moe_stream_kernel(const bf16* __restr
 #pragma unroll
       for (int s = 0; s < SPC; ++s)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) wn[s][t] = ld16<bf16x8>(wr[t] + (size_t)(kc / 32 + s) * ws.ks);
+        for (int t = 0; t < NT; ++t) wn[s][t] = ld16_nt<bf16x8>(wr[t] + (size_t)(kc / 32 + s) * ws.ks);
     };
     f32x4 acc[NT][MT];
 #pragma unroll
