@@ -10,8 +10,9 @@ workload -- over one batch of seeded synthetic inputs that are resident in HBM
 before timing starts.  The main line is the 70B decode (32 sequences, one new
 token each after a 2048-token context); the extra lines are the 70B prefills
 (4 x 2048 and 1 x 32768), the 70B ragged decode through 4 layers, the
-Qwen3-MoE layer and one GPU's TP = 8 share of the 70B layer.  Prints one
-JSON line.
+Qwen3-MoE layer, one GPU's TP = 8 share of the 70B layer, the mixed step
+(32 decode rows + a 512-row prefill chunk) and the 80-layer body replayed
+from one HIP graph.  Prints one JSON line.
 
 Per workload:
   * value / ms_per_step: K steps back to back between two events, with a
@@ -43,7 +44,7 @@ METRIC = "70B-shape layer tokens/s (prefill, decode) + % MFMA/HBM peak, 1 MI355X
 FLUSH_BYTES = 1 << 30
 DEFAULT_EXTRA = ("llama70b_prefill_4x2048,llama70b_prefill_1x32768,llama70b_ragged_decode_b64_4layer,"
                  "qwen3moe_decode_b32_ctx2048,qwen3moe_prefill_4x2048,llama70b_tp8shard_decode_b32_ctx2048,"
-                 "llama70b_tp8shard_prefill_4x2048")
+                 "llama70b_tp8shard_prefill_4x2048,llama70b_mixed_chunk512_decode32,llama70b_stack80_decode_b32_ctx2048")
 # timed calls with a cache flush between them, per workload (the rest: 10)
 FLUSHED_CALLS = {"llama70b_decode_b32_ctx2048": 20, "llama70b_ragged_decode_b64_4layer": 20,
                  "llama70b_prefill_4x2048": 10, "llama70b_prefill_1x32768": 5}
@@ -53,7 +54,40 @@ FLUSHED_CALLS = {"llama70b_decode_b32_ctx2048": 20, "llama70b_ragged_decode_b64_
 # source the kernel's code and launch plan come from is the one the counters were taken on.
 PLAN_SOURCES = ("llama_decoder_layer_amd/csrc/common.h", "llama_decoder_layer_amd/csrc/kernels.h",
                 "llama_decoder_layer_amd/csrc/api.cpp")
-COUNTER_TRAFFIC = {}
+COUNTER_TRAFFIC = {
+    ('llama70b_decode_b32_ctx2048', 'gate_up_silu'): {
+        "bytes": 945640992, "sha1": '5eb0674626e58e809b6c3ca881a3612f42e65113',
+        "sources": ('llama_decoder_layer_amd/csrc/gemm_skinny.hip',),
+        "summary": 'profiles/gate_up_silu_decode_b32_ctx2048_counters.md'},
+    ('llama70b_prefill_4x2048', 'gate_up_silu'): {
+        "bytes": 11744310592, "sha1": 'fc5b8507cb4d0a6430bc524a175ee5f27ef9eab4',
+        "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
+        "summary": 'profiles/gate_up_silu_prefill_4x2048_counters.md'},
+    ('llama70b_prefill_1x32768', 'gate_up_silu'): {
+        "bytes": 47532537216, "sha1": 'fc5b8507cb4d0a6430bc524a175ee5f27ef9eab4',
+        "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
+        "summary": 'profiles/gate_up_silu_prefill_1x32768_counters.md'},
+    ('llama70b_ragged_decode_b64_4layer', 'attention'): {
+        "bytes": 4469750662, "sha1": '0a3680c26e7fb1c4efe0d5163a3c414e355032a6',
+        "sources": ('llama_decoder_layer_amd/csrc/attention_decode.hip', 'llama_decoder_layer_amd/csrc/attention.hip'),
+        "summary": 'profiles/attention_ragged_decode_b64_4layer_counters.md'},
+    ('qwen3moe_decode_b32_ctx2048', 'moe_gate_up_silu'): {
+        "bytes": 699528320, "sha1": '32d0b0a98825cd52e3c955ed4c8613c42a6db3df',
+        "sources": ('llama_decoder_layer_amd/csrc/moe.hip',),
+        "summary": 'profiles/moe_gate_up_silu_qwen3moe_decode_b32_ctx2048_counters.md'},
+    ('qwen3moe_prefill_4x2048', 'moe_gate_up_silu'): {
+        "bytes": 1891999696, "sha1": '32d0b0a98825cd52e3c955ed4c8613c42a6db3df',
+        "sources": ('llama_decoder_layer_amd/csrc/moe.hip',),
+        "summary": 'profiles/moe_gate_up_silu_qwen3moe_prefill_4x2048_counters.md'},
+    ('llama70b_tp8shard_decode_b32_ctx2048', 'gate_up'): {
+        "bytes": 129028448, "sha1": '5eb0674626e58e809b6c3ca881a3612f42e65113',
+        "sources": ('llama_decoder_layer_amd/csrc/gemm_skinny.hip',),
+        "summary": 'profiles/gate_up_tp8shard_decode_b32_ctx2048_counters.md'},
+    ('llama70b_tp8shard_prefill_4x2048', 'gate_up_silu'): {
+        "bytes": 1535366224, "sha1": 'fc5b8507cb4d0a6430bc524a175ee5f27ef9eab4',
+        "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
+        "summary": 'profiles/gate_up_silu_tp8shard_prefill_4x2048_counters.md'},
+}
 
 
 def sources_sha1(paths):
@@ -278,6 +312,7 @@ def measure_stack(wl, steps, warmup, flushed_calls, flush_buf, graph=True):
     final = synth.draw_final_norm(model, wl.index, dev)
     stack = lda.Stack(model.config_dict(), [src[l % n_src] for l in range(wl.layers)], final)
     weight_bytes = sum(v.numel() * v.element_size() for v in src[0].values())
+    w0 = src[0]  # kept for the oracle baseline's sampled layer
     del src
     torch.cuda.empty_cache()
     pools = [synth.build_kv_pool(wl, batch, l, dev) for l in range(wl.layers)]
@@ -337,7 +372,9 @@ def measure_stack(wl, steps, warmup, flushed_calls, flush_buf, graph=True):
     if graph:
         g.close()
     stack.close()
-    return res, None
+    # the oracle baseline samples layer 0 and scales its time by the layer count
+    per_layer = [{"weights": w0, "k_pool": pools[0][0], "v_pool": pools[0][1]}] + [None] * (wl.layers - 1)
+    return res, (batch, hidden, None, per_layer)
 
 
 def hbm_read_ceiling(steps=10):
@@ -404,9 +441,10 @@ def cpu_info():
 def cpu_baseline(wl, batch, hidden, residual, per_layer, min_seconds):
     """The oracle (float64 numpy, as it stands) on a bounded sample of the
     same step, its inputs and weights widened before the timed region.
-    Decode: every row of the step (the ragged batch: its first 4 sequences),
-    through every layer (the ragged batch: through layer 0, the time scaled
-    by its 4 layers).  Prefill: the first 256 token rows of the step.
+    Decode: every row of the step through every layer; with several layers
+    (the ragged 4-layer batch, the 80-layer stack) the first 4 sequences
+    through layer 0, the time scaled by the layer count (the stack's final
+    norm left out).  Prefill and mixed steps: the first 256 token rows.
     Repeated until about `min_seconds` of CPU work have run."""
     import numpy as np
 
