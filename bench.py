@@ -415,6 +415,47 @@ def hbm_read_ceiling(steps=10):
     return out
 
 
+def cold_read_by_size(reps=7):
+    """The nontemporal read-only kernel (one 7-wave workgroup per CU) over
+    each of the 70B decode step's streams -- the four projection weights and
+    the 32 x 2048 batch's K/V -- each read right after a 1 GiB cache flush:
+    the time a kernel that only reads those bytes needs, ramp and tail
+    included, against which each decode kernel's time is set.  Median of
+    `reps` flushed reads per size."""
+    import torch
+
+    import llama_decoder_layer_amd as lda
+    import synth
+
+    m = synth.LLAMA70B
+    H, I, D = m.hidden_size, m.intermediate_size, m.head_dim
+    kv_heads, q_heads = m.num_key_value_heads, m.num_attention_heads
+    sizes = (("qkv_proj", (q_heads + 2 * kv_heads) * D * H * 2), ("o_proj", H * q_heads * D * 2),
+             ("down_proj", H * I * 2), ("gate_up", 2 * I * H * 2), ("kv_32x2048", 32 * 2048 * 2 * kv_heads * D * 2))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    flush_buf = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(cus * 448, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, nbytes in sizes:
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        lda.stream_read(src, cus, 448, sink, nontemporal=True)
+        us = []
+        for _ in range(reps):
+            _flush(flush_buf)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            lda.stream_read(src, cus, 448, sink, nontemporal=True)
+            b.record()
+            torch.cuda.synchronize()
+            us.append(a.elapsed_time(b) * 1e3)
+        med = statistics.median(us)
+        out[name] = {"bytes": nbytes, "median_us": round(med, 2), "min_us": round(min(us), 2),
+                     "GB_per_s": round(nbytes / (med / 1e6) / 1e9, 1)}
+        del src
+    return out
+
+
 def cpu_info():
     model = "unknown"
     try:
@@ -529,7 +570,8 @@ def main():
                     help="only run a plain device-to-device copy of BYTES bytes, 3 times (a reference for "
                          "the HBM byte counters of a profiler), and exit")
     ap.add_argument("--ceiling-only", action="store_true",
-                    help="only run the read-only streaming kernel (the HBM read ceiling) and exit")
+                    help="only run the read-only streaming kernel (the HBM read ceiling, and cold reads of "
+                         "each decode stream's size) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -550,7 +592,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "launches": 3}))
         return
     if args.ceiling_only:
-        print(json.dumps({"hbm_read_ceiling": hbm_read_ceiling()}))
+        print(json.dumps({"hbm_read_ceiling": hbm_read_ceiling(), "cold_read_by_size": cold_read_by_size()}))
         return
 
     flush_buf = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
@@ -563,6 +605,7 @@ def main():
             extra.append(run_workload(name, max(3, args.steps // 4), min(args.warmup, 2), calls(name), flush_buf,
                                       cpu_s / 2))
     ceiling = hbm_read_ceiling()
+    cold = cold_read_by_size()
     wl = synth.WORKLOADS[args.workload]
     out = {
         "metric": METRIC,
@@ -587,6 +630,7 @@ def main():
         **({"experts_with_tokens": main_res["experts_with_tokens"]} if "experts_with_tokens" in main_res else {}),
         "wall_s_timed_region": main_res["wall_s_timed_region"],
         "hbm_read_ceiling": ceiling,
+        "cold_read_by_size": cold,
         "extra": extra,
     }
     print(json.dumps(out))
