@@ -399,21 +399,48 @@ hipError_t linear_f32(const float* x, const float* w, int M, int N, int K, float
 
 TilePlan tile_plan(int M, int wrows, int K, int num_cus) {
   TilePlan p;
-  // 256-row weight tiles need wrows % 256 == 0.  Token tiles of 256 rows,
-  // or of 192 when those pad M by more than a ninth less (e.g. 544 tokens:
-  // 3 x 192 = 576 rows computed instead of 3 x 256 = 768); fewer than 256
-  // tokens take 128 x 128.
-  const bool wide = M >= 256 && wrows % 256 == 0;
-  p.bm = 128;
-  if (wide) {
-    const int pad256 = (M + 255) / 256 * 256, pad192 = (M + 191) / 192 * 192;
-    p.bm = pad256 * 9 <= pad192 * 10 ? 256 : 192;
-  }
-  const int bn = wide ? 256 : 128;
-  const int tiles = ((M + p.bm - 1) / p.bm) * (wrows / bn);
   const int cus = num_cus > 0 ? num_cus : 256;
+  p.bm = 128;
   p.splits = 1;
-  for (int s = 2; s <= 8 && tiles * p.splits < cus && K % (s * kTBK) == 0; s *= 2) p.splits = s;
+  if (M >= 256 && wrows % 256 == 0) {
+    // 256-row weight tiles, token tiles of 256 or 192 rows, K unsplit or
+    // split in 2, 4 or 8 (fp32 partials, then a reduce kernel).  Each plan
+    // is priced from measurements on gfx950 and the cheapest taken:
+    //   * one 64-deep k stage of a 256 x 256 tile takes ~1.63 us when every
+    //     CU runs one workgroup, of a 192 x 256 tile 0.79 of that;
+    //   * the workgroups run in rounds of one per CU, and a partly filled
+    //     last round costs 0.75 + 0.25 x its fill of a full one;
+    //   * the partials cost 8 bytes per element and split (written, read
+    //     back) at ~5 TB/s.
+    // Fitted to 14 shapes (70B prefill and mixed-step projections, one GPU's
+    // TP = 8 share, the Qwen3-MoE attention projections, 300 and 1000
+    // tokens), it picks the measured fastest of the 8 plans for each: e.g.
+    // 8192 x 1280 x 8192 (TP = 8 qkv) 192-row tiles unsplit, 153 us against
+    // 215 us for 256-row tiles split in 2 (320 workgroups: a second round
+    // for a quarter of the CUs).
+    constexpr double kStageUs = 1.63, kBm192 = 0.79, kReduceBytesPerUs = 5.0e6;
+    double best = 0.0;
+    for (const int bm : {256, 192}) {
+      const long long tiles = (long long)((M + bm - 1) / bm) * (wrows / 256);
+      for (int s = 1; s <= 8; s *= 2) {
+        if (K % (s * kTBK) != 0) break;
+        const long long wgs = tiles * s, full = wgs / cus, rem = wgs % cus;
+        const double rounds = (double)full + (rem ? 0.75 + 0.25 * (double)rem / cus : 0.0);
+        double c = rounds * (double)(K / s / kTBK) * kStageUs * (bm == 256 ? 1.0 : kBm192);
+        if (s > 1) c += 8.0 * s * (double)M * wrows / kReduceBytesPerUs;
+        if (best == 0.0 || c < best) {  // ties keep the larger tile and fewer splits
+          best = c;
+          p.bm = bm;
+          p.splits = s;
+        }
+      }
+    }
+  } else {
+    // fewer than 256 tokens, or weight rows not a multiple of 256: 128 x 128
+    // tiles, K split while the tiles alone leave CUs idle
+    const int tiles = ((M + 127) / 128) * (wrows / 128);
+    for (int s = 2; s <= 8 && tiles * p.splits < cus && K % (s * kTBK) == 0; s *= 2) p.splits = s;
+  }
   p.partial_bytes = p.splits > 1 ? (size_t)p.splits * M * wrows * sizeof(float) : 0;
   return p;
 }

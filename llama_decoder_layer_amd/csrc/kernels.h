@@ -41,9 +41,10 @@ hipError_t launch_linear(int dtype, const void* x, const void* w, int M, int N, 
                          void* out, hipStream_t s, int layout = kRowMajor, float* part = nullptr,
                          size_t part_cap = 0);
 // Tiled-kernel plan for M > kSkinnyMaxM: bm token rows x 256 weight rows
-// (bm = 256, or 192 where that pads M less; 128 x 128 tiles for few tokens or
-// weight rows not a multiple of 256), and K split in 2, 4 or 8 while the
-// tiles alone number fewer than the CUs.
+// (bm = 256 or 192) and K unsplit or split in 2, 4 or 8, whichever a cost
+// model measured on gfx950 prices lowest; 128 x 128 tiles for fewer than 256
+// tokens or weight rows not a multiple of 256, K split while those tiles
+// alone number fewer than the CUs.
 struct TilePlan {
   int bm;
   int splits;
