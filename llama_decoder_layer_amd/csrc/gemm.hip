@@ -244,11 +244,15 @@ hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, WS
     attr_set = true;
   }
   const int nb = ((M + BM - 1) / BM) * (wrows / BN);
-  // Up to 32 token tiles the plain order already runs 4 token x 8 weight
-  // tiles together on each XCD (round-robin dispatch) and measured best;
-  // beyond that, grouped order (26.9 -> 25.8 ms on 32768 x 57344 x 8192).
+  // XCD-grouped order wherever the weight tiles divide by 8: every token
+  // tile of a weight tile runs on the XCD that owns it.  The plain order
+  // (token tiles fastest) spreads them over the XCDs, so each XCD's L2
+  // fetches the weight tile again: measured on 12 shapes, grouped is as fast
+  // or faster everywhere (544 x 57344 x 8192: 603 -> 563 us; 1536 tokens:
+  // 1358 -> 1287 us; 8192 x 8192 x 8192: 917 -> 882 us; 32768 x 57344 x
+  // 8192: 26.9 -> 25.8 ms).
   const int num_m = (M + BM - 1) / BM;
-  const int group_m = num_m > 32 && (wrows / BN) % 8 == 0 ? kGroupM : 0;
+  const int group_m = (wrows / BN) % 8 == 0 ? kGroupM : 0;
   // weight chunks of 32 tiles where 32 tiles of this K fit in 160 MB
   const int ntot = wrows / BN;
   const int cw = ntot % 32 == 0 && (size_t)32 * BN * K * sizeof(bf16) <= ((size_t)160 << 20) ? 32 : ntot;
