@@ -8,8 +8,8 @@
 // and "模型库与算子层 — 代码走读" (vllm-learning.pages.dev), section
 // "Attention 层" (attention through the block table).
 //
-// HBM-bound: every K/V byte of the context is read once and serves all G
-// query heads of its group.  One workgroup = (token, KV head, key partition;
+// HBM-bound: every K/V byte of the context is read once (loads with the
+// nontemporal hint) and serves all G query heads of its group.  One workgroup = (token, KV head, key partition;
 // a (token, KV head) is split only when that is needed to occupy every CU);
 // its 4 waves take the partition's 16-slot blocks round-robin, each with its
 // own running max and sum, and merge through LDS at the end.  Per block and

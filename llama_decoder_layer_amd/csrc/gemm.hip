@@ -17,11 +17,11 @@
 // agree between A and B, which lets the loads be laid out for coalescing.
 //
 //   skinny kernel (M <= 128 tokens, decode): gemm_skinny.hip.
-//   tiled kernel (prefill): 256 tokens x 256 weight rows per workgroup with
-//     8 waves of 128 x 64 (128 KiB of LDS), or 128 x 128 with 4 waves of
-//     64 x 64 for shapes the large tile does not fit; K in steps of 64 loaded
-//     straight from global memory into double-buffered, XOR-swizzled LDS;
-//     XCD-aware tile order.
+//   tiled kernel (prefill): 256 (or 192) tokens x 256 weight rows per
+//     workgroup with 8 waves (128 KiB of LDS), or 128 x 128 with 4 waves
+//     for fewer than 256 tokens; tile height and split-K from a measured
+//     cost model (tile_plan); K in steps of 64 loaded straight from global
+//     memory into double-buffered, XOR-swizzled LDS; XCD-grouped tile order.
 //   fp32 kernel: plain LDS-tiled FMA kernel for fp32 layers.
 //
 // SiluAndMul layout: the bf16 gate_up weight is re-ordered once (in create)

@@ -15,7 +15,8 @@
 //     memory traffic is W plus a small fraction of x;
 //   * W fragments are loaded straight from global memory into MFMA operand
 //     registers (A = W rows, 16-byte loads, 64 contiguous bytes per row per
-//     instruction), one full chunk ahead of the MFMAs that use them;
+//     instruction), one full chunk ahead of the MFMAs that use them, with
+//     the nontemporal hint (each weight byte is read once per step);
 //   * v_mfma_f32_16x16x32_bf16 computes D[n][m] = W[n,:] . x[m,:]; a lane
 //     ends with four consecutive output features of one token.
 // Epilogues: bf16 store, residual add (in place), SiluAndMul on the re-ordered

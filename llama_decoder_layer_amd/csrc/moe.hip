@@ -29,7 +29,8 @@
 //                      rows into act [P, I] (sorted order), then down with the
 //                      routing weight applied before the bf16 store, scattered
 //                      to part [P, H] by pair.  Few pairs per expert (decode):
-//                      weight-streaming kernel over the active experts; many
+//                      weight-streaming kernel over the active experts (each
+//                      expert's weight read once, nontemporal loads); many
 //                      (prefill): 256 x 256 MFMA tiles over the tile table;
 //   moe_sum_kernel     out[t] = sum over slots of part[t*k + slot], in slot
 //                      order, fp32 accumulation.
