@@ -56,35 +56,35 @@ PLAN_SOURCES = ("llama_decoder_layer_amd/csrc/common.h", "llama_decoder_layer_am
                 "llama_decoder_layer_amd/csrc/api.cpp")
 COUNTER_TRAFFIC = {
     ('llama70b_decode_b32_ctx2048', 'gate_up_silu'): {
-        "bytes": 945641088, "sha1": '1781413a2af140fb40cc5a338b8478fbd726e3a4',
+        "bytes": 945640864, "sha1": 'a57a58c8a8f4d30035e7348471378ed326fb5f8e',
         "sources": ('llama_decoder_layer_amd/csrc/gemm_skinny.hip',),
         "summary": 'profiles/gate_up_silu_decode_b32_ctx2048_counters.md'},
     ('llama70b_prefill_4x2048', 'gate_up_silu'): {
-        "bytes": 11744307040, "sha1": '72280f5ff1771ed36104687d9a877ed905967e3b',
+        "bytes": 11792284760, "sha1": 'ee05b63e72916ec8eb3cbcbe2a240db4d4af03cb',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_prefill_4x2048_counters.md'},
     ('llama70b_prefill_1x32768', 'gate_up_silu'): {
-        "bytes": 47256637504, "sha1": '72280f5ff1771ed36104687d9a877ed905967e3b',
+        "bytes": 47927832040, "sha1": 'ee05b63e72916ec8eb3cbcbe2a240db4d4af03cb',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_prefill_1x32768_counters.md'},
     ('llama70b_ragged_decode_b64_4layer', 'attention'): {
-        "bytes": 4469789954, "sha1": '68d6ddee1b51c1f7d4c89e42701c13cd95986fb2',
+        "bytes": 4469737146, "sha1": '9cbbed96b6f5520980782437f62a75b1b2ccc523',
         "sources": ('llama_decoder_layer_amd/csrc/attention_decode.hip', 'llama_decoder_layer_amd/csrc/attention.hip'),
         "summary": 'profiles/attention_ragged_decode_b64_4layer_counters.md'},
     ('qwen3moe_decode_b32_ctx2048', 'moe_gate_up_silu'): {
-        "bytes": 699528320, "sha1": '8285f376b99d51a2e44fa2a3785dc43407bc106f',
+        "bytes": 699528384, "sha1": '4bce3983ddba46e4cf5f436cd2b3ea60d90a2315',
         "sources": ('llama_decoder_layer_amd/csrc/moe.hip',),
         "summary": 'profiles/moe_gate_up_silu_qwen3moe_decode_b32_ctx2048_counters.md'},
     ('qwen3moe_prefill_4x2048', 'moe_gate_up_silu'): {
-        "bytes": 1883967032, "sha1": '8285f376b99d51a2e44fa2a3785dc43407bc106f',
+        "bytes": 1890359200, "sha1": '4bce3983ddba46e4cf5f436cd2b3ea60d90a2315',
         "sources": ('llama_decoder_layer_amd/csrc/moe.hip',),
         "summary": 'profiles/moe_gate_up_silu_qwen3moe_prefill_4x2048_counters.md'},
     ('llama70b_tp8shard_decode_b32_ctx2048', 'gate_up'): {
-        "bytes": 129028528, "sha1": '1781413a2af140fb40cc5a338b8478fbd726e3a4',
+        "bytes": 129028624, "sha1": 'a57a58c8a8f4d30035e7348471378ed326fb5f8e',
         "sources": ('llama_decoder_layer_amd/csrc/gemm_skinny.hip',),
         "summary": 'profiles/gate_up_tp8shard_decode_b32_ctx2048_counters.md'},
     ('llama70b_tp8shard_prefill_4x2048', 'gate_up_silu'): {
-        "bytes": 1535366344, "sha1": '72280f5ff1771ed36104687d9a877ed905967e3b',
+        "bytes": 1535366544, "sha1": 'ee05b63e72916ec8eb3cbcbe2a240db4d4af03cb',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_tp8shard_prefill_4x2048_counters.md'},
 }
