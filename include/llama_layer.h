@@ -264,7 +264,8 @@ LLAMA_API llama_status llama_layer_forward_noalloc(llama_layer* layer, const voi
                                                    int32_t max_seq_len, void* hidden_out, void* residual_out,
                                                    void* stream);
 
-/* Frees the layer's device memory (synchronises the device first). */
+/* Frees the layer's device memory (synchronises the layer's device first;
+ * any device may be current, and the caller's current device is kept). */
 LLAMA_API void llama_layer_destroy(llama_layer* layer);
 
 /* Message of the calling thread's last failed call ("" if none). */
@@ -304,7 +305,8 @@ LLAMA_API llama_status llama_stack_forward(llama_stack* stack, const void* hidde
                                            int32_t num_seqs, int32_t max_seq_len, void* out, void* workspace,
                                            void* stream);
 
-/* Frees the stack's device memory (synchronises the device first). */
+/* Frees the stack's device memory (synchronises the stack's device first;
+ * any device may be current, and the caller's current device is kept). */
 LLAMA_API void llama_stack_destroy(llama_stack* stack);
 
 /* A HIP graph of one llama_stack_forward with exactly these arguments,
@@ -324,7 +326,8 @@ LLAMA_API llama_status llama_stack_graph_create(llama_stack* stack, const void* 
                                                 void* stream, llama_graph** graph);
 /* Launches the graph on `stream` (asynchronous). */
 LLAMA_API llama_status llama_graph_launch(llama_graph* graph, void* stream);
-/* Frees the graph (synchronises the device first). */
+/* Frees the graph (synchronises the graph's device first; any device may
+ * be current, and the caller's current device is kept). */
 LLAMA_API void llama_graph_destroy(llama_graph* graph);
 
 /* ---- inspection -------------------------------------------------------- */

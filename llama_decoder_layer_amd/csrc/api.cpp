@@ -32,6 +32,19 @@ llama_status hip_fail(hipError_t e, const char* what) {
   return fail(LLAMA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Makes `dev` the current device for the scope's lifetime and restores the
+// caller's afterwards: the destroy calls may come with another device current.
+struct DeviceScope {
+  int prev = -1;
+  explicit DeviceScope(int dev) {
+    int cur = -1;
+    if (dev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != dev && hipSetDevice(dev) == hipSuccess) prev = cur;
+  }
+  ~DeviceScope() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
 #define HIP_TRY(expr, what)                      \
   do {                                           \
     hipError_t e_ = (expr);                      \
@@ -845,6 +858,7 @@ llama_status llama_layer_forward_noalloc(llama_layer* L, const void* hidden, con
 
 void llama_layer_destroy(llama_layer* L) {
   if (!L) return;
+  DeviceScope on(L->device);
   (void)hipDeviceSynchronize();
   free_layer(L);
 }
@@ -963,6 +977,7 @@ struct llama_stack {
 struct llama_graph {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  int device = -1;
 };
 
 namespace {
@@ -1080,6 +1095,7 @@ llama_status llama_stack_forward(llama_stack* S, const void* hidden, const int32
 
 void llama_stack_destroy(llama_stack* S) {
   if (!S) return;
+  DeviceScope on(S->layers.empty() ? -1 : S->layers[0]->device);
   (void)hipDeviceSynchronize();
   free_stack(S);
 }
@@ -1110,6 +1126,7 @@ llama_status llama_stack_graph_create(llama_stack* S, const void* hidden, const 
   if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
   llama_graph* G = new llama_graph();
   G->graph = g;
+  G->device = S->layers.empty() ? -1 : S->layers[0]->device;
   e = hipGraphInstantiate(&G->exec, g, nullptr, nullptr, 0);
   if (e != hipSuccess) {
     (void)hipGraphDestroy(g);
@@ -1129,6 +1146,7 @@ llama_status llama_graph_launch(llama_graph* G, void* stream) {
 
 void llama_graph_destroy(llama_graph* G) {
   if (!G) return;
+  DeviceScope on(G->device);
   (void)hipDeviceSynchronize();
   if (G->exec) (void)hipGraphExecDestroy(G->exec);
   if (G->graph) (void)hipGraphDestroy(G->graph);

@@ -237,12 +237,12 @@ hipError_t launch_tile(const bf16* x, int M, const bf16* w, int wrows, int K, WS
                        hipStream_t s, int splits = 1) {
   auto fn = gemm_tile_bf16<BM, BN, WM, WN, EPI>;
   const size_t lds = (size_t)2 * (BM + BN) * kTBK * sizeof(bf16);
-  static bool attr_set = false;  // per instantiation; the attribute is per function
-  if (lds > 65536 && !attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // more than 64 KiB of dynamic LDS needs the function's opt-in: done once
+  // per instantiation (a thread-safe function-local static)
+  static const hipError_t attr =
+      lds > 65536 ? hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+                  : hipSuccess;
+  if (attr != hipSuccess) return attr;
   const int nb = ((M + BM - 1) / BM) * (wrows / BN);
   // XCD-grouped order wherever the weight tiles divide by 8: every token
   // tile of a weight tile runs on the XCD that owns it.  The plain order

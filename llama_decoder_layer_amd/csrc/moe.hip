@@ -683,12 +683,12 @@ hipError_t launch_moe_tile(const bf16* x, int topk, const bf16* w, int wrows, in
                            bf16* out, int ldo, hipStream_t s) {
   auto fn = moe_tile_kernel<BM, BN, WM, WN, EPI>;
   const size_t lds = (size_t)2 * (BM + BN) * kTBK * sizeof(bf16);
-  static bool attr_set = false;
-  if (lds > 65536 && !attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // more than 64 KiB of dynamic LDS needs the function's opt-in: done once
+  // per instantiation (a thread-safe function-local static)
+  static const hipError_t attr =
+      lds > 65536 ? hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+                  : hipSuccess;
+  if (attr != hipSuccess) return attr;
   const int nn = wrows / BN;
   const size_t C8 = (size_t)8 * nn * kEntriesPerChunk;
   const size_t work = (size_t)r.tile_cap * nn;
