@@ -481,3 +481,12 @@ WIDE = synth.ModelShape(8192, 32, 8, 128, 1024, 1e-5, 500000.0, synth.LLAMA3_SCA
 def test_wide_decode_in_workgroup_split_k():
     for idx, b in ((54, 8), (55, 32), (56, 64)):  # 1, 2 and 4 token tiles
         _run(synth.Workload(idx, "wide_decode_b%d" % b, WIDE, b, 1, (10, 300)))
+
+
+def test_mid_positions_at_the_configured_maximum():
+    # the last position max_position_embeddings - 1 = 131071: the far end of
+    # the llama3 RoPE table, decode over 64 key partitions of 2048 (merged by
+    # the combine), and a 64-row chunk on a 131008-token context whose query
+    # tiles split their keys into 8 partitions
+    _run(synth.Workload(66, "mid_decode_maxpos", MID, 2, 1, 0), ctx_lens=[131071, 70000])
+    _run(synth.Workload(67, "mid_chunk_maxpos", MID, 1, 64, 0), ctx_lens=[131008])
