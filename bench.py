@@ -382,7 +382,8 @@ def hbm_read_ceiling(steps=10):
     of the decode step's largest kernel (the 70B gate_up weight, one
     workgroup of 7 waves per CU), and over 4 GiB in 256 workgroups of 256
     threads; each with plain loads and with the nontemporal hint the decode
-    path's weight and KV streams use."""
+    path's weight and KV streams use.  Then 4 GiB gathered as 4 KiB blocks in
+    random and in sequential order (nontemporal)."""
     import torch
 
     import llama_decoder_layer_amd as lda
@@ -412,6 +413,34 @@ def hbm_read_ceiling(steps=10):
                 "GB_per_s": round(nbytes / (us / 1e6) / 1e9, 1),
                 "frac_of_peak": round(nbytes / (us / 1e6) / 1e9 / PEAK_HBM_GBS, 4)}
         del src, sink
+    # 4 GiB read as 4 KiB blocks (one KV head's K or V block of the cache) in a
+    # seeded random order and in order, nontemporal: the decode attention's
+    # access pattern over a paged cache
+    nbytes, bb, wgs = 4 << 30, 4096, 2048
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.empty(wgs * bb // 16, dtype=torch.int32, device="cuda")
+    g = torch.Generator().manual_seed(11)
+    for name, ids in (("4GiB_4KiB_blocks_random", torch.randperm(nbytes // bb, generator=g)),
+                      ("4GiB_4KiB_blocks_in_order", torch.arange(nbytes // bb))):
+        ids = ids.to(torch.int32).to("cuda")
+        lda.block_read(src, ids, bb, wgs, sink, nontemporal=True)  # checks the ids once
+        for _ in range(2):
+            lda.block_read(src, ids, bb, wgs, sink, nontemporal=True, check_ids=False)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            lda.block_read(src, ids, bb, wgs, sink, nontemporal=True, check_ids=False)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        out[name + "_nontemporal"] = {
+            "bytes": nbytes, "workgroups": wgs, "threads": bb // 16, "avg_us": round(us, 2),
+            "GB_per_s": round(nbytes / (us / 1e6) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (us / 1e6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del ids
+    del src, sink
     return out
 
 

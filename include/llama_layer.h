@@ -425,6 +425,19 @@ LLAMA_API llama_status llama_op_add_rmsnorm(int32_t dtype, const void* x, const 
 LLAMA_API llama_status llama_diag_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t threads,
                                               int32_t nontemporal, void* sink, void* stream);
 
+/* The same reads gathered by block, as the decode attention reads a paged
+ * cache: src holds src_bytes / block_bytes blocks of block_bytes bytes (a
+ * multiple of 1024, at most 16384); block_ids [num_ids] (int32, device) lists
+ * the blocks to read, each in [0, src_bytes / block_bytes) -- the caller's
+ * guarantee, not checked on the device.  Each of `workgroups` workgroups of
+ * block_bytes / 16 threads reads a contiguous range of the list, one 16-byte
+ * word per thread and block, several blocks in flight, and writes one 32-bit
+ * word per thread to sink [workgroups * block_bytes / 16] (device).
+ * nontemporal as llama_diag_stream_read.  Errors: INVALID_ARGUMENT, HIP. */
+LLAMA_API llama_status llama_diag_block_read(const void* src, size_t src_bytes, const int32_t* block_ids,
+                                             int32_t num_ids, int32_t block_bytes, int32_t workgroups,
+                                             int32_t nontemporal, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -120,6 +120,8 @@ def lib() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_int64), i32]
     L.llama_diag_stream_read.restype = st
     L.llama_diag_stream_read.argtypes = [vp, ctypes.c_size_t, i32, i32, i32, vp, vp]
+    L.llama_diag_block_read.restype = st
+    L.llama_diag_block_read.argtypes = [vp, ctypes.c_size_t, vp, i32, i32, i32, i32, vp, vp]
     L.llama_op_linear.restype = st
     L.llama_op_linear.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, vp]
     L.llama_op_reorder_gate_up.restype = st
@@ -150,7 +152,8 @@ EXPORTED = ["llama_layer_config_validate", "llama_layer_create", "llama_layer_wo
             "llama_layer_workspace_tensor", "llama_layer_rope_table", "llama_layer_set_timing", "llama_layer_timing_read",
             "llama_op_linear", "llama_op_reorder_gate_up", "llama_op_add_rmsnorm",
             "llama_stack_create", "llama_stack_workspace_bytes", "llama_stack_forward", "llama_stack_destroy",
-            "llama_stack_graph_create", "llama_graph_launch", "llama_graph_destroy", "llama_diag_stream_read"]
+            "llama_stack_graph_create", "llama_graph_launch", "llama_graph_destroy", "llama_diag_stream_read",
+            "llama_diag_block_read"]
 
 
 _hip_rt = None
@@ -534,6 +537,26 @@ def stream_read(src: torch.Tensor, workgroups: int, threads: int, sink: torch.Te
         raise ValueError("sink too small")
     _check(lib().llama_diag_stream_read(_ptr(src), src.numel() * src.element_size(), workgroups, threads,
                                         int(bool(nontemporal)), _ptr(sink), _stream(stream)))
+
+
+def block_read(src: torch.Tensor, block_ids: torch.Tensor, block_bytes: int, workgroups: int, sink: torch.Tensor,
+               nontemporal: bool = False, stream=None, check_ids: bool = True) -> None:
+    """llama_diag_block_read: reads the blocks block_ids (int32, device) of
+    block_bytes each from src (device, contiguous); sink holds
+    workgroups * block_bytes / 16 int32.  check_ids: verify on the host that
+    every id is in range first (a device reduction and a synchronisation;
+    a timing loop checks once and passes False)."""
+    _dev(src, "src")
+    _dev(block_ids, "block_ids", torch.int32)
+    _dev(sink, "sink")
+    nb = src.numel() * src.element_size() // block_bytes
+    if check_ids and block_ids.numel() and (int(block_ids.min()) < 0 or int(block_ids.max()) >= nb):
+        raise ValueError("block id out of range")
+    if sink.numel() * sink.element_size() < workgroups * block_bytes // 16 * 4:
+        raise ValueError("sink too small")
+    _check(lib().llama_diag_block_read(_ptr(src), src.numel() * src.element_size(), _ptr(block_ids),
+                                       block_ids.numel(), block_bytes, workgroups, int(bool(nontemporal)),
+                                       _ptr(sink), _stream(stream)))
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, epilogue: Epilogue = Epilogue.STORE, out=None, stream=None):

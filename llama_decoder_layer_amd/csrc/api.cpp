@@ -933,6 +933,20 @@ llama_status llama_diag_stream_read(const void* src, size_t bytes, int32_t workg
   return LLAMA_OK;
 }
 
+llama_status llama_diag_block_read(const void* src, size_t src_bytes, const int32_t* block_ids, int32_t num_ids,
+                                   int32_t block_bytes, int32_t workgroups, int32_t nontemporal, void* sink,
+                                   void* stream) {
+  if (!src || !block_ids || !sink) return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (block_bytes < 1024 || block_bytes > 16384 || block_bytes % 1024 || !aligned16(src))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "block_bytes a multiple of 1024 in [1024, 16384], src 16-byte aligned");
+  if (num_ids < 0 || workgroups <= 0 || workgroups > (1 << 20) || src_bytes < (size_t)block_bytes)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "num_ids >= 0, workgroups in [1, 2^20], src at least one block");
+  hipError_t e = llk::launch_block_read(src, block_ids, num_ids, block_bytes, workgroups, sink, nontemporal != 0,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "block_read");
+  return LLAMA_OK;
+}
+
 llama_status llama_op_reorder_gate_up(const void* src, int32_t inter, int32_t K, void* dst, void* stream) {
   if (!src || !dst) return fail(LLAMA_ERR_INVALID_ARGUMENT, "NULL pointer");
   if (inter <= 0 || K <= 0 || inter % 16 || K % 8)

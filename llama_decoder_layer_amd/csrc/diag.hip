@@ -36,7 +36,46 @@ __global__ void stream_read_kernel(const uint4* __restrict__ src, size_t n16, un
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// The same reads gathered by block: workgroup w takes a contiguous range of
+// the id list and reads each listed block of blockDim.x 16-byte words (one
+// word per thread), kUnroll blocks in flight -- the access pattern of the
+// decode attention over a paged cache whose blocks sit in random order.
+template <bool NT>
+__global__ void block_read_kernel(const uint4* __restrict__ src, const int* __restrict__ ids, int n,
+                                  unsigned* __restrict__ sink) {
+  const int per = (n + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int b0 = (int)blockIdx.x * per;
+  const int b1 = b0 + per < n ? b0 + per : n;
+  const size_t words = blockDim.x;
+  unsigned acc = 0;
+  for (int b = b0; b < b1; b += kUnroll) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      v[u] = uint4{0u, 0u, 0u, 0u};
+      if (b + u < b1) {
+        const uint4* p = &src[(size_t)ids[b + u] * words + threadIdx.x];
+        v[u] = NT ? ld16_nt<uint4>(p) : *p;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_block_read(const void* src, const int* ids, int n, int block_bytes, int workgroups, void* sink,
+                             bool nontemporal, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int threads = block_bytes / 16;
+  if (nontemporal)
+    block_read_kernel<true><<<workgroups, threads, 0, s>>>((const uint4*)src, ids, n, (unsigned*)sink);
+  else
+    block_read_kernel<false><<<workgroups, threads, 0, s>>>((const uint4*)src, ids, n, (unsigned*)sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, size_t bytes, int workgroups, int threads, void* sink,
                               bool nontemporal, hipStream_t s) {

@@ -245,6 +245,11 @@ hipError_t launch_moe_sum(const void* part, int T, int topk, int H, void* out, h
 // [workgroups * threads] so that the loads are not dropped.
 hipError_t launch_stream_read(const void* src, size_t bytes, int workgroups, int threads, void* sink, bool nontemporal,
                               hipStream_t s);
+// diag.hip: the blocks ids[0..n) of block_bytes each (64 * k, at most 16 KiB)
+// from src, one 16-byte word per thread and block; one word per thread to
+// sink [workgroups * block_bytes / 16].
+hipError_t launch_block_read(const void* src, const int* ids, int n, int block_bytes, int workgroups, void* sink,
+                             bool nontemporal, hipStream_t s);
 
 // noalloc.hip: the device array that holds the workspace of the forward
 // entry point that allocates nothing.  setup looks up a device's address

@@ -129,3 +129,24 @@ def test_add_rmsnorm_fp32():
     he, re_ = oracle.fused_add_rms_norm(np64(x), np64(r), np64(w), 1e-5)
     compare("rmsnorm_f32", np64(h), he, dtype="fp32")
     compare("residual_f32", np64(ro), re_, dtype="fp32")
+
+
+def test_diag_block_read_reads_the_listed_blocks():
+    # each thread folds word t of every block its workgroup reads: compare
+    # with the same fold on the host (uneven split: 37 blocks, 4 workgroups)
+    rng = np.random.default_rng(3)
+    nb, bb, wgs = 64, 4096, 4
+    words = rng.integers(0, 2 ** 32, size=(nb, bb // 16, 4), dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32).reshape(-1)).to(DEV)
+    ids = rng.permutation(nb)[:37].astype(np.int32)
+    sink = torch.empty(wgs * bb // 16, dtype=torch.int32, device=DEV)
+    for nt in (False, True):
+        lda.block_read(src, torch.from_numpy(ids).to(DEV), bb, wgs, sink, nontemporal=nt)
+        torch.cuda.synchronize()
+        got = sink.cpu().numpy().view(np.uint32).reshape(wgs, bb // 16)
+        per = (len(ids) + wgs - 1) // wgs
+        fold = np.bitwise_xor.reduce(words, axis=2)  # [nb, words]
+        for w in range(wgs):
+            sel = ids[w * per:(w + 1) * per]
+            want = np.bitwise_xor.reduce(fold[sel], axis=0) if len(sel) else np.zeros(bb // 16, np.uint32)
+            assert np.array_equal(got[w], want), (nt, w)
