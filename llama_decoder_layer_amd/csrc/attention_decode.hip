@@ -167,6 +167,19 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
       const int h = e / D, c = e - h * D;
       return h < G ? (g * G + h) * D + c : (h == G ? (nq + g) * D + c : (nq + nkv + g) * D + c);
     };
+    // the new key's cache block and this thread's cos/sin pairs do not
+    // depend on the sums: their loads are issued first, so their latency
+    // overlaps the partials' instead of following it
+    // (G + 1) * D / 2 pairs, G <= 16, over the workgroup's threads
+    constexpr int kRopeItems = (17 * (D / 2) + kWaves * kWave - 1) / (kWaves * kWave);
+    const int blk = block_table[(size_t)b * max_blocks + p / kKvBlock];
+    const float2* cs = fz.table + (size_t)p * half;
+    float2 cpre[kRopeItems];
+#pragma unroll
+    for (int k = 0; k < kRopeItems; ++k) {
+      const int idx = threadIdx.x + k * kWaves * kWave;
+      cpre[k] = idx < (G + 1) * half ? cs[idx % half] : float2{0.f, 0.f};
+    }
     // two 4-element items per thread in flight at once (G + 2 heads of D
     // make at most 2.25 passes of the workgroup for G <= 16)
     constexpr int kStride = kWaves * kWave * 4;
@@ -203,10 +216,11 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
     __syncthreads();
     // ---- ... the q/k norm, RoPE of the G q heads and the k head, and the
     // new token's k_rot and v into its cache slot
-    const int blk = block_table[(size_t)b * max_blocks + p / kKvBlock];
     const int slot = p % kKvBlock;
-    const float2* cs = fz.table + (size_t)p * half;
-    for (int idx = threadIdx.x; idx < (G + 1) * half; idx += kWaves * kWave) {
+#pragma unroll
+    for (int k = 0; k < kRopeItems; ++k) {
+      const int idx = threadIdx.x + k * kWaves * kWave;
+      if (idx >= (G + 1) * half) break;
       const int h = idx / half, i = idx - h * half;  // h == G: the k head
       float x0 = sx[h * D + i], x1 = sx[h * D + i + half];
       if (fz.qn) {
@@ -219,7 +233,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_attention_mfma(
         x0 = to_f32(static_cast<bf16>(x0 * inv * to_f32(wn[i])));
         x1 = to_f32(static_cast<bf16>(x1 * inv * to_f32(wn[i + half])));
       }
-      const float2 c = cs[i];
+      const float2 c = cpre[k];
       const bf16 y0 = static_cast<bf16>(fmaf(x0, c.x, -(x1 * c.y)));
       const bf16 y1 = static_cast<bf16>(fmaf(x1, c.x, x0 * c.y));
       if (h < G) {
