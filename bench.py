@@ -56,37 +56,41 @@ PLAN_SOURCES = ("llama_decoder_layer_amd/csrc/common.h", "llama_decoder_layer_am
                 "llama_decoder_layer_amd/csrc/api.cpp")
 COUNTER_TRAFFIC = {
     ('llama70b_decode_b32_ctx2048', 'gate_up_silu'): {
-        "bytes": 945640864, "sha1": 'a57a58c8a8f4d30035e7348471378ed326fb5f8e',
+        "bytes": 945640960, "sha1": '5814c607f1d0d8e4bd64c6eea2d037d684026e67',
         "sources": ('llama_decoder_layer_amd/csrc/gemm_skinny.hip',),
         "summary": 'profiles/gate_up_silu_decode_b32_ctx2048_counters.md'},
     ('llama70b_prefill_4x2048', 'gate_up_silu'): {
-        "bytes": 11792284760, "sha1": 'ee05b63e72916ec8eb3cbcbe2a240db4d4af03cb',
+        "bytes": 11769860136, "sha1": '761668c6a6cbb34b90824e7589581648a2128150',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_prefill_4x2048_counters.md'},
     ('llama70b_prefill_1x32768', 'gate_up_silu'): {
-        "bytes": 47927832040, "sha1": 'ee05b63e72916ec8eb3cbcbe2a240db4d4af03cb',
+        "bytes": 47224896288, "sha1": '761668c6a6cbb34b90824e7589581648a2128150',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_prefill_1x32768_counters.md'},
     ('llama70b_ragged_decode_b64_4layer', 'attention'): {
-        "bytes": 4469737146, "sha1": '9cbbed96b6f5520980782437f62a75b1b2ccc523',
+        "bytes": 4469649868, "sha1": '109f265b3f84eb2649e8821cc6d09cc372539ff2',
         "sources": ('llama_decoder_layer_amd/csrc/attention_decode.hip', 'llama_decoder_layer_amd/csrc/attention.hip'),
         "summary": 'profiles/attention_ragged_decode_b64_4layer_counters.md'},
     ('qwen3moe_decode_b32_ctx2048', 'moe_gate_up_silu'): {
-        "bytes": 699528384, "sha1": '4bce3983ddba46e4cf5f436cd2b3ea60d90a2315',
+        "bytes": 699528320, "sha1": '46bffcf1bfb71ecde513a05ac004f02c7c5c9f01',
         "sources": ('llama_decoder_layer_amd/csrc/moe.hip',),
         "summary": 'profiles/moe_gate_up_silu_qwen3moe_decode_b32_ctx2048_counters.md'},
     ('qwen3moe_prefill_4x2048', 'moe_gate_up_silu'): {
-        "bytes": 1890359200, "sha1": '4bce3983ddba46e4cf5f436cd2b3ea60d90a2315',
+        "bytes": 1889146576, "sha1": '46bffcf1bfb71ecde513a05ac004f02c7c5c9f01',
         "sources": ('llama_decoder_layer_amd/csrc/moe.hip',),
         "summary": 'profiles/moe_gate_up_silu_qwen3moe_prefill_4x2048_counters.md'},
     ('llama70b_tp8shard_decode_b32_ctx2048', 'gate_up'): {
-        "bytes": 129028624, "sha1": 'a57a58c8a8f4d30035e7348471378ed326fb5f8e',
+        "bytes": 129028592, "sha1": '5814c607f1d0d8e4bd64c6eea2d037d684026e67',
         "sources": ('llama_decoder_layer_amd/csrc/gemm_skinny.hip',),
         "summary": 'profiles/gate_up_tp8shard_decode_b32_ctx2048_counters.md'},
     ('llama70b_tp8shard_prefill_4x2048', 'gate_up_silu'): {
-        "bytes": 1535366544, "sha1": 'ee05b63e72916ec8eb3cbcbe2a240db4d4af03cb',
+        "bytes": 1535366256, "sha1": '761668c6a6cbb34b90824e7589581648a2128150',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_tp8shard_prefill_4x2048_counters.md'},
+    ('llama70b_mixed_chunk512_decode32', 'gate_up_silu'): {
+        "bytes": 1251943808, "sha1": '761668c6a6cbb34b90824e7589581648a2128150',
+        "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
+        "summary": 'profiles/gate_up_silu_mixed_chunk512_decode32_counters.md'},
 }
 
 
