@@ -259,6 +259,8 @@ def measure(wl, steps, warmup, flushed_calls, flush_buf):
                 "avg_launch_us": dur * 1e6, "share_of_step": kernel_step_ms[dom] / ms}
         if roof["traffic"] is not None and kernel_bytes(model, dom, T, kv_tokens) is not None:
             roof["algorithmic_bytes_per_launch"] = kernel_bytes(model, dom, T, kv_tokens)
+        if dom == "gate_up_silu":  # a dense bf16 product the vendor GEMM can be timed on
+            roof["product_mnk"] = [T, 2 * model.intermediate_size, model.hidden_size]
     wbytes = sum(v.numel() * v.element_size() for k, v in per_layer[0]["weights"].items()
                  if not k.startswith("experts_"))
     if model.num_experts:  # only the routed-to experts' weights are read
@@ -588,6 +590,80 @@ def run_workload(name, steps, warmup, flushed_calls, flush_buf, cpu_seconds):
     return res
 
 
+def vendor_gemm_tflops(M, N, K, reps=5):
+    """hipBLASLt (torch.matmul) on one bf16 product out[M, N] = x[M, K] w[N, K]^T:
+    TFLOP/s over `reps` event-timed calls after 2 untimed ones."""
+    import torch
+
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = (torch.randn(M, K, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    for _ in range(2):
+        torch.matmul(x, w.t())
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        torch.matmul(x, w.t())
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    del x, w
+    return 2.0 * M * N * K / us / 1e6
+
+
+def device_record():
+    """What the box reports: name, architecture and CU count from the device
+    properties, the maximum shader clock from rocminfo (null if unavailable)."""
+    import subprocess
+
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    rec = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+           "memory_bytes": p.total_memory, "max_clock_mhz": None}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        gpu = False
+        for line in out.splitlines():
+            t = line.strip()
+            if t.startswith("Name:"):
+                gpu = t.split(":", 1)[1].strip().startswith("gfx")
+            elif gpu and t.startswith("Max Clock Freq. (MHz):"):
+                rec["max_clock_mhz"] = int(t.split(":", 1)[1].strip())
+                break
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    return rec
+
+
+def attach_measured_ceilings(lines, ceiling):
+    """Each line's dominant kernel against a ceiling measured on the same box
+    and in the same process, beside the datasheet fraction: HBM-bound lines
+    against the nontemporal read-only kernel (streaming in the decode gate_up
+    launch shape; gathering 4 KiB blocks in random order where attention
+    dominates), GEMM-bound lines against the vendor GEMM (hipBLASLt) on the
+    same bf16 product.  Lines whose dominant kernel has no such counterpart
+    (the grouped expert GEMMs) get none."""
+    vendor = {}
+    for r in lines:
+        rf = r["roofline"]
+        if rf.get("bound") == "hbm":
+            key = "4GiB_4KiB_blocks_random_nontemporal" if rf.get("kernel") == "attention" else \
+                "gate_up_shape_nontemporal"
+            c = ceiling[key]["GB_per_s"]
+            rf["measured_ceiling"] = {"source": "read-only kernel: " + key, "value": c, "unit": "GB/s",
+                                      "frac": rf["achieved"] / c}
+        elif rf.get("bound") == "mfma" and rf.get("product_mnk"):
+            mnk = tuple(rf["product_mnk"])
+            if mnk not in vendor:
+                vendor[mnk] = vendor_gemm_tflops(*mnk)
+            c = vendor[mnk]
+            rf["measured_ceiling"] = {"source": "hipBLASLt on the same product (M, N, K) = %d, %d, %d" % mnk,
+                                      "value": round(c, 1), "unit": "TFLOP/s", "frac": rf["achieved"] / c}
+
+
 def library_gemm_reference(reps=5):
     """The vendor GEMM (hipBLASLt, through torch.matmul) beside this
     library's tiled kernel (llama_op_linear, plain store) on the 70B prefill
@@ -687,6 +763,7 @@ def main():
                                       cpu_s / 2))
     ceiling = hbm_read_ceiling()
     cold = cold_read_by_size()
+    attach_measured_ceilings([main_res] + extra, ceiling)
     wl = synth.WORKLOADS[args.workload]
     out = {
         "metric": METRIC,
@@ -712,6 +789,7 @@ def main():
         "wall_s_timed_region": main_res["wall_s_timed_region"],
         "hbm_read_ceiling": ceiling,
         "cold_read_by_size": cold,
+        "device": device_record(),
         "extra": extra,
     }
     print(json.dumps(out))
