@@ -262,6 +262,25 @@ def test_mid16_mixed_and_prefill_key_partitions():
     _run(synth.Workload(44, "mid16_prefill_1x48_ctx1500", MID16, 1, 48, 1500))
 
 
+# the two remaining (head_dim, heads per KV head) forms of the prefill kernel:
+# 128 x 16 (two heads per wave, 16-query tiles) and 64 x 8 (one head per wave)
+MID128G16 = synth.ModelShape(2048, 16, 1, 128, 2816, 1e-5, 500000.0, synth.LLAMA3_SCALING, 131072, "bf16")
+MID64G8 = synth.ModelShape(512, 8, 1, 64, 1408, 1e-5, 10000.0, None, 8192, "bf16")
+
+
+@pytest.mark.parametrize("model, tag, base", [(MID128G16, "mid128g16", 214), (MID64G8, "mid64g8", 218)])
+def test_remaining_prefill_forms_and_their_decode(model, tag, base):
+    # prefill chunks on cached contexts, a ragged last query tile
+    _run(synth.Workload(base, tag + "_prefill_3x37_ctx", model, 3, 37, 0), ctx_lens=[5, 300, 64])
+    # a uniform chunk on a long context: key partitions and the combine
+    _run(synth.Workload(base + 1, tag + "_prefill_1x64_ctx2000", model, 1, 64, 2000))
+    # a mixed batch: decode rows beside prefill chunks, with key partitions
+    mix = ((1, 700), (40, 1100), (3, 50), (1, 1))
+    _run(synth.Workload(base + 2, tag + "_mixed", model, len(mix), 0, mix=mix))
+    # uniform decode: the attention kernel sums the qkv partials itself
+    _run(synth.Workload(base + 3, tag + "_decode_b7", model, 7, 1, (1, 1800)))
+
+
 def test_mid8_uniform_prefill_split_keys():
     # a uniform (no query_start_loc) chunk on a long context splits too
     _run(synth.Workload(45, "mid8_prefill_1x64_ctx2000", MID8, 1, 64, 2000), repeat=True)
