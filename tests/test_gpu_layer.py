@@ -281,6 +281,22 @@ def test_remaining_prefill_forms_and_their_decode(model, tag, base):
     _run(synth.Workload(base + 3, tag + "_decode_b7", model, 7, 1, (1, 1800)))
 
 
+# hidden sizes that give the decode qkv projection 2 and 4 split-K planes (the
+# 70B-like shapes above all give 8), which the decode attention kernel sums
+# in its prologue; the query width (8 x 64) differs from the hidden size
+SPLIT2 = synth.ModelShape(640, 8, 2, 64, 1536, 1e-5, 10000.0, None, 8192, "bf16")
+SPLIT4 = synth.ModelShape(768, 8, 2, 64, 1536, 1e-5, 10000.0, None, 8192, "bf16")
+
+
+@pytest.mark.parametrize("model, tag, base", [(SPLIT2, "h640", 222), (SPLIT4, "h768", 226)])
+def test_decode_qkv_partial_plane_counts(model, tag, base):
+    _run(synth.Workload(base, tag + "_decode_b7", model, 7, 1, (1, 1800)))
+    _run(synth.Workload(base + 1, tag + "_decode_b24", model, 24, 1, (100, 900)))
+    _run(synth.Workload(base + 2, tag + "_prefill_2x70_ctx", model, 2, 70, 0), ctx_lens=[0, 333])
+    mix = ((1, 500), (30, 200), (1, 17))
+    _run(synth.Workload(base + 3, tag + "_mixed", model, len(mix), 0, mix=mix))
+
+
 def test_mid8_uniform_prefill_split_keys():
     # a uniform (no query_start_loc) chunk on a long context splits too
     _run(synth.Workload(45, "mid8_prefill_1x64_ctx2000", MID8, 1, 64, 2000), repeat=True)
