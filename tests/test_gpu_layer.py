@@ -134,8 +134,21 @@ def _check_placement(model, batch, kp0, vp0, kp, vp):
     mask = _new_slot_mask(batch).to(kp.device)
     mk = mask[:, None, :, None].expand_as(kp)
     mv = mask[:, None, None, :].expand_as(vp)
-    assert torch.equal(kp.view(ibits)[~mk], kp0.view(ibits)[~mk])
-    assert torch.equal(vp.view(ibits)[~mv], vp0.view(ibits)[~mv])
+    for name, new, old, m in (("K", kp, kp0, mk), ("V", vp, vp0, mv)):
+        bad = (new.view(ibits) != old.view(ibits)) & ~m
+        if bad.any():
+            idx = bad.nonzero()[:8].tolist()  # (block, kv head, slot or component, component or slot)
+            blk, hd = idx[0][0], idx[0][1]
+            slot = idx[0][2] if name == "K" else idx[0][3]
+            owner = (batch.block_table == blk).nonzero().tolist()  # (sequence, block index in its table)
+            where = [(s, j * 16 + slot, batch.ctx_lens[s]) for s, j in owner]  # (sequence, position, context)
+            row_old = old[blk, hd, slot, :4] if name == "K" else old[blk, hd, :4, slot]
+            row_new = new[blk, hd, slot, :4] if name == "K" else new[blk, hd, :4, slot]
+            raise AssertionError(
+                "%s plane changed outside the new slots at %d entries, first %s; that block belongs to "
+                "(sequence, position, context) %s; old %s new %s; changed (block, head) pairs %s" % (
+                    name, int(bad.sum()), idx, where, row_old.tolist(), row_new.tolist(),
+                    sorted(set((b, h) for b, h, _, _ in bad.nonzero().tolist()))[:12]))
     # and every new slot was written (no sentinel left)
     assert not torch.isnan(kp[mk].float()).any() and not torch.isnan(vp[mv].float()).any()
 
@@ -295,6 +308,20 @@ def test_decode_qkv_partial_plane_counts(model, tag, base):
     _run(synth.Workload(base + 2, tag + "_prefill_2x70_ctx", model, 2, 70, 0), ctx_lens=[0, 333])
     mix = ((1, 500), (30, 200), (1, 17))
     _run(synth.Workload(base + 3, tag + "_mixed", model, len(mix), 0, mix=mix))
+
+
+# the weight-streaming kernel's tall-weight forms (gate_up of at least 49152
+# rows, K % 256 == 0): 7 waves of 32 rows when the rows tile exactly onto 256
+# CUs (57344 rows, the 70B gate_up's count), else 4 waves (49152 rows); each
+# at 1, 2, 4 and 8 token tiles (12, 32, 64, 100 rows)
+TALL7 = synth.ModelShape(512, 8, 2, 64, 28672, 1e-5, 10000.0, None, 8192, "bf16")
+TALL4 = synth.ModelShape(512, 8, 2, 64, 24576, 1e-5, 10000.0, None, 8192, "bf16")
+
+
+@pytest.mark.parametrize("model, tag, base", [(TALL7, "tall7", 230), (TALL4, "tall4", 234)])
+def test_tall_gate_up_forms(model, tag, base):
+    for i, rows in enumerate((12, 32, 64, 100)):
+        _run(synth.Workload(base + i, "%s_decode_b%d" % (tag, rows), model, rows, 1, (1, 600)))
 
 
 def test_mid8_uniform_prefill_split_keys():
@@ -525,3 +552,10 @@ def test_mid_positions_at_the_configured_maximum():
     # tiles split their keys into 8 partitions
     _run(synth.Workload(66, "mid_decode_maxpos", MID, 2, 1, 0), ctx_lens=[131071, 70000])
     _run(synth.Workload(67, "mid_chunk_maxpos", MID, 1, 64, 0), ctx_lens=[131008])
+
+
+def test_decode_new_token_opens_a_block_head_dim_64():
+    # every new token at slot 0 of a fresh block (contexts multiples of 16)
+    _run(synth.Workload(238, "mid64_decode_b6_block_starts", MID64, 6, 1, 0), ctx_lens=[16, 32, 416, 64, 0, 160])
+    _run(synth.Workload(239, "h640_decode_b12_block_starts", SPLIT2, 12, 1, 0),
+         ctx_lens=[92, 493, 425, 25, 546, 529, 141, 232, 145, 367, 504, 416])
