@@ -324,6 +324,18 @@ def test_tall_gate_up_forms(model, tag, base):
         _run(synth.Workload(base + i, "%s_decode_b%d" % (tag, rows), model, rows, 1, (1, 600)))
 
 
+# a 5120-row qkv (32 query heads, 4 KV heads of 128, as the Qwen3-MoE layer's
+# attention) is the weight the 5-wave single-tile forms of the weight-streaming
+# kernel suit: 4 split-K planes at 33..128 rows, which the decode attention then
+# sums in its prologue at head_dim 128
+QDENSE = synth.ModelShape(2048, 32, 4, 128, 2816, 1e-6, 1e7, None, 32768, "bf16")
+
+
+def test_five_wave_qkv_forms():
+    _run(synth.Workload(240, "qdense_decode_b48", QDENSE, 48, 1, (1, 900)))
+    _run(synth.Workload(241, "qdense_decode_b100", QDENSE, 100, 1, (1, 400)))
+
+
 def test_mid8_uniform_prefill_split_keys():
     # a uniform (no query_start_loc) chunk on a long context splits too
     _run(synth.Workload(45, "mid8_prefill_1x64_ctx2000", MID8, 1, 64, 2000), repeat=True)
