@@ -258,7 +258,7 @@ struct Marker {
 // a different region of it at once.  A physically contiguous allocation is
 // mapped with the largest page fragments, so those concurrent streams need
 // few address translations; measured on the 939 MB gate_up weight, scattered
-// placements streamed up to 9% slower.  The driver may refuse the request on
+// placements streamed up to 9% slower.  The runtime may refuse the request on
 // fragmented memory: plain hipMalloc then.
 hipError_t alloc_weight(void** p, size_t bytes) {
   if (hipExtMallocWithFlags(p, bytes, hipDeviceMallocContiguous) == hipSuccess) return hipSuccess;

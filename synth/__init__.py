@@ -16,9 +16,8 @@ Value distributions: linear weights N(0, 0.02^2) (``initializer_range``),
 RMSNorm weights 1 + N(0, 0.02^2), hidden states, residual stream and cached
 K/V contexts N(0, 1).  Seeds follow ``1000*(workload_index+1) + 97*layer +
 tensor_id`` with one generator per tensor.  Float draws happen on the device
-the tensor will live on (a GPU machine and this CPU therefore see different
-values, which never matters: every comparison runs both sides on the same
-tensors); integer draws (context lengths, block permutations) always happen
+the tensor will live on (a GPU and a CPU therefore see different values,
+which never matters: every comparison runs both sides on the same tensors); integer draws (context lengths, block permutations) always happen
 on the CPU so they are the same everywhere.
 """
 from __future__ import annotations
