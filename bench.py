@@ -56,39 +56,39 @@ PLAN_SOURCES = ("llama_decoder_layer_amd/csrc/common.h", "llama_decoder_layer_am
                 "llama_decoder_layer_amd/csrc/api.cpp")
 COUNTER_TRAFFIC = {
     ('llama70b_decode_b32_ctx2048', 'gate_up_silu'): {
-        "bytes": 945640960, "sha1": '5814c607f1d0d8e4bd64c6eea2d037d684026e67',
+        "bytes": 945640960, "sha1": 'cb80f7e7d58f8324e231e15be63b6e7fc1a2e247',
         "sources": ('llama_decoder_layer_amd/csrc/gemm_skinny.hip',),
         "summary": 'profiles/gate_up_silu_decode_b32_ctx2048_counters.md'},
     ('llama70b_prefill_4x2048', 'gate_up_silu'): {
-        "bytes": 11769860136, "sha1": '761668c6a6cbb34b90824e7589581648a2128150',
+        "bytes": 11769860136, "sha1": '18d4c16099ea8a4dfe1a3dd026d7dcc9eb895271',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_prefill_4x2048_counters.md'},
     ('llama70b_prefill_1x32768', 'gate_up_silu'): {
-        "bytes": 47224896288, "sha1": '761668c6a6cbb34b90824e7589581648a2128150',
+        "bytes": 47224896288, "sha1": '18d4c16099ea8a4dfe1a3dd026d7dcc9eb895271',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_prefill_1x32768_counters.md'},
     ('llama70b_ragged_decode_b64_4layer', 'attention'): {
-        "bytes": 4469649868, "sha1": '109f265b3f84eb2649e8821cc6d09cc372539ff2',
+        "bytes": 4469649868, "sha1": '9a5eb220a8bdd6807ae69859328fb0f75ae3ff8a',
         "sources": ('llama_decoder_layer_amd/csrc/attention_decode.hip', 'llama_decoder_layer_amd/csrc/attention.hip'),
         "summary": 'profiles/attention_ragged_decode_b64_4layer_counters.md'},
     ('qwen3moe_decode_b32_ctx2048', 'moe_gate_up_silu'): {
-        "bytes": 699528320, "sha1": '46bffcf1bfb71ecde513a05ac004f02c7c5c9f01',
+        "bytes": 699528320, "sha1": '1952190a6e5aa9cd4bde4c91f4976f45cea67fcd',
         "sources": ('llama_decoder_layer_amd/csrc/moe.hip',),
         "summary": 'profiles/moe_gate_up_silu_qwen3moe_decode_b32_ctx2048_counters.md'},
     ('qwen3moe_prefill_4x2048', 'moe_gate_up_silu'): {
-        "bytes": 1889146576, "sha1": '46bffcf1bfb71ecde513a05ac004f02c7c5c9f01',
+        "bytes": 1889146576, "sha1": '1952190a6e5aa9cd4bde4c91f4976f45cea67fcd',
         "sources": ('llama_decoder_layer_amd/csrc/moe.hip',),
         "summary": 'profiles/moe_gate_up_silu_qwen3moe_prefill_4x2048_counters.md'},
     ('llama70b_tp8shard_decode_b32_ctx2048', 'gate_up'): {
-        "bytes": 129028592, "sha1": '5814c607f1d0d8e4bd64c6eea2d037d684026e67',
+        "bytes": 129028592, "sha1": 'cb80f7e7d58f8324e231e15be63b6e7fc1a2e247',
         "sources": ('llama_decoder_layer_amd/csrc/gemm_skinny.hip',),
         "summary": 'profiles/gate_up_tp8shard_decode_b32_ctx2048_counters.md'},
     ('llama70b_tp8shard_prefill_4x2048', 'gate_up_silu'): {
-        "bytes": 1535366256, "sha1": '761668c6a6cbb34b90824e7589581648a2128150',
+        "bytes": 1535366256, "sha1": '18d4c16099ea8a4dfe1a3dd026d7dcc9eb895271',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_tp8shard_prefill_4x2048_counters.md'},
     ('llama70b_mixed_chunk512_decode32', 'gate_up_silu'): {
-        "bytes": 1251943808, "sha1": '761668c6a6cbb34b90824e7589581648a2128150',
+        "bytes": 1251943808, "sha1": '18d4c16099ea8a4dfe1a3dd026d7dcc9eb895271',
         "sources": ('llama_decoder_layer_amd/csrc/gemm.hip',),
         "summary": 'profiles/gate_up_silu_mixed_chunk512_decode32_counters.md'},
 }
