@@ -624,18 +624,27 @@ def device_record():
     rec = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
            "memory_bytes": p.total_memory, "max_clock_mhz": None}
     try:
-        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
-        gpu = False
-        for line in out.splitlines():
-            t = line.strip()
-            if t.startswith("Name:"):
-                gpu = t.split(":", 1)[1].strip().startswith("gfx")
-            elif gpu and t.startswith("Max Clock Freq. (MHz):"):
-                rec["max_clock_mhz"] = int(t.split(":", 1)[1].strip())
-                break
-    except (OSError, subprocess.SubprocessError, ValueError):
+        rec["max_clock_mhz"] = gpu_max_clock_mhz(
+            subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout)
+    except (OSError, subprocess.SubprocessError):
         pass
     return rec
+
+
+def gpu_max_clock_mhz(rocminfo_text):
+    """The first GPU agent's "Max Clock Freq. (MHz)" in rocminfo's output
+    (agents whose Name is a gfx target), or None."""
+    gpu = False
+    for line in rocminfo_text.splitlines():
+        t = line.strip()
+        if t.startswith("Name:"):
+            gpu = t.split(":", 1)[1].strip().startswith("gfx")
+        elif gpu and t.startswith("Max Clock Freq. (MHz):"):
+            try:
+                return int(t.split(":", 1)[1].strip())
+            except ValueError:
+                return None
+    return None
 
 
 def attach_measured_ceilings(lines, ceiling):
