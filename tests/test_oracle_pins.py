@@ -321,9 +321,10 @@ def _layer_unfused_torch(cfg, w, stream, positions, k_ctx, v_ctx, freqs):
     return hidden.numpy()
 
 
-@pytest.mark.parametrize("scaling,ctx", [(None, 0), (None, 5), (synth.LLAMA3_SCALING, 9)])
-def test_layer_matches_unfused_library_formulation(scaling, ctx):
-    cfg = _cfg(theta=5e5 if scaling else 1e4, scaling=scaling)
+# the last case: a query width (4 x 16) other than the hidden size (80)
+@pytest.mark.parametrize("scaling,ctx,H", [(None, 0, 64), (None, 5, 64), (synth.LLAMA3_SCALING, 9, 64), (None, 7, 80)])
+def test_layer_matches_unfused_library_formulation(scaling, ctx, H):
+    cfg = _cfg(H=H, theta=5e5 if scaling else 1e4, scaling=scaling)
     rng = np.random.default_rng(7)
     w = _weights(cfg, rng)
     T = 11
